@@ -1,0 +1,236 @@
+"""Decode-step benchmark (one JSON line on stdout).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode-7b-p4000] [--seed 0]
+
+One step = one vv_decode_step (28 layers: fused QKV GEMV, attention with KV append, o GEMV,
+gate/up GEMV + SiLU, down GEMV, then lm_head + argmax) replayed from a hipGraph on seeded
+synthetic weights, KV cache and input already resident in HBM.  The timed region is K
+back-to-back replays bracketed by torch.cuda.synchronize().
+
+Also reported:
+  roofline     achieved HBM GB/s of the dominant kernel (the gate/up GEMV: most time per step),
+               = its algorithmic bytes per launch / its mean duration measured with HIP events
+               on the launch stream during an instrumented eager pass right after the timed
+               region; traffic from committed rocprofv3 counters when they match the kernel source.
+  cpu_baseline the fp64 oracle's decode step timed on a bounded sample of the same workload
+               (one layer + a vocabulary slice, scaled to a full step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def algorithmic_bytes(shape, batch, lens):
+    """Bytes one step must read: packed nibbles + fp16 scales + fp16 lm_head + fp16 K/V over P+1."""
+    per_layer_w = sum(n * k // 2 + n * (k // 32) * 2 for _, n, k in shape.proj_shapes())
+    w = per_layer_w * shape.layers
+    kv = sum(int(L) + 1 for L in lens) * shape.n_kv * shape.head_dim * 2 * 2 * shape.layers
+    lm = shape.vocab * shape.hidden * 2
+    return w, kv, lm
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "vv_internal.h"):
+        with open(os.path.join(ROOT, "int4_blockwise_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from profiles/traffic_<tag>.txt if it was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_inputs(wl, seed):
+    import torch
+    from int4_blockwise_gemv_amd import synth
+    from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
+    s = wl.shape
+    lens = synth.past_lengths(wl, seed)
+    t0 = time.time()
+    dm = DeviceModel(s, seed, max_batch=wl.batch, progress=lambda m: None)
+    log(f"packed {s.layers} layers + lm_head on the GPU in {time.time() - t0:.1f}s")
+    ds = DeviceState(dm, wl.batch, wl.cap)
+    for li in range(s.layers):
+        K, V = synth.layer_cache(wl, seed, li, lens)
+        ds.load_cache_layer(li, K, V)
+    g = synth.model_globals(s, seed, wl.batch, with_lm=False)
+    ds.emb.copy_(torch.from_numpy(g["emb"].view(np.int16)).view(torch.float16).cuda())
+    ds.pos.copy_(torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    log(f"inputs resident ({time.time() - t0:.1f}s total)")
+    return dm, ds, lens
+
+
+def kernel_breakdown(ds, n_layers, reps=3):
+    """Mean duration (ms) per kernel kind from HIP events recorded between the kernels of eager steps."""
+    import ctypes as C
+    import torch
+    n_kern = 5 * n_layers + 2
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_kern + 1)]
+    arr = (C.c_void_p * (n_kern + 1))(*[C.c_void_p(e.cuda_event) for e in evs])
+    ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
+    ds.struct.n_events = n_kern + 1
+    kinds = ["qkv", "attn", "o", "gateup", "down"]
+    acc = {k: [] for k in kinds + ["prep", "lm_head"]}
+    try:
+        for _ in range(reps):
+            ds.step()
+            torch.cuda.synchronize()
+            t = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_kern)]
+            acc["prep"].append(t[0])
+            for l in range(n_layers):
+                for j, k in enumerate(kinds):
+                    acc[k].append(t[1 + 5 * l + j])
+            acc["lm_head"].append(t[-1])
+    finally:
+        ds.struct.events = None
+        ds.struct.n_events = 0
+    return {k: float(np.mean(v)) for k, v in acc.items() if v}
+
+
+def cpu_baseline(wl, seed, budget_s=25.0):
+    """The oracle's decode step on a bounded sample: one layer and a slice of the vocabulary."""
+    from threadpoolctl import threadpool_info
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import vv_oracle as O
+    from int4_blockwise_gemv_amd import synth
+    from helpers import oracle_model
+    s = wl.shape
+    lens = synth.past_lengths(wl, seed)
+    li = 0
+    m = oracle_model(s, seed, [li], with_lm=False, batch=wl.batch)
+    K, V = synth.layer_cache(wl, seed, li, lens)
+    h = synth.model_globals(s, seed, wl.batch, with_lm=False)["emb"].astype(np.float64)
+    t0 = time.perf_counter()
+    O.layer_step(m.layers[0], m, h, lens, K, V)
+    t_layer = time.perf_counter() - t0
+    frac_rows = 16384
+    lm = synth.fp16_normal(seed, synth.GLOBAL_LAYER, synth.T_LM, (frac_rows, s.hidden), std=0.02)
+    f = O.rmsnorm(h, m.gf, m.eps)
+    t0 = time.perf_counter()
+    O.lm_head_argmax(lm, f)
+    t_lm = (time.perf_counter() - t0) * s.vocab / frac_rows
+    t_step = t_layer * s.layers + t_lm
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": 1.0 / t_step, "unit": "decode steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {s.layers} layers (layer {li}) + {frac_rows} of {s.vocab} lm_head rows of "
+                      f"{wl.name}, seed {seed}, fp64 numpy; scaled to one full step "
+                      f"({t_layer:.2f} s/layer, {t_lm:.2f} s lm_head)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode-7b-p4000")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this decode step is not sharded across GPUs "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_blockwise_gemv_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    dm, ds, lens = build_inputs(wl, args.seed)
+    s = wl.shape
+
+    g = ds.graph()
+    for _ in range(args.warmup):
+        g.launch()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} graph replays")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.launch()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    g.close()
+    tok = int(ds.token.cpu()[0])
+
+    wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
+    total = wb + kvb + lmb
+    kb = kernel_breakdown(ds, s.layers)
+    log("kernel means (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
+    gu_bytes = 2 * s.inter * s.hidden // 2 + 2 * s.inter * (s.hidden // 32) * 2
+    gu_ms = kb["gateup"]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    traffic = read_traffic("gateup_" + ("7b" if s.hidden == 3584 else "1p5b"))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        cpu = cpu_baseline(wl, args.seed)
+
+    sum_kern = sum(kb[k] for k in ("qkv", "attn", "o", "gateup", "down")) * s.layers + kb["prep"] + kb["lm_head"]
+    out = {
+        "metric": "decode steps/s (HBM GB/s, % of 8 TB/s roofline)",
+        "value": 1e3 / ms,
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) fp32 masters ternarised on the GPU, fp16 N(0,1) KV/inputs)",
+        "config": {"workload": wl.name, "layers": s.layers, "hidden": s.hidden, "inter": s.inter,
+                   "n_q": s.n_q, "n_kv": s.n_kv, "head_dim": s.head_dim, "vocab": s.vocab, "batch": wl.batch,
+                   "past": int(lens.max()), "quant": s.mode, "seed": args.seed},
+        "hbm": {"algorithmic_bytes_per_step": total, "weights": wb, "kv": kvb, "lm_head": lmb,
+                "GB_per_s": total / (ms * 1e-3) / 1e9,
+                "frac_of_8TBps": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "roofline": {"bound": "hbm", "kernel": "gate/up int4 GEMV (+SiLU*up)", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "bytes_per_launch": gu_bytes, "mean_launch_us": gu_ms * 1e3},
+        "kernels_us": {k: v * 1e3 for k, v in kb.items()},
+        "eager_kernel_sum_us": sum_kern * 1e3,
+        "token": tok,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+/*
+ * vv.h — C ABI of the int4 block-32 decode-step library for MI355X (gfx950).
+ *
+ * The library implements the single-token decode step of the Qwen2 decoder that the
+ * VibeVoice ONNX pages describe:
+ *   - int4 block-32 symmetric projections (com.microsoft::MatMulNBits: block 32, zero point 8,
+ *     q = w/s + 8, one fp16 scale per block), with the ternary export rule
+ *     s = 1/mean(|W|), W' = round(clamp(W*s, -1, 1))/s
+ *     ("vibevoice-asr-bitnet-onnx" model page: ternarisation paragraph and MatMulNBits note);
+ *   - grouped-query attention over a device-resident fp16 KV cache
+ *     (decoder_step graph contract on the same page: past K/V [28,1,kv,P,128] -> present [.., P+1, 128];
+ *     GPU-resident KV: "VibeVoice-ASR — ONNX export for Vernacula", Highlights);
+ *   - the fp16 lm_head GEMV and a greedy argmax (bitnet-onnx page: lm_head/embeddings stay fp16;
+ *     decoding note: greedy decode).
+ *
+ * Conventions for every call:
+ *   - All pointers named "device" are device (HBM) addresses owned by the caller; the library never
+ *     allocates, frees or retains device memory, except that a vv_graph keeps raw pointers until
+ *     vv_decode_graph_destroy.  fp16 tensors are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call is asynchronous on that
+ *     stream; none reads device data on the host or synchronises.
+ *   - Every argument is validated before anything is enqueued: a call that returns an error has
+ *     launched nothing.  Device faults surface at the caller's next synchronisation.
+ *   - Workspaces: calls that take `ws`/`ws_bytes` need a device buffer of at least the size their
+ *     *_workspace() query returns, ZERO-FILLED before its first use (vv_workspace_init does this);
+ *     every completed call leaves its arrival counters at zero again, so a workspace can be reused
+ *     by later calls on the same stream without re-initialisation.  Two calls that run
+ *     concurrently must not share a workspace.
+ *   - Return value: VV_OK or a negative vv_status; vv_last_error() gives a thread-local message.
+ */
+#ifndef VV_H
+#define VV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VV_OK = 0,
+  VV_ERR_NULL = -1,        /* a required pointer is NULL */
+  VV_ERR_SHAPE = -2,       /* a dimension is not supported (e.g. K % 32 != 0, head_dim != 128) */
+  VV_ERR_RANGE = -3,       /* a size or index is out of range (e.g. batch < 1, cap too small) */
+  VV_ERR_DTYPE = -4,       /* unknown dtype / mode / layout code */
+  VV_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace() query */
+  VV_ERR_UNSUPPORTED = -6, /* valid but not implemented combination */
+  VV_ERR_HIP = -7          /* a HIP runtime call failed (message in vv_last_error) */
+} vv_status;
+
+/* quantisation modes of vv_pack_int4* */
+enum { VV_Q_TERNARY = 0, VV_Q_ABSMAX = 1 };
+/* element types */
+enum { VV_F16 = 1, VV_F32 = 2 };
+/* packed weight layouts */
+enum { VV_LAYOUT_ROWMAJOR = 0, VV_LAYOUT_TILED = 1 };
+
+/*
+ * Packed weight layouts (N rows = output features, K columns = input features, K % 32 == 0,
+ * nb = K/32 blocks per row).  The code of element k of row n is q in 0..15; its value is
+ * (q - 8) * scale[n][k/32].
+ *
+ * VV_LAYOUT_ROWMAJOR — the MatMulNBits byte order:
+ *   packed uint8 [N][nb][16]: byte j of block b holds element 32b+2j in the low nibble and
+ *   32b+2j+1 in the high nibble; scales uint16 (fp16 bits) [N][nb].
+ *
+ * VV_LAYOUT_TILED — the device order read by the GEMV kernels.  Rows are grouped in tiles of
+ *   64 (rows beyond N up to the tile boundary are padding: code 8, scale 0).  For tile t,
+ *   block b, lane i (row 64t+i) the 16 bytes of the block sit at byte offset
+ *   ((t*nb + b)*64 + i)*16, as four little-endian dwords; dword w holds elements 8w..8w+7 of
+ *   the block with the even elements 8w, 8w+2, 8w+4, 8w+6 in nibbles 0..3 and the odd elements
+ *   8w+1, 8w+3, 8w+5, 8w+7 in nibbles 4..7.  Scales: ng = ceil(nb/8) groups per row; the 8
+ *   fp16 scales of blocks 8g..8g+7 of row 64t+i sit at uint16 offset ((t*ng + g)*64 + i)*8
+ *   (blocks >= nb hold 0).  Total bytes: vv_packed_bytes / vv_scale_bytes.
+ *   A tiled buffer may hold several matrices as row ranges: the *_tiled packers place source
+ *   row r in destination tile (r/64)*tile_stride + tile_offset (row (r%64) of that tile).
+ */
+size_t vv_packed_bytes(int64_t rows, int64_t K, int layout);
+size_t vv_scale_bytes(int64_t rows, int64_t K, int layout);
+
+/* ---------------------------------------------------------------------------------------------
+ * Packer (bitnet-onnx page, ternarisation paragraph + MatMulNBits note).
+ *
+ *   W: device fp32 [N][K] row-major master weights (finite values).
+ *   mode VV_Q_TERNARY: m = mean(|W|) over the whole tensor, computed as the exact sum of |W|
+ *     correctly rounded to fp64, divided by N*K in fp64; t = sign(W) if |W| > m/2 else 0 (the
+ *     exact value of round(clamp(W/m, -1, 1)) with ties to even); q = t + 8 in {7,8,9}; every
+ *     block scale = fp16(m), one round-to-nearest-even step from fp64.  All-zero W gives q = 8,
+ *     scale 0.
+ *   mode VV_Q_ABSMAX (general int4): per block scale = fp16(absmax/7) (one RNE step from the
+ *     fp64 quotient); q = clamp(rint(w / scale) + 8, 0, 15) with the division in fp64 and ties
+ *     to even; a block whose scale is 0 gets q = 8.
+ *   Output: vv_pack_int4 writes VV_LAYOUT_ROWMAJOR into packed [N*nb*16] / scales [N*nb];
+ *   vv_pack_int4_tiled writes VV_LAYOUT_TILED rows into a destination of dst_tiles tiles
+ *   (see the layout note for tile_offset / tile_stride; every destination tile touched is
+ *   written completely, including its padding rows).
+ *   ws: device workspace of vv_pack_int4_workspace(N, K, mode) bytes (any content; it is
+ *   cleared by the call).  Errors: NULL pointers, K % 32, N < 1, unknown mode, a destination
+ *   tile outside [0, dst_tiles), small workspace.
+ * ------------------------------------------------------------------------------------------- */
+size_t vv_pack_int4_workspace(int64_t N, int64_t K, int mode);
+int vv_pack_int4(const float* W, int64_t N, int64_t K, int mode, uint8_t* packed, uint16_t* scales,
+                 void* ws, size_t ws_bytes, void* stream);
+int vv_pack_int4_tiled(const float* W, int64_t N, int64_t K, int mode, int64_t tile_offset,
+                       int64_t tile_stride, int64_t dst_tiles, uint8_t* packed, uint16_t* scales,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Row-major (MatMulNBits) -> tiled, a pure permutation of nibbles and scales (same destination
+ * placement rules as vv_pack_int4_tiled).  Lets a MatMulNBits blob from elsewhere feed the
+ * GEMV kernels. */
+int vv_repack_int4_tiled(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                         int64_t tile_offset, int64_t tile_stride, int64_t dst_tiles,
+                         uint8_t* tiled, uint16_t* tiled_scales, void* stream);
+
+/* Dequantiser: W[n][k] = (q - 8) * scale as fp32 (exact for both modes: a 4-bit integer times an
+ * fp16 value needs at most 15 significant bits).  `layout` says how packed/scales are stored;
+ * for VV_LAYOUT_TILED, rows 0..N-1 of tiles 0..ceil(N/64)-1 are read. */
+int vv_dequant_int4(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int layout,
+                    float* W, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * int4 GEMV (MatMulNBits with float activations; bitnet-onnx page: activations run in float).
+ *   y[m][n] = sum_k deq(W)[n][k] * x[m][k] + bias[n]
+ *   packed/scales: VV_LAYOUT_TILED with ceil(N/64) tiles; x: device fp16 [M][K]; bias: device
+ *   fp16 [N] or NULL; y: device [M][N] of y_dtype (VV_F32 or VV_F16).  M in 1..16.
+ *   Accumulation is fp32 (products of fp16 x and exact small integers, block sums scaled once).
+ *   ws: vv_gemv_int4_workspace(M, N, K) bytes, zero-filled before first use.
+ * ------------------------------------------------------------------------------------------- */
+size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K);
+int vv_gemv_int4(const uint8_t* packed, const uint16_t* scales, const uint16_t* bias,
+                 const uint16_t* x, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * GQA decode attention (GroupQueryAttention over a GPU-resident KV cache).
+ *   q: device [B][nq][head_dim] of q_dtype (VV_F32 / VV_F16);
+ *   k_cache, v_cache: device fp16 [B][nkv][cap][head_dim];
+ *   lens: device int32 [B]; sequence b attends over positions [0, lens[b]) (1 <= lens[b] <= cap,
+ *     not checked on the host: out-of-range lengths are clamped to [1, cap] on the device);
+ *   query head h reads KV head h / (nq/nkv); softmax scale `softmax_scale` (1/sqrt(head_dim)
+ *   for Qwen2); scores, softmax and the weighted sum are fp32.
+ *   out: device [B][nq][head_dim] of out_dtype.  head_dim must be 128, nq % nkv == 0,
+ *   nq/nkv <= 8.  ws: vv_gqa_decode_workspace(B, nq, nkv, cap) bytes, zero-filled before first use.
+ * ------------------------------------------------------------------------------------------- */
+size_t vv_gqa_decode_workspace(int B, int nq, int nkv, int cap);
+int vv_gqa_decode(const void* q, int q_dtype, const uint16_t* k_cache, const uint16_t* v_cache,
+                  const int32_t* lens, int B, int nq, int nkv, int cap, int head_dim,
+                  float softmax_scale, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * lm_head GEMV + greedy argmax (bitnet-onnx page: lm_head stays fp16; greedy decoding).
+ *   W: device fp16 [V][H] row-major; x: device [B][H] of x_dtype (VV_F32 / VV_F16);
+ *   logits: device fp32 [B][V] or NULL; token: device int32 [B] = index of the largest logit
+ *   (the smallest such index on ties; NaN logits never win).  H % 8 == 0, B in 1..16.
+ *   ws: vv_lm_head_argmax_workspace(B, V, H) bytes, zero-filled before first use.
+ * ------------------------------------------------------------------------------------------- */
+size_t vv_lm_head_argmax_workspace(int B, int V, int H);
+int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H,
+                      float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Decode step (bitnet-onnx page, decoder_step contract:
+ *   input_embeds [B,H], position_ids [B], past K/V [L,B,nkv,P,128]
+ *   -> logits [B,V], present K/V [L,B,nkv,P+1,128]),
+ * on the Qwen2 layer of the 1.5B STATUS page's Architecture section (pre-RMSNorm, q/k/v bias,
+ * GQA, SiLU-gated MLP, residual adds), with rotate-half RoPE (theta = rope_theta, disabled
+ * when <= 0) on q and the new k.
+ *
+ * Per layer l and sequence b at position p = pos[b]:
+ *   a = RMSNorm(h; g1), [q|k|v] = W_qkv a + b_qkv, q,k = RoPE(q,k; p),
+ *   K[l][b][:,p] = fp16(k), V[l][b][:,p] = fp16(v), o = GQA(q, K[..,0..p], V[..,0..p]),
+ *   h += W_o o, m = RMSNorm(h; g2), h += W_down (silu(W_gate m) * (W_up m));
+ * then logits = lm_head RMSNorm(h; gf), token = argmax.
+ *
+ * Weights use VV_LAYOUT_TILED:
+ *   qkv: one tiled matrix of nq*d + 2*nkv*d rows (q rows, then k rows, then v rows), K = H;
+ *   o:   H rows, K = nq*d;
+ *   gu:  gate and up interleaved by tile (tile 2j = gate rows 64j..64j+63, tile 2j+1 = the same
+ *        up rows; pack gate with tile_offset 0 and up with tile_offset 1, tile_stride 2),
+ *        2*ceil(I/64) tiles, K = H;
+ *   down: H rows, K = I.
+ * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct vv_layer {
+  const uint8_t* qkv_q;   const uint16_t* qkv_s;    /* device, tiled */
+  const uint8_t* o_q;     const uint16_t* o_s;
+  const uint8_t* gu_q;    const uint16_t* gu_s;
+  const uint8_t* down_q;  const uint16_t* down_s;
+  const uint16_t* qkv_bias;                         /* device fp16 [nq*d + 2*nkv*d] or NULL */
+  const uint16_t* g1;     const uint16_t* g2;       /* device fp16 [H] RMSNorm weights */
+} vv_layer;
+
+typedef struct vv_model {
+  int n_layers, hidden, inter, n_q, n_kv, head_dim, vocab;
+  int max_batch;            /* largest batch a vv_state may use with this model (1..16) */
+  float eps;                /* RMSNorm epsilon */
+  float rope_theta;         /* RoPE base; <= 0 disables RoPE */
+  const vv_layer* layers;   /* HOST array [n_layers]; copied by the calls that take it */
+  const uint16_t* gf;       /* device fp16 [H] final RMSNorm weight */
+  const uint16_t* lm_head;  /* device fp16 [V][H] */
+} vv_model;
+
+typedef struct vv_state {
+  int batch;                       /* 1..max_batch */
+  int cap;                         /* cache capacity in positions */
+  const uint16_t* input_embeds;    /* device fp16 [B][H] */
+  const int32_t* pos;              /* device int32 [B]; 0 <= pos[b] < cap (clamped on device) */
+  uint16_t* k_cache;               /* device fp16 [L][B][nkv][cap][head_dim] */
+  uint16_t* v_cache;
+  float* logits;                   /* device fp32 [B][V] or NULL */
+  int32_t* token;                  /* device int32 [B] */
+  float* h_trace;                  /* device fp32 [L+1][B][H] residual stream before each layer
+                                      and after the last, or NULL */
+  void* workspace;                 /* device, vv_decode_step_workspace(model, batch, cap) bytes,
+                                      zero-filled before first use */
+  size_t workspace_bytes;
+  void** events;                   /* optional HOST array of hipEvent_t used to time the kernels of
+                                      an eager vv_decode_step: event i is recorded on the stream
+                                      before kernel i and event 5*n_layers+2 after the last kernel
+                                      (kernels: prep, then per layer qkv, attention, o, gate/up,
+                                      down, then lm_head).  NULL disables; graphs reject it. */
+  int n_events;                    /* entries in events (>= 5*n_layers + 3 when events is set) */
+} vv_state;
+
+size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap);
+int vv_decode_step(const vv_model* m, const vv_state* s, void* stream);
+
+/* hipGraph capture of one vv_decode_step (one host->GPU crossing per step).  The graph keeps the
+ * device pointers of m and s; pos/input_embeds are read from device memory at replay, so one
+ * graph serves every step whose shapes and buffers stay the same. */
+typedef struct vv_graph vv_graph;
+int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, vv_graph** out);
+int vv_decode_graph_launch(vv_graph* g, void* stream);
+int vv_decode_graph_destroy(vv_graph* g);
+
+/* Zero-fills a workspace (one fill kernel, capture-safe) */
+int vv_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostics */
+const char* vv_status_string(int status);
+const char* vv_last_error(void);
+int vv_version(void);   /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VV_H */

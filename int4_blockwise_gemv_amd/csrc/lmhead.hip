@@ -1,0 +1,218 @@
+// fp16 lm_head GEMV with a fused greedy argmax.
+//
+// The lm_head (and the embedding table it is tied to in the 1.5B model) stays fp16, row-major
+// [V][H] ("vibevoice-asr-bitnet-onnx" page: lm_head/embeddings stay fp16; embed_tokens.bin is a
+// raw fp16 row-major table); decoding is greedy.  Each wave streams whole rows (lane i reads
+// 16-byte chunks i, i+64, ... of a row: 1 KiB contiguous per load instruction), keeps its slice
+// of the activation in registers, and reduces each row across the wave.  The largest logit is
+// tracked as a 64-bit key (order-preserving float bits, then the complemented index, so ties go
+// to the smallest index); each workgroup publishes its best key and the last one to finish picks
+// the winner in a fixed order.
+#include "vv_internal.h"
+
+namespace vv {
+namespace {
+
+constexpr int kRowsPerIter = 2;
+constexpr int kMaxChunksPerLane = 8;   // H <= 8 * 64 * 8 = 4096
+
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  return ((uint64_t)float_order_key(v) << 32) | (uint64_t)(0xffffffffu - idx);
+}
+
+template <int CPL, int BT>
+__global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restrict__ W) {
+  __shared__ uint64_t best_w[4][BT];
+  __shared__ unsigned s_last;
+  const int H = p.H, V = p.V;
+  const int nch = H / 8;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wg = blockIdx.x;
+  const int r0 = wg * p.rows_per_wg;
+  const int r1 = min(V, r0 + p.rows_per_wg);
+  const int rpw = (p.rows_per_wg + 3) / 4;
+  const int wr0 = r0 + w * rpw;
+  const int wr1 = min(r1, wr0 + rpw);
+
+  for (int bb = 0; bb < p.B; bb += BT) {
+    const int nbt = min(BT, p.B - bb);
+    // activation slice in registers: chunk c = lane + 64*j holds x[8c .. 8c+7]
+    float xr[BT][CPL][8];
+    float rs[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      rs[t] = 1.f;
+      if (t < nbt && p.rs_parts)
+        rs[t] = rstd_from_parts(p.rs_parts + (size_t)(bb + t) * p.rs_nparts, p.rs_nparts, p.rs_inv_n, p.eps);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xr[t][j][i] = 0.f;
+        if (t < nbt && c < nch) {
+          if (p.x_f16) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + (size_t)(bb + t) * H + 8 * c);
+            const uint32_t d4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              xr[t][j][2 * i] = (float)as_h2(d4[i]).x;
+              xr[t][j][2 * i + 1] = (float)as_h2(d4[i]).y;
+            }
+          } else {
+            const float* xs = reinterpret_cast<const float*>(p.x) + (size_t)(bb + t) * H + 8 * c;
+            const float4 a = *reinterpret_cast<const float4*>(xs);
+            const float4 b = *reinterpret_cast<const float4*>(xs + 4);
+            xr[t][j][0] = a.x; xr[t][j][1] = a.y; xr[t][j][2] = a.z; xr[t][j][3] = a.w;
+            xr[t][j][4] = b.x; xr[t][j][5] = b.y; xr[t][j][6] = b.z; xr[t][j][7] = b.w;
+          }
+        }
+      }
+    }
+    uint64_t best[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) best[t] = 0;
+
+    for (int r = wr0; r < wr1; r += kRowsPerIter) {
+      u32x4 wv[kRowsPerIter][CPL];
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerIter; ++rr)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + 64 * j;
+          wv[rr][j] = u32x4{0, 0, 0, 0};
+          if (r + rr < wr1 && c < nch) wv[rr][j] = __builtin_nontemporal_load(W + (size_t)(r + rr) * nch + c);
+        }
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerIter; ++rr) {
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+          if (t >= nbt) continue;
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const uint32_t d4[4] = {wv[rr][j].x, wv[rr][j].y, wv[rr][j].z, wv[rr][j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const h2_t hv = as_h2(d4[i]);
+              a = fmaf((float)hv.x, xr[t][j][2 * i], a);
+              a = fmaf((float)hv.y, xr[t][j][2 * i + 1], a);
+            }
+          }
+          a = wave_sum(a) * rs[t];
+          const int row = r + rr;
+          if (row < wr1) {
+            if (p.logits && lane == 0) p.logits[(size_t)(bb + t) * V + row] = a;
+            const uint64_t k = make_key(a, (uint32_t)row);
+            best[t] = k > best[t] ? k : best[t];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BT; ++t)
+      if (lane == 0) best_w[w][t] = best[t];
+    __syncthreads();
+    if (tid < nbt) {
+      uint64_t k = best_w[0][tid];
+      for (int i = 1; i < 4; ++i) k = best_w[i][tid] > k ? best_w[i][tid] : k;
+      p.keys[(size_t)(bb + tid) * gridDim.x + wg] = k;
+    }
+    __syncthreads();
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(p.cnt, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  // one wave per batch row: max over the workgroup keys
+  for (int b = w; b < p.B; b += 4) {
+    uint64_t k = 0;
+    for (int i = lane; i < (int)gridDim.x; i += 64) {
+      const uint64_t v = __builtin_nontemporal_load(p.keys + (size_t)b * gridDim.x + i);
+      k = v > k ? v : k;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t v = __shfl_xor(k, o, 64);
+      k = v > k ? v : k;
+    }
+    if (lane == 0) p.token[b] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
+  }
+  if (tid == 0) *p.cnt = 0u;
+}
+
+}  // namespace
+
+void lm_plan(LmParams& p) {
+  int grid = (int)cdiv(p.V, 64);            // at least 16 rows per wave
+  grid = grid > 1024 ? 1024 : (grid < 1 ? 1 : grid);
+  p.rows_per_wg = (int)cdiv(p.V, grid);
+  p.rows_per_wg = (int)cdiv(p.rows_per_wg, 4 * kRowsPerIter) * 4 * kRowsPerIter;
+  p.grid = (int)cdiv(p.V, p.rows_per_wg);
+}
+
+size_t lm_workspace_bytes(int B, int V, int H) {
+  LmParams p{};
+  p.B = B; p.V = V; p.H = H;
+  lm_plan(p);
+  return align_up((size_t)B * p.grid * sizeof(uint64_t), 256) + 256;
+}
+
+void lm_set_workspace(LmParams& p, void* ws) {
+  p.keys = reinterpret_cast<uint64_t*>(ws);
+  p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up((size_t)p.B * p.grid * sizeof(uint64_t), 256));
+}
+
+hipError_t lm_launch(const LmParams& p, hipStream_t st) {
+  const int cpl = (int)cdiv(p.H / 8, 64);
+  const u32x4* W = reinterpret_cast<const u32x4*>(p.W);
+#define VV_LM_CASE(C)                                                                   \
+  case C:                                                                               \
+    if (p.B == 1) hipLaunchKernelGGL((k_lmhead<C, 1>), dim3(p.grid), dim3(256), 0, st, p, W); \
+    else hipLaunchKernelGGL((k_lmhead<C, 2>), dim3(p.grid), dim3(256), 0, st, p, W);          \
+    break;
+  switch (cpl) {
+    VV_LM_CASE(1) VV_LM_CASE(2) VV_LM_CASE(3) VV_LM_CASE(4) VV_LM_CASE(5) VV_LM_CASE(6) VV_LM_CASE(7)
+    VV_LM_CASE(8)
+    default: break;
+  }
+#undef VV_LM_CASE
+  return hipGetLastError();
+}
+
+}  // namespace vv
+
+using namespace vv;
+
+extern "C" {
+
+size_t vv_lm_head_argmax_workspace(int B, int V, int H) {
+  if (B < 1 || V < 1 || H < 8) return 0;
+  return lm_workspace_bytes(B, V, H);
+}
+
+int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H, float* logits,
+                      int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  VV_REQUIRE(W && x && token, VV_ERR_NULL, "vv_lm_head_argmax: NULL pointer");
+  VV_REQUIRE(B >= 1 && B <= 16, VV_ERR_RANGE, "vv_lm_head_argmax: B = %d not in 1..16", B);
+  VV_REQUIRE(V >= 1, VV_ERR_RANGE, "vv_lm_head_argmax: V = %d < 1", V);
+  VV_REQUIRE(H >= 8 && H % 8 == 0 && H <= 8 * 64 * kMaxChunksPerLane, VV_ERR_SHAPE,
+             "vv_lm_head_argmax: H = %d must be a multiple of 8 in [8, 4096]", H);
+  VV_REQUIRE(x_dtype == VV_F16 || x_dtype == VV_F32, VV_ERR_DTYPE, "vv_lm_head_argmax: unknown x dtype");
+  VV_REQUIRE(((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(x)) & 15) == 0, VV_ERR_RANGE,
+             "vv_lm_head_argmax: W and x must be 16-byte aligned");
+  const size_t need = vv_lm_head_argmax_workspace(B, V, H);
+  VV_REQUIRE(ws && ws_bytes >= need, VV_ERR_WORKSPACE, "vv_lm_head_argmax: workspace needs %zu bytes", need);
+  LmParams p{};
+  p.W = W; p.V = V; p.H = H; p.B = B;
+  p.x = x; p.x_f16 = x_dtype == VV_F16;
+  p.logits = logits; p.token = token;
+  lm_plan(p);
+  lm_set_workspace(p, ws);
+  VV_HIP(lm_launch(p, as_stream(stream)));
+  return VV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,332 @@
+// Decode-step launcher and its hipGraph wrapper.
+//
+// decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts):
+//   input_embeds [B,H], position_ids [B], past K/V -> logits [B,V], present K/V (one more slot)
+// on the Qwen2 layer of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA,
+// SiLU-gated MLP, residual adds.  One step is 1 + 5 L + 1 kernels:
+//   prep (embeddings -> residual stream, RoPE table)
+//   per layer: QKV GEMV (RMSNorm folded in) | attention (+RoPE, KV append, split merge)
+//              | o GEMV + residual | gate/up GEMV + SiLU*up | down GEMV + residual
+//   lm_head + argmax (final RMSNorm folded in).
+// RMSNorm is folded into the GEMVs: the producer of h writes fp16(gamma * h) and per-tile sums of
+// h^2; the consumer scales its row sums by rstd = 1/sqrt(mean(h^2) + eps).  Positions are read
+// from device memory, so one captured graph serves every step.
+#include <new>
+#include <vector>
+
+#include "vv_internal.h"
+
+namespace vv {
+namespace {
+
+constexpr int kHeadDim = 128;
+
+// h = fp32(input_embeds); g = fp16(gamma * h) (or gf = gamma * h in fp32 when there are no
+// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs.
+__global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ emb, int H, int ntiles,
+                                                  const uint16_t* __restrict__ gamma, float* __restrict__ h,
+                                                  uint16_t* __restrict__ g, float* __restrict__ gf,
+                                                  float* __restrict__ sumsq, float* __restrict__ trace,
+                                                  const int32_t* __restrict__ pos, int cap, double theta,
+                                                  float* __restrict__ rope) {
+  const int t = blockIdx.x % ntiles, b = blockIdx.x / ntiles;
+  const int lane = threadIdx.x;
+  const int n = t * 64 + lane;
+  const size_t i = (size_t)b * H + n;
+  const float hv = h2f(emb[i]);
+  h[i] = hv;
+  if (trace) trace[i] = hv;
+  const float gv = h2f(gamma[n]) * hv;
+  if (g) g[i] = f2h(gv);
+  if (gf) gf[i] = gv;
+  const float ss = wave_sum(hv * hv);
+  if (lane == 0) sumsq[(size_t)b * ntiles + t] = ss;
+  if (t == 0 && theta > 0.0) {
+    int P = pos[b];
+    P = P < 0 ? 0 : (P >= cap ? cap - 1 : P);
+    const double inv = pow(theta, -(double)(2 * lane) / (double)kHeadDim);
+    double s, c;
+    sincos((double)P * inv, &s, &c);
+    rope[((size_t)b * 64 + lane) * 2] = (float)c;
+    rope[((size_t)b * 64 + lane) * 2 + 1] = (float)s;
+  }
+}
+
+struct Layout {
+  size_t h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, total;
+};
+
+struct Dims {
+  int L, H, I, nq, nkv, V, B, cap, nqkv, ntH, ntI;
+};
+
+Dims dims_of(const vv_model* m, int B, int cap) {
+  Dims d;
+  d.L = m->n_layers; d.H = m->hidden; d.I = m->inter; d.nq = m->n_q; d.nkv = m->n_kv; d.V = m->vocab;
+  d.B = B; d.cap = cap;
+  d.nqkv = (m->n_q + 2 * m->n_kv) * kHeadDim;
+  d.ntH = m->hidden / kTileRows;
+  d.ntI = m->inter / kTileRows;
+  return d;
+}
+
+Layout layout_of(const Dims& d) {
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
+  l.h = take((size_t)d.B * d.H * 4);
+  l.g = take((size_t)d.B * d.H * 2);
+  l.gf = take((size_t)d.B * d.H * 4);
+  l.qkv = take((size_t)d.B * d.nqkv * 4);
+  l.o = take((size_t)d.B * d.nq * kHeadDim * 2);
+  l.act = take((size_t)d.B * d.I * 2);
+  l.sumsq = take((size_t)d.B * d.ntH * 4);
+  l.rope = take((size_t)d.B * 64 * 2 * 4);
+  l.ws_qkv = take(gemv_workspace_bytes(d.B, (int)cdiv(d.nqkv, kTileRows), 1, d.H / kBlock));
+  l.ws_o = take(gemv_workspace_bytes(d.B, d.ntH, 1, d.nq * kHeadDim / kBlock));
+  l.ws_gu = take(gemv_workspace_bytes(d.B, 2 * d.ntI, 2, d.H / kBlock));
+  l.ws_down = take(gemv_workspace_bytes(d.B, d.ntH, 1, d.I / kBlock));
+  AttnParams ap{};
+  ap.B = d.B; ap.nq = d.nq; ap.nkv = d.nkv; ap.cap = d.cap;
+  attn_plan(ap);
+  l.ws_attn = take(attn_workspace_bytes(d.B, d.nq, d.nkv, ap.nsplit));
+  l.ws_lm = take(lm_workspace_bytes(d.B, d.V, d.H));
+  l.total = off;
+  return l;
+}
+
+int validate(const vv_model* m, const vv_state* s, const char* fn) {
+  VV_REQUIRE(m && s, VV_ERR_NULL, "%s: model or state is NULL", fn);
+  VV_REQUIRE(m->n_layers >= 0 && m->n_layers <= 4096, VV_ERR_RANGE, "%s: n_layers out of range", fn);
+  VV_REQUIRE(m->head_dim == kHeadDim, VV_ERR_SHAPE, "%s: head_dim %d != 128", fn, m->head_dim);
+  VV_REQUIRE(m->hidden >= 64 && m->hidden % 64 == 0 && m->hidden <= 4096, VV_ERR_SHAPE,
+             "%s: hidden %d must be a multiple of 64 in [64, 4096]", fn, m->hidden);
+  VV_REQUIRE(m->inter >= 64 && m->inter % 64 == 0 && m->inter <= (1 << 20), VV_ERR_SHAPE,
+             "%s: inter %d must be a positive multiple of 64", fn, m->inter);
+  VV_REQUIRE(m->n_q >= 1 && m->n_kv >= 1 && m->n_q % m->n_kv == 0 && m->n_q / m->n_kv <= 8, VV_ERR_SHAPE,
+             "%s: n_q %% n_kv must be 0 with n_q/n_kv <= 8", fn);
+  VV_REQUIRE(m->vocab >= 1, VV_ERR_RANGE, "%s: vocab < 1", fn);
+  VV_REQUIRE(m->max_batch >= 1 && m->max_batch <= 16, VV_ERR_RANGE, "%s: max_batch not in 1..16", fn);
+  VV_REQUIRE(m->eps >= 0.f, VV_ERR_RANGE, "%s: eps < 0", fn);
+  VV_REQUIRE(m->gf && m->lm_head, VV_ERR_NULL, "%s: gf or lm_head is NULL", fn);
+  VV_REQUIRE(m->n_layers == 0 || m->layers, VV_ERR_NULL, "%s: layers is NULL", fn);
+  for (int l = 0; l < m->n_layers; ++l) {
+    const vv_layer& y = m->layers[l];
+    VV_REQUIRE(y.qkv_q && y.qkv_s && y.o_q && y.o_s && y.gu_q && y.gu_s && y.down_q && y.down_s && y.g1 && y.g2,
+               VV_ERR_NULL, "%s: layer %d has a NULL weight pointer", fn, l);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(y.qkv_q) | reinterpret_cast<uintptr_t>(y.qkv_s) |
+                        reinterpret_cast<uintptr_t>(y.o_q) | reinterpret_cast<uintptr_t>(y.o_s) |
+                        reinterpret_cast<uintptr_t>(y.gu_q) | reinterpret_cast<uintptr_t>(y.gu_s) |
+                        reinterpret_cast<uintptr_t>(y.down_q) | reinterpret_cast<uintptr_t>(y.down_s);
+    VV_REQUIRE((a & 15) == 0, VV_ERR_RANGE, "%s: layer %d weights must be 16-byte aligned", fn, l);
+  }
+  VV_REQUIRE((reinterpret_cast<uintptr_t>(m->lm_head) & 15) == 0, VV_ERR_RANGE, "%s: lm_head must be 16-byte aligned",
+             fn);
+  VV_REQUIRE(s->batch >= 1 && s->batch <= m->max_batch, VV_ERR_RANGE, "%s: batch %d not in 1..max_batch", fn,
+             s->batch);
+  VV_REQUIRE(s->cap >= 1, VV_ERR_RANGE, "%s: cap < 1", fn);
+  VV_REQUIRE(s->input_embeds && s->pos && s->token, VV_ERR_NULL, "%s: input_embeds, pos or token is NULL", fn);
+  VV_REQUIRE(m->n_layers == 0 || (s->k_cache && s->v_cache), VV_ERR_NULL, "%s: KV cache is NULL", fn);
+  VV_REQUIRE(((reinterpret_cast<uintptr_t>(s->k_cache) | reinterpret_cast<uintptr_t>(s->v_cache)) & 15) == 0,
+             VV_ERR_RANGE, "%s: KV caches must be 16-byte aligned", fn);
+  const Dims d = dims_of(m, s->batch, s->cap);
+  const size_t need = layout_of(d).total;
+  VV_REQUIRE(s->workspace && s->workspace_bytes >= need, VV_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
+             need);
+  VV_REQUIRE((reinterpret_cast<uintptr_t>(s->workspace) & 255) == 0, VV_ERR_RANGE,
+             "%s: workspace must be 256-byte aligned", fn);
+  VV_REQUIRE(!s->events || s->n_events >= 5 * m->n_layers + 3, VV_ERR_RANGE,
+             "%s: events needs at least 5*n_layers+3 entries", fn);
+  return VV_OK;
+}
+
+int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
+  const Dims d = dims_of(m, s->batch, s->cap);
+  const Layout lay = layout_of(d);
+  char* ws = static_cast<char*>(s->workspace);
+  float* h = reinterpret_cast<float*>(ws + lay.h);
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + lay.g);
+  float* gf = reinterpret_cast<float*>(ws + lay.gf);
+  float* qkv = reinterpret_cast<float*>(ws + lay.qkv);
+  uint16_t* o = reinterpret_cast<uint16_t*>(ws + lay.o);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + lay.act);
+  float* sumsq = reinterpret_cast<float*>(ws + lay.sumsq);
+  float* rope = reinterpret_cast<float*>(ws + lay.rope);
+  const int B = d.B, H = d.H;
+  const float inv_h = 1.0f / (float)H;
+  int ev = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!s->events) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st);
+  };
+
+  VV_HIP(mark());
+  hipLaunchKernelGGL(k_step_prep, dim3(B * d.ntH), dim3(64), 0, st, s->input_embeds, H, d.ntH,
+                     d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
+                     s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
+  VV_HIP(hipGetLastError());
+
+  const size_t layer_kv = (size_t)B * d.nkv * (size_t)s->cap * kHeadDim;
+  for (int l = 0; l < d.L; ++l) {
+    const vv_layer& y = m->layers[l];
+    {  // fused q|k|v projection, RMSNorm_1 folded in, bias added
+      GemvParams p{};
+      p.q = y.qkv_q; p.s = y.qkv_s; p.x = g;
+      p.M = B; p.N = d.nqkv; p.K = H;
+      p.ntiles = (int)cdiv(d.nqkv, kTileRows); p.unit_tiles = 1;
+      p.epi = EPI_STORE; p.bias = y.qkv_bias; p.y = qkv; p.y_f16 = 0; p.ldy = d.nqkv;
+      p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
+      gemv_plan(p);
+      gemv_set_workspace(p, ws + lay.ws_qkv);
+      VV_HIP(mark());
+      VV_HIP(gemv_launch(p, st));
+    }
+    {  // attention with RoPE and KV append
+      AttnParams a{};
+      a.B = B; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
+      attn_plan(a);
+      attn_set_workspace(a, ws + lay.ws_attn);
+      a.qkv = qkv; a.ldqkv = d.nqkv; a.pos = s->pos; a.rope_theta = m->rope_theta;
+      a.kc = s->k_cache + (size_t)l * layer_kv; a.vc = s->v_cache + (size_t)l * layer_kv;
+      a.scale = 1.0f / sqrtf((float)kHeadDim);
+      a.out = o; a.out_f16 = 1;
+      VV_HIP(mark());
+      VV_HIP(attn_launch_with_rope(a, rope, st));
+    }
+    {  // o projection + residual; writes fp16(g2 * h) and sum(h^2) for the MLP
+      GemvParams p{};
+      p.q = y.o_q; p.s = y.o_s; p.x = o;
+      p.M = B; p.N = H; p.K = d.nq * kHeadDim;
+      p.ntiles = d.ntH; p.unit_tiles = 1;
+      p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.sumsq_out = sumsq;
+      gemv_plan(p);
+      gemv_set_workspace(p, ws + lay.ws_o);
+      VV_HIP(mark());
+      VV_HIP(gemv_launch(p, st));
+    }
+    {  // gate/up (tile-interleaved) + SiLU(gate) * up, RMSNorm_2 folded in
+      GemvParams p{};
+      p.q = y.gu_q; p.s = y.gu_s; p.x = g;
+      p.M = B; p.N = d.I; p.K = H;
+      p.ntiles = 2 * d.ntI; p.unit_tiles = 2;
+      p.epi = EPI_SILU; p.act = act;
+      p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
+      gemv_plan(p);
+      gemv_set_workspace(p, ws + lay.ws_gu);
+      VV_HIP(mark());
+      VV_HIP(gemv_launch(p, st));
+    }
+    {  // down projection + residual; feeds the next layer (or the lm_head)
+      const bool last = l == d.L - 1;
+      GemvParams p{};
+      p.q = y.down_q; p.s = y.down_s; p.x = act;
+      p.M = B; p.N = H; p.K = d.I;
+      p.ntiles = d.ntH; p.unit_tiles = 1;
+      p.epi = EPI_RESID; p.h = h;
+      p.gamma = last ? m->gf : m->layers[l + 1].g1;
+      p.g_out = last ? nullptr : g;
+      p.gf_out = last ? gf : nullptr;
+      p.sumsq_out = sumsq;
+      p.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * B * H : nullptr;
+      gemv_plan(p);
+      gemv_set_workspace(p, ws + lay.ws_down);
+      VV_HIP(mark());
+      VV_HIP(gemv_launch(p, st));
+    }
+  }
+  {  // final RMSNorm folded into the lm_head; greedy argmax
+    LmParams p{};
+    p.W = m->lm_head; p.V = d.V; p.H = H; p.B = B;
+    p.x = gf; p.x_f16 = 0;
+    p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
+    p.logits = s->logits; p.token = s->token;
+    lm_plan(p);
+    lm_set_workspace(p, ws + lay.ws_lm);
+    VV_HIP(mark());
+    VV_HIP(lm_launch(p, st));
+  }
+  VV_HIP(mark());
+  return VV_OK;
+}
+
+}  // namespace
+}  // namespace vv
+
+struct vv_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+using namespace vv;
+
+extern "C" {
+
+size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap) {
+  if (!m || batch < 1 || cap < 1 || m->hidden < 64 || m->inter < 64 || m->n_kv < 1 || m->n_q < 1) return 0;
+  return layout_of(dims_of(m, batch, cap)).total;
+}
+
+int vv_decode_step(const vv_model* m, const vv_state* s, void* stream) {
+  clear_error();
+  const int rc = validate(m, s, "vv_decode_step");
+  if (rc) return rc;
+  return enqueue_step(m, s, as_stream(stream));
+}
+
+int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, vv_graph** out) {
+  clear_error();
+  VV_REQUIRE(out != nullptr, VV_ERR_NULL, "vv_decode_graph_create: out is NULL");
+  *out = nullptr;
+  int rc = validate(m, s, "vv_decode_graph_create");
+  if (rc) return rc;
+  VV_REQUIRE(s->events == nullptr, VV_ERR_UNSUPPORTED, "vv_decode_graph_create: timing events are eager-only");
+  (void)stream;
+  hipStream_t cs;
+  VV_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(cs);
+    return hip_fail(e, "hipStreamBeginCapture");
+  }
+  rc = enqueue_step(m, s, cs);
+  e = hipStreamEndCapture(cs, &graph);
+  hipStreamDestroy(cs);
+  if (rc) {
+    if (graph) hipGraphDestroy(graph);
+    return rc;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  vv_graph* gph = new (std::nothrow) vv_graph{graph, exec};
+  if (!gph) {
+    hipGraphExecDestroy(exec);
+    hipGraphDestroy(graph);
+    return fail(VV_ERR_RANGE, "vv_decode_graph_create: out of host memory");
+  }
+  *out = gph;
+  return VV_OK;
+}
+
+int vv_decode_graph_launch(vv_graph* gph, void* stream) {
+  clear_error();
+  VV_REQUIRE(gph != nullptr, VV_ERR_NULL, "vv_decode_graph_launch: graph is NULL");
+  VV_HIP(hipGraphLaunch(gph->exec, as_stream(stream)));
+  return VV_OK;
+}
+
+int vv_decode_graph_destroy(vv_graph* gph) {
+  clear_error();
+  if (!gph) return VV_OK;
+  hipGraphExecDestroy(gph->exec);
+  hipGraphDestroy(gph->graph);
+  delete gph;
+  return VV_OK;
+}
+
+}  // extern "C"

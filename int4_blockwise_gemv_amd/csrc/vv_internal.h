@@ -1,0 +1,153 @@
+// Internal declarations shared by the HIP sources of libvv (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/vv.h"
+
+namespace vv {
+
+// ---------------------------------------------------------------------------------------------
+// host-side error reporting
+// ---------------------------------------------------------------------------------------------
+int fail(int status, const char* fmt, ...);           // records a message, returns status
+int hip_fail(hipError_t e, const char* what);          // VV_ERR_HIP with the HIP error string
+void clear_error();
+
+#define VV_REQUIRE(cond, status, ...) \
+  do { if (!(cond)) return ::vv::fail((status), __VA_ARGS__); } while (0)
+#define VV_HIP(call) \
+  do { hipError_t e_ = (call); if (e_ != hipSuccess) return ::vv::hip_fail(e_, #call); } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int kBlock = 32;       // quantisation block (elements)
+constexpr int kTileRows = 64;    // rows per tile of the tiled layout (= lanes of a wave)
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups are dealt round-robin
+
+// ---------------------------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------------------------
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Maps a workgroup id so that consecutive logical ids land on the same XCD (workgroups are
+// dispatched round-robin over the XCDs).  Requires gridDim.x % kNumXcd == 0.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t wg, uint32_t nwg) {
+  const uint32_t per = nwg / kNumXcd;
+  return (wg % kNumXcd) * per + wg / kNumXcd;
+}
+
+__device__ __forceinline__ uint32_t wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+__device__ __forceinline__ uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Monotone key for a float: larger float -> larger key; NaN maps below every number.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN never wins
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// rstd = 1/sqrt(sum/n + eps) from per-tile partial sums (fixed summation order)
+__device__ __forceinline__ float rstd_from_parts(const float* parts, int nparts, float inv_n, float eps) {
+  float s = 0.f;
+  for (int i = 0; i < nparts; ++i) s += parts[i];
+  return 1.0f / sqrtf(s * inv_n + eps);
+}
+
+// ---------------------------------------------------------------------------------------------
+// internal launchers used by the decode step (enqueue only; arguments already validated)
+// ---------------------------------------------------------------------------------------------
+enum EpiKind { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2 };
+
+struct GemvParams {
+  const uint8_t* q;          // tiled nibbles
+  const uint16_t* s;         // tiled scales
+  const uint16_t* x;         // fp16 [M][K]
+  int M, N, K;               // N valid rows (for EPI_SILU: rows of gate = rows of up)
+  int ntiles;                // tiles in the matrix
+  int unit_tiles;            // 1, or 2 for gate/up pairs (EPI_SILU)
+  float* part;               // workspace partials
+  unsigned* cnt;             // workspace counters
+  int kb, wpt, grid;         // decomposition (filled by gemv_plan)
+  int epi;
+  // EPI_STORE
+  const uint16_t* bias;      // fp16 [N] or null
+  void* y; int y_f16; int ldy;
+  // rstd source (EPI_STORE / EPI_SILU), optional
+  const float* rs_parts; int rs_nparts; float rs_inv_n; float eps;
+  // EPI_RESID
+  float* h;                  // fp32 [M][N]
+  const uint16_t* gamma;     // fp16 [N]
+  uint16_t* g_out;           // fp16 [M][N] = fp16(gamma * h)   (if gamma and g_out)
+  float* gf_out;             // fp32 [M][N] = gamma * h          (if gamma and gf_out)
+  float* sumsq_out;          // fp32 [M][ntiles]
+  float* trace;              // fp32 [M][N] copy of h or null
+  // EPI_SILU
+  uint16_t* act;             // fp16 [M][N]
+};
+
+void gemv_plan(GemvParams& p);                       // fills kb/wpt/grid
+size_t gemv_workspace_bytes(int M, int ntiles, int unit_tiles, int nb);
+void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
+hipError_t gemv_launch(const GemvParams& p, hipStream_t st);
+
+struct AttnParams {
+  int B, nq, nkv, cap, split, nsplit;
+  // step flavour: q/k/v from the fused projection output (fp32 [B][ldqkv])
+  const float* qkv; int ldqkv;
+  const int32_t* pos;        // step: new token position; attention over pos+1 positions
+  float rope_theta;
+  // stand-alone flavour
+  const void* q; int q_f16;
+  const int32_t* lens;
+  uint16_t* kc; uint16_t* vc;   // [B][nkv][cap][128]
+  float scale;
+  void* out; int out_f16;       // [B][nq][128]
+  float* part; unsigned* cnt;
+};
+void attn_plan(AttnParams& p);
+size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit);
+void attn_set_workspace(AttnParams& p, void* ws);
+hipError_t attn_launch(const AttnParams& p, hipStream_t st);
+// step flavour: rope_cs = [B][64][2] (cos, sin) of the new positions
+hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st);
+
+struct LmParams {
+  const uint16_t* W; int V, H, B;
+  const void* x; int x_f16;
+  const float* rs_parts; int rs_nparts; float rs_inv_n; float eps;
+  float* logits; int32_t* token;
+  uint64_t* keys; unsigned* cnt;
+  int grid, rows_per_wg;
+};
+void lm_plan(LmParams& p);
+size_t lm_workspace_bytes(int B, int V, int H);
+void lm_set_workspace(LmParams& p, void* ws);
+hipError_t lm_launch(const LmParams& p, hipStream_t st);
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace vv

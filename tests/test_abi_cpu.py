@@ -1,0 +1,160 @@
+"""The C-ABI library loads, exports every symbol include/vv.h declares, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed for these paths)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vv.h")
+
+vvmod = pytest.importorskip("int4_blockwise_gemv_amd.vv")
+
+
+def _lib():
+    if not os.path.exists(vvmod.LIB_PATH):
+        pytest.skip("libvv.so not built (run __graft_entry__.build())")
+    return vvmod.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("vv_pack_int4", "vv_gemv_int4", "vv_gqa_decode", "vv_decode_step", "vv_lm_head_argmax",
+                     "vv_decode_graph_create", "vv_decode_graph_launch", "vv_decode_graph_destroy"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(_declared_functions()) == set(vvmod.exported_symbols())
+
+
+def test_status_strings_and_version():
+    _lib()
+    assert vvmod.status_string(0) == "ok"
+    assert "workspace" in vvmod.status_string(vvmod.VV_ERR_WORKSPACE)
+    assert vvmod.version() >= 100
+
+
+def test_layout_sizes():
+    _lib()
+    # 1536 x 1536: 48 blocks per row, 24 tiles
+    assert vvmod.packed_bytes(1536, 1536, vvmod.VV_LAYOUT_ROWMAJOR) == 1536 * 48 * 16
+    assert vvmod.scale_bytes(1536, 1536, vvmod.VV_LAYOUT_ROWMAJOR) == 1536 * 48 * 2
+    assert vvmod.packed_bytes(100, 96, vvmod.VV_LAYOUT_TILED) == 2 * 3 * 64 * 16
+    assert vvmod.scale_bytes(100, 96, vvmod.VV_LAYOUT_TILED) == 2 * 1 * 64 * 16
+    assert vvmod.packed_bytes(10, 33, vvmod.VV_LAYOUT_TILED) == 0
+
+
+def _call(fn, *args):
+    L = _lib()
+    return getattr(L, fn)(*args)
+
+
+P = C.c_void_p
+
+
+def test_pack_validation():
+    L = _lib()
+    dummy = P(64)
+    assert L.vv_pack_int4(None, 4, 32, 0, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_NULL
+    assert L.vv_pack_int4(dummy, 4, 33, 0, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_pack_int4(dummy, 0, 32, 0, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_pack_int4(dummy, 4, 32, 7, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_DTYPE
+    assert L.vv_pack_int4(dummy, 4, 32, 0, dummy, dummy, dummy, 16, None) == vvmod.VV_ERR_WORKSPACE
+    # destination tile out of range: 100 rows -> 2 tiles, stride 2 offset 1 -> tile 3 >= 3
+    assert L.vv_pack_int4_tiled(dummy, 100, 32, 0, 1, 2, 3, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_RANGE
+    assert "tile" in vvmod.last_error()
+    assert L.vv_repack_int4_tiled(dummy, None, 4, 32, 0, 1, 1, dummy, dummy, None) == vvmod.VV_ERR_NULL
+    assert L.vv_dequant_int4(dummy, dummy, 4, 32, 5, dummy, None) == vvmod.VV_ERR_DTYPE
+
+
+def test_gemv_validation():
+    L = _lib()
+    d = P(64)
+    assert L.vv_gemv_int4(None, d, None, d, 1, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_NULL
+    assert L.vv_gemv_int4(d, d, None, d, 0, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_gemv_int4(d, d, None, d, 17, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 48, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, d, 9, d, 1 << 20, None) == vvmod.VV_ERR_DTYPE
+    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, d, 2, d, 4, None) == vvmod.VV_ERR_WORKSPACE
+    assert L.vv_gemv_int4(P(65), d, None, d, 1, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+    assert vvmod.gemv_workspace(1, 1536, 1536) > 0
+
+
+def test_gqa_validation():
+    L = _lib()
+    d = P(64)
+    big = 1 << 24
+    assert L.vv_gqa_decode(d, 2, d, d, d, 1, 12, 2, 256, 64, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_gqa_decode(d, 2, d, d, d, 1, 12, 5, 256, 128, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_gqa_decode(d, 2, d, d, d, 1, 18, 2, 256, 128, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_gqa_decode(d, 2, d, d, None, 1, 12, 2, 256, 128, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_NULL
+    assert L.vv_gqa_decode(d, 3, d, d, d, 1, 12, 2, 256, 128, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_DTYPE
+    assert L.vv_gqa_decode(d, 2, d, d, d, 0, 12, 2, 256, 128, 0.1, d, 2, d, big, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_gqa_decode(d, 2, d, d, d, 1, 12, 2, 256, 128, 0.1, d, 2, d, 8, None) == vvmod.VV_ERR_WORKSPACE
+
+
+def test_lm_head_validation():
+    L = _lib()
+    d = P(64)
+    big = 1 << 24
+    assert L.vv_lm_head_argmax(d, d, 2, 1, 1000, 12, None, d, d, big, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_lm_head_argmax(d, d, 2, 17, 1000, 64, None, d, d, big, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_lm_head_argmax(d, d, 2, 1, 1000, 64, None, None, d, big, None) == vvmod.VV_ERR_NULL
+    assert L.vv_lm_head_argmax(d, d, 2, 1, 1000, 64, None, d, d, 8, None) == vvmod.VV_ERR_WORKSPACE
+
+
+def _model_struct(**over):
+    vv = vvmod
+    layers = (vv.vv_layer * 1)()
+    layers[0] = vv.vv_layer(*([64] * 8), None, 64, 64)
+    kw = dict(n_layers=1, hidden=256, inter=512, n_q=4, n_kv=2, head_dim=128, vocab=1000, max_batch=4, eps=1e-6,
+              rope_theta=1e6, layers=C.cast(layers, C.POINTER(vv.vv_layer)), gf=64, lm_head=64)
+    kw.update(over)
+    m = vv.vv_model(**kw)
+    m._keep = layers
+    return m
+
+
+def _state(ws_bytes, **over):
+    kw = dict(batch=1, cap=64, input_embeds=64, pos=64, k_cache=64, v_cache=64, logits=None, token=64, h_trace=None,
+              workspace=256, workspace_bytes=ws_bytes, events=None, n_events=0)
+    kw.update(over)
+    return vvmod.vv_state(**kw)
+
+
+def test_decode_step_validation():
+    L = _lib()
+    m = _model_struct()
+    need = vvmod.step_workspace(m, 1, 64)
+    assert need > 0
+    s = _state(need)
+    assert L.vv_decode_step(C.byref(_model_struct(head_dim=64)), C.byref(s), None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_decode_step(C.byref(_model_struct(hidden=200)), C.byref(s), None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_decode_step(C.byref(_model_struct(n_kv=3)), C.byref(s), None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, batch=5)), None) == vvmod.VV_ERR_RANGE
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need - 1)), None) == vvmod.VV_ERR_WORKSPACE
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, pos=None)), None) == vvmod.VV_ERR_NULL
+    assert L.vv_decode_step(C.byref(_model_struct(lm_head=None)), C.byref(s), None) == vvmod.VV_ERR_NULL
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, workspace=300)), None) == vvmod.VV_ERR_RANGE
+    evs = (C.c_void_p * 4)()
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=C.cast(evs, C.POINTER(C.c_void_p)),
+                                                      n_events=4)), None) == vvmod.VV_ERR_RANGE
+    h = C.c_void_p()
+    assert L.vv_decode_graph_create(C.byref(m), C.byref(_state(need, events=C.cast(evs, C.POINTER(C.c_void_p)),
+                                                              n_events=8)), None, C.byref(h)) == vvmod.VV_ERR_UNSUPPORTED
+    assert L.vv_decode_graph_create(C.byref(_model_struct(head_dim=64)), C.byref(s), None,
+                                    C.byref(h)) == vvmod.VV_ERR_SHAPE
+    assert h.value is None
+    assert L.vv_decode_graph_launch(None, None) == vvmod.VV_ERR_NULL
+    assert L.vv_decode_graph_destroy(None) == vvmod.VV_OK

@@ -1,0 +1,183 @@
+"""GPU parity: packer / repacker / dequantiser (bit-exact) and the int4 GEMV (2e-3) against the
+fp64 oracle, on the projection shapes of the 1.5B- and 7B-shaped decoders and on edge cases."""
+import numpy as np
+import pytest
+
+from oracle import vv_oracle as O
+from int4_blockwise_gemv_amd import synth
+from gpu_util import dev, host, host_u16, codes_to_tiled, rel_err
+
+pytestmark = pytest.mark.gpu
+
+# (N, K): every projection shape of the 1.5B- and 7B-shaped layers, plus ragged edge cases
+PROJ_SHAPES = [(1536, 1536), (256, 1536), (8960, 1536), (1536, 8960),
+               (3584, 3584), (512, 3584), (18944, 3584), (3584, 18944)]
+EDGE_SHAPES = [(1, 32), (100, 96), (65, 64), (130, 288), (7, 1024)]
+TOL = 2e-3
+
+
+def _pack_gpu(W, mode, tiled=False):
+    import torch
+    from int4_blockwise_gemv_amd import vv
+    N, K = W.shape
+    Wd = dev(W)
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    lay = vv.VV_LAYOUT_TILED if tiled else vv.VV_LAYOUT_ROWMAJOR
+    q = torch.empty(vv.packed_bytes(N, K, lay), dtype=torch.uint8, device="cuda")
+    s = torch.empty(vv.scale_bytes(N, K, lay) // 2, dtype=torch.int16, device="cuda")
+    if tiled:
+        vv.pack_int4_tiled(Wd, mode, 0, 1, -(-N // 64), q, s, ws)
+    else:
+        vv.pack_int4(Wd, mode, q, s, ws)
+    torch.cuda.synchronize()
+    return q, s
+
+
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", PROJ_SHAPES + EDGE_SHAPES)
+def test_pack_rowmajor_bitexact(cuda, shape, mode):
+    N, K = shape
+    W = synth.master_weight(3, 1, synth.T_GATE, N, K)
+    ref_q, ref_s = O.pack(W, mode)
+    q, s = _pack_gpu(W, mode)
+    assert np.array_equal(host(q).reshape(ref_q.shape), ref_q)
+    assert np.array_equal(host_u16(s).reshape(ref_s.shape), ref_s)
+
+
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", [(1536, 1536), (256, 1536), (3584, 18944)] + EDGE_SHAPES)
+def test_pack_tiled_repack_dequant_bitexact(cuda, shape, mode):
+    import torch
+    from int4_blockwise_gemv_amd import vv
+    N, K = shape
+    W = synth.master_weight(4, 2, synth.T_DOWN, N, K)
+    ref_q, ref_s = O.pack(W, mode)
+    want_q, want_s = codes_to_tiled(O.unpack_nibbles(ref_q), ref_s)
+    q, s = _pack_gpu(W, mode, tiled=True)
+    assert np.array_equal(host(q), want_q)
+    assert np.array_equal(host_u16(s), want_s)
+    # row-major -> tiled permutation of the GPU's own row-major output
+    rq, rs = _pack_gpu(W, mode)
+    tq = torch.empty_like(q)
+    ts = torch.empty_like(s)
+    vv.repack_int4_tiled(rq, rs, N, K, 0, 1, -(-N // 64), tq, ts)
+    torch.cuda.synchronize()
+    assert torch.equal(tq, q) and torch.equal(ts, s)
+    # dequantised weights are exact in fp32 for both layouts
+    ref_w = O.dequant(ref_q, ref_s)
+    for lay, (pq, ps) in ((vv.VV_LAYOUT_ROWMAJOR, (rq, rs)), (vv.VV_LAYOUT_TILED, (q, s))):
+        out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        vv.dequant_int4(pq, ps, N, K, lay, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).astype(np.float64), ref_w)
+
+
+def test_pack_golden_blocks(cuda):
+    from fractions import Fraction
+    import os
+    gold = os.path.join(os.path.dirname(__file__), "golden")
+    for name, mode in (("ternary_hand_block.txt", "ternary"), ("absmax_hand_block.txt", "absmax")):
+        d = {}
+        for line in open(os.path.join(gold, name)):
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                d[k.strip()] = v.split()
+        W = np.array([[float(Fraction(w)) for w in d["W"]]], np.float32)
+        q, s = _pack_gpu(W, mode)
+        assert [int(b) for b in host(q)] == [int(b, 16) for b in d["bytes"]]
+        assert int(host_u16(s)[0]) == int(d["scale_bits"][0], 16)
+
+
+def test_pack_into_fused_buffer(cuda):
+    """q|k|v row ranges and gate/up tile interleaving land where the layout note says."""
+    import torch
+    from int4_blockwise_gemv_amd import vv
+    K = 256
+    Wa = synth.master_weight(5, 0, synth.T_GATE, 128, K)
+    Wb = synth.master_weight(5, 0, synth.T_UP, 128, K)
+    T = 4
+    q = torch.zeros(vv.packed_bytes(T * 64, K, vv.VV_LAYOUT_TILED), dtype=torch.uint8, device="cuda")
+    s = torch.zeros(vv.scale_bytes(T * 64, K, vv.VV_LAYOUT_TILED) // 2, dtype=torch.int16, device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    vv.pack_int4_tiled(dev(Wa), "ternary", 0, 2, T, q, s, ws)
+    vv.pack_int4_tiled(dev(Wb), "ternary", 1, 2, T, q, s, ws)
+    torch.cuda.synchronize()
+    qa, sa = O.pack(Wa, "ternary")
+    qb, sb = O.pack(Wb, "ternary")
+    ca, cb = O.unpack_nibbles(qa), O.unpack_nibbles(qb)
+    inter = np.concatenate([ca[:64], cb[:64], ca[64:], cb[64:]])
+    inter_s = np.concatenate([sa[:64], sb[:64], sa[64:], sb[64:]])
+    want_q, want_s = codes_to_tiled(inter, inter_s)
+    assert np.array_equal(host(q), want_q) and np.array_equal(host_u16(s), want_s)
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------------------------
+
+def _gemv_gpu(q, s, N, K, x16, bias16=None, out_f16=False):
+    import torch
+    from int4_blockwise_gemv_amd import vv
+    M = x16.shape[0]
+    ws = torch.zeros(vv.gemv_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16 if out_f16 else torch.float32, device="cuda")
+    xd = dev(x16)
+    bd = dev(bias16) if bias16 is not None else None
+    vv.gemv_int4(q, s, bd, xd, N, K, y, ws)
+    torch.cuda.synchronize()
+    return host(y).astype(np.float64)
+
+
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", PROJ_SHAPES)
+def test_gemv_projection_shapes(cuda, shape, mode):
+    N, K = shape
+    W = synth.master_weight(0, 0, synth.T_Q, N, K)
+    x = synth.fp16_normal(0, 0, synth.T_X, (1, K))
+    ref = O.gemv(*O.pack(W, mode), x)
+    q, s = _pack_gpu(W, mode, tiled=True)
+    y = _gemv_gpu(q, s, N, K, x)
+    err = rel_err(y, ref)
+    print(f"gemv {shape} {mode}: max rel err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 16])
+@pytest.mark.parametrize("shape", [(100, 96), (1, 32), (130, 288), (1536, 1536), (256, 8960)])
+def test_gemv_batched_ragged_with_bias(cuda, shape, M):
+    N, K = shape
+    W = synth.master_weight(1, 0, synth.T_K, N, K)
+    x = synth.fp16_normal(1, M, synth.T_X, (M, K))
+    b = synth.bias(1, 0, synth.T_BK, N)
+    ref = O.gemv(*O.pack(W, "absmax"), x, b)
+    q, s = _pack_gpu(W, "absmax", tiled=True)
+    y = _gemv_gpu(q, s, N, K, x, b)
+    assert rel_err(y, ref) <= TOL
+    y16 = _gemv_gpu(q, s, N, K, x, b, out_f16=True)
+    assert rel_err(y16, ref) <= TOL
+
+
+def test_gemv_one_hot_columns_exact(cuda):
+    """x = e_k returns column k of the dequantised matrix exactly (one product per output)."""
+    N, K = 192, 512
+    W = synth.master_weight(2, 0, synth.T_O, N, K)
+    pq, ps = O.pack(W, "absmax")
+    deq = O.dequant(pq, ps)
+    q, s = _pack_gpu(W, "absmax", tiled=True)
+    ks = [0, 1, 7, 31, 32, 255, 511]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1
+    y = _gemv_gpu(q, s, N, K, x)
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i], deq[:, k])
+
+
+def test_gemv_deterministic(cuda):
+    N, K = 3584, 18944
+    W = synth.master_weight(0, 0, synth.T_DOWN, N, K)
+    x = synth.fp16_normal(0, 0, synth.T_X, (1, K))
+    q, s = _pack_gpu(W, "ternary", tiled=True)
+    a = _gemv_gpu(q, s, N, K, x)
+    b = _gemv_gpu(q, s, N, K, x)
+    assert np.array_equal(a, b)
