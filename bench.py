@@ -100,6 +100,9 @@ def kernel_breakdown(ds, n_layers, reps=3):
     import torch
     n_kern = 5 * n_layers + 2
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_kern + 1)]
+    for e in evs:  # torch creates the HIP event on first record
+        e.record()
+    torch.cuda.synchronize()
     arr = (C.c_void_p * (n_kern + 1))(*[C.c_void_p(e.cuda_event) for e in evs])
     ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
     ds.struct.n_events = n_kern + 1
@@ -186,6 +189,7 @@ def main():
     ms = dt * 1e3 / args.steps
     g.close()
     tok = int(ds.token.cpu()[0])
+    log(f"{ms * 1e3:.1f} us/step ({1e3 / ms:.1f} steps/s), token {tok}")
 
     wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
     total = wb + kvb + lmb

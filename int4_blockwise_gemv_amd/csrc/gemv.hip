@@ -5,12 +5,12 @@
 // activation block is the same for all lanes (wave-uniform loads).
 //
 // In-register dequantisation: a packed dword holds 8 codes with the even elements in nibbles
-// 0..3 and the odd ones in nibbles 4..7, so one AND-OR with a magic exponent turns a nibble pair
-// into an fp16 pair (64 + q_2i, 64 + q_2i+1) or (4 + q, 4 + q) that lines up with the natural
-// fp16 pair (x_2i, x_2i+1) of the activation; v_dot2_f32_f16 then multiplies both with exact
-// products and fp32 accumulation.  The offsets and the zero point 8 are removed once per block
-// by subtracting C_b = sum_j (off_j + 8) x_j, computed once per wave for its blocks; the block
-// sum is scaled by the block's fp16 scale in fp32.
+// 0..3 and the odd ones in nibbles 4..7, so a shift and one AND-OR with the fp16 exponent of
+// 64.0 turn nibble pair (i, 4+i) into the fp16 pair (64 + q_2i, 64 + q_2i+1), which lines up
+// with the natural fp16 pair (x_2i, x_2i+1) of the activation; v_dot2_f32_f16 then multiplies
+// both with exact products and fp32 accumulation.  The offset 64 and the zero point 8 are
+// removed once per block by subtracting C_b = 72 * sum_j x_j, computed once per wave for its
+// blocks; the block sum is scaled by the block's fp16 scale in fp32.
 //
 // Split-K: the kb-block ranges of a tile are spread over the 4 waves of a workgroup (reduced in
 // LDS) and over `wpt` workgroups; the last workgroup to arrive at a tile (atomic counter) adds
@@ -31,11 +31,13 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
   return r;
 }
 
-__device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, float acc, uint32_t m64, uint32_t m4) {
-  const uint32_t p01 = ((d << 4) & 0x00F000F0u) | m64;  // (64+e0, 64+e1)
-  const uint32_t p23 = (d & 0x00F000F0u) | m64;         // (64+e2, 64+e3)
-  const uint32_t p45 = (d & 0x0F000F00u) | m4;          // (4+e4, 4+e5)
-  const uint32_t p67 = ((d >> 4) & 0x0F000F00u) | m4;   // (4+e6, 4+e7)
+__device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, float acc, uint32_t m64) {
+  // the fp16 magic 64.0 (0x5400) has ulp 1/16, so a code in mantissa bits 4..7 of either half
+  // reads as 64 + q exactly; the even/odd codes of pair i sit in nibbles i and 4+i
+  const uint32_t p01 = ((d << 4) & 0x00F000F0u) | m64;  // nibbles 0, 4: (64+e0, 64+e1)
+  const uint32_t p23 = (d & 0x00F000F0u) | m64;         // nibbles 1, 5: (64+e2, 64+e3)
+  const uint32_t p45 = ((d >> 4) & 0x00F000F0u) | m64;  // nibbles 2, 6: (64+e4, 64+e5)
+  const uint32_t p67 = ((d >> 8) & 0x00F000F0u) | m64;  // nibbles 3, 7: (64+e6, 64+e7)
   acc = __builtin_amdgcn_fdot2(as_h2(p01), as_h2(x4[0]), acc, false);
   acc = __builtin_amdgcn_fdot2(as_h2(p23), as_h2(x4[1]), acc, false);
   acc = __builtin_amdgcn_fdot2(as_h2(p45), as_h2(x4[2]), acc, false);
@@ -43,18 +45,16 @@ __device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, floa
   return acc;
 }
 
-// C for one quarter (8 elements) of a block: 72*(x0+x1+x2+x3) + 12*(x4+x5+x6+x7)
+// C for one quarter (8 elements) of a block: (64 + 8) * (x0 + ... + x7)
 __device__ __forceinline__ float corr_quarter(u32x4 xv) {
   const uint32_t c72 = 0x54805480u;  // fp16 (72, 72)
-  const uint32_t c12 = 0x4A004A00u;  // fp16 (12, 12)
   float c = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(c72), 0.f, false);
   c = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(c72), c, false);
-  c = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(c12), c, false);
-  c = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(c12), c, false);
+  c = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(c72), c, false);
+  c = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(c72), c, false);
   return c;
 }
 
-// scale j (compile-time 0..7) of a group of 8 fp16 scales
 __device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
   const uint32_t d = (j >> 1) == 0 ? s.x : (j >> 1) == 1 ? s.y : (j >> 1) == 2 ? s.z : s.w;
   return (j & 1) ? (float)__builtin_bit_cast(h2_t, d).y : (float)__builtin_bit_cast(h2_t, d).x;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
 #pragma unroll
   for (int j = 0; j < SG; ++j)
     if (8 * j < nblk) sv[j] = __builtin_nontemporal_load(sp + (size_t)j * kTileRows);
-  const uint32_t m64 = vconst(0x54005400u), m4 = vconst(0x44004400u);
+  const uint32_t m64 = vconst(0x54005400u);
 
   float corr[MT];
 #pragma unroll
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
           const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + (size_t)m * K + (size_t)b * kBlock);
           float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
 #pragma unroll
-          for (int k = 0; k < 4; ++k) t = dot8_pairs(d[k], xb + 4 * k, t, m64, m4);
+          for (int k = 0; k < 4; ++k) t = dot8_pairs(d[k], xb + 4 * k, t, m64);
           acc[m] = fmaf(sc, t, acc[m]);
         }
       }
@@ -217,15 +217,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
   float* my = p.part + ((size_t)tile * p.wpt + kg) * MT * kTileRows;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
-    if (m < M) my[m * kTileRows + lane] = tot[0][m];
-  __threadfence();
+    if (m < M) publish_f32(&my[m * kTileRows + lane], tot[0][m]);
+  wait_published();
   const int unit = tile / p.unit_tiles;
   unsigned prev = 0;
-  if (lane == 0) prev = atomicAdd(&p.cnt[unit], 1u);
+  if (lane == 0) prev = arrive(&p.cnt[unit]);
   prev = __shfl(prev, 0, kWave);
   const unsigned arrivals = (unsigned)(p.wpt * p.unit_tiles);
   if (prev != arrivals - 1) return;
-  __threadfence();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (u >= p.unit_tiles) continue;
@@ -235,11 +234,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
       if (m >= M) continue;
       float s = 0.f;
       for (int k = 0; k < p.wpt; ++k)
-        s += __builtin_nontemporal_load(p.part + (((size_t)t * p.wpt + k) * MT + m) * kTileRows + lane);
+        s += collect_f32(p.part + (((size_t)t * p.wpt + k) * MT + m) * kTileRows + lane);
       tot[u][m] = s;
     }
   }
-  if (lane == 0) p.cnt[unit] = 0u;  // leave the counter ready for the next launch
+  if (lane == 0) reset_counter(&p.cnt[unit]);  // ready for the next launch
   epilogue<MT>(p, unit, tot, lane);
 }
 

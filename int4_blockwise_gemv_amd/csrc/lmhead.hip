@@ -115,21 +115,20 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
     if (tid < nbt) {
       uint64_t k = best_w[0][tid];
       for (int i = 1; i < 4; ++i) k = best_w[i][tid] > k ? best_w[i][tid] : k;
-      p.keys[(size_t)(bb + tid) * gridDim.x + wg] = k;
+      publish_u64(&p.keys[(size_t)(bb + tid) * gridDim.x + wg], k);
     }
     __syncthreads();
   }
-  __threadfence();
+  wait_published();
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(p.cnt, 1u) == gridDim.x - 1;
+  if (tid == 0) s_last = arrive(p.cnt) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   // one wave per batch row: max over the workgroup keys
   for (int b = w; b < p.B; b += 4) {
     uint64_t k = 0;
     for (int i = lane; i < (int)gridDim.x; i += 64) {
-      const uint64_t v = __builtin_nontemporal_load(p.keys + (size_t)b * gridDim.x + i);
+      const uint64_t v = collect_u64(p.keys + (size_t)b * gridDim.x + i);
       k = v > k ? v : k;
     }
 #pragma unroll
@@ -139,7 +138,7 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
     }
     if (lane == 0) p.token[b] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
   }
-  if (tid == 0) *p.cnt = 0u;
+  if (tid == 0) reset_counter(p.cnt);
 }
 
 }  // namespace

@@ -124,7 +124,7 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
              fn);
   VV_REQUIRE(s->batch >= 1 && s->batch <= m->max_batch, VV_ERR_RANGE, "%s: batch %d not in 1..max_batch", fn,
              s->batch);
-  VV_REQUIRE(s->cap >= 1, VV_ERR_RANGE, "%s: cap < 1", fn);
+  VV_REQUIRE(s->cap >= 1 && s->cap <= 131072, VV_ERR_RANGE, "%s: cap %d not in 1..131072", fn, s->cap);
   VV_REQUIRE(s->input_embeds && s->pos && s->token, VV_ERR_NULL, "%s: input_embeds, pos or token is NULL", fn);
   VV_REQUIRE(m->n_layers == 0 || (s->k_cache && s->v_cache), VV_ERR_NULL, "%s: KV cache is NULL", fn);
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(s->k_cache) | reinterpret_cast<uintptr_t>(s->v_cache)) & 15) == 0,

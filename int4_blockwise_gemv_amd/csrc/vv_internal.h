@@ -70,6 +70,40 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Cross-workgroup hand-off inside one kernel.  The 8 XCDs have separate L2 caches, and an
+// agent-scope fence writes back and invalidates the whole L2.  Data published to another
+// workgroup therefore goes through agent-scope atomic stores and loads (coherent by themselves:
+// they are not served from a stale line of another XCD's L2), and the publisher waits for its
+// stores to complete before the arrival counter is bumped.  No fence touches the L2.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void publish_f32(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect_f32(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint64_t collect_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all of this wave's earlier memory operations have completed (s_waitcnt 0); also a compiler barrier
+__device__ __forceinline__ void wait_published() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// arrival counter: returns the previous count (agent scope, performed coherently across XCDs)
+__device__ __forceinline__ unsigned arrive(unsigned* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(unsigned* c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // rstd = 1/sqrt(sum/n + eps) from per-tile partial sums (fixed summation order)
 __device__ __forceinline__ float rstd_from_parts(const float* parts, int nparts, float inv_n, float eps) {
   float s = 0.f;
@@ -126,7 +160,7 @@ struct AttnParams {
   uint16_t* kc; uint16_t* vc;   // [B][nkv][cap][128]
   float scale;
   void* out; int out_f16;       // [B][nq][128]
-  float* part; unsigned* cnt;
+  float* part; float* part2; unsigned* cnt;
 };
 void attn_plan(AttnParams& p);
 size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit);
