@@ -73,8 +73,11 @@ enum { VV_LAYOUT_ROWMAJOR = 0, VV_LAYOUT_TILED = 1 };
  *   8w+1, 8w+3, 8w+5, 8w+7 in nibbles 4..7.  Scales: ng = ceil(nb/8) groups per row; the 8
  *   fp16 scales of blocks 8g..8g+7 of row 64t+i sit at uint16 offset ((t*ng + g)*64 + i)*8
  *   (blocks >= nb hold 0).  Total bytes: vv_packed_bytes / vv_scale_bytes.
- *   A tiled buffer may hold several matrices as row ranges: the *_tiled packers place source
- *   row r in destination tile (r/64)*tile_stride + tile_offset (row (r%64) of that tile).
+ *   A tiled buffer may hold several matrices: the *_tiled packers place source row r at
+ *   destination row (r / row_group) * group_stride + row_offset + r % row_group (tile = row/64,
+ *   lane = row%64).  Plain placement is row_group = group_stride = 64, row_offset = 0.  Source
+ *   rows run to the end of their last row group; rows beyond N there are padding (code 8,
+ *   scale 0).
  */
 size_t vv_packed_bytes(int64_t rows, int64_t K, int layout);
 size_t vv_scale_bytes(int64_t rows, int64_t K, int layout);
@@ -92,26 +95,25 @@ size_t vv_scale_bytes(int64_t rows, int64_t K, int layout);
  *     fp64 quotient); q = clamp(rint(w / scale) + 8, 0, 15) with the division in fp64 and ties
  *     to even; a block whose scale is 0 gets q = 8.
  *   Output: vv_pack_int4 writes VV_LAYOUT_ROWMAJOR into packed [N*nb*16] / scales [N*nb];
- *   vv_pack_int4_tiled writes VV_LAYOUT_TILED rows into a destination of dst_tiles tiles
- *   (see the layout note for tile_offset / tile_stride; every destination tile touched is
- *   written completely, including its padding rows).
+ *   vv_pack_int4_tiled writes VV_LAYOUT_TILED rows into a destination of dst_rows rows
+ *   (a multiple of 64) placed as the layout note says.
  *   ws: device workspace of vv_pack_int4_workspace(N, K, mode) bytes (any content; it is
  *   cleared by the call).  Errors: NULL pointers, K % 32, N < 1, unknown mode, a destination
- *   tile outside [0, dst_tiles), small workspace.
+ *   row outside [0, dst_rows), small workspace.
  * ------------------------------------------------------------------------------------------- */
 size_t vv_pack_int4_workspace(int64_t N, int64_t K, int mode);
 int vv_pack_int4(const float* W, int64_t N, int64_t K, int mode, uint8_t* packed, uint16_t* scales,
                  void* ws, size_t ws_bytes, void* stream);
-int vv_pack_int4_tiled(const float* W, int64_t N, int64_t K, int mode, int64_t tile_offset,
-                       int64_t tile_stride, int64_t dst_tiles, uint8_t* packed, uint16_t* scales,
-                       void* ws, size_t ws_bytes, void* stream);
+int vv_pack_int4_tiled(const float* W, int64_t N, int64_t K, int mode, int64_t row_group,
+                       int64_t group_stride, int64_t row_offset, int64_t dst_rows, uint8_t* packed,
+                       uint16_t* scales, void* ws, size_t ws_bytes, void* stream);
 
 /* Row-major (MatMulNBits) -> tiled, a pure permutation of nibbles and scales (same destination
  * placement rules as vv_pack_int4_tiled).  Lets a MatMulNBits blob from elsewhere feed the
  * GEMV kernels. */
 int vv_repack_int4_tiled(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
-                         int64_t tile_offset, int64_t tile_stride, int64_t dst_tiles,
-                         uint8_t* tiled, uint16_t* tiled_scales, void* stream);
+                         int64_t row_group, int64_t group_stride, int64_t row_offset,
+                         int64_t dst_rows, uint8_t* tiled, uint16_t* tiled_scales, void* stream);
 
 /* Dequantiser: W[n][k] = (q - 8) * scale as fp32 (exact for both modes: a 4-bit integer times an
  * fp16 value needs at most 15 significant bits).  `layout` says how packed/scales are stored;
@@ -177,11 +179,11 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  * Weights use VV_LAYOUT_TILED:
  *   qkv: one tiled matrix of nq*d + 2*nkv*d rows (q rows, then k rows, then v rows), K = H;
  *   o:   H rows, K = nq*d;
- *   gu:  gate and up interleaved by tile (tile 2j = gate rows 64j..64j+63, tile 2j+1 = the same
- *        up rows; pack gate with tile_offset 0 and up with tile_offset 1, tile_stride 2),
- *        2*ceil(I/64) tiles, K = H;
+ *   gu:  gate and up rows interleaved in each tile: lanes 0-31 of tile j hold gate rows
+ *        32j..32j+31 and lanes 32-63 the same up rows (pack gate with row_group 32,
+ *        group_stride 64, row_offset 0 and up with row_offset 32), 2*I rows, K = H;
  *   down: H rows, K = I.
- * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8.
+ * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8, cap <= 131072.
  * ------------------------------------------------------------------------------------------- */
 typedef struct vv_layer {
   const uint8_t* qkv_q;   const uint16_t* qkv_s;    /* device, tiled */

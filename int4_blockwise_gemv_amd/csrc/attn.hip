@@ -6,10 +6,10 @@
 //
 // Work unit: (sequence b, KV head, split of 64/128/256 positions).  A workgroup of 8 waves issues
 // every K and V row load of its split up front (16 lanes x 16 B per row, 4 rows = 1 KiB per wave
-// load) and serves all g = nq/nkv query heads of the group with them.  It publishes
-// (max, sum, unnormalised output) per head; the last of each group of 8 splits to finish merges
-// that group (online-softmax rescaling, fixed order) and the last group merger merges the group
-// results, so no single workgroup reads more than 64 records.
+// load) and serves all g = nq/nkv query heads of the group with them.  It writes
+// (max, sum, unnormalised output) per head; a second small kernel, one workgroup per query
+// head, merges the splits (online-softmax rescaling, fixed order).  The kernel boundary is the
+// hand-off, so no workgroup waits on another.
 //
 // Decode-step flavour: q/k/v come from the fused projection output; the workgroup rotates q
 // (and, for the split that holds the new position, k) with RoPE, writes fp16 k and v into the
@@ -24,69 +24,6 @@ constexpr int kMaxG = 8;          // query heads per KV head
 constexpr int kPS = 132;          // partial record: m, l, pad, pad, o[128]
 constexpr int kWaves = 8;         // 512 threads per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kGroup = 8;         // splits merged per first-level merge
-constexpr int kMaxMerge = 64;     // partials one merge reads (kGroup, or the number of groups)
-
-struct MergeLds {
-  float m[kMaxMerge][kMaxG];
-  float w[kMaxMerge][kMaxG];      // e^(m_s - M), 0 for empty partials
-  float M[kMaxG], L[kMaxG];
-  float O[kMaxG][kD];
-};
-
-// Merges n partial records (m, l, o) per head into (M, L, O = sum e^(m_s-M) o_s) in LDS.
-__device__ void merge_parts(const float* parts, int n, int g, MergeLds& ml, int tid) {
-  for (int i = tid; i < n * g; i += kThreads) {
-    const int s = i / g, hh = i % g;
-    ml.m[s][hh] = collect_f32(parts + ((size_t)s * kMaxG + hh) * kPS);
-  }
-  __syncthreads();
-  if (tid < g) {
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, ml.m[s][tid]);
-    ml.M[tid] = M;
-  }
-  __syncthreads();
-  for (int i = tid; i < n * g; i += kThreads) {
-    const int s = i / g, hh = i % g;
-    const float ms = ml.m[s][hh];
-    ml.w[s][hh] = (ms == -INFINITY) ? 0.f : expf(ms - ml.M[hh]);
-  }
-  __syncthreads();
-  if (tid < g) {
-    float L = 0.f;
-    for (int s = 0; s < n; ++s)
-      if (ml.w[s][tid] != 0.f) L = fmaf(ml.w[s][tid], collect_f32(parts + ((size_t)s * kMaxG + tid) * kPS + 1), L);
-    ml.L[tid] = L;
-  }
-  for (int i = tid; i < g * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    float O = 0.f;
-    int s = 0;
-    for (; s + 8 <= n; s += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = collect_f32(parts + ((size_t)(s + u) * kMaxG + hh) * kPS + 4 + d);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) O = fmaf(ml.w[s + u][hh], v[u], O);
-    }
-    for (; s < n; ++s) O = fmaf(ml.w[s][hh], collect_f32(parts + ((size_t)s * kMaxG + hh) * kPS + 4 + d), O);
-    ml.O[hh][d] = O;
-  }
-  __syncthreads();
-}
-
-__device__ void publish_record(float* rec, int g, const float* M, const float* L, const float (*O)[kD], int tid) {
-  for (int i = tid; i < g * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    publish_f32(rec + (size_t)hh * kPS + 4 + d, O[hh][d]);
-  }
-  if (tid < g) {
-    publish_f32(rec + (size_t)tid * kPS + 0, M[tid]);
-    publish_f32(rec + (size_t)tid * kPS + 1, L[tid]);
-  }
-  wait_published();
-}
 
 __device__ void write_out(const AttnParams& p, int b, int kvh, int g, const float (*O)[kD], const float* L, int tid) {
   for (int i = tid; i < g * kD; i += kThreads) {
@@ -117,8 +54,6 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   __shared__ float red[kWaves][kMaxG][kD];
   __shared__ uint16_t knew[kD], vnew[kD];
   __shared__ float mh[kMaxG], lh[kMaxG];
-  __shared__ MergeLds ml;
-  __shared__ unsigned s_flag;
 
   const int g = p.nq / p.nkv;
   const int wg = blockIdx.x;
@@ -128,82 +63,92 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool step = p.qkv != nullptr;
 
-  int len, P = -1;
-  if (step) {
-    P = p.pos[b];
-    P = P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P);
-    len = P + 1;
-  } else {
-    len = p.lens[b];
-    len = len < 1 ? 1 : (len > p.cap ? p.cap : len);
-  }
+  // ---- every global load of the workgroup is issued before any result is used ----------------
+  // (K/V rows of the whole split do not depend on the sequence length: rows past it are read
+  // from inside the cache and masked out below; the new position's stale row is replaced)
   const int s0 = sidx * S;
-  const int npos = max(0, min(s0 + S, len) - s0);
   const size_t kvbase = ((size_t)b * p.nkv + kvh) * (size_t)p.cap * kD;
   const uint16_t* Kc = p.kc + kvbase;
   const uint16_t* Vc = p.vc + kvbase;
-
-  // ---- issue every K and V row load of this wave first ----------------------------------------
   const int sl = lane & 15;            // dims 8*sl .. 8*sl+7
   const int pg = lane >> 4;            // position within a pass
   const int jw = w * 4 * NP;           // first local position of this wave
   u32x4 kr[NP], vr[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int j = jw + 4 * i + pg;
-    const int pos = s0 + j;
+    const int pos = s0 + jw + 4 * i + pg;
     kr[i] = u32x4{0, 0, 0, 0};
     vr[i] = u32x4{0, 0, 0, 0};
-    if (j < npos && pos != P) {
+    if (pos < p.cap) {
       kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kc + (size_t)pos * kD + 8 * sl));
       vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vc + (size_t)pos * kD + 8 * sl));
     }
   }
-
-  // ---- q (and the new k, v) into LDS ---------------------------------------------------------
+  const int pos_raw = step ? p.pos[b] : p.lens[b];
+  // q pair (j, j+64) of head hh = tid/64 (step: raw projection output + RoPE coefficients)
+  const int qh_ = tid >> 6, qj = tid & 63;
+  float q1 = 0.f, q2 = 0.f, rc = 1.f, rsn = 0.f, k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+  float qsa[2] = {0.f, 0.f};           // stand-alone flavour: two q values per thread
   if (step) {
     const float* row = p.qkv + (size_t)b * p.ldqkv;
-    const float* cs = rope_cs + (size_t)b * 64 * 2;
-    const bool rope = p.rope_theta > 0.f;
-    for (int i = tid; i < g * 64; i += kThreads) {
-      const int hh = i / 64, j = i % 64;
-      const float* qh = row + (size_t)(kvh * g + hh) * kD;
-      const float x1 = qh[j], x2 = qh[j + 64];
-      if (rope) {
-        const float c = cs[2 * j], s = cs[2 * j + 1];
-        qs[hh][j] = x1 * c - x2 * s;
-        qs[hh][j + 64] = x2 * c + x1 * s;
-      } else {
-        qs[hh][j] = x1;
-        qs[hh][j + 64] = x2;
-      }
+    if (qh_ < g) {
+      const float* qh = row + (size_t)(kvh * g + qh_) * kD;
+      q1 = qh[qj];
+      q2 = qh[qj + 64];
     }
-    if (P >= s0 && P < s0 + npos && tid < 64) {
+    if (p.rope_theta > 0.f) {
+      const float* cs = rope_cs + ((size_t)b * 64 + qj) * 2;
+      rc = cs[0];
+      rsn = cs[1];
+    }
+    if (tid < 64) {
       const float* kh = row + (size_t)p.nq * kD + (size_t)kvh * kD;
       const float* vh = row + (size_t)(p.nq + p.nkv) * kD + (size_t)kvh * kD;
-      const int j = tid;
-      float k1 = kh[j], k2 = kh[j + 64];
-      if (rope) {
-        const float c = cs[2 * j], s = cs[2 * j + 1];
-        const float r1 = k1 * c - k2 * s, r2 = k2 * c + k1 * s;
-        k1 = r1;
-        k2 = r2;
-      }
-      const uint16_t a = f2h(k1), bb = f2h(k2), c1 = f2h(vh[j]), c2 = f2h(vh[j + 64]);
-      knew[j] = a; knew[j + 64] = bb; vnew[j] = c1; vnew[j + 64] = c2;
-      uint16_t* kd = p.kc + kvbase + (size_t)P * kD;
-      uint16_t* vd = p.vc + kvbase + (size_t)P * kD;
-      kd[j] = a; kd[j + 64] = bb; vd[j] = c1; vd[j + 64] = c2;
+      k1 = kh[qj]; k2 = kh[qj + 64]; v1 = vh[qj]; v2 = vh[qj + 64];
     }
   } else {
-    for (int i = tid; i < g * kD; i += kThreads) {
-      const int hh = i / kD, j = i % kD;
-      const size_t qi = ((size_t)b * p.nq + (size_t)kvh * g + hh) * kD + j;
-      qs[hh][j] = p.q_f16 ? h2f(reinterpret_cast<const uint16_t*>(p.q)[qi]) : reinterpret_cast<const float*>(p.q)[qi];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < g * kD) {
+        const size_t qi = ((size_t)b * p.nq + (size_t)kvh * g + i / kD) * kD + i % kD;
+        qsa[u] = p.q_f16 ? h2f(reinterpret_cast<const uint16_t*>(p.q)[qi]) : reinterpret_cast<const float*>(p.q)[qi];
+      }
+    }
+  }
+
+  int len, P = -1;
+  if (step) {
+    P = pos_raw < 0 ? 0 : (pos_raw >= p.cap ? p.cap - 1 : pos_raw);
+    len = P + 1;
+  } else {
+    len = pos_raw < 1 ? 1 : (pos_raw > p.cap ? p.cap : pos_raw);
+  }
+  const int npos = max(0, min(s0 + S, len) - s0);
+  const bool has_new = P >= s0 && P < s0 + npos;
+
+  // ---- q (and the new k, v) into LDS -----------------------------------------------------------
+  if (step) {
+    if (qh_ < g) {
+      qs[qh_][qj] = q1 * rc - q2 * rsn;
+      qs[qh_][qj + 64] = q2 * rc + q1 * rsn;
+    }
+    if (has_new && tid < 64) {
+      const uint16_t a = f2h(k1 * rc - k2 * rsn), bb = f2h(k2 * rc + k1 * rsn), c1 = f2h(v1), c2 = f2h(v2);
+      knew[qj] = a; knew[qj + 64] = bb; vnew[qj] = c1; vnew[qj + 64] = c2;
+      uint16_t* kd = p.kc + kvbase + (size_t)P * kD;
+      uint16_t* vd = p.vc + kvbase + (size_t)P * kD;
+      kd[qj] = a; kd[qj + 64] = bb; vd[qj] = c1; vd[qj + 64] = c2;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < g * kD) qs[i / kD][i % kD] = qsa[u];
     }
   }
   __syncthreads();
-  if (P >= s0 && P < s0 + npos) {  // the new position reads the rows just written to LDS
+  if (has_new) {  // the new position reads the rows just written to LDS
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if (s0 + jw + 4 * i + pg == P) {
@@ -229,10 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
         float a = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) a = fmaf(qr[hh][t], kf[t], a);
-        a += __shfl_xor(a, 1, 64);
-        a += __shfl_xor(a, 2, 64);
-        a += __shfl_xor(a, 4, 64);
-        a += __shfl_xor(a, 8, 64);
+        a = row16_sum(a);
         if (sl == 0) sc[hh][j] = j < npos ? a * p.scale : -INFINITY;
       }
     }
@@ -280,9 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
     if (hh < g) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        float a = acc[hh][t];
-        a += __shfl_xor(a, 16, 64);
-        a += __shfl_xor(a, 32, 64);
+        const float a = rows_lanewise_sum(acc[hh][t]);
         if (pg == 0) red[w][hh][8 * sl + t] = a;
       }
     }
@@ -297,36 +237,76 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
   __syncthreads();
 
-  // ---- finish: one split writes directly; otherwise two-level merge of the split records -------
+  // ---- finish: one split writes the output; otherwise its record goes to the merge kernel -----
   if (p.nsplit == 1) {
     write_out(p, b, kvh, g, red[0], lh, tid);
     return;
   }
-  const int ngroups = (p.nsplit + kGroup - 1) / kGroup;
-  const int grp = sidx / kGroup;
-  const int gcount = min(kGroup, p.nsplit - grp * kGroup);
-  float* part1 = p.part + (size_t)bh * p.nsplit * kMaxG * kPS;
-  publish_record(part1 + (size_t)sidx * kMaxG * kPS, g, mh, lh, red[0], tid);
-  __syncthreads();
-  if (tid == 0) s_flag = arrive(&p.cnt[(size_t)bh * ngroups + grp]) == (unsigned)(gcount - 1);
-  __syncthreads();
-  if (!s_flag) return;
-  merge_parts(part1 + (size_t)grp * kGroup * kMaxG * kPS, gcount, g, ml, tid);
-  if (tid == 0) reset_counter(&p.cnt[(size_t)bh * ngroups + grp]);
-  if (ngroups == 1) {
-    write_out(p, b, kvh, g, ml.O, ml.L, tid);
-    return;
+  float* rec = p.part + ((size_t)bh * p.nsplit + sidx) * kMaxG * kPS;
+  for (int i = tid; i < g * kD; i += kThreads) {
+    const int hh = i / kD, d = i % kD;
+    rec[(size_t)hh * kPS + 4 + d] = red[0][hh][d];
   }
-  float* part2 = p.part2 + (size_t)bh * ngroups * kMaxG * kPS;
-  publish_record(part2 + (size_t)grp * kMaxG * kPS, g, ml.M, ml.L, ml.O, tid);
+  if (tid < g) {
+    rec[(size_t)tid * kPS + 0] = mh[tid];
+    rec[(size_t)tid * kPS + 1] = lh[tid];
+  }
+}
+
+// One workgroup per (sequence, query head), one thread per output dimension: combines the split
+// records with the online-softmax rescaling M = max m_s, L = sum e^(m_s-M) l_s,
+// o = sum e^(m_s-M) o_s / L, splits in a fixed order.  All loads are issued before any use.
+__global__ __launch_bounds__(kD) void k_attn_merge(AttnParams p) {
+  constexpr int kChunk = 32;           // splits whose outputs one thread holds at a time
+  __shared__ float ms_[512], ls_[512], wsc[512];
+  __shared__ float Ms, Ls;
+  const int g = p.nq / p.nkv;
+  const int bq = blockIdx.x;                 // b * nq + head
+  const int b = bq / p.nq, h = bq % p.nq;
+  const int kvh = h / g, hh = h % g;
+  const int bh = b * p.nkv + kvh;
+  const int d = threadIdx.x;
+  const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
+  const size_t stride = (size_t)kMaxG * kPS;
+  const int n = p.nsplit;
+  // issue the (m, l) loads and the first chunk of outputs together
+  for (int s = d; s < n; s += kD) {
+    ms_[s] = rec0[s * stride];
+    ls_[s] = rec0[s * stride + 1];
+  }
+  float v[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) v[u] = u < n ? rec0[u * stride + 4 + d] : 0.f;
   __syncthreads();
-  unsigned* cnt2 = p.cnt + (size_t)p.B * p.nkv * ngroups;
-  if (tid == 0) s_flag = arrive(&cnt2[bh]) == (unsigned)(ngroups - 1);
+  if (d < 64) {
+    float M = -INFINITY;
+    for (int s = d; s < n; s += 64) M = fmaxf(M, ms_[s]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s = d; s < n; s += 64) {
+      const float e = ms_[s] == -INFINITY ? 0.f : expf(ms_[s] - M);
+      wsc[s] = e;
+      L = fmaf(e, ls_[s], L);
+    }
+    L = wave_sum(L);
+    if (d == 0) { Ms = M; Ls = L; }
+  }
   __syncthreads();
-  if (!s_flag) return;
-  merge_parts(part2, ngroups, g, ml, tid);
-  if (tid == 0) reset_counter(&cnt2[bh]);
-  write_out(p, b, kvh, g, ml.O, ml.L, tid);
+  float O = 0.f;
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    if (u < n) O = fmaf(wsc[u], v[u], O);
+  for (int s0 = kChunk; s0 < n; s0 += kChunk) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) v[u] = s0 + u < n ? rec0[(s0 + u) * stride + 4 + d] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (s0 + u < n) O = fmaf(wsc[s0 + u], v[u], O);
+  }
+  const float o = O / Ls;
+  const size_t oi = ((size_t)b * p.nq + h) * kD + d;
+  if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
+  else reinterpret_cast<float*>(p.out)[oi] = o;
 }
 
 int pow2ceil(int64_t v) {
@@ -337,7 +317,8 @@ int pow2ceil(int64_t v) {
 
 }  // namespace
 
-// Split size 64/128/256 positions: aims at ~192 workgroups, at most 512 splits per sequence.
+// Split size 64/128/256 positions: aims at ~192 workgroups, at most 512 splits per sequence
+// (the merge kernel keeps one weight per split in LDS).
 void attn_plan(AttnParams& p) {
   const int64_t work = (int64_t)p.B * p.nkv * p.cap;
   int S = pow2ceil(cdiv(work, 192));
@@ -348,23 +329,13 @@ void attn_plan(AttnParams& p) {
 
 size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit) {
   (void)nq;
-  const size_t ngroups = (size_t)cdiv(nsplit, kGroup);
-  const size_t rec = (size_t)kMaxG * kPS * sizeof(float);
-  const size_t part1 = (size_t)B * nkv * nsplit * rec;
-  const size_t part2 = (size_t)B * nkv * ngroups * rec;
-  const size_t cnt = (size_t)B * nkv * (ngroups + 1) * sizeof(unsigned);
-  return align_up(part1, 256) + align_up(part2, 256) + align_up(cnt, 256);
+  return align_up((size_t)B * nkv * nsplit * kMaxG * kPS * sizeof(float), 256);
 }
 
 void attn_set_workspace(AttnParams& p, void* ws) {
-  const size_t ngroups = (size_t)cdiv(p.nsplit, kGroup);
-  const size_t rec = (size_t)kMaxG * kPS * sizeof(float);
-  const size_t part1 = (size_t)p.B * p.nkv * p.nsplit * rec;
-  const size_t part2 = (size_t)p.B * p.nkv * ngroups * rec;
-  char* c = static_cast<char*>(ws);
-  p.part = reinterpret_cast<float*>(c);
-  p.part2 = reinterpret_cast<float*>(c + align_up(part1, 256));
-  p.cnt = reinterpret_cast<unsigned*>(c + align_up(part1, 256) + align_up(part2, 256));
+  p.part = reinterpret_cast<float*>(ws);
+  p.part2 = nullptr;
+  p.cnt = nullptr;
 }
 
 hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st) {
@@ -374,6 +345,9 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
     case 128: hipLaunchKernelGGL(k_attn<4>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs); break;
     default: hipLaunchKernelGGL(k_attn<8>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3(p.B * p.nq), dim3(kD), 0, st, p);
   return hipGetLastError();
 }
 

@@ -1,27 +1,31 @@
 // int4 block-32 GEMV on the tiled layout (MatMulNBits semantics with float activations).
 //
-// One wave owns one 64-row tile and a contiguous range of kb blocks: lane i accumulates row
-// 64t+i, so every 16-byte block load of the wave is one contiguous 1 KiB line run, and the
-// activation block is the same for all lanes (wave-uniform loads).
+// One wave owns one 64-row tile and a contiguous range of kb blocks (a multiple of 8, so every
+// batch of 8 blocks shares one 16-byte scale load): lane i accumulates row 64t+i, so every
+// 16-byte block load of the wave is one contiguous 1 KiB run, and the activation block is the
+// same for all lanes (wave-uniform scalar loads).  Batches of 8 blocks are double-buffered: the
+// next batch is in flight while the current one is dequantised.
 //
 // In-register dequantisation: a packed dword holds 8 codes with the even elements in nibbles
 // 0..3 and the odd ones in nibbles 4..7, so a shift and one AND-OR with the fp16 exponent of
 // 64.0 turn nibble pair (i, 4+i) into the fp16 pair (64 + q_2i, 64 + q_2i+1), which lines up
 // with the natural fp16 pair (x_2i, x_2i+1) of the activation; v_dot2_f32_f16 then multiplies
 // both with exact products and fp32 accumulation.  The offset 64 and the zero point 8 are
-// removed once per block by subtracting C_b = 72 * sum_j x_j, computed once per wave for its
-// blocks; the block sum is scaled by the block's fp16 scale in fp32.
+// removed once per block by subtracting C_b = 72 * sum_j x_j; the block sum is scaled by the
+// block's fp16 scale in fp32.
 //
-// Split-K: the kb-block ranges of a tile are spread over the 4 waves of a workgroup (reduced in
-// LDS) and over `wpt` workgroups; the last workgroup to arrive at a tile (atomic counter) adds
-// the partials in a fixed order and runs the epilogue, so results do not depend on timing.
+// Split-K: the block ranges of a tile are spread over the 4 waves of a workgroup (reduced in
+// LDS) and, for matrices with few tiles, over `wpt` workgroups; then the last workgroup to
+// arrive at a tile adds the partials in a fixed order and runs the epilogue, so results do not
+// depend on timing.  With wpt = 1 the workgroup finishes its tile directly.
 #include "vv_internal.h"
 
 namespace vv {
 namespace {
 
 constexpr int kWavesPerWG = 4;
-constexpr int kTargetWaves = 4096;
+constexpr int kBatch = 8;        // blocks per load batch (one scale group)
+constexpr int kFillWGs = 256;    // workgroups wanted for a full chip
 
 // A VGPR holding a constant, opaque to the optimiser: lets (d & mask) | magic become one
 // v_and_or_b32 (mask in an SGPR, magic in a VGPR; the GFX9 VOP3 encoding takes no literal).
@@ -55,6 +59,7 @@ __device__ __forceinline__ float corr_quarter(u32x4 xv) {
   return c;
 }
 
+// scale j (compile-time 0..7) of a group of 8 fp16 scales
 __device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
   const uint32_t d = (j >> 1) == 0 ? s.x : (j >> 1) == 1 ? s.y : (j >> 1) == 2 ? s.z : s.w;
   return (j & 1) ? (float)__builtin_bit_cast(h2_t, d).y : (float)__builtin_bit_cast(h2_t, d).x;
@@ -62,61 +67,144 @@ __device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Epilogue for one tile's finished row sums (called by one wave, lane = row within the tile).
+// One batch of up to 8 blocks in flight: packed blocks, their scale group, and the activation
+// quarters for the per-block corrections (lane 4i+q holds quarter q of block i, lanes < 32).
 template <int MT>
-__device__ void epilogue(const GemvParams& p, int unit, const float (&tot)[2][MT], int lane) {
+struct Batch {
+  u32x4 w[kBatch];
+  u32x4 s;
+  u32x4 xq[MT];
+};
+
+template <int MT>
+__device__ __forceinline__ void load_batch(Batch<MT>& B, const u32x4* qp, const u32x4* sp, const uint16_t* x,
+                                           int K, int M, int bb, int nb_here, int lane) {
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i)
+    if (i < nb_here) B.w[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
+  B.s = __builtin_nontemporal_load(sp);
+  const int bl = lane >> 2, qd = lane & 3;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    B.xq[m] = u32x4{0, 0, 0, 0};
+    if (m < M && bl < nb_here)
+      B.xq[m] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + (size_t)(bb + bl) * kBlock + qd * 8);
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void compute_batch(const Batch<MT>& B, const uint16_t* __restrict__ x, int K, int M,
+                                              int bb, int nb_here, uint32_t m64, float (&acc)[MT]) {
+  float corr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    corr[m] = quad_sum(corr_quarter(B.xq[m]));
+  }
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    if (i < nb_here) {
+      const float sc = pick_scale(B.s, i);
+      const uint32_t d[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + (size_t)m * K + (size_t)(bb + i) * kBlock);
+          float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) t = dot8_pairs(d[k], xb + 4 * k, t, m64);
+          acc[m] = fmaf(sc, t, acc[m]);
+        }
+      }
+    }
+  }
+}
+
+// Operands of the epilogue, loaded by wave 0 of every workgroup before the weight stream so the
+// workgroup that finishes a tile does not wait on them.
+template <int MT>
+struct EpiPre {
+  float rs[MT];     // 1/sqrt(mean(h^2) + eps) of the input rows (or 1)
+  float bias;       // bias of this lane's row (EPI_STORE)
+  float gam;        // gamma of this lane's row (EPI_RESID)
+  float h[MT];      // residual of this lane's row (EPI_RESID)
+};
+
+// row of lane `lane` of tile `tile` in the output vector (EPI_SILU: lanes 0-31 gate, 32-63 up
+// of the same 32 rows)
+__device__ __forceinline__ int out_row(const GemvParams& p, int tile, int lane) {
+  return p.epi == EPI_SILU ? tile * 32 + (lane & 31) : tile * kTileRows + lane;
+}
+
+template <int MT>
+__device__ __forceinline__ void epi_prefetch(const GemvParams& p, int tile, int lane, EpiPre<MT>& e,
+                                             float (&rsp)[MT]) {
+  const int n = out_row(p, tile, lane);
+  const bool ok = n < p.N;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    rsp[m] = 0.f;
+    e.h[m] = 0.f;
+    if (m < p.M && p.rs_parts && lane < p.rs_nparts) rsp[m] = p.rs_parts[m * p.rs_nparts + lane];
+    if (m < p.M && p.epi == EPI_RESID && ok) e.h[m] = p.h[(size_t)m * p.N + n];
+  }
+  e.bias = (p.epi == EPI_STORE && ok && p.bias) ? h2f(p.bias[n]) : 0.f;
+  e.gam = (p.epi == EPI_RESID && ok && p.gamma) ? h2f(p.gamma[n]) : 0.f;
+}
+
+// rstd from the per-tile sums of squares (lane l holds part l; fixed reduction tree)
+template <int MT>
+__device__ __forceinline__ void epi_finish_rs(const GemvParams& p, EpiPre<MT>& e, const float (&rsp)[MT]) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m) e.rs[m] = p.rs_parts ? 1.0f / sqrtf(wave_sum(rsp[m]) * p.rs_inv_n + p.eps) : 1.f;
+}
+
+// Epilogue for one tile's finished row sums (one wave, lane = row within the tile).
+template <int MT>
+__device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], const EpiPre<MT>& e, int lane) {
   const int M = p.M;
+  const int n = out_row(p, tile, lane);
+  const bool ok = n < p.N;
   if (p.epi == EPI_STORE) {
-    const int n = unit * kTileRows + lane;
-    const bool ok = n < p.N;
-    const float bias = (ok && p.bias) ? h2f(p.bias[n]) : 0.f;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
-      const float rs = p.rs_parts ? rstd_from_parts(p.rs_parts + m * p.rs_nparts, p.rs_nparts, p.rs_inv_n, p.eps) : 1.f;
-      const float v = tot[0][m] * rs + bias;
+      const float v = tot[m] * e.rs[m] + e.bias;
       if (ok) {
         if (p.y_f16) reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.ldy + n] = f2h(v);
         else reinterpret_cast<float*>(p.y)[(size_t)m * p.ldy + n] = v;
       }
     }
   } else if (p.epi == EPI_RESID) {
-    const int n = unit * kTileRows + lane;
-    const bool ok = n < p.N;
-    const float gam = (ok && p.gamma) ? h2f(p.gamma[n]) : 0.f;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
       float hn = 0.f;
       if (ok) {
         const size_t i = (size_t)m * p.N + n;
-        hn = p.h[i] + tot[0][m];
+        hn = e.h[m] + tot[m];
         p.h[i] = hn;
         if (p.trace) p.trace[i] = hn;
         if (p.gamma) {
-          const float gv = gam * hn;
+          const float gv = e.gam * hn;
           if (p.g_out) p.g_out[i] = f2h(gv);
           if (p.gf_out) p.gf_out[i] = gv;
         }
       }
       const float ss = wave_sum(hn * hn);
-      if (p.sumsq_out && lane == 0) p.sumsq_out[m * p.ntiles + unit] = ss;
+      if (p.sumsq_out && lane == 0) p.sumsq_out[m * p.ntiles + tile] = ss;
     }
-  } else {  // EPI_SILU: unit j = (gate tile 2j, up tile 2j+1)
-    const int n = unit * kTileRows + lane;
-    const bool ok = n < p.N;
+  } else {  // EPI_SILU: lane i < 32 holds the gate row, lane i + 32 the up row of the same output
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
-      const float rs = p.rs_parts ? rstd_from_parts(p.rs_parts + m * p.rs_nparts, p.rs_nparts, p.rs_inv_n, p.eps) : 1.f;
-      const float g = tot[0][m] * rs;
-      const float u = tot[1][m] * rs;
-      if (ok) p.act[(size_t)m * p.N + n] = f2h(silu(g) * u);
+      const float g = tot[m] * e.rs[m];
+      const float u = __shfl(tot[m], (lane & 31) + 32, kWave) * e.rs[m];
+      if (ok && lane < 32) p.act[(size_t)m * p.N + n] = f2h(silu(g) * u);
     }
   }
 }
 
-template <int MT, int KBMAX>
+template <int MT>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                               const uint4* __restrict__ sw, const uint16_t* __restrict__ x) {
   __shared__ float red[kWavesPerWG][MT][kTileRows];
@@ -131,67 +219,36 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
   const int kg = L % p.wpt;
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
-  const int b0 = (kg * kWavesPerWG + w) * p.kb;
+  const int b0 = (kg * kWavesPerWG + w) * p.kb;  // multiple of 8
   int nblk = nb - b0;
   nblk = nblk < 0 ? 0 : (nblk > p.kb ? p.kb : nblk);
+  const int nbt = (nblk + kBatch - 1) / kBatch;
 
-  // activation quarters for the per-block correction C_b (lane 4i+q: quarter q of block b0+i)
-  u32x4 xq[MT];
-  {
-    const int bl = lane >> 2, qd = lane & 3;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      xq[m] = u32x4{0, 0, 0, 0};
-      if (m < M && bl < nblk)
-        xq[m] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + (size_t)(b0 + bl) * kBlock + qd * 8);
-    }
-  }
+  EpiPre<MT> ep;
+  float rsp[MT];
+  if (w == 0) epi_prefetch<MT>(p, tile, lane, ep, rsp);
 
-  // weights and scales of this wave: all loads issued before any use
-  u32x4 wv[KBMAX];
   const u32x4* qp = reinterpret_cast<const u32x4*>(qw) + ((size_t)tile * nb + b0) * kTileRows + lane;
-#pragma unroll
-  for (int i = 0; i < KBMAX; ++i)
-    if (i < nblk) wv[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
-  constexpr int SG = KBMAX / 8;  // b0 is a multiple of 8: block i of the wave is scale (i/8, i%8)
-  u32x4 sv[SG];
-  const int g0 = b0 >> 3;
-  const u32x4* sp = reinterpret_cast<const u32x4*>(sw) + ((size_t)tile * ng + g0) * kTileRows + lane;
-#pragma unroll
-  for (int j = 0; j < SG; ++j)
-    if (8 * j < nblk) sv[j] = __builtin_nontemporal_load(sp + (size_t)j * kTileRows);
+  const u32x4* sp = reinterpret_cast<const u32x4*>(sw) + ((size_t)tile * ng + (b0 >> 3)) * kTileRows + lane;
   const uint32_t m64 = vconst(0x54005400u);
-
-  float corr[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    float c = corr_quarter(xq[m]);
-    c += __shfl_xor(c, 1, kWave);
-    c += __shfl_xor(c, 2, kWave);
-    corr[m] = c;
-  }
-
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 
-#pragma unroll
-  for (int i = 0; i < KBMAX; ++i) {
-    if (i < nblk) {
-      const int b = b0 + i;
-      const float sc = pick_scale(sv[i / 8], i % 8);
-      const u32x4 q4 = wv[i];
-      const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + (size_t)m * K + (size_t)b * kBlock);
-          float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) t = dot8_pairs(d[k], xb + 4 * k, t, m64);
-          acc[m] = fmaf(sc, t, acc[m]);
-        }
-      }
+  Batch<MT> A, B;
+  if (nbt > 0) load_batch<MT>(A, qp, sp, x, K, M, b0, min(kBatch, nblk), lane);
+  for (int bt = 0; bt < nbt; bt += 2) {
+    const int bbA = b0 + bt * kBatch;
+    const bool hasB = bt + 1 < nbt;
+    if (hasB)
+      load_batch<MT>(B, qp + (size_t)(bt + 1) * kBatch * kTileRows, sp + (size_t)(bt + 1) * kTileRows, x, K, M,
+                     bbA + kBatch, min(kBatch, nblk - (bt + 1) * kBatch), lane);
+    compute_batch<MT>(A, x, K, M, bbA, min(kBatch, nblk - bt * kBatch), m64, acc);
+    if (hasB) {
+      if (bt + 2 < nbt)
+        load_batch<MT>(A, qp + (size_t)(bt + 2) * kBatch * kTileRows, sp + (size_t)(bt + 2) * kTileRows, x, K, M,
+                       bbA + 2 * kBatch, min(kBatch, nblk - (bt + 2) * kBatch), lane);
+      compute_batch<MT>(B, x, K, M, bbA + kBatch, min(kBatch, nblk - (bt + 1) * kBatch), m64, acc);
     }
   }
 
@@ -200,75 +257,57 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
     if (m < M) red[w][m][lane] = acc[m];
   __syncthreads();
   if (w != 0) return;
+  epi_finish_rs<MT>(p, ep, rsp);
 
-  float tot[2][MT];
+  float tot[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    tot[0][m] = 0.f;
-    tot[1][m] = 0.f;
-    if (m < M) tot[0][m] = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
+    tot[m] = 0.f;
+    if (m < M) tot[m] = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
   }
-
-  if (p.wpt == 1 && p.unit_tiles == 1) {
-    epilogue<MT>(p, tile, tot, lane);
+  if (p.wpt == 1) {
+    epilogue<MT>(p, tile, tot, ep, lane);
     return;
   }
-  // publish this workgroup's partial, then count arrivals for the unit
+  // publish this workgroup's partial, then count arrivals at the tile
   float* my = p.part + ((size_t)tile * p.wpt + kg) * MT * kTileRows;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
-    if (m < M) publish_f32(&my[m * kTileRows + lane], tot[0][m]);
+    if (m < M) publish_f32(&my[m * kTileRows + lane], tot[m]);
   wait_published();
-  const int unit = tile / p.unit_tiles;
   unsigned prev = 0;
-  if (lane == 0) prev = arrive(&p.cnt[unit]);
+  if (lane == 0) prev = arrive(&p.cnt[tile]);
   prev = __shfl(prev, 0, kWave);
-  const unsigned arrivals = (unsigned)(p.wpt * p.unit_tiles);
-  if (prev != arrivals - 1) return;
+  if (prev != (unsigned)(p.wpt - 1)) return;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (u >= p.unit_tiles) continue;
-    const int t = unit * p.unit_tiles + u;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= M) continue;
-      float s = 0.f;
-      for (int k = 0; k < p.wpt; ++k)
-        s += collect_f32(p.part + (((size_t)t * p.wpt + k) * MT + m) * kTileRows + lane);
-      tot[u][m] = s;
-    }
+  for (int m = 0; m < MT; ++m) {
+    if (m >= M) continue;
+    float s = 0.f;
+    for (int k = 0; k < p.wpt; ++k) s += collect_f32(p.part + (((size_t)tile * p.wpt + k) * MT + m) * kTileRows + lane);
+    tot[m] = s;
   }
-  if (lane == 0) reset_counter(&p.cnt[unit]);  // ready for the next launch
-  epilogue<MT>(p, unit, tot, lane);
+  if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
+  epilogue<MT>(p, tile, tot, ep, lane);
 }
 
 int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
 struct Plan { int kb, wpt, grid; };
 
-// Blocks per wave: 8 or 16 (ranges start on scale-group boundaries), 16 only when the matrix
-// offers more than kTargetWaves waves of 8 blocks.
+// wpt (workgroups per tile): the fewest that give ~kFillWGs workgroups, bounded by one batch of
+// 8 blocks per wave; kb = the blocks each wave takes, a multiple of 8.
 Plan make_plan(int M, int ntiles, int nb) {
   (void)M;
-  const int kb = (int64_t)ntiles * cdiv(nb, 8) > kTargetWaves ? 16 : 8;
-  const int nkc = (int)cdiv(nb, kb);
-  const int wpt = (int)cdiv(nkc, kWavesPerWG);
+  const int nb8 = (int)cdiv(nb, kBatch);
+  int wpt = (int)cdiv(kFillWGs, ntiles);
+  const int wmax = (int)cdiv(nb8, kWavesPerWG);
+  wpt = wpt < 1 ? 1 : (wpt > wmax ? wmax : wpt);
+  const int gpw = (int)cdiv(nb8, (int64_t)kWavesPerWG * wpt);
   Plan pl;
-  pl.kb = kb;
+  pl.kb = gpw * kBatch;
   pl.wpt = wpt;
   pl.grid = (int)(cdiv((int64_t)ntiles * wpt, kNumXcd) * kNumXcd);
   return pl;
-}
-
-template <int MT>
-hipError_t launch_mt(const GemvParams& p, hipStream_t st) {
-  const uint4* q = reinterpret_cast<const uint4*>(p.q);
-  const uint4* s = reinterpret_cast<const uint4*>(p.s);
-  if (p.kb <= 8)
-    hipLaunchKernelGGL((k_gemv<MT, 8>), dim3(p.grid), dim3(256), 0, st, p, q, s, p.x);
-  else
-    hipLaunchKernelGGL((k_gemv<MT, 16>), dim3(p.grid), dim3(256), 0, st, p, q, s, p.x);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -280,11 +319,11 @@ void gemv_plan(GemvParams& p) {
   p.grid = pl.grid;
 }
 
-size_t gemv_workspace_bytes(int M, int ntiles, int unit_tiles, int nb) {
+size_t gemv_workspace_bytes(int M, int ntiles, int nb) {
   const Plan pl = make_plan(M, ntiles, nb);
   const int MT = mt_of(M);
   const size_t part = (size_t)ntiles * pl.wpt * MT * kTileRows * sizeof(float);
-  const size_t cnt = (size_t)cdiv(ntiles, unit_tiles) * sizeof(unsigned);
+  const size_t cnt = (size_t)ntiles * sizeof(unsigned);
   return align_up(part, 256) + align_up(cnt, 256);
 }
 
@@ -297,13 +336,16 @@ void gemv_set_workspace(GemvParams& p, void* ws) {
 }
 
 hipError_t gemv_launch(const GemvParams& p, hipStream_t st) {
+  const uint4* q = reinterpret_cast<const uint4*>(p.q);
+  const uint4* s = reinterpret_cast<const uint4*>(p.s);
   switch (mt_of(p.M)) {
-    case 1: return launch_mt<1>(p, st);
-    case 2: return launch_mt<2>(p, st);
-    case 4: return launch_mt<4>(p, st);
-    case 8: return launch_mt<8>(p, st);
-    default: return launch_mt<16>(p, st);
+    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
+    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
+    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
+    case 8: hipLaunchKernelGGL(k_gemv<8>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
+    default: hipLaunchKernelGGL(k_gemv<16>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
   }
+  return hipGetLastError();
 }
 
 }  // namespace vv
@@ -314,7 +356,7 @@ extern "C" {
 
 size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || M > 16 || N < 1 || K < kBlock || K % kBlock) return 0;
-  return gemv_workspace_bytes((int)M, (int)cdiv(N, kTileRows), 1, (int)(K / kBlock));
+  return gemv_workspace_bytes((int)M, (int)cdiv(N, kTileRows), (int)(K / kBlock));
 }
 
 int vv_gemv_int4(const uint8_t* packed, const uint16_t* scales, const uint16_t* bias, const uint16_t* x, int64_t M,
@@ -335,7 +377,6 @@ int vv_gemv_int4(const uint8_t* packed, const uint16_t* scales, const uint16_t* 
   p.q = packed; p.s = scales; p.x = x;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.ntiles = (int)cdiv(N, kTileRows);
-  p.unit_tiles = 1;
   p.epi = EPI_STORE;
   p.bias = bias; p.y = y; p.y_f16 = y_dtype == VV_F16; p.ldy = (int)N;
   p.eps = 0.f;

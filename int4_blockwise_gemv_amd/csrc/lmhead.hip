@@ -42,8 +42,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
       rs[t] = 1.f;
-      if (t < nbt && p.rs_parts)
-        rs[t] = rstd_from_parts(p.rs_parts + (size_t)(bb + t) * p.rs_nparts, p.rs_nparts, p.rs_inv_n, p.eps);
+      if (t < nbt && p.rs_parts) {  // lane l adds part l (at most 64 parts), fixed reduction tree
+        const float v = lane < p.rs_nparts ? p.rs_parts[(size_t)(bb + t) * p.rs_nparts + lane] : 0.f;
+        rs[t] = 1.0f / sqrtf(wave_sum(v) * p.rs_inv_n + p.eps);
+      }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;

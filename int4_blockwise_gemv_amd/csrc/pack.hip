@@ -125,11 +125,18 @@ __global__ void k_mean_finalize(const unsigned long long* __restrict__ bins, uns
   *s16_out = f64_to_f16_rne(m);
 }
 
+// Destination placement: source row r goes to destination row
+//   (r / row_group) * group_stride + row_offset + r % row_group
+// (tiled layout: tile = row / 64, lane = row % 64).
 struct Dst {
   int layout;
-  int64_t tile_offset, tile_stride;
+  int64_t row_group, group_stride, row_offset;
   int nb, ng;
 };
+
+__device__ __forceinline__ int64_t dst_row(const Dst& D, int64_t r) {
+  return (r / D.row_group) * D.group_stride + D.row_offset + (r % D.row_group);
+}
 
 // 32 codes (low nibble of each byte of c[]) -> 4 dwords in the destination layout
 __device__ __forceinline__ uint4 encode_block(const uint8_t* c, int layout) {
@@ -171,17 +178,17 @@ __device__ __forceinline__ void decode_block(uint4 q, int layout, uint8_t* c) {
 
 __device__ __forceinline__ size_t nib_index(const Dst& D, int64_t r, int b, int64_t nrows) {
   if (D.layout == VV_LAYOUT_ROWMAJOR) return (size_t)(r * D.nb + b);  // in 16-B units
-  const int64_t t = (r / kTileRows) * D.tile_stride + D.tile_offset;
-  return (size_t)((t * D.nb + b) * kTileRows + (r % kTileRows));
+  const int64_t d = dst_row(D, r);
+  return (size_t)(((d / kTileRows) * D.nb + b) * kTileRows + (d % kTileRows));
 }
 __device__ __forceinline__ size_t scale_index(const Dst& D, int64_t r, int b) {
   if (D.layout == VV_LAYOUT_ROWMAJOR) return (size_t)(r * D.nb + b);
-  const int64_t t = (r / kTileRows) * D.tile_stride + D.tile_offset;
-  return (size_t)(((t * D.ng + b / 8) * kTileRows + (r % kTileRows)) * 8 + (b % 8));
+  const int64_t d = dst_row(D, r);
+  return (size_t)((((d / kTileRows) * D.ng + b / 8) * kTileRows + (d % kTileRows)) * 8 + (b % 8));
 }
 
-// One thread per (row, block-slot).  Rows run to the end of the last tile for the tiled layout
-// (padding rows get code 8 and scale 0); block slots run to ng*8 (scale padding 0).
+// One thread per (row, block-slot).  For the tiled layout, rows run to the end of the last row
+// group (padding rows get code 8 and scale 0) and block slots to ng*8 (scale padding 0).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_quant(const float* __restrict__ W, int64_t N, int K, int64_t nrows,
                                                int nslots, Dst D, const double* __restrict__ mptr,
@@ -285,12 +292,15 @@ int check_common(const void* W, int64_t N, int64_t K, const char* fn) {
   return VV_OK;
 }
 
-int check_tiles(int64_t N, int64_t tile_offset, int64_t tile_stride, int64_t dst_tiles, const char* fn) {
-  VV_REQUIRE(tile_stride >= 1 && tile_offset >= 0 && dst_tiles >= 1, VV_ERR_RANGE,
-             "%s: tile_offset/tile_stride/dst_tiles out of range", fn);
-  const int64_t last = (cdiv(N, kTileRows) - 1) * tile_stride + tile_offset;
-  VV_REQUIRE(last < dst_tiles, VV_ERR_RANGE, "%s: source rows reach tile %lld >= dst_tiles %lld", fn,
-             (long long)last, (long long)dst_tiles);
+int check_place(int64_t N, int64_t row_group, int64_t group_stride, int64_t row_offset, int64_t dst_rows,
+                const char* fn) {
+  VV_REQUIRE(row_group >= 1 && group_stride >= row_group && row_offset >= 0, VV_ERR_RANGE,
+             "%s: need row_group >= 1, group_stride >= row_group, row_offset >= 0", fn);
+  VV_REQUIRE(dst_rows >= 1 && dst_rows % kTileRows == 0, VV_ERR_RANGE, "%s: dst_rows must be a positive multiple of 64",
+             fn);
+  const int64_t last = (cdiv(N, row_group) - 1) * group_stride + row_offset + row_group - 1;
+  VV_REQUIRE(last < dst_rows, VV_ERR_RANGE, "%s: source rows reach destination row %lld >= dst_rows %lld", fn,
+             (long long)last, (long long)dst_rows);
   return VV_OK;
 }
 
@@ -304,7 +314,7 @@ int pack_impl(const float* W, int64_t N, int64_t K, int mode, Dst D, uint8_t* pa
              VV_ERR_RANGE, "%s: W and packed must be 16-byte aligned", fn);
   const size_t need = vv_pack_int4_workspace(N, K, mode);
   if (need) VV_REQUIRE(ws && ws_bytes >= need, VV_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  const int64_t nrows = D.layout == VV_LAYOUT_TILED ? cdiv(N, kTileRows) * kTileRows : N;
+  const int64_t nrows = D.layout == VV_LAYOUT_TILED ? cdiv(N, D.row_group) * D.row_group : N;
   const int nslots = D.layout == VV_LAYOUT_TILED ? D.ng * 8 : D.nb;
   const int64_t total = nrows * nslots;
   const int grid = (int)cdiv(total, 256);
@@ -344,35 +354,35 @@ size_t vv_pack_int4_workspace(int64_t N, int64_t K, int mode) {
 int vv_pack_int4(const float* W, int64_t N, int64_t K, int mode, uint8_t* packed, uint16_t* scales, void* ws,
                  size_t ws_bytes, void* stream) {
   clear_error();
-  Dst D{VV_LAYOUT_ROWMAJOR, 0, 1, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
+  Dst D{VV_LAYOUT_ROWMAJOR, N, N, 0, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
   return pack_impl(W, N, K, mode, D, packed, scales, ws, ws_bytes, as_stream(stream), "vv_pack_int4");
 }
 
-int vv_pack_int4_tiled(const float* W, int64_t N, int64_t K, int mode, int64_t tile_offset, int64_t tile_stride,
-                       int64_t dst_tiles, uint8_t* packed, uint16_t* scales, void* ws, size_t ws_bytes,
-                       void* stream) {
+int vv_pack_int4_tiled(const float* W, int64_t N, int64_t K, int mode, int64_t row_group, int64_t group_stride,
+                       int64_t row_offset, int64_t dst_rows, uint8_t* packed, uint16_t* scales, void* ws,
+                       size_t ws_bytes, void* stream) {
   clear_error();
   int rc = check_common(W, N, K, "vv_pack_int4_tiled");
   if (rc) return rc;
-  rc = check_tiles(N, tile_offset, tile_stride, dst_tiles, "vv_pack_int4_tiled");
+  rc = check_place(N, row_group, group_stride, row_offset, dst_rows, "vv_pack_int4_tiled");
   if (rc) return rc;
-  Dst D{VV_LAYOUT_TILED, tile_offset, tile_stride, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
+  Dst D{VV_LAYOUT_TILED, row_group, group_stride, row_offset, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
   return pack_impl(W, N, K, mode, D, packed, scales, ws, ws_bytes, as_stream(stream), "vv_pack_int4_tiled");
 }
 
-int vv_repack_int4_tiled(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t tile_offset,
-                         int64_t tile_stride, int64_t dst_tiles, uint8_t* tiled, uint16_t* tiled_scales,
-                         void* stream) {
+int vv_repack_int4_tiled(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t row_group,
+                         int64_t group_stride, int64_t row_offset, int64_t dst_rows, uint8_t* tiled,
+                         uint16_t* tiled_scales, void* stream) {
   clear_error();
   int rc = check_common(packed, N, K, "vv_repack_int4_tiled");
   if (rc) return rc;
   VV_REQUIRE(scales && tiled && tiled_scales, VV_ERR_NULL, "vv_repack_int4_tiled: NULL pointer");
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(tiled)) & 15) == 0,
              VV_ERR_RANGE, "vv_repack_int4_tiled: packed buffers must be 16-byte aligned");
-  rc = check_tiles(N, tile_offset, tile_stride, dst_tiles, "vv_repack_int4_tiled");
+  rc = check_place(N, row_group, group_stride, row_offset, dst_rows, "vv_repack_int4_tiled");
   if (rc) return rc;
-  Dst D{VV_LAYOUT_TILED, tile_offset, tile_stride, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
-  const int64_t nrows = cdiv(N, kTileRows) * kTileRows;
+  Dst D{VV_LAYOUT_TILED, row_group, group_stride, row_offset, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
+  const int64_t nrows = cdiv(N, row_group) * row_group;
   const int nslots = D.ng * 8;
   hipLaunchKernelGGL(k_repack, dim3((unsigned)cdiv(nrows * nslots, 256)), dim3(256), 0, as_stream(stream),
                      reinterpret_cast<const uint4*>(packed), scales, N, nrows, nslots, D,
@@ -391,7 +401,7 @@ int vv_dequant_int4(const uint8_t* packed, const uint16_t* scales, int64_t N, in
              "vv_dequant_int4: unknown layout %d", layout);
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(W)) & 15) == 0, VV_ERR_RANGE,
              "vv_dequant_int4: packed and W must be 16-byte aligned");
-  Dst D{layout, 0, 1, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
+  Dst D{layout, kTileRows, kTileRows, 0, (int)(K / kBlock), (int)cdiv(K / kBlock, 8)};
   hipLaunchKernelGGL(k_dequant, dim3((unsigned)cdiv(N * D.nb, 256)), dim3(256), 0, as_stream(stream),
                      reinterpret_cast<const uint4*>(packed), scales, N, D, W);
   VV_HIP(hipGetLastError());

@@ -82,10 +82,10 @@ Layout layout_of(const Dims& d) {
   l.act = take((size_t)d.B * d.I * 2);
   l.sumsq = take((size_t)d.B * d.ntH * 4);
   l.rope = take((size_t)d.B * 64 * 2 * 4);
-  l.ws_qkv = take(gemv_workspace_bytes(d.B, (int)cdiv(d.nqkv, kTileRows), 1, d.H / kBlock));
-  l.ws_o = take(gemv_workspace_bytes(d.B, d.ntH, 1, d.nq * kHeadDim / kBlock));
-  l.ws_gu = take(gemv_workspace_bytes(d.B, 2 * d.ntI, 2, d.H / kBlock));
-  l.ws_down = take(gemv_workspace_bytes(d.B, d.ntH, 1, d.I / kBlock));
+  l.ws_qkv = take(gemv_workspace_bytes(d.B, (int)cdiv(d.nqkv, kTileRows), d.H / kBlock));
+  l.ws_o = take(gemv_workspace_bytes(d.B, d.ntH, d.nq * kHeadDim / kBlock));
+  l.ws_gu = take(gemv_workspace_bytes(d.B, 2 * d.ntI, d.H / kBlock));
+  l.ws_down = take(gemv_workspace_bytes(d.B, d.ntH, d.I / kBlock));
   AttnParams ap{};
   ap.B = d.B; ap.nq = d.nq; ap.nkv = d.nkv; ap.cap = d.cap;
   attn_plan(ap);
@@ -173,7 +173,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       GemvParams p{};
       p.q = y.qkv_q; p.s = y.qkv_s; p.x = g;
       p.M = B; p.N = d.nqkv; p.K = H;
-      p.ntiles = (int)cdiv(d.nqkv, kTileRows); p.unit_tiles = 1;
+      p.ntiles = (int)cdiv(d.nqkv, kTileRows);
       p.epi = EPI_STORE; p.bias = y.qkv_bias; p.y = qkv; p.y_f16 = 0; p.ldy = d.nqkv;
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
@@ -197,18 +197,18 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       GemvParams p{};
       p.q = y.o_q; p.s = y.o_s; p.x = o;
       p.M = B; p.N = H; p.K = d.nq * kHeadDim;
-      p.ntiles = d.ntH; p.unit_tiles = 1;
+      p.ntiles = d.ntH;
       p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.sumsq_out = sumsq;
       gemv_plan(p);
       gemv_set_workspace(p, ws + lay.ws_o);
       VV_HIP(mark());
       VV_HIP(gemv_launch(p, st));
     }
-    {  // gate/up (tile-interleaved) + SiLU(gate) * up, RMSNorm_2 folded in
+    {  // gate/up (32 gate + 32 up rows per tile) + SiLU(gate) * up, RMSNorm_2 folded in
       GemvParams p{};
       p.q = y.gu_q; p.s = y.gu_s; p.x = g;
       p.M = B; p.N = d.I; p.K = H;
-      p.ntiles = 2 * d.ntI; p.unit_tiles = 2;
+      p.ntiles = 2 * d.ntI;
       p.epi = EPI_SILU; p.act = act;
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
@@ -221,7 +221,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       GemvParams p{};
       p.q = y.down_q; p.s = y.down_s; p.x = act;
       p.M = B; p.N = H; p.K = d.I;
-      p.ntiles = d.ntH; p.unit_tiles = 1;
+      p.ntiles = d.ntH;
       p.epi = EPI_RESID; p.h = h;
       p.gamma = last ? m->gf : m->layers[l + 1].g1;
       p.g_out = last ? nullptr : g;

@@ -52,15 +52,54 @@ __device__ __forceinline__ uint32_t wave_id() {
 }
 __device__ __forceinline__ uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Cross-lane reductions with DPP (VALU-latency data movement, no LDS round trip).  Every lane
+// of the wave must be active.  The reduction trees are fixed, so results are reproducible.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over each group of 4 lanes (every lane gets its group's sum)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// sum / max over each row of 16 lanes (every lane gets its row's result)
+__device__ __forceinline__ float row16_sum(float v) {
+  v = quad_sum(v);
+  v += dpp_f<0x141>(v);  // row_half_mirror: pairs the two quads of each half-row
+  v += dpp_f<0x140>(v);  // row_mirror: pairs the two half-rows
   return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+// lane-wise sum over the 4 rows of the wave (every lane l gets sum_r v[16r + l%16])
+__device__ __forceinline__ float rows_lanewise_sum(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+// sum / max over the whole wave (uniform result)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Monotone key for a float: larger float -> larger key; NaN maps below every number.
@@ -104,13 +143,6 @@ __device__ __forceinline__ void reset_counter(unsigned* c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// rstd = 1/sqrt(sum/n + eps) from per-tile partial sums (fixed summation order)
-__device__ __forceinline__ float rstd_from_parts(const float* parts, int nparts, float inv_n, float eps) {
-  float s = 0.f;
-  for (int i = 0; i < nparts; ++i) s += parts[i];
-  return 1.0f / sqrtf(s * inv_n + eps);
-}
-
 // ---------------------------------------------------------------------------------------------
 // internal launchers used by the decode step (enqueue only; arguments already validated)
 // ---------------------------------------------------------------------------------------------
@@ -120,9 +152,8 @@ struct GemvParams {
   const uint8_t* q;          // tiled nibbles
   const uint16_t* s;         // tiled scales
   const uint16_t* x;         // fp16 [M][K]
-  int M, N, K;               // N valid rows (for EPI_SILU: rows of gate = rows of up)
+  int M, N, K;               // N valid output rows (EPI_SILU: rows of gate = rows of up)
   int ntiles;                // tiles in the matrix
-  int unit_tiles;            // 1, or 2 for gate/up pairs (EPI_SILU)
   float* part;               // workspace partials
   unsigned* cnt;             // workspace counters
   int kb, wpt, grid;         // decomposition (filled by gemv_plan)
@@ -144,7 +175,7 @@ struct GemvParams {
 };
 
 void gemv_plan(GemvParams& p);                       // fills kb/wpt/grid
-size_t gemv_workspace_bytes(int M, int ntiles, int unit_tiles, int nb);
+size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
 hipError_t gemv_launch(const GemvParams& p, hipStream_t st);
 

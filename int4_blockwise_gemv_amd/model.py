@@ -1,8 +1,9 @@
 """Device-side model and state for the decode step, built from seeded fp32 masters.
 
 Orchestration only: the masters are uploaded and packed on the GPU by vv_pack_int4_tiled into
-the fused layouts the decode step reads (q|k|v rows in one tiled matrix, gate/up tiles
-interleaved), and the ctypes structs of include/vv.h are filled with the device pointers.
+the fused layouts the decode step reads (q|k|v rows in one tiled matrix; each gate/up tile holds
+32 gate rows and the same 32 up rows), and the ctypes structs of include/vv.h are filled with the
+device pointers.
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ def _dev_u16(a: np.ndarray, device):
 
 
 class TiledMatrix:
-    """A tiled int4 buffer holding one or more projections as row ranges."""
+    """A tiled int4 buffer holding one or more projections (placed by row groups)."""
 
     def __init__(self, tiles: int, K: int, device):
         import torch
@@ -37,8 +38,8 @@ class TiledMatrix:
         self.q = torch.empty(vv.packed_bytes(rows, K, vv.VV_LAYOUT_TILED), dtype=torch.uint8, device=device)
         self.s = torch.empty(vv.scale_bytes(rows, K, vv.VV_LAYOUT_TILED) // 2, dtype=torch.int16, device=device)
 
-    def pack(self, W_dev, mode: str, tile_offset: int, tile_stride: int, ws):
-        vv.pack_int4_tiled(W_dev, mode, tile_offset, tile_stride, self.tiles, self.q, self.s, ws)
+    def pack(self, W_dev, mode: str, row_offset: int, ws, row_group: int = TILE, group_stride: int = TILE):
+        vv.pack_int4_tiled(W_dev, mode, row_group, group_stride, row_offset, self.tiles * TILE, self.q, self.s, ws)
 
 
 @dataclass
@@ -76,13 +77,14 @@ class DeviceModel:
             L = DeviceLayer(qkv=TiledMatrix(nqkv // TILE, H, device), o=TiledMatrix(H // TILE, nq_rows, device),
                             gu=TiledMatrix(2 * (I // TILE), H, device), down=TiledMatrix(H // TILE, I, device),
                             bias=None, g1=_dev_u16(sm["g1"], device), g2=_dev_u16(sm["g2"], device))
-            L.qkv.pack(dev["q"], shape.mode, 0, 1, ws)
-            L.qkv.pack(dev["k"], shape.mode, nq_rows // TILE, 1, ws)
-            L.qkv.pack(dev["v"], shape.mode, (nq_rows + nkv_rows) // TILE, 1, ws)
-            L.o.pack(dev["o"], shape.mode, 0, 1, ws)
-            L.gu.pack(dev["gate"], shape.mode, 0, 2, ws)
-            L.gu.pack(dev["up"], shape.mode, 1, 2, ws)
-            L.down.pack(dev["down"], shape.mode, 0, 1, ws)
+            L.qkv.pack(dev["q"], shape.mode, 0, ws)
+            L.qkv.pack(dev["k"], shape.mode, nq_rows, ws)
+            L.qkv.pack(dev["v"], shape.mode, nq_rows + nkv_rows, ws)
+            L.o.pack(dev["o"], shape.mode, 0, ws)
+            # each gate/up tile: 32 gate rows (lanes 0-31) then the same 32 up rows (lanes 32-63)
+            L.gu.pack(dev["gate"], shape.mode, 0, ws, row_group=32, group_stride=TILE)
+            L.gu.pack(dev["up"], shape.mode, 32, ws, row_group=32, group_stride=TILE)
+            L.down.pack(dev["down"], shape.mode, 0, ws)
             if shape.qkv_bias:
                 L.bias = _dev_u16(np.concatenate([sm["bq"], sm["bk"], sm["bv"]]), device)
             torch.cuda.synchronize()

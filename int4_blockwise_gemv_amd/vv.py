@@ -54,8 +54,8 @@ _SIGS = {
     "vv_scale_bytes": (_SZ, [_I64, _I64, _I]),
     "vv_pack_int4_workspace": (_SZ, [_I64, _I64, _I]),
     "vv_pack_int4": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _SZ, _P]),
-    "vv_pack_int4_tiled": (_I, [_P, _I64, _I64, _I, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
-    "vv_repack_int4_tiled": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "vv_pack_int4_tiled": (_I, [_P, _I64, _I64, _I, _I64, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "vv_repack_int4_tiled": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "vv_dequant_int4": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
     "vv_gemv_int4_workspace": (_SZ, [_I64, _I64, _I64]),
     "vv_gemv_int4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
@@ -144,16 +144,17 @@ def pack_int4(W, mode, packed, scales, ws, stream=None):
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "vv_pack_int4")
 
 
-def pack_int4_tiled(W, mode, tile_offset, tile_stride, dst_tiles, packed, scales, ws, stream=None):
+def pack_int4_tiled(W, mode, row_group, group_stride, row_offset, dst_rows, packed, scales, ws, stream=None):
     N, K = W.shape
-    _check(lib().vv_pack_int4_tiled(_ptr(W), N, K, MODE.get(mode, mode), tile_offset, tile_stride, dst_tiles,
+    _check(lib().vv_pack_int4_tiled(_ptr(W), N, K, MODE.get(mode, mode), row_group, group_stride, row_offset, dst_rows,
                                     _ptr(packed), _ptr(scales), _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "vv_pack_int4_tiled")
 
 
-def repack_int4_tiled(packed, scales, N, K, tile_offset, tile_stride, dst_tiles, tiled, tiled_scales, stream=None):
-    _check(lib().vv_repack_int4_tiled(_ptr(packed), _ptr(scales), N, K, tile_offset, tile_stride, dst_tiles,
+def repack_int4_tiled(packed, scales, N, K, row_group, group_stride, row_offset, dst_rows, tiled, tiled_scales,
+                      stream=None):
+    _check(lib().vv_repack_int4_tiled(_ptr(packed), _ptr(scales), N, K, row_group, group_stride, row_offset, dst_rows,
                                       _ptr(tiled), _ptr(tiled_scales), _stream(stream)), "vv_repack_int4_tiled")
 
 

@@ -71,10 +71,15 @@ def test_pack_validation():
     assert L.vv_pack_int4(dummy, 0, 32, 0, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_RANGE
     assert L.vv_pack_int4(dummy, 4, 32, 7, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_DTYPE
     assert L.vv_pack_int4(dummy, 4, 32, 0, dummy, dummy, dummy, 16, None) == vvmod.VV_ERR_WORKSPACE
-    # destination tile out of range: 100 rows -> 2 tiles, stride 2 offset 1 -> tile 3 >= 3
-    assert L.vv_pack_int4_tiled(dummy, 100, 32, 0, 1, 2, 3, dummy, dummy, dummy, 4096, None) == vvmod.VV_ERR_RANGE
-    assert "tile" in vvmod.last_error()
-    assert L.vv_repack_int4_tiled(dummy, None, 4, 32, 0, 1, 1, dummy, dummy, None) == vvmod.VV_ERR_NULL
+    # destination row out of range: 100 rows in groups of 64 -> rows up to 127 + offset 64 >= 128
+    assert L.vv_pack_int4_tiled(dummy, 100, 32, 0, 64, 64, 64, 128, dummy, dummy, dummy, 4096,
+                                None) == vvmod.VV_ERR_RANGE
+    assert "destination row" in vvmod.last_error()
+    assert L.vv_pack_int4_tiled(dummy, 100, 32, 0, 64, 64, 0, 100, dummy, dummy, dummy, 4096,
+                                None) == vvmod.VV_ERR_RANGE
+    assert L.vv_pack_int4_tiled(dummy, 100, 32, 0, 32, 16, 0, 256, dummy, dummy, dummy, 4096,
+                                None) == vvmod.VV_ERR_RANGE
+    assert L.vv_repack_int4_tiled(dummy, None, 4, 32, 64, 64, 0, 64, dummy, dummy, None) == vvmod.VV_ERR_NULL
     assert L.vv_dequant_int4(dummy, dummy, 4, 32, 5, dummy, None) == vvmod.VV_ERR_DTYPE
 
 

@@ -26,7 +26,7 @@ def _pack_gpu(W, mode, tiled=False):
     q = torch.empty(vv.packed_bytes(N, K, lay), dtype=torch.uint8, device="cuda")
     s = torch.empty(vv.scale_bytes(N, K, lay) // 2, dtype=torch.int16, device="cuda")
     if tiled:
-        vv.pack_int4_tiled(Wd, mode, 0, 1, -(-N // 64), q, s, ws)
+        vv.pack_int4_tiled(Wd, mode, 64, 64, 0, 64 * -(-N // 64), q, s, ws)
     else:
         vv.pack_int4(Wd, mode, q, s, ws)
     torch.cuda.synchronize()
@@ -60,7 +60,7 @@ def test_pack_tiled_repack_dequant_bitexact(cuda, shape, mode):
     rq, rs = _pack_gpu(W, mode)
     tq = torch.empty_like(q)
     ts = torch.empty_like(s)
-    vv.repack_int4_tiled(rq, rs, N, K, 0, 1, -(-N // 64), tq, ts)
+    vv.repack_int4_tiled(rq, rs, N, K, 64, 64, 0, 64 * -(-N // 64), tq, ts)
     torch.cuda.synchronize()
     assert torch.equal(tq, q) and torch.equal(ts, s)
     # dequantised weights are exact in fp32 for both layouts
@@ -89,26 +89,36 @@ def test_pack_golden_blocks(cuda):
 
 
 def test_pack_into_fused_buffer(cuda):
-    """q|k|v row ranges and gate/up tile interleaving land where the layout note says."""
+    """Row-range (q|k|v) and 32-row interleaved (gate/up) placement land where the layout note says."""
     import torch
     from int4_blockwise_gemv_amd import vv
     K = 256
-    Wa = synth.master_weight(5, 0, synth.T_GATE, 128, K)
-    Wb = synth.master_weight(5, 0, synth.T_UP, 128, K)
-    T = 4
-    q = torch.zeros(vv.packed_bytes(T * 64, K, vv.VV_LAYOUT_TILED), dtype=torch.uint8, device="cuda")
-    s = torch.zeros(vv.scale_bytes(T * 64, K, vv.VV_LAYOUT_TILED) // 2, dtype=torch.int16, device="cuda")
+    Wa = synth.master_weight(5, 0, synth.T_GATE, 96, K)
+    Wb = synth.master_weight(5, 0, synth.T_UP, 96, K)
+    rows = 192
+    q = torch.zeros(vv.packed_bytes(rows, K, vv.VV_LAYOUT_TILED), dtype=torch.uint8, device="cuda")
+    s = torch.zeros(vv.scale_bytes(rows, K, vv.VV_LAYOUT_TILED) // 2, dtype=torch.int16, device="cuda")
     ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
-    vv.pack_int4_tiled(dev(Wa), "ternary", 0, 2, T, q, s, ws)
-    vv.pack_int4_tiled(dev(Wb), "ternary", 1, 2, T, q, s, ws)
+    vv.pack_int4_tiled(dev(Wa), "ternary", 32, 64, 0, rows, q, s, ws)
+    vv.pack_int4_tiled(dev(Wb), "ternary", 32, 64, 32, rows, q, s, ws)
     torch.cuda.synchronize()
     qa, sa = O.pack(Wa, "ternary")
     qb, sb = O.pack(Wb, "ternary")
     ca, cb = O.unpack_nibbles(qa), O.unpack_nibbles(qb)
-    inter = np.concatenate([ca[:64], cb[:64], ca[64:], cb[64:]])
-    inter_s = np.concatenate([sa[:64], sb[:64], sa[64:], sb[64:]])
+    inter = np.concatenate([ca[0:32], cb[0:32], ca[32:64], cb[32:64], ca[64:96], cb[64:96]])
+    inter_s = np.concatenate([sa[0:32], sb[0:32], sa[32:64], sb[32:64], sa[64:96], sb[64:96]])
     want_q, want_s = codes_to_tiled(inter, inter_s)
     assert np.array_equal(host(q), want_q) and np.array_equal(host_u16(s), want_s)
+    # row-range placement: a 64-row block after 128 rows of something else
+    q2 = torch.zeros_like(q)
+    s2 = torch.zeros_like(s)
+    vv.pack_int4_tiled(dev(Wa[:64]), "ternary", 64, 64, 128, rows, q2, s2, ws)
+    torch.cuda.synchronize()
+    qa2, sa2 = O.pack(Wa[:64], "ternary")
+    want_q2, want_s2 = codes_to_tiled(O.unpack_nibbles(qa2), sa2)
+    assert np.array_equal(host(q2)[-len(want_q2):], want_q2)
+    assert np.array_equal(host_u16(s2)[-len(want_s2):], want_s2)
+    assert not host(q2)[:-len(want_q2)].any()
 
 
 # ---------------------------------------------------------------------------------------------
