@@ -5,13 +5,15 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode-7b-p4000]
 One step = one vv_decode_step (28 layers: fused QKV GEMV, attention with KV append, o GEMV,
 gate/up GEMV + SiLU, down GEMV, then lm_head + argmax) replayed from a hipGraph on seeded
 synthetic weights, KV cache and input already resident in HBM.  The timed region is K
-back-to-back replays bracketed by torch.cuda.synchronize().
+back-to-back replays bracketed by torch.cuda.synchronize().  --path picks the implementation
+(auto = layered: one launch per stage; persistent = all layers in one launch).
 
 Also reported:
-  roofline     achieved HBM GB/s of the dominant kernel (the gate/up GEMV: most time per step),
-               = its algorithmic bytes per launch / its mean duration measured with HIP events
-               on the launch stream during an instrumented eager pass right after the timed
-               region; traffic from committed rocprofv3 counters when they match the kernel source.
+  roofline     achieved HBM GB/s of the dominant kernel, = its algorithmic bytes per launch / its
+               mean duration measured with HIP events on the launch stream during instrumented
+               eager steps right after the timed region.  Persistent path: the layer kernel
+               (int4 weights + scales + K/V of every layer); layered path: the gate/up GEMV.
+               traffic: from committed rocprofv3 counters when they match the kernel source.
   cpu_baseline the fp64 oracle's decode step timed on a bounded sample of the same workload
                (one layer + a vocabulary slice, scaled to a full step).
 """
@@ -47,15 +49,15 @@ def algorithmic_bytes(shape, batch, lens):
     return w, kv, lm
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=("gemv.hip", "gemv_core.h", "vv_internal.h")):
     h = hashlib.sha256()
-    for f in ("gemv.hip", "vv_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "int4_blockwise_gemv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_tag):
+def read_traffic(kernel_tag, files):
     """HBM bytes per launch from profiles/traffic_<tag>.txt if it was taken on the current source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
     if not os.path.exists(path):
@@ -65,7 +67,7 @@ def read_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != kernel_source_hash():
+    if kv.get("source_hash") != kernel_source_hash(files):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -73,7 +75,7 @@ def read_traffic(kernel_tag):
         return None
 
 
-def build_inputs(wl, seed):
+def build_inputs(wl, seed, path="auto"):
     import torch
     from int4_blockwise_gemv_amd import synth
     from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
@@ -82,7 +84,7 @@ def build_inputs(wl, seed):
     t0 = time.time()
     dm = DeviceModel(s, seed, max_batch=wl.batch, progress=lambda m: None)
     log(f"packed {s.layers} layers + lm_head on the GPU in {time.time() - t0:.1f}s")
-    ds = DeviceState(dm, wl.batch, wl.cap)
+    ds = DeviceState(dm, wl.batch, wl.cap, path=path)
     for li in range(s.layers):
         K, V = synth.layer_cache(wl, seed, li, lens)
         ds.load_cache_layer(li, K, V)
@@ -92,6 +94,32 @@ def build_inputs(wl, seed):
     torch.cuda.synchronize()
     log(f"inputs resident ({time.time() - t0:.1f}s total)")
     return dm, ds, lens
+
+
+def kernel_breakdown_persistent(ds, n_layers, reps=5):
+    """Mean duration (ms) of the persistent layer launch(es) and of the lm_head (HIP events)."""
+    import ctypes as C
+    import torch
+    n_launch = -(-n_layers // 32)
+    n_ev = n_launch + 2
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    arr = (C.c_void_p * n_ev)(*[C.c_void_p(e.cuda_event) for e in evs])
+    ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
+    ds.struct.n_events = n_ev
+    layers, lm = [], []
+    try:
+        for _ in range(reps):
+            ds.step()
+            torch.cuda.synchronize()
+            layers.append(evs[0].elapsed_time(evs[n_launch]))
+            lm.append(evs[n_launch].elapsed_time(evs[n_launch + 1]))
+    finally:
+        ds.struct.events = None
+        ds.struct.n_events = 0
+    return {"layers": float(np.median(layers)), "lm_head": float(np.median(lm))}
 
 
 def kernel_breakdown(ds, n_layers, reps=3):
@@ -162,6 +190,7 @@ def main():
     ap.add_argument("--workload", default="decode-7b-p4000")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=["auto", "persistent", "layered"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this decode step is not sharded across GPUs "
@@ -173,8 +202,10 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
-    dm, ds, lens = build_inputs(wl, args.seed)
+    from int4_blockwise_gemv_amd import vv
+    dm, ds, lens = build_inputs(wl, args.seed, args.path)
     s = wl.shape
+    persistent = args.path == "persistent"
 
     g = ds.graph()
     for _ in range(args.warmup):
@@ -189,23 +220,36 @@ def main():
     ms = dt * 1e3 / args.steps
     g.close()
     tok = int(ds.token.cpu()[0])
-    log(f"{ms * 1e3:.1f} us/step ({1e3 / ms:.1f} steps/s), token {tok}")
+    status = ds.status()
+    log(f"{ms * 1e3:.1f} us/step ({1e3 / ms:.1f} steps/s), token {tok}, status {status}")
+    if status != 0:
+        raise SystemExit("persistent step reported an in-kernel wait that gave up")
 
     wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
     total = wb + kvb + lmb
-    kb = kernel_breakdown(ds, s.layers)
-    log("kernel means (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
-    gu_bytes = 2 * s.inter * s.hidden // 2 + 2 * s.inter * (s.hidden // 32) * 2
-    gu_ms = kb["gateup"]
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    traffic = read_traffic("gateup_" + ("7b" if s.hidden == 3584 else "1p5b"))
+    tag = "7b" if s.hidden == 3584 else "1p5b"
+    if persistent:
+        kb = kernel_breakdown_persistent(ds, s.layers)
+        log("kernel medians (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
+        dom_bytes, dom_ms = wb + kvb, kb["layers"]
+        dom_name = "persistent decode-layer kernel (all layers: int4 GEMVs + attention)"
+        traffic = read_traffic("persistent_" + tag, ("mega.hip", "gemv_core.h", "vv_internal.h"))
+        sum_kern = kb["layers"] + kb["lm_head"]
+    else:
+        kb = kernel_breakdown(ds, s.layers)
+        log("kernel means (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
+        dom_bytes = 2 * s.inter * s.hidden // 2 + 2 * s.inter * (s.hidden // 32) * 2
+        dom_ms = kb["gateup"]
+        dom_name = "gate/up int4 GEMV (+SiLU*up)"
+        traffic = read_traffic("gateup_" + tag, ("gemv.hip", "gemv_core.h", "vv_internal.h"))
+        sum_kern = sum(kb[k] for k in ("qkv", "attn", "o", "gateup", "down")) * s.layers + kb["prep"] + kb["lm_head"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         cpu = cpu_baseline(wl, args.seed)
 
-    sum_kern = sum(kb[k] for k in ("qkv", "attn", "o", "gateup", "down")) * s.layers + kb["prep"] + kb["lm_head"]
     out = {
         "metric": "decode steps/s (HBM GB/s, % of 8 TB/s roofline)",
         "value": 1e3 / ms,
@@ -221,13 +265,14 @@ def main():
         "data": "synthetic (seeded N(0,0.02) fp32 masters ternarised on the GPU, fp16 N(0,1) KV/inputs)",
         "config": {"workload": wl.name, "layers": s.layers, "hidden": s.hidden, "inter": s.inter,
                    "n_q": s.n_q, "n_kv": s.n_kv, "head_dim": s.head_dim, "vocab": s.vocab, "batch": wl.batch,
-                   "past": int(lens.max()), "quant": s.mode, "seed": args.seed},
+                   "past": int(lens.max()), "quant": s.mode, "seed": args.seed,
+                   "path": "persistent" if persistent else "layered"},
         "hbm": {"algorithmic_bytes_per_step": total, "weights": wb, "kv": kvb, "lm_head": lmb,
                 "GB_per_s": total / (ms * 1e-3) / 1e9,
                 "frac_of_8TBps": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "roofline": {"bound": "hbm", "kernel": "gate/up int4 GEMV (+SiLU*up)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "bytes_per_launch": gu_bytes, "mean_launch_us": gu_ms * 1e3},
+                     "traffic": traffic, "bytes_per_launch": dom_bytes, "mean_launch_us": dom_ms * 1e3},
         "kernels_us": {k: v * 1e3 for k, v in kb.items()},
         "eager_kernel_sum_us": sum_kern * 1e3,
         "token": tok,

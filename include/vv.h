@@ -184,7 +184,23 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  *        group_stride 64, row_offset 0 and up with row_offset 32), 2*I rows, K = H;
  *   down: H rows, K = I.
  * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8, cap <= 131072.
+ *
+ * Two implementations compute the same step (vv_state.path):
+ *   VV_PATH_PERSISTENT  all layers in one launch of a persistent kernel (at most 32 layers per
+ *                       launch), then the lm_head: batch 1..2, n_layers >= 1, H <= 4096.  Its
+ *                       workgroups hand results to each other through counters in the
+ *                       workspace, so it needs every workgroup of its grid resident at once
+ *                       (the grid is sized from the occupancy of the current device) and must
+ *                       not share the GPU with another persistent launch.  Each wait is bounded:
+ *                       a wait that gives up sets a sticky nonzero status word instead of hanging
+ *                       (vv_decode_status reads it; clear it with vv_workspace_init).
+ *   VV_PATH_LAYERED     one launch per stage (1 + 5 L + 1 kernels): any batch up to max_batch.
+ *   VV_PATH_AUTO        the layered path (measured faster on MI355X: the persistent kernel's
+ *                       per-item hand-offs through memory cost more than the launches it saves).
+ * Results of the two paths agree to rounding (the K-splits differ), and each is deterministic.
  * ------------------------------------------------------------------------------------------- */
+enum { VV_PATH_AUTO = 0, VV_PATH_LAYERED = 1, VV_PATH_PERSISTENT = 2 };
+
 typedef struct vv_layer {
   const uint8_t* qkv_q;   const uint16_t* qkv_s;    /* device, tiled */
   const uint8_t* o_q;     const uint16_t* o_s;
@@ -220,14 +236,23 @@ typedef struct vv_state {
   size_t workspace_bytes;
   void** events;                   /* optional HOST array of hipEvent_t used to time the kernels of
                                       an eager vv_decode_step: event i is recorded on the stream
-                                      before kernel i and event 5*n_layers+2 after the last kernel
-                                      (kernels: prep, then per layer qkv, attention, o, gate/up,
-                                      down, then lm_head).  NULL disables; graphs reject it. */
-  int n_events;                    /* entries in events (>= 5*n_layers + 3 when events is set) */
+                                      before kernel i and one more after the last kernel.
+                                      Layered path: prep, then per layer qkv, attention, o,
+                                      gate/up, down, then lm_head (5*n_layers + 3 events).
+                                      Persistent path: one launch per 32 layers, then lm_head
+                                      (ceil(n_layers/32) + 2 events).  NULL disables; graphs
+                                      reject it. */
+  int n_events;                    /* entries in events */
+  int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_PERSISTENT */
 } vv_state;
 
 size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap);
 int vv_decode_step(const vv_model* m, const vv_state* s, void* stream);
+
+/* Copies the persistent path's sticky status word to *status (host) and waits for the stream:
+ * 0 = every wait of every launch so far was satisfied; nonzero = a wait gave up (results of that
+ * step and later ones are invalid until vv_workspace_init clears the workspace). */
+int vv_decode_status(const vv_model* m, const vv_state* s, int32_t* status, void* stream);
 
 /* hipGraph capture of one vv_decode_step (one host->GPU crossing per step).  The graph keeps the
  * device pointers of m and s; pos/input_embeds are read from device memory at replay, so one

@@ -1,10 +1,16 @@
 // int4 block-32 GEMV on the tiled layout (MatMulNBits semantics with float activations).
 //
-// One wave owns one 64-row tile and a contiguous range of kb blocks (a multiple of 8, so every
-// batch of 8 blocks shares one 16-byte scale load): lane i accumulates row 64t+i, so every
-// 16-byte block load of the wave is one contiguous 1 KiB run, and the activation block is the
-// same for all lanes (wave-uniform scalar loads).  Batches of 8 blocks are double-buffered: the
-// next batch is in flight while the current one is dequantised.
+// Decomposition: a wave owns one 64-row tile and one group of 8 consecutive blocks (lane i
+// accumulates row 64t+i, so each 16-byte block load of the wave is one contiguous 1 KiB run, and
+// the group's 8 fp16 scales are one more 16-byte load); a workgroup takes 4 consecutive groups of
+// one tile, and a tile's groups are spread over `wpt` = ceil(groups / 4) workgroups.  All nine
+// loads of a wave are in flight at once, and the grid is far larger than the CU count: short
+// waves keep the HBM busiest.
+//
+// Activations: before any weight load, the workgroup's 1024-element slice of x (per batch row)
+// goes to LDS with one vector load per thread; the waves then read their block's 32 values as
+// LDS broadcasts.  (Scalar loads issued block by block would put one L2 latency per block on the
+// path.)
 //
 // In-register dequantisation: a packed dword holds 8 codes with the even elements in nibbles
 // 0..3 and the odd ones in nibbles 4..7, so a shift and one AND-OR with the fp16 exponent of
@@ -14,110 +20,17 @@
 // removed once per block by subtracting C_b = 72 * sum_j x_j; the block sum is scaled by the
 // block's fp16 scale in fp32.
 //
-// Split-K: the block ranges of a tile are spread over the 4 waves of a workgroup (reduced in
-// LDS) and, for matrices with few tiles, over `wpt` workgroups; then the last workgroup to
+// Split-K: the 4 waves of a workgroup are reduced in LDS; with wpt > 1 the last workgroup to
 // arrive at a tile adds the partials in a fixed order and runs the epilogue, so results do not
 // depend on timing.  With wpt = 1 the workgroup finishes its tile directly.
 #include "vv_internal.h"
+#include "gemv_core.h"
 
 namespace vv {
 namespace {
 
 constexpr int kWavesPerWG = 4;
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
-constexpr int kFillWGs = 256;    // workgroups wanted for a full chip
-
-// A VGPR holding a constant, opaque to the optimiser: lets (d & mask) | magic become one
-// v_and_or_b32 (mask in an SGPR, magic in a VGPR; the GFX9 VOP3 encoding takes no literal).
-__device__ __forceinline__ uint32_t vconst(uint32_t c) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-  return r;
-}
-
-__device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, float acc, uint32_t m64) {
-  // the fp16 magic 64.0 (0x5400) has ulp 1/16, so a code in mantissa bits 4..7 of either half
-  // reads as 64 + q exactly; the even/odd codes of pair i sit in nibbles i and 4+i
-  const uint32_t p01 = ((d << 4) & 0x00F000F0u) | m64;  // nibbles 0, 4: (64+e0, 64+e1)
-  const uint32_t p23 = (d & 0x00F000F0u) | m64;         // nibbles 1, 5: (64+e2, 64+e3)
-  const uint32_t p45 = ((d >> 4) & 0x00F000F0u) | m64;  // nibbles 2, 6: (64+e4, 64+e5)
-  const uint32_t p67 = ((d >> 8) & 0x00F000F0u) | m64;  // nibbles 3, 7: (64+e6, 64+e7)
-  acc = __builtin_amdgcn_fdot2(as_h2(p01), as_h2(x4[0]), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(p23), as_h2(x4[1]), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(p45), as_h2(x4[2]), acc, false);
-  acc = __builtin_amdgcn_fdot2(as_h2(p67), as_h2(x4[3]), acc, false);
-  return acc;
-}
-
-// C for one quarter (8 elements) of a block: (64 + 8) * (x0 + ... + x7)
-__device__ __forceinline__ float corr_quarter(u32x4 xv) {
-  const uint32_t c72 = 0x54805480u;  // fp16 (72, 72)
-  float c = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(c72), 0.f, false);
-  c = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(c72), c, false);
-  c = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(c72), c, false);
-  c = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(c72), c, false);
-  return c;
-}
-
-// scale j (compile-time 0..7) of a group of 8 fp16 scales
-__device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
-  const uint32_t d = (j >> 1) == 0 ? s.x : (j >> 1) == 1 ? s.y : (j >> 1) == 2 ? s.z : s.w;
-  return (j & 1) ? (float)__builtin_bit_cast(h2_t, d).y : (float)__builtin_bit_cast(h2_t, d).x;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// One batch of up to 8 blocks in flight: packed blocks, their scale group, and the activation
-// quarters for the per-block corrections (lane 4i+q holds quarter q of block i, lanes < 32).
-template <int MT>
-struct Batch {
-  u32x4 w[kBatch];
-  u32x4 s;
-  u32x4 xq[MT];
-};
-
-template <int MT>
-__device__ __forceinline__ void load_batch(Batch<MT>& B, const u32x4* qp, const u32x4* sp, const uint16_t* x,
-                                           int K, int M, int bb, int nb_here, int lane) {
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i)
-    if (i < nb_here) B.w[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
-  B.s = __builtin_nontemporal_load(sp);
-  const int bl = lane >> 2, qd = lane & 3;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    B.xq[m] = u32x4{0, 0, 0, 0};
-    if (m < M && bl < nb_here)
-      B.xq[m] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + (size_t)(bb + bl) * kBlock + qd * 8);
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void compute_batch(const Batch<MT>& B, const uint16_t* __restrict__ x, int K, int M,
-                                              int bb, int nb_here, uint32_t m64, float (&acc)[MT]) {
-  float corr[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    corr[m] = quad_sum(corr_quarter(B.xq[m]));
-  }
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    if (i < nb_here) {
-      const float sc = pick_scale(B.s, i);
-      const uint32_t d[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + (size_t)m * K + (size_t)(bb + i) * kBlock);
-          float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) t = dot8_pairs(d[k], xb + 4 * k, t, m64);
-          acc[m] = fmaf(sc, t, acc[m]);
-        }
-      }
-    }
-  }
-}
 
 // Operands of the epilogue, loaded by wave 0 of every workgroup before the weight stream so the
 // workgroup that finishes a tile does not wait on them.
@@ -204,13 +117,16 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
   }
 }
 
+constexpr int kItemK = kWavesPerWG * kBatch * kBlock;   // K elements per workgroup (1024)
+
 template <int MT>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                               const uint4* __restrict__ sw, const uint16_t* __restrict__ x) {
+  __shared__ __align__(16) uint16_t xs[MT][kItemK];
   __shared__ float red[kWavesPerWG][MT][kTileRows];
   const int K = p.K;
   const int nb = K / kBlock;
-  const int ng = (nb + 7) >> 3;
+  const int ng = (nb + kBatch - 1) / kBatch;
   const int M = p.M;
   const uint32_t nwg = (uint32_t)p.ntiles * p.wpt;
   const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -219,36 +135,66 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
   const int kg = L % p.wpt;
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
-  const int b0 = (kg * kWavesPerWG + w) * p.kb;  // multiple of 8
-  int nblk = nb - b0;
-  nblk = nblk < 0 ? 0 : (nblk > p.kb ? p.kb : nblk);
-  const int nbt = (nblk + kBatch - 1) / kBatch;
+  const int e0 = kg * kItemK;                       // first K element of this workgroup
+  const int ne = min(K - e0, kItemK);
+
+  // activation slice first (its loads return before the weights), 8 bytes per thread per row
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int e = 4 * (int)threadIdx.x;
+    if (m < M && e < ne)
+      *reinterpret_cast<uint2*>(&xs[m][e]) = *reinterpret_cast<const uint2*>(x + (size_t)m * K + e0 + e);
+  }
+  // this wave's group: 8 blocks and their 8 scales
+  const int grp = kg * kWavesPerWG + w;
+  const int b0 = grp * kBatch;
+  const int nblk = min(max(nb - b0, 0), kBatch);
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qw) + ((size_t)tile * nb + b0) * kTileRows + lane;
+  u32x4 wv[kBatch];
+  u32x4 sv = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i)
+    if (i < nblk) wv[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
+  if (nblk > 0) sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sw) + ((size_t)tile * ng + grp) * kTileRows + lane);
 
   EpiPre<MT> ep;
   float rsp[MT];
   if (w == 0) epi_prefetch<MT>(p, tile, lane, ep, rsp);
+  __syncthreads();
 
-  const u32x4* qp = reinterpret_cast<const u32x4*>(qw) + ((size_t)tile * nb + b0) * kTileRows + lane;
-  const u32x4* sp = reinterpret_cast<const u32x4*>(sw) + ((size_t)tile * ng + (b0 >> 3)) * kTileRows + lane;
   const uint32_t m64 = vconst(0x54005400u);
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-
-  Batch<MT> A, B;
-  if (nbt > 0) load_batch<MT>(A, qp, sp, x, K, M, b0, min(kBatch, nblk), lane);
-  for (int bt = 0; bt < nbt; bt += 2) {
-    const int bbA = b0 + bt * kBatch;
-    const bool hasB = bt + 1 < nbt;
-    if (hasB)
-      load_batch<MT>(B, qp + (size_t)(bt + 1) * kBatch * kTileRows, sp + (size_t)(bt + 1) * kTileRows, x, K, M,
-                     bbA + kBatch, min(kBatch, nblk - (bt + 1) * kBatch), lane);
-    compute_batch<MT>(A, x, K, M, bbA, min(kBatch, nblk - bt * kBatch), m64, acc);
-    if (hasB) {
-      if (bt + 2 < nbt)
-        load_batch<MT>(A, qp + (size_t)(bt + 2) * kBatch * kTileRows, sp + (size_t)(bt + 2) * kTileRows, x, K, M,
-                       bbA + 2 * kBatch, min(kBatch, nblk - (bt + 2) * kBatch), lane);
-      compute_batch<MT>(B, x, K, M, bbA + kBatch, min(kBatch, nblk - (bt + 1) * kBatch), m64, acc);
+  if (nblk > 0) {
+    const int xb0 = w * kBatch * kBlock;            // this wave's first element in the slice
+    float corr[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      u32x4 xv = u32x4{0, 0, 0, 0};
+      if (m < M && lane < 4 * nblk) xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + lane * 8]);
+      corr[m] = quad_sum(corr_quarter(xv));           // lane 4i+q: quarter q of block i
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (i < nblk) {
+        const float sc = pick_scale(sv, i);
+        const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < M) {
+            const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
+            float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const u32x4 xv = xb[k];
+              const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+              t = dot8_pairs(d[k], x4, t, m64);
+            }
+            acc[m] = fmaf(sc, t, acc[m]);
+          }
+        }
+      }
     }
   }
 
@@ -282,9 +228,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= M) continue;
-    float s = 0.f;
-    for (int k = 0; k < p.wpt; ++k) s += collect_f32(p.part + (((size_t)tile * p.wpt + k) * MT + m) * kTileRows + lane);
-    tot[m] = s;
+    tot[m] = collect_sum_f32(p.part + ((size_t)tile * p.wpt * MT + m) * kTileRows + lane, p.wpt,
+                             (size_t)MT * kTileRows);
   }
   if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
   epilogue<MT>(p, tile, tot, ep, lane);
@@ -294,19 +239,18 @@ int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16
 
 struct Plan { int kb, wpt, grid; };
 
-// wpt (workgroups per tile): the fewest that give ~kFillWGs workgroups, bounded by one batch of
-// 8 blocks per wave; kb = the blocks each wave takes, a multiple of 8.
+// One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave
+// and four consecutive groups per workgroup, so a tile is split over ceil(groups / 4)
+// workgroups.  Short waves and a grid well beyond the CU count keep the HBM busiest (a wave that
+// streams tens of KiB serialises its own latency), at the price of one cross-workgroup
+// reduction per tile.
 Plan make_plan(int M, int ntiles, int nb) {
   (void)M;
   const int nb8 = (int)cdiv(nb, kBatch);
-  int wpt = (int)cdiv(kFillWGs, ntiles);
-  const int wmax = (int)cdiv(nb8, kWavesPerWG);
-  wpt = wpt < 1 ? 1 : (wpt > wmax ? wmax : wpt);
-  const int gpw = (int)cdiv(nb8, (int64_t)kWavesPerWG * wpt);
   Plan pl;
-  pl.kb = gpw * kBatch;
-  pl.wpt = wpt;
-  pl.grid = (int)(cdiv((int64_t)ntiles * wpt, kNumXcd) * kNumXcd);
+  pl.kb = kBatch;
+  pl.wpt = (int)cdiv(nb8, kWavesPerWG);
+  pl.grid = (int)(cdiv((int64_t)ntiles * pl.wpt, kNumXcd) * kNumXcd);
   return pl;
 }
 

@@ -1,5 +1,9 @@
 // Decode-step launcher and its hipGraph wrapper.
 //
+// Two implementations of the same step share the entry points: the persistent kernel of
+// mega.hip (one launch for all layers, then the lm_head; used for batch 1..2) and the layered
+// path below (one launch per stage; any batch up to 16).  vv_state.path picks one.
+//
 // decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts):
 //   input_embeds [B,H], position_ids [B], past K/V -> logits [B,V], present K/V (one more slot)
 // on the Qwen2 layer of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA,
@@ -95,6 +99,20 @@ Layout layout_of(const Dims& d) {
   return l;
 }
 
+// bytes of the layered path's region; the persistent region follows it
+size_t layered_bytes(const vv_model* m, int B, int cap) { return align_up(layout_of(dims_of(m, B, cap)).total, 256); }
+
+size_t step_bytes(const vv_model* m, int B, int cap) {
+  return layered_bytes(m, B, cap) + persistent_workspace_bytes(m, B, cap);
+}
+
+// AUTO takes the layered path: on MI355X it is the faster of the two at present (the persistent
+// kernel's per-item hand-offs cost more than the launches they save); see the path notes in vv.h
+bool use_persistent(const vv_model* m, const vv_state* s) {
+  (void)m;
+  return s->path == VV_PATH_PERSISTENT;
+}
+
 int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(m && s, VV_ERR_NULL, "%s: model or state is NULL", fn);
   VV_REQUIRE(m->n_layers >= 0 && m->n_layers <= 4096, VV_ERR_RANGE, "%s: n_layers out of range", fn);
@@ -129,18 +147,52 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(m->n_layers == 0 || (s->k_cache && s->v_cache), VV_ERR_NULL, "%s: KV cache is NULL", fn);
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(s->k_cache) | reinterpret_cast<uintptr_t>(s->v_cache)) & 15) == 0,
              VV_ERR_RANGE, "%s: KV caches must be 16-byte aligned", fn);
-  const Dims d = dims_of(m, s->batch, s->cap);
-  const size_t need = layout_of(d).total;
+  VV_REQUIRE(s->path == VV_PATH_AUTO || s->path == VV_PATH_LAYERED || s->path == VV_PATH_PERSISTENT, VV_ERR_RANGE,
+             "%s: unknown path %d", fn, s->path);
+  VV_REQUIRE(s->path != VV_PATH_PERSISTENT || persistent_supported(m, s->batch), VV_ERR_UNSUPPORTED,
+             "%s: the persistent path needs n_layers >= 1, batch <= 2, hidden <= 4096", fn);
+  const size_t need = step_bytes(m, s->batch, s->cap);
   VV_REQUIRE(s->workspace && s->workspace_bytes >= need, VV_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
              need);
   VV_REQUIRE((reinterpret_cast<uintptr_t>(s->workspace) & 255) == 0, VV_ERR_RANGE,
              "%s: workspace must be 256-byte aligned", fn);
-  VV_REQUIRE(!s->events || s->n_events >= 5 * m->n_layers + 3, VV_ERR_RANGE,
-             "%s: events needs at least 5*n_layers+3 entries", fn);
+  const int nev = use_persistent(m, s) ? (int)cdiv(m->n_layers, 32) + 2 : 5 * m->n_layers + 3;
+  VV_REQUIRE(!s->events || s->n_events >= nev, VV_ERR_RANGE, "%s: events needs at least %d entries", fn, nev);
+  return VV_OK;
+}
+
+int enqueue_lm(const vv_model* m, const vv_state* s, const float* gf32, const float* sumsq, char* ws_lm,
+               hipStream_t st) {
+  LmParams p{};
+  p.W = m->lm_head; p.V = m->vocab; p.H = m->hidden; p.B = s->batch;
+  p.x = gf32; p.x_f16 = 0;
+  p.rs_parts = sumsq; p.rs_nparts = m->hidden / kTileRows; p.rs_inv_n = 1.0f / (float)m->hidden; p.eps = m->eps;
+  p.logits = s->logits; p.token = s->token;
+  lm_plan(p);
+  lm_set_workspace(p, ws_lm);
+  VV_HIP(lm_launch(p, st));
+  return VV_OK;
+}
+
+int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
+  char* ws = static_cast<char*>(s->workspace);
+  char* pws = ws + layered_bytes(m, s->batch, s->cap);
+  const Layout lay = layout_of(dims_of(m, s->batch, s->cap));
+  int ev = 0;
+  int rc = persistent_enqueue(m, s, pws, st, s->events, &ev);
+  if (rc) return rc;
+  const float* gf32;
+  const float* sumsq;
+  persistent_lm_inputs(m, s, pws, &gf32, &sumsq);
+  if (s->events) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st));
+  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st);
+  if (rc) return rc;
+  if (s->events) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st));
   return VV_OK;
 }
 
 int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
+  if (use_persistent(m, s)) return enqueue_persistent(m, s, st);
   const Dims d = dims_of(m, s->batch, s->cap);
   const Layout lay = layout_of(d);
   char* ws = static_cast<char*>(s->workspace);
@@ -234,17 +286,10 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       VV_HIP(gemv_launch(p, st));
     }
   }
-  {  // final RMSNorm folded into the lm_head; greedy argmax
-    LmParams p{};
-    p.W = m->lm_head; p.V = d.V; p.H = H; p.B = B;
-    p.x = gf; p.x_f16 = 0;
-    p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
-    p.logits = s->logits; p.token = s->token;
-    lm_plan(p);
-    lm_set_workspace(p, ws + lay.ws_lm);
-    VV_HIP(mark());
-    VV_HIP(lm_launch(p, st));
-  }
+  // final RMSNorm folded into the lm_head; greedy argmax
+  VV_HIP(mark());
+  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st);
+  if (rc) return rc;
   VV_HIP(mark());
   return VV_OK;
 }
@@ -262,8 +307,21 @@ using namespace vv;
 extern "C" {
 
 size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap) {
-  if (!m || batch < 1 || cap < 1 || m->hidden < 64 || m->inter < 64 || m->n_kv < 1 || m->n_q < 1) return 0;
-  return layout_of(dims_of(m, batch, cap)).total;
+  if (!m || batch < 1 || cap < 1 || m->hidden < 64 || m->inter < 64 || m->n_kv < 1 || m->n_q < 1 ||
+      m->n_q % m->n_kv)
+    return 0;
+  return step_bytes(m, batch, cap);
+}
+
+int vv_decode_status(const vv_model* m, const vv_state* s, int32_t* status, void* stream) {
+  clear_error();
+  VV_REQUIRE(m && s && status, VV_ERR_NULL, "vv_decode_status: NULL argument");
+  VV_REQUIRE(s->workspace && s->batch >= 1 && s->cap >= 1, VV_ERR_RANGE, "vv_decode_status: bad state");
+  const char* pws = static_cast<const char*>(s->workspace) + layered_bytes(m, s->batch, s->cap);
+  hipStream_t st = as_stream(stream);
+  VV_HIP(hipMemcpyAsync(status, pws, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  VV_HIP(hipStreamSynchronize(st));
+  return VV_OK;
 }
 
 int vv_decode_step(const vv_model* m, const vv_state* s, void* stream) {
@@ -281,6 +339,8 @@ int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, v
   if (rc) return rc;
   VV_REQUIRE(s->events == nullptr, VV_ERR_UNSUPPORTED, "vv_decode_graph_create: timing events are eager-only");
   (void)stream;
+  // size the persistent grid before capturing (the occupancy query is not a stream operation)
+  if (use_persistent(m, s)) VV_REQUIRE(persistent_grid() > 0, VV_ERR_HIP, "vv_decode_graph_create: no resident grid");
   hipStream_t cs;
   VV_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   hipGraph_t graph = nullptr;

@@ -135,6 +135,19 @@ __device__ __forceinline__ void wait_published() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// sum_{k < n} p[k * stride] in k order, with the loads issued 16 at a time (a runtime-length
+// loop of agent-scope loads would wait for each one before issuing the next)
+__device__ __forceinline__ float collect_sum_f32(const float* p, int n, size_t stride) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = k0 + k < n ? collect_f32(p + (size_t)(k0 + k) * stride) : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += v[k];
+  }
+  return s;
+}
 // arrival counter: returns the previous count (agent scope, performed coherently across XCDs)
 __device__ __forceinline__ unsigned arrive(unsigned* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -214,5 +227,12 @@ void lm_set_workspace(LmParams& p, void* ws);
 hipError_t lm_launch(const LmParams& p, hipStream_t st);
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// persistent (single-launch) decode step; its workspace region starts with a sticky status word
+bool persistent_supported(const vv_model* m, int batch);
+int persistent_grid();   // resident workgroups on the current device (queried once per device)
+size_t persistent_workspace_bytes(const vv_model* m, int batch, int cap);
+int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, void** events, int* ev);
+void persistent_lm_inputs(const vv_model* m, const vv_state* s, char* ws, const float** gf32, const float** sumsq);
 
 }  // namespace vv

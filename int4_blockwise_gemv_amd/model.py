@@ -122,7 +122,7 @@ class DeviceState:
     """KV caches, inputs, outputs and workspace of one decode step."""
 
     def __init__(self, model: DeviceModel, batch: int, cap: int, device="cuda", trace: bool = False,
-                 logits: bool = True):
+                 logits: bool = True, path: str = "auto"):
         import torch
         s = model.shape
         self.model, self.batch, self.cap = model, batch, cap
@@ -139,7 +139,7 @@ class DeviceState:
         self.struct = vv.vv_state(batch, cap, self.emb.data_ptr(), self.pos.data_ptr(), self.k.data_ptr(),
                                   self.v.data_ptr(), self.logits.data_ptr() if logits else None,
                                   self.token.data_ptr(), self.trace.data_ptr() if trace else None,
-                                  self.ws.data_ptr(), nbytes)
+                                  self.ws.data_ptr(), nbytes, None, 0, vv.PATH[path])
 
     def load_cache_layer(self, idx: int, K: np.ndarray, V: np.ndarray):
         import torch
@@ -148,6 +148,9 @@ class DeviceState:
 
     def step(self, stream=None):
         vv.decode_step(self.model.struct, self.struct, stream)
+
+    def status(self, stream=None) -> int:
+        return vv.decode_status(self.model.struct, self.struct, stream)
 
     def graph(self, stream=None) -> vv.DecodeGraph:
         return vv.DecodeGraph(self.model.struct, self.struct, stream)

@@ -18,6 +18,8 @@ VV_ERR_WORKSPACE, VV_ERR_UNSUPPORTED, VV_ERR_HIP = -5, -6, -7
 VV_Q_TERNARY, VV_Q_ABSMAX = 0, 1
 VV_F16, VV_F32 = 1, 2
 VV_LAYOUT_ROWMAJOR, VV_LAYOUT_TILED = 0, 1
+VV_PATH_AUTO, VV_PATH_LAYERED, VV_PATH_PERSISTENT = 0, 1, 2
+PATH = {"auto": VV_PATH_AUTO, "layered": VV_PATH_LAYERED, "persistent": VV_PATH_PERSISTENT}
 MODE = {"ternary": VV_Q_TERNARY, "absmax": VV_Q_ABSMAX}
 
 
@@ -44,7 +46,7 @@ class vv_state(C.Structure):
     _fields_ = [("batch", C.c_int), ("cap", C.c_int), ("input_embeds", C.c_void_p), ("pos", C.c_void_p),
                 ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("logits", C.c_void_p), ("token", C.c_void_p),
                 ("h_trace", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int)]
+                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int), ("path", C.c_int)]
 
 
 _I64, _SZ, _P, _I, _F = C.c_int64, C.c_size_t, C.c_void_p, C.c_int, C.c_float
@@ -65,6 +67,7 @@ _SIGS = {
     "vv_lm_head_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "vv_decode_step_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
     "vv_decode_step": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P]),
+    "vv_decode_status": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), C.POINTER(C.c_int32), _P]),
     "vv_decode_graph_create": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P, C.POINTER(_P)]),
     "vv_decode_graph_launch": (_I, [_P, _P]),
     "vv_decode_graph_destroy": (_I, [_P]),
@@ -202,6 +205,13 @@ def step_workspace(model: vv_model, batch: int, cap: int) -> int:
 
 def decode_step(model: vv_model, state: vv_state, stream=None):
     _check(lib().vv_decode_step(C.byref(model), C.byref(state), _stream(stream)), "vv_decode_step")
+
+
+def decode_status(model: vv_model, state: vv_state, stream=None) -> int:
+    """Sticky status word of the persistent path (0 = every in-kernel wait was satisfied)."""
+    out = C.c_int32(-1)
+    _check(lib().vv_decode_status(C.byref(model), C.byref(state), C.byref(out), _stream(stream)), "vv_decode_status")
+    return int(out.value)
 
 
 class DecodeGraph:

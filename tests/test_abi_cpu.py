@@ -133,7 +133,7 @@ def _model_struct(**over):
 
 def _state(ws_bytes, **over):
     kw = dict(batch=1, cap=64, input_embeds=64, pos=64, k_cache=64, v_cache=64, logits=None, token=64, h_trace=None,
-              workspace=256, workspace_bytes=ws_bytes, events=None, n_events=0)
+              workspace=256, workspace_bytes=ws_bytes, events=None, n_events=0, path=0)
     kw.update(over)
     return vvmod.vv_state(**kw)
 
@@ -153,8 +153,23 @@ def test_decode_step_validation():
     assert L.vv_decode_step(C.byref(_model_struct(lm_head=None)), C.byref(s), None) == vvmod.VV_ERR_NULL
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, workspace=300)), None) == vvmod.VV_ERR_RANGE
     evs = (C.c_void_p * 4)()
-    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=C.cast(evs, C.POINTER(C.c_void_p)),
-                                                      n_events=4)), None) == vvmod.VV_ERR_RANGE
+    ev = C.cast(evs, C.POINTER(C.c_void_p))
+    lay, per = vvmod.VV_PATH_LAYERED, vvmod.VV_PATH_PERSISTENT
+    # layered: 5 L + 3 events; persistent: ceil(L/32) + 2
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=4, path=lay)), None) == \
+        vvmod.VV_ERR_RANGE
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=2, path=per)), None) == \
+        vvmod.VV_ERR_RANGE
+    # unknown path; persistent path with a batch it does not take, or without layers
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, path=7)), None) == vvmod.VV_ERR_RANGE
+    need3 = vvmod.step_workspace(m, 3, 64)
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need3, batch=3, path=per)), None) == vvmod.VV_ERR_UNSUPPORTED
+    m0 = _model_struct(n_layers=0)
+    assert L.vv_decode_step(C.byref(m0), C.byref(_state(vvmod.step_workspace(m0, 1, 64), path=per)), None) == \
+        vvmod.VV_ERR_UNSUPPORTED
+    st = C.c_int32(0)
+    assert L.vv_decode_status(None, C.byref(s), C.byref(st), None) == vvmod.VV_ERR_NULL
+    assert L.vv_decode_status(C.byref(m), C.byref(s), None, None) == vvmod.VV_ERR_NULL
     h = C.c_void_p()
     assert L.vv_decode_graph_create(C.byref(m), C.byref(_state(need, events=C.cast(evs, C.POINTER(C.c_void_p)),
                                                               n_events=8)), None, C.byref(h)) == vvmod.VV_ERR_UNSUPPORTED

@@ -1,5 +1,6 @@
-"""GPU parity of the whole decode step (vv_decode_step) against the oracle's decode step, plus
-graph replay == eager and run-to-run determinism."""
+"""GPU parity of the whole decode step (vv_decode_step) against the oracle's decode step, for both
+implementations (the persistent single-launch kernel and the layered one-launch-per-stage path),
+plus graph replay == eager and run-to-run determinism."""
 import numpy as np
 import pytest
 
@@ -15,7 +16,8 @@ TOL = 2e-3
 class Case:
     """Seeded inputs of one decode step, on the GPU (packed by the library) and in the oracle."""
 
-    def __init__(self, shape, seed, layer_ids, pos, cap, outlier_frac=0.0, trace=False, with_lm=True):
+    def __init__(self, shape, seed, layer_ids, pos, cap, outlier_frac=0.0, trace=False, with_lm=True,
+                 path="auto"):
         import torch
         from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
         self.shape, self.seed, self.layer_ids = shape, seed, list(layer_ids)
@@ -25,7 +27,8 @@ class Case:
         self.glob = synth.model_globals(shape, seed, B, with_lm)
         self.dm = DeviceModel(shape, seed, self.layer_ids, with_lm=with_lm, max_batch=B, lm=self.glob.get("lm"),
                               gf=self.glob["gf"])
-        self.ds = DeviceState(self.dm, B, cap, trace=trace, logits=with_lm)
+        self.path = path
+        self.ds = DeviceState(self.dm, B, cap, trace=trace, logits=with_lm, path=path)
         self.K, self.V = [], []
         for i, li in enumerate(self.layer_ids):
             K, V = synth.layer_cache(self.w, seed, li, self.pos)
@@ -47,6 +50,7 @@ class Case:
         import torch
         self.ds.step()
         torch.cuda.synchronize()
+        assert self.ds.status() == 0, "an in-kernel wait of the persistent step gave up"
 
 
 def _check_tokens(tok, ref_logits):
@@ -81,26 +85,57 @@ def _compare(case, ref):
 TINY = synth.TinyShape(layers=2, hidden=256, n_q=4, n_kv=2, head_dim=128, inter=512, vocab=1000)
 
 
-@pytest.mark.parametrize("pos", [[33], [0], [47, 0, 12]])
-def test_step_tiny(cuda, pos):
-    case = Case(TINY, 0, range(2), pos, 48)
+PATHS = ["persistent", "layered"]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("pos", [[33], [0], [47], [63], [64], [100]])
+def test_step_tiny(cuda, pos, path):
+    """B = 1 at positions on both sides of the 64-position attention split edges."""
+    case = Case(TINY, 0, range(2), pos, 130, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
-def test_step_tiny_absmax_group7(cuda):
+def test_step_tiny_batched_layered(cuda):
+    case = Case(TINY, 0, range(2), [47, 0, 12], 48, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
+def test_step_persistent_rejects_batch3(cuda):
+    from int4_blockwise_gemv_amd import vv
+    with pytest.raises(vv.VVError) as e:
+        Case(TINY, 0, range(2), [47, 0, 12], 48, path="persistent").run()
+    assert e.value.status == vv.VV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_step_tiny_absmax_group7(cuda, path):
     shp = synth.TinyShape(layers=3, hidden=384, n_q=7, n_kv=1, head_dim=128, inter=640, vocab=777, mode="absmax")
-    case = Case(shp, 1, range(3), [20, 5], 40)
+    case = Case(shp, 1, range(3), [20] if path == "persistent" else [20, 5], 40, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
-def test_step_no_rope_no_bias(cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_step_no_rope_no_bias(cuda, path):
     shp = synth.TinyShape(layers=1, hidden=256, n_q=2, n_kv=2, head_dim=128, inter=256, vocab=300, qkv_bias=False,
                           rope_theta=0.0)
-    case = Case(shp, 2, range(1), [9], 16)
+    case = Case(shp, 2, range(1), [9], 16, path=path)
     case.run()
     _compare(case, case.oracle())
+
+
+def test_step_persistent_more_layers_than_one_launch(cuda):
+    """34 layers: the persistent path splits them over two launches (32 + 2)."""
+    shp = synth.TinyShape(layers=34, hidden=256, n_q=4, n_kv=2, head_dim=128, inter=256, vocab=500)
+    case = Case(shp, 6, range(34), [70], 80, path="persistent", trace=True)
+    case.run()
+    _compare(case, case.oracle())
+    lay = Case(shp, 6, range(34), [70], 80, path="layered", trace=True)
+    lay.run()
+    assert rel_err(host(case.ds.trace).astype(np.float64), host(lay.ds.trace).astype(np.float64)) <= TOL
 
 
 def test_step_zero_layers(cuda):
@@ -111,24 +146,27 @@ def test_step_zero_layers(cuda):
 
 
 @pytest.mark.timeout(300)
-def test_step_1p5b_width_two_layers(cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_step_1p5b_width_two_layers(cuda, path):
     """Two layers at full 1.5B width, P = 4096, full 151936-row lm_head."""
-    case = Case(synth.QWEN2_1P5B, 0, [0, 27], [4096], 4097)
+    case = Case(synth.QWEN2_1P5B, 0, [0, 27], [4096], 4097, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
 @pytest.mark.timeout(300)
-def test_step_7b_width_one_layer(cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_step_7b_width_one_layer(cuda, path):
     """One layer at full 7B width, P = 4000, full lm_head."""
-    case = Case(synth.QWEN2_7B, 0, [5], [4000], 4001)
+    case = Case(synth.QWEN2_7B, 0, [5], [4000], 4001, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
-def test_graph_replay_equals_eager_and_determinism(cuda):
+@pytest.mark.parametrize("path,pos", [("layered", [30, 7]), ("persistent", [30])])
+def test_graph_replay_equals_eager_and_determinism(cuda, path, pos):
     import torch
-    case = Case(TINY, 4, range(2), [30, 7], 40, trace=True)
+    case = Case(TINY, 4, range(2), pos, 40, trace=True, path=path)
     case.run()
     ref = [host(case.ds.logits).copy(), host(case.ds.token).copy(), host_u16(case.ds.k).copy(),
            host(case.ds.trace).copy()]
@@ -150,10 +188,11 @@ def test_graph_replay_equals_eager_and_determinism(cuda):
         g.close()
 
 
-def test_graph_follows_device_positions(cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_graph_follows_device_positions(cuda, path):
     """One captured graph serves successive positions: replays at pos, pos+1 == eager steps."""
     import torch
-    case = Case(TINY, 5, range(2), [10], 16)
+    case = Case(TINY, 5, range(2), [10], 16, path=path)
     g = case.ds.graph()
     try:
         outs = []
@@ -163,7 +202,7 @@ def test_graph_follows_device_positions(cuda):
             torch.cuda.synchronize()
             outs.append(host(case.ds.logits).copy())
         # eager from the same starting cache
-        case2 = Case(TINY, 5, range(2), [10], 16)
+        case2 = Case(TINY, 5, range(2), [10], 16, path=path)
         for i, p in enumerate((10, 11)):
             case2.ds.pos.fill_(p)
             case2.run()
@@ -173,12 +212,13 @@ def test_graph_follows_device_positions(cuda):
 
 
 @pytest.mark.timeout(600)
-def test_step_1p5b_full_depth_layerwise(cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_step_1p5b_full_depth_layerwise(cuda, path):
     """28 layers at 1.5B width (P = 4096, seed 0): every layer's GPU output h is checked against
     the oracle layer applied to the GPU's own input h for sampled layers, and the logits against
     the oracle lm_head on the GPU's final h."""
     shape = synth.QWEN2_1P5B
-    case = Case(shape, 0, range(shape.layers), [4096], 4097, trace=True)
+    case = Case(shape, 0, range(shape.layers), [4096], 4097, trace=True, path=path)
     case.run()
     tr = host(case.ds.trace).astype(np.float64)
     assert np.all(np.isfinite(tr))
