@@ -4,12 +4,14 @@
 // "VibeVoice-ASR — ONNX export for Vernacula", Highlights), with fp32 scores, softmax and
 // accumulation (the same page reports fp32 attention as the accuracy fix over bf16).
 //
-// Work unit: (sequence b, KV head, split of 64/128/256 positions).  A workgroup of 8 waves issues
-// every K and V row load of its split up front (16 lanes x 16 B per row, 4 rows = 1 KiB per wave
-// load) and serves all g = nq/nkv query heads of the group with them.  It writes
-// (max, sum, unnormalised output) per head; a second small kernel, one workgroup per query
-// head, merges the splits (online-softmax rescaling, fixed order).  The kernel boundary is the
-// hand-off, so no workgroup waits on another.
+// Work unit: (sequence b, KV head, split of S = 64 or 128 positions), one workgroup of 4 waves
+// serving all g = nq/nkv query heads of the group.  The group's q (a few KiB) is loaded first and
+// staged in LDS; then every K and V row of the split is loaded at once (lane = 8 dims of one
+// position, 16 lanes per 256-byte row, so each wave load is 1 KiB contiguous): 8 to 16 KiB in
+// flight per wave, and B * nkv * ceil(cap / S) workgroups.  Each split writes
+// (max, sum, unnormalised output) per head; a second small kernel, one workgroup per query head,
+// merges the splits (online-softmax rescaling, fixed order).  The kernel boundary is the
+// hand-off, so no workgroup waits on another.  Splits past the sequence exit at once.
 //
 // Decode-step flavour: q/k/v come from the fused projection output; the workgroup rotates q
 // (and, for the split that holds the new position, k) with RoPE, writes fp16 k and v into the
@@ -22,171 +24,162 @@ namespace {
 constexpr int kD = 128;           // head_dim
 constexpr int kMaxG = 8;          // query heads per KV head
 constexpr int kPS = 132;          // partial record: m, l, pad, pad, o[128]
-constexpr int kWaves = 8;         // 512 threads per workgroup
+constexpr int kWaves = 4;         // 256 threads per workgroup
 constexpr int kThreads = kWaves * 64;
+constexpr int kMaxSplits = 1024;  // splits per sequence the merge kernel takes
 
-__device__ void write_out(const AttnParams& p, int b, int kvh, int g, const float (*O)[kD], const float* L, int tid) {
-  for (int i = tid; i < g * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    const float o = O[hh][d] / L[hh];
-    const size_t oi = ((size_t)b * p.nq + (size_t)kvh * g + hh) * kD + d;
-    if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
-    else reinterpret_cast<float*>(p.out)[oi] = o;
+// Geometry of one workgroup's split.
+struct Geo { int b, kvh, bh, sidx, s0, npos, P; bool has_new; };
+
+__device__ __forceinline__ Geo geo(const AttnParams& p, int S) {
+  Geo g;
+  const int wg = blockIdx.x;
+  g.sidx = wg % p.nsplit;
+  g.bh = wg / p.nsplit;
+  g.b = g.bh / p.nkv;
+  g.kvh = g.bh % p.nkv;
+  g.s0 = g.sidx * S;
+  int len;
+  g.P = -1;
+  if (p.qkv) {
+    const int P = p.pos[g.b];
+    g.P = P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P);
+    len = g.P + 1;
+  } else {
+    const int l = p.lens[g.b];
+    len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
   }
+  g.npos = max(0, min(g.s0 + S, len) - g.s0);
+  g.has_new = g.P >= g.s0 && g.P < g.s0 + g.npos;
+  return g;
 }
 
-__device__ __forceinline__ void h8_to_f32(const u32x4& v, float* f) {
-  const uint32_t d4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const h2_t hv = as_h2(d4[i]);
-    f[2 * i] = (float)hv.x;
-    f[2 * i + 1] = (float)hv.y;
-  }
-}
-
-// NP passes of 4 positions per wave: split = 8 waves * 4 * NP positions
+// NP passes of 4 positions per wave: split S = 4 waves * 4 * NP positions
 template <int NP>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __restrict__ rope_cs) {
   constexpr int S = kWaves * 4 * NP;
-  __shared__ float qs[kMaxG][kD];
+  __shared__ __align__(16) float qs[kMaxG][kD];
   __shared__ float sc[kMaxG][S];
-  __shared__ float red[kWaves][kMaxG][kD];
-  __shared__ uint16_t knew[kD], vnew[kD];
+  __shared__ __align__(16) float red[kWaves][4][kMaxG][kD];   // [wave][position group][head][dim]
+  __shared__ __align__(16) uint16_t knew[kD], vnew[kD];
   __shared__ float mh[kMaxG], lh[kMaxG];
 
   const int g = p.nq / p.nkv;
-  const int wg = blockIdx.x;
-  const int sidx = wg % p.nsplit;
-  const int bh = wg / p.nsplit;            // b * nkv + kvh
-  const int b = bh / p.nkv, kvh = bh % p.nkv;
+  const Geo G = geo(p, S);
+  if (G.npos == 0) return;                 // past the sequence: the merge skips this split
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool step = p.qkv != nullptr;
 
-  // ---- every global load of the workgroup is issued before any result is used ----------------
-  // (K/V rows of the whole split do not depend on the sequence length: rows past it are read
-  // from inside the cache and masked out below; the new position's stale row is replaced)
-  const int s0 = sidx * S;
-  const size_t kvbase = ((size_t)b * p.nkv + kvh) * (size_t)p.cap * kD;
-  const uint16_t* Kc = p.kc + kvbase;
-  const uint16_t* Vc = p.vc + kvbase;
-  const int sl = lane & 15;            // dims 8*sl .. 8*sl+7
-  const int pg = lane >> 4;            // position within a pass
-  const int jw = w * 4 * NP;           // first local position of this wave
+  // ---- q first (it is needed first and is small), then every K/V row of the split ----------------
+  // step: thread t < 16 g rotates dims 4c..4c+3 with 64+4c..64+4c+3 of head t/16 (c = t%16);
+  //       the next 16 threads rotate the new k, the 16 after them take the new v
+  // stand-alone: thread t < 32 g takes dims 4(t%32)..+3 of head t/32
+  float4 qa = make_float4(0.f, 0.f, 0.f, 0.f), qb = qa, ca = make_float4(1.f, 0.f, 1.f, 0.f), cb = ca;
+  const int c16 = tid & 15;
+  if (step) {
+    const float* row = p.qkv + (size_t)G.b * p.ldqkv;
+    const float* src = nullptr;
+    if (tid < 16 * g) src = row + (size_t)(G.kvh * g + (tid >> 4)) * kD;
+    else if (tid < 16 * g + 16) src = row + (size_t)p.nq * kD + (size_t)G.kvh * kD;
+    else if (tid < 16 * g + 32) src = row + (size_t)(p.nq + p.nkv) * kD + (size_t)G.kvh * kD;
+    if (src) {
+      qa = *reinterpret_cast<const float4*>(src + 4 * c16);
+      qb = *reinterpret_cast<const float4*>(src + 64 + 4 * c16);
+      if (p.rope_theta > 0.f && tid < 16 * g + 16) {
+        ca = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2);
+        cb = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2 + 4);
+      }
+    }
+  } else if (tid < 32 * g) {
+    const size_t qi = ((size_t)G.b * p.nq + (size_t)G.kvh * g + (tid >> 5)) * kD + 4 * (tid & 31);
+    if (p.q_f16) {
+      const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.q) + qi);
+      const h2_t h0 = as_h2(h.x), h1 = as_h2(h.y);
+      qa = make_float4((float)h0.x, (float)h0.y, (float)h1.x, (float)h1.y);
+    } else {
+      qa = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + qi);
+    }
+  }
+  const size_t kvbase = ((size_t)G.b * p.nkv + G.kvh) * (size_t)p.cap * kD;
+  const int sl = lane & 15, pg = lane >> 4;
+  const int jw = w * 4 * NP;               // first local position of this wave
   u32x4 kr[NP], vr[NP];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int pos = s0 + jw + 4 * i + pg;
-    kr[i] = u32x4{0, 0, 0, 0};
-    vr[i] = u32x4{0, 0, 0, 0};
-    if (pos < p.cap) {
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kc + (size_t)pos * kD + 8 * sl));
-      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vc + (size_t)pos * kD + 8 * sl));
-    }
+  for (int r = 0; r < NP; ++r) {
+    const int pos = min(G.s0 + jw + 4 * r + pg, p.cap - 1);   // clamped rows are masked below
+    kr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.kc + kvbase + (size_t)pos * kD + 8 * sl));
+    vr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.vc + kvbase + (size_t)pos * kD + 8 * sl));
   }
-  const int pos_raw = step ? p.pos[b] : p.lens[b];
-  // q pair (j, j+64) of head hh = tid/64 (step: raw projection output + RoPE coefficients)
-  const int qh_ = tid >> 6, qj = tid & 63;
-  float q1 = 0.f, q2 = 0.f, rc = 1.f, rsn = 0.f, k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-  float qsa[2] = {0.f, 0.f};           // stand-alone flavour: two q values per thread
+
+  // ---- q (rotated) and the new k/v into LDS; the new position's cache slot ----------------------
   if (step) {
-    const float* row = p.qkv + (size_t)b * p.ldqkv;
-    if (qh_ < g) {
-      const float* qh = row + (size_t)(kvh * g + qh_) * kD;
-      q1 = qh[qj];
-      q2 = qh[qj + 64];
-    }
-    if (p.rope_theta > 0.f) {
-      const float* cs = rope_cs + ((size_t)b * 64 + qj) * 2;
-      rc = cs[0];
-      rsn = cs[1];
-    }
-    if (tid < 64) {
-      const float* kh = row + (size_t)p.nq * kD + (size_t)kvh * kD;
-      const float* vh = row + (size_t)(p.nq + p.nkv) * kD + (size_t)kvh * kD;
-      k1 = kh[qj]; k2 = kh[qj + 64]; v1 = vh[qj]; v2 = vh[qj + 64];
-    }
-  } else {
+    // pair (j, j+64), j = 4c + i: (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin); v is not rotated
+    const bool rot = tid < 16 * g + 16;
+    const float c4[4] = {ca.x, ca.z, cb.x, cb.z}, s4[4] = {ca.y, ca.w, cb.y, cb.w};
+    const float x1[4] = {qa.x, qa.y, qa.z, qa.w}, x2[4] = {qb.x, qb.y, qb.z, qb.w};
+    float r1[4], r2[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = tid + u * kThreads;
-      if (i < g * kD) {
-        const size_t qi = ((size_t)b * p.nq + (size_t)kvh * g + i / kD) * kD + i % kD;
-        qsa[u] = p.q_f16 ? h2f(reinterpret_cast<const uint16_t*>(p.q)[qi]) : reinterpret_cast<const float*>(p.q)[qi];
+    for (int i = 0; i < 4; ++i) {
+      r1[i] = rot ? x1[i] * c4[i] - x2[i] * s4[i] : x1[i];
+      r2[i] = rot ? x2[i] * c4[i] + x1[i] * s4[i] : x2[i];
+    }
+    if (tid < 16 * g) {
+      const int hh = tid >> 4;
+      *reinterpret_cast<float4*>(&qs[hh][4 * c16]) = make_float4(r1[0], r1[1], r1[2], r1[3]);
+      *reinterpret_cast<float4*>(&qs[hh][64 + 4 * c16]) = make_float4(r2[0], r2[1], r2[2], r2[3]);
+    } else if (G.has_new && tid < 16 * g + 32) {
+      uint16_t* dst = tid < 16 * g + 16 ? knew : vnew;
+      uint16_t* cache = (tid < 16 * g + 16 ? p.kc : p.vc) + kvbase + (size_t)G.P * kD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t a = f2h(r1[i]), bb = f2h(r2[i]);
+        dst[4 * c16 + i] = a;
+        dst[64 + 4 * c16 + i] = bb;
+        cache[4 * c16 + i] = a;
+        cache[64 + 4 * c16 + i] = bb;
       }
     }
-  }
-
-  int len, P = -1;
-  if (step) {
-    P = pos_raw < 0 ? 0 : (pos_raw >= p.cap ? p.cap - 1 : pos_raw);
-    len = P + 1;
-  } else {
-    len = pos_raw < 1 ? 1 : (pos_raw > p.cap ? p.cap : pos_raw);
-  }
-  const int npos = max(0, min(s0 + S, len) - s0);
-  const bool has_new = P >= s0 && P < s0 + npos;
-
-  // ---- q (and the new k, v) into LDS -----------------------------------------------------------
-  if (step) {
-    if (qh_ < g) {
-      qs[qh_][qj] = q1 * rc - q2 * rsn;
-      qs[qh_][qj + 64] = q2 * rc + q1 * rsn;
-    }
-    if (has_new && tid < 64) {
-      const uint16_t a = f2h(k1 * rc - k2 * rsn), bb = f2h(k2 * rc + k1 * rsn), c1 = f2h(v1), c2 = f2h(v2);
-      knew[qj] = a; knew[qj + 64] = bb; vnew[qj] = c1; vnew[qj + 64] = c2;
-      uint16_t* kd = p.kc + kvbase + (size_t)P * kD;
-      uint16_t* vd = p.vc + kvbase + (size_t)P * kD;
-      kd[qj] = a; kd[qj + 64] = bb; vd[qj] = c1; vd[qj + 64] = c2;
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = tid + u * kThreads;
-      if (i < g * kD) qs[i / kD][i % kD] = qsa[u];
-    }
+  } else if (tid < 32 * g) {
+    *reinterpret_cast<float4*>(&qs[tid >> 5][4 * (tid & 31)]) = qa;
   }
   __syncthreads();
-  if (has_new) {  // the new position reads the rows just written to LDS
+  if (G.has_new) {  // the new position's row was loaded from the cache before it was written
 #pragma unroll
-    for (int i = 0; i < NP; ++i)
-      if (s0 + jw + 4 * i + pg == P) {
-        kr[i] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
-        vr[i] = *reinterpret_cast<const u32x4*>(&vnew[8 * sl]);
+    for (int r = 0; r < NP; ++r)
+      if (G.s0 + jw + 4 * r + pg == G.P) {
+        kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
+        vr[r] = *reinterpret_cast<const u32x4*>(&vnew[8 * sl]);
       }
   }
+  // rows past the sequence get probability 0; zero their V so that whatever the cache holds there
+  // (it is never part of the attention) cannot turn 0 * v into a NaN
+#pragma unroll
+  for (int r = 0; r < NP; ++r)
+    if (jw + 4 * r + pg >= G.npos) vr[r] = u32x4{0, 0, 0, 0};
 
-  // ---- scores (16 lanes per position, reduced across the 16) ----------------------------------
-  float qr[kMaxG][8];
+  // ---- scores: 16 lanes per position, reduced across the 16 ---------------------------------------
+#pragma unroll 1
+  for (int hh = 0; hh < g; ++hh) {
+    float q8[8];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh)
+    for (int t = 0; t < 8; ++t) q8[t] = qs[hh][8 * sl + t];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qr[hh][i] = hh < g ? qs[hh][8 * sl + i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int j = jw + 4 * i + pg;
-    float kf[8];
-    h8_to_f32(kr[i], kf);
-#pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
-      if (hh < g) {
-        float a = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) a = fmaf(qr[hh][t], kf[t], a);
-        a = row16_sum(a);
-        if (sl == 0) sc[hh][j] = j < npos ? a * p.scale : -INFINITY;
-      }
+    for (int r = 0; r < NP; ++r) {
+      float a = row16_sum(dot8_mix(q8, kr[r], 0.f));
+      const int j = jw + 4 * r + pg;
+      if (sl == 0) sc[hh][j] = j < G.npos ? a * p.scale : -INFINITY;
     }
   }
   __syncthreads();
 
-  // ---- split-local softmax statistics ---------------------------------------------------------
+  // ---- split-local softmax statistics, one wave per head -----------------------------------------
   for (int hh = w; hh < g; hh += kWaves) {
     float m = -INFINITY;
+#pragma unroll
     for (int j = lane; j < S; j += 64) m = fmaxf(m, sc[hh][j]);
     m = wave_max(m);
     float l = 0.f;
+#pragma unroll
     for (int j = lane; j < S; j += 64) {
       const float e = (m == -INFINITY) ? 0.f : expf(sc[hh][j] - m);
       sc[hh][j] = e;
@@ -197,134 +190,130 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
   __syncthreads();
 
-  // ---- weighted sum of V ------------------------------------------------------------------------
-  float acc[kMaxG][8];
+  // ---- P.V: lane holds 8 dims of one position per pass; its sums over its NP positions go to LDS
+  // as they are (no cross-lane shuffles), the 16 (wave, position group) partials are added below
+#pragma unroll 1
+  for (int hh = 0; hh < g; ++hh) {
+    float acc[8];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh)
+    for (int t = 0; t < 8; ++t) acc[t] = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[hh][t] = 0.f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int j = jw + 4 * i + pg;
-    float vf[8];
-    h8_to_f32(vr[i], vf);
-#pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
-      if (hh < g) {
-        const float pj = sc[hh][j];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[hh][t] = fmaf(pj, vf[t], acc[hh][t]);
-      }
+    for (int r = 0; r < NP; ++r) {
+      const float pj = sc[hh][jw + 4 * r + pg];
+      const u32x4 v = vr[r];
+      acc[0] = fma_mix_lo(pj, v.x, acc[0]); acc[1] = fma_mix_hi(pj, v.x, acc[1]);
+      acc[2] = fma_mix_lo(pj, v.y, acc[2]); acc[3] = fma_mix_hi(pj, v.y, acc[3]);
+      acc[4] = fma_mix_lo(pj, v.z, acc[4]); acc[5] = fma_mix_hi(pj, v.z, acc[5]);
+      acc[6] = fma_mix_lo(pj, v.w, acc[6]); acc[7] = fma_mix_hi(pj, v.w, acc[7]);
     }
-  }
-#pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
-    if (hh < g) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float a = rows_lanewise_sum(acc[hh][t]);
-        if (pg == 0) red[w][hh][8 * sl + t] = a;
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < g * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    float o = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) o += red[v][hh][d];
-    red[0][hh][d] = o;
+    float* dst = &red[w][pg][hh][8 * sl];
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
   __syncthreads();
 
-  // ---- finish: one split writes the output; otherwise its record goes to the merge kernel -----
-  if (p.nsplit == 1) {
-    write_out(p, b, kvh, g, red[0], lh, tid);
-    return;
-  }
-  float* rec = p.part + ((size_t)bh * p.nsplit + sidx) * kMaxG * kPS;
+  // ---- the split's output: final when it is the only split, else a record for the merge ----------
+  const bool single = p.nsplit == 1;
+  float* rec = p.part + ((size_t)G.bh * p.nsplit + G.sidx) * kMaxG * kPS;
   for (int i = tid; i < g * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    rec[(size_t)hh * kPS + 4 + d] = red[0][hh][d];
+    const int hh = i >> 7, d = i & 127;
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o += red[ww][q][hh][d];
+    if (single) {
+      const size_t oi = ((size_t)G.b * p.nq + (size_t)G.kvh * g + hh) * kD + d;
+      if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o / lh[hh]);
+      else reinterpret_cast<float*>(p.out)[oi] = o / lh[hh];
+    } else {
+      rec[(size_t)hh * kPS + 4 + d] = o;
+    }
   }
-  if (tid < g) {
+  if (!single && tid < g) {
     rec[(size_t)tid * kPS + 0] = mh[tid];
     rec[(size_t)tid * kPS + 1] = lh[tid];
   }
 }
 
-// One workgroup per (sequence, query head), one thread per output dimension: combines the split
-// records with the online-softmax rescaling M = max m_s, L = sum e^(m_s-M) l_s,
-// o = sum e^(m_s-M) o_s / L, splits in a fixed order.  All loads are issued before any use.
-__global__ __launch_bounds__(kD) void k_attn_merge(AttnParams p) {
-  constexpr int kChunk = 32;           // splits whose outputs one thread holds at a time
-  __shared__ float ms_[512], ls_[512], wsc[512];
-  __shared__ float Ms, Ls;
+// One workgroup per (sequence, query head): thread (half, d) holds dim d of the splits of its
+// half.  All record loads are issued at once; the split weights e_s = exp(m_s - M) are computed
+// once in LDS.  o = sum_s e_s o_s / sum_s e_s l_s, splits in a fixed order.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int S) {
+  constexpr int kChunk = 32;
+  __shared__ float ms_[kMaxSplits], ls_[kMaxSplits], ws_[kMaxSplits];
+  __shared__ float part[2][kD];
+  __shared__ float Ls;
   const int g = p.nq / p.nkv;
   const int bq = blockIdx.x;                 // b * nq + head
   const int b = bq / p.nq, h = bq % p.nq;
   const int kvh = h / g, hh = h % g;
   const int bh = b * p.nkv + kvh;
-  const int d = threadIdx.x;
+  int len;
+  if (p.qkv) {
+    const int P = p.pos[b];
+    len = (P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P)) + 1;
+  } else {
+    const int l = p.lens[b];
+    len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
+  }
+  const int n = (len + S - 1) / S;           // splits that hold positions
+  const int tid = threadIdx.x, d = tid & 127, half = tid >> 7;
+  const int per = (n + 1) >> 1;
+  const int s_beg = half * per, s_end = min(n, s_beg + per);
   const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
   const size_t stride = (size_t)kMaxG * kPS;
-  const int n = p.nsplit;
-  // issue the (m, l) loads and the first chunk of outputs together
-  for (int s = d; s < n; s += kD) {
+  for (int s = tid; s < n; s += 256) {
     ms_[s] = rec0[s * stride];
     ls_[s] = rec0[s * stride + 1];
   }
   float v[kChunk];
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u) v[u] = u < n ? rec0[u * stride + 4 + d] : 0.f;
+  for (int u = 0; u < kChunk; ++u) v[u] = s_beg + u < s_end ? rec0[(s_beg + u) * stride + 4 + d] : 0.f;
   __syncthreads();
-  if (d < 64) {
+  if (tid < 64) {
     float M = -INFINITY;
-    for (int s = d; s < n; s += 64) M = fmaxf(M, ms_[s]);
+    for (int s = tid; s < n; s += 64) M = fmaxf(M, ms_[s]);
     M = wave_max(M);
     float L = 0.f;
-    for (int s = d; s < n; s += 64) {
-      const float e = ms_[s] == -INFINITY ? 0.f : expf(ms_[s] - M);
-      wsc[s] = e;
+    for (int s = tid; s < n; s += 64) {
+      const float e = expf(ms_[s] - M);
+      ws_[s] = e;
       L = fmaf(e, ls_[s], L);
     }
     L = wave_sum(L);
-    if (d == 0) { Ms = M; Ls = L; }
+    if (tid == 0) Ls = L;
   }
   __syncthreads();
   float O = 0.f;
 #pragma unroll
   for (int u = 0; u < kChunk; ++u)
-    if (u < n) O = fmaf(wsc[u], v[u], O);
-  for (int s0 = kChunk; s0 < n; s0 += kChunk) {
+    if (s_beg + u < s_end) O = fmaf(ws_[s_beg + u], v[u], O);
+  for (int c0 = s_beg + kChunk; c0 < s_end; c0 += kChunk) {
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = s0 + u < n ? rec0[(s0 + u) * stride + 4 + d] : 0.f;
+    for (int u = 0; u < kChunk; ++u) v[u] = c0 + u < s_end ? rec0[(c0 + u) * stride + 4 + d] : 0.f;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u)
-      if (s0 + u < n) O = fmaf(wsc[s0 + u], v[u], O);
+      if (c0 + u < s_end) O = fmaf(ws_[c0 + u], v[u], O);
   }
-  const float o = O / Ls;
-  const size_t oi = ((size_t)b * p.nq + h) * kD + d;
-  if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
-  else reinterpret_cast<float*>(p.out)[oi] = o;
-}
-
-int pow2ceil(int64_t v) {
-  int r = 1;
-  while (r < v) r <<= 1;
-  return r;
+  part[half][d] = O;
+  __syncthreads();
+  if (half == 0) {
+    const float o = (part[0][d] + part[1][d]) / Ls;
+    const size_t oi = ((size_t)b * p.nq + h) * kD + d;
+    if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
+    else reinterpret_cast<float*>(p.out)[oi] = o;
+  }
 }
 
 }  // namespace
 
-// Split size 64/128/256 positions: aims at ~192 workgroups, at most 512 splits per sequence
-// (the merge kernel keeps one weight per split in LDS).
+// Split size 64 positions, or 128 when that would give more than ~2048 workgroups; at most
+// 1024 splits per sequence (cap <= 131072).
 void attn_plan(AttnParams& p) {
-  const int64_t work = (int64_t)p.B * p.nkv * p.cap;
-  int S = pow2ceil(cdiv(work, 192));
-  S = S < 64 ? 64 : (S > 256 ? 256 : S);
-  p.split = S;
-  p.nsplit = (int)cdiv(p.cap, S);
+  const int64_t wgs64 = (int64_t)p.B * p.nkv * cdiv(p.cap, 64);
+  p.split = wgs64 > 2048 ? 128 : 64;
+  p.nsplit = (int)cdiv(p.cap, p.split);
 }
 
 size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit) {
@@ -340,14 +329,11 @@ void attn_set_workspace(AttnParams& p, void* ws) {
 
 hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st) {
   const int grid = p.B * p.nkv * p.nsplit;
-  switch (p.split) {
-    case 64: hipLaunchKernelGGL(k_attn<2>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs); break;
-    case 128: hipLaunchKernelGGL(k_attn<4>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs); break;
-    default: hipLaunchKernelGGL(k_attn<8>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs); break;
-  }
+  if (p.split == 64) hipLaunchKernelGGL(k_attn<4>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs);
+  else hipLaunchKernelGGL(k_attn<8>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(p.B * p.nq), dim3(kD), 0, st, p);
+  hipLaunchKernelGGL(k_attn_merge, dim3(p.B * p.nq), dim3(256), 0, st, p, p.split);
   return hipGetLastError();
 }
 
@@ -380,7 +366,7 @@ int vv_gqa_decode(const void* q, int q_dtype, const uint16_t* k_cache, const uin
   VV_REQUIRE(out_dtype == VV_F16 || out_dtype == VV_F32, VV_ERR_DTYPE, "vv_gqa_decode: unknown out dtype");
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15) == 0,
              VV_ERR_RANGE, "vv_gqa_decode: caches must be 16-byte aligned");
-  VV_REQUIRE(cap <= 256 * 512, VV_ERR_RANGE, "vv_gqa_decode: cap %d > 131072 positions", cap);
+  VV_REQUIRE(cap <= 128 * kMaxSplits, VV_ERR_RANGE, "vv_gqa_decode: cap %d > 131072 positions", cap);
   const size_t need = vv_gqa_decode_workspace(B, nq, nkv, cap);
   VV_REQUIRE(ws && ws_bytes >= need, VV_ERR_WORKSPACE, "vv_gqa_decode: workspace needs %zu bytes", need);
   AttnParams p{};

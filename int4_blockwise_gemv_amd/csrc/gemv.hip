@@ -2,12 +2,11 @@
 //
 // Decomposition: a wave owns one 64-row tile and one group of 8 consecutive blocks (lane i
 // accumulates row 64t+i, so each 16-byte block load of the wave is one contiguous 1 KiB run, and
-// the group's 8 fp16 scales are one more 16-byte load); a workgroup takes 4 consecutive groups of
-// one tile, and a tile's groups are spread over `wpt` = ceil(groups / 4) workgroups.  All nine
-// loads of a wave are in flight at once, and the grid is far larger than the CU count: short
-// waves keep the HBM busiest.
+// the group's 8 fp16 scales are one more 16-byte load); a workgroup takes `wpg` consecutive
+// groups of one tile (up to 16), and a tile's groups are spread over `wpt` workgroups.  All nine
+// loads of a wave are in flight at once: short waves keep the HBM busiest.
 //
-// Activations: before any weight load, the workgroup's 1024-element slice of x (per batch row)
+// Activations: before any weight load, the workgroup's slice of x (256 elements per wave, per row)
 // goes to LDS with one vector load per thread; the waves then read their block's 32 values as
 // LDS broadcasts.  (Scalar loads issued block by block would put one L2 latency per block on the
 // path.)
@@ -20,7 +19,7 @@
 // removed once per block by subtracting C_b = 72 * sum_j x_j; the block sum is scaled by the
 // block's fp16 scale in fp32.
 //
-// Split-K: the 4 waves of a workgroup are reduced in LDS; with wpt > 1 the last workgroup to
+// Split-K: the waves of a workgroup are reduced in LDS; with wpt > 1 the last workgroup to
 // arrive at a tile adds the partials in a fixed order and runs the epilogue, so results do not
 // depend on timing.  With wpt = 1 the workgroup finishes its tile directly.
 #include "vv_internal.h"
@@ -29,7 +28,8 @@
 namespace vv {
 namespace {
 
-constexpr int kWavesPerWG = 4;
+constexpr int kWavesSmallM = 4;   // most waves (groups) per workgroup for M <= 2 (wider was slower)
+constexpr int kWavesLargeM = 4;   // for M > 2 (LDS holds M activation slices)
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
 
 // Operands of the epilogue, loaded by wave 0 of every workgroup before the weight stream so the
@@ -117,13 +117,18 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
   }
 }
 
-constexpr int kItemK = kWavesPerWG * kBatch * kBlock;   // K elements per workgroup (1024)
+template <int MT> struct WavesFor { static constexpr int value = MT <= 2 ? kWavesSmallM : kWavesLargeM; };
 
+// WMAX waves at most; the launch uses p.wpg = blockDim.x / 64 of them (one 8-block group each)
 template <int MT>
-__global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
-                                              const uint4* __restrict__ sw, const uint16_t* __restrict__ x) {
+__global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
+                                                                  const uint4* __restrict__ sw,
+                                                                  const uint16_t* __restrict__ x) {
+  constexpr int WMAX = WavesFor<MT>::value;
+  constexpr int kItemK = WMAX * kBatch * kBlock;  // K elements per workgroup at most
   __shared__ __align__(16) uint16_t xs[MT][kItemK];
-  __shared__ float red[kWavesPerWG][MT][kTileRows];
+  __shared__ float red[WMAX][MT][kTileRows];
+  const int W = p.wpg;
   const int K = p.K;
   const int nb = K / kBlock;
   const int ng = (nb + kBatch - 1) / kBatch;
@@ -135,8 +140,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
   const int kg = L % p.wpt;
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
-  const int e0 = kg * kItemK;                       // first K element of this workgroup
-  const int ne = min(K - e0, kItemK);
+  const int e0 = kg * W * kBatch * kBlock;          // first K element of this workgroup
+  const int ne = min(K - e0, W * kBatch * kBlock);
 
   // activation slice first (its loads return before the weights), 8 bytes per thread per row
 #pragma unroll
@@ -145,8 +150,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
     if (m < M && e < ne)
       *reinterpret_cast<uint2*>(&xs[m][e]) = *reinterpret_cast<const uint2*>(x + (size_t)m * K + e0 + e);
   }
+  static_assert(kItemK <= 4 * 64 * WMAX, "one 8-byte activation load per thread covers the slice");
   // this wave's group: 8 blocks and their 8 scales
-  const int grp = kg * kWavesPerWG + w;
+  const int grp = kg * W + w;
   const int b0 = grp * kBatch;
   const int nblk = min(max(nb - b0, 0), kBatch);
   const u32x4* qp = reinterpret_cast<const u32x4*>(qw) + ((size_t)tile * nb + b0) * kTileRows + lane;
@@ -209,7 +215,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     tot[m] = 0.f;
-    if (m < M) tot[m] = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
+    if (m < M) {
+      float t = 0.f;
+      for (int v = 0; v < W; ++v) t += red[v][m][lane];
+      tot[m] = t;
+    }
   }
   if (p.wpt == 1) {
     epilogue<MT>(p, tile, tot, ep, lane);
@@ -237,19 +247,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p, const uint4* __restr
 
 int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
-struct Plan { int kb, wpt, grid; };
+struct Plan { int kb, wpg, wpt, grid; };
 
-// One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave
-// and four consecutive groups per workgroup, so a tile is split over ceil(groups / 4)
-// workgroups.  Short waves and a grid well beyond the CU count keep the HBM busiest (a wave that
-// streams tens of KiB serialises its own latency), at the price of one cross-workgroup
-// reduction per tile.
+// One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave.
+// Batch <= 2: up to 16 waves (groups) per workgroup, the groups of a tile spread evenly over
+// wpt = ceil(groups / 16) workgroups; a tile of <= 16 groups is one workgroup and needs no
+// cross-workgroup reduction.  Larger batches: 4 waves per workgroup (LDS holds M slices).
 Plan make_plan(int M, int ntiles, int nb) {
-  (void)M;
-  const int nb8 = (int)cdiv(nb, kBatch);
+  const int ng = (int)cdiv(nb, kBatch);
+  const int wmax = M <= 2 ? kWavesSmallM : kWavesLargeM;
   Plan pl;
   pl.kb = kBatch;
-  pl.wpt = (int)cdiv(nb8, kWavesPerWG);
+  pl.wpt = (int)cdiv(ng, wmax);
+  pl.wpg = (int)cdiv(ng, pl.wpt);
   pl.grid = (int)(cdiv((int64_t)ntiles * pl.wpt, kNumXcd) * kNumXcd);
   return pl;
 }
@@ -259,6 +269,7 @@ Plan make_plan(int M, int ntiles, int nb) {
 void gemv_plan(GemvParams& p) {
   const Plan pl = make_plan(p.M, p.ntiles, p.K / kBlock);
   p.kb = pl.kb;
+  p.wpg = pl.wpg;
   p.wpt = pl.wpt;
   p.grid = pl.grid;
 }
@@ -283,11 +294,11 @@ hipError_t gemv_launch(const GemvParams& p, hipStream_t st) {
   const uint4* q = reinterpret_cast<const uint4*>(p.q);
   const uint4* s = reinterpret_cast<const uint4*>(p.s);
   switch (mt_of(p.M)) {
-    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
-    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
-    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
-    case 8: hipLaunchKernelGGL(k_gemv<8>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
-    default: hipLaunchKernelGGL(k_gemv<16>, dim3(p.grid), dim3(256), 0, st, p, q, s, p.x); break;
+    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
+    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
+    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
+    case 8: hipLaunchKernelGGL(k_gemv<8>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
+    default: hipLaunchKernelGGL(k_gemv<16>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
   }
   return hipGetLastError();
 }

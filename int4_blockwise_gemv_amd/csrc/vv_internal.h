@@ -78,11 +78,15 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f<0x140>(v));
   return v;
 }
-// lane-wise sum over the 4 rows of the wave (every lane l gets sum_r v[16r + l%16])
+// lane-wise sum over the 4 rows of the wave (every lane l gets sum_r v[16r + l%16]):
+// v_permlane16_swap exchanges the odd rows of its first operand with the even rows of its
+// second, so with both operands = v the two results add up to (r0+r1, r0+r1, r2+r3, r2+r3);
+// v_permlane32_swap then does the same with the two halves.  Fixed order, no LDS traffic.
 __device__ __forceinline__ float rows_lanewise_sum(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 // sum / max over the whole wave (uniform result)
 __device__ __forceinline__ float wave_sum(float v) {
@@ -100,6 +104,26 @@ __device__ __forceinline__ float wave_max(float v) {
   const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// a * fp16(lo or hi half of h) + c in fp32 (v_fma_mix_f32: the fp16 operand is used exactly)
+__device__ __forceinline__ float fma_mix_lo(float a, uint32_t h, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(h), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float fma_mix_hi(float a, uint32_t h, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(h), "v"(c));
+  return d;
+}
+// sum_t a[t] * fp16 element t of the 8 packed in v, from c
+__device__ __forceinline__ float dot8_mix(const float* a, const u32x4& v, float c) {
+  c = fma_mix_lo(a[0], v.x, c); c = fma_mix_hi(a[1], v.x, c);
+  c = fma_mix_lo(a[2], v.y, c); c = fma_mix_hi(a[3], v.y, c);
+  c = fma_mix_lo(a[4], v.z, c); c = fma_mix_hi(a[5], v.z, c);
+  c = fma_mix_lo(a[6], v.w, c); c = fma_mix_hi(a[7], v.w, c);
+  return c;
 }
 
 // Monotone key for a float: larger float -> larger key; NaN maps below every number.
@@ -169,7 +193,7 @@ struct GemvParams {
   int ntiles;                // tiles in the matrix
   float* part;               // workspace partials
   unsigned* cnt;             // workspace counters
-  int kb, wpt, grid;         // decomposition (filled by gemv_plan)
+  int kb, wpg, wpt, grid;    // decomposition (filled by gemv_plan): waves per workgroup, workgroups per tile
   int epi;
   // EPI_STORE
   const uint16_t* bias;      // fp16 [N] or null
@@ -187,7 +211,7 @@ struct GemvParams {
   uint16_t* act;             // fp16 [M][N]
 };
 
-void gemv_plan(GemvParams& p);                       // fills kb/wpt/grid
+void gemv_plan(GemvParams& p);                       // fills kb/wpg/wpt/grid
 size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
 hipError_t gemv_launch(const GemvParams& p, hipStream_t st);

@@ -57,6 +57,7 @@ def test_gqa_tiny_brute_shape(cuda):
     (12, 2, 700, [513, 1, 77, 700]),  # ragged batch
     (8, 8, 64, [64, 31]),             # group of 1
     (16, 2, 300, [300]),              # group of 8
+    (8, 8, 17000, [17000, 5]),        # > 2048 workgroups at 64 positions: 128-position splits
 ])
 def test_gqa_shapes_and_ragged(cuda, nq, nkv, cap, lens):
     B = len(lens)
