@@ -96,60 +96,37 @@ def build_inputs(wl, seed, path="auto"):
     return dm, ds, lens
 
 
-def kernel_breakdown_persistent(ds, n_layers, reps=5):
-    """Mean duration (ms) of the persistent layer launch(es) and of the lm_head (HIP events)."""
+def kernel_breakdown(ds, n_layers, steps, persistent):
+    """Mean kernel time (ms) per operation of the step over `steps` eager steps.
+
+    Each operation's kernels are launched with hipExtLaunchKernel start/stop events, which
+    receive the kernels' own dispatch start and end times (the values rocprofv3 reports), not the
+    time the stream reaches a marker."""
     import ctypes as C
     import torch
-    n_launch = -(-n_layers // 32)
-    n_ev = n_launch + 2
+    if persistent:
+        names = ["layers", "lm_head"]
+    else:
+        names = ["prep"] + ["qkv", "attn", "o", "gateup", "down"] * n_layers + ["lm_head"]
+    n_ev = 2 * len(names)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    for e in evs:
+    for e in evs:  # torch creates the HIP event on first record
         e.record()
     torch.cuda.synchronize()
     arr = (C.c_void_p * n_ev)(*[C.c_void_p(e.cuda_event) for e in evs])
     ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
     ds.struct.n_events = n_ev
-    layers, lm = [], []
+    acc = {k: [] for k in names}
     try:
-        for _ in range(reps):
+        for _ in range(steps):
             ds.step()
             torch.cuda.synchronize()
-            layers.append(evs[0].elapsed_time(evs[n_launch]))
-            lm.append(evs[n_launch].elapsed_time(evs[n_launch + 1]))
+            for i, k in enumerate(names):
+                acc[k].append(evs[2 * i].elapsed_time(evs[2 * i + 1]))
     finally:
         ds.struct.events = None
         ds.struct.n_events = 0
-    return {"layers": float(np.median(layers)), "lm_head": float(np.median(lm))}
-
-
-def kernel_breakdown(ds, n_layers, reps=3):
-    """Mean duration (ms) per kernel kind from HIP events recorded between the kernels of eager steps."""
-    import ctypes as C
-    import torch
-    n_kern = 5 * n_layers + 2
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_kern + 1)]
-    for e in evs:  # torch creates the HIP event on first record
-        e.record()
-    torch.cuda.synchronize()
-    arr = (C.c_void_p * (n_kern + 1))(*[C.c_void_p(e.cuda_event) for e in evs])
-    ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
-    ds.struct.n_events = n_kern + 1
-    kinds = ["qkv", "attn", "o", "gateup", "down"]
-    acc = {k: [] for k in kinds + ["prep", "lm_head"]}
-    try:
-        for _ in range(reps):
-            ds.step()
-            torch.cuda.synchronize()
-            t = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_kern)]
-            acc["prep"].append(t[0])
-            for l in range(n_layers):
-                for j, k in enumerate(kinds):
-                    acc[k].append(t[1 + 5 * l + j])
-            acc["lm_head"].append(t[-1])
-    finally:
-        ds.struct.events = None
-        ds.struct.n_events = 0
-    return {k: float(np.mean(v)) for k, v in acc.items() if v}
+    return {k: float(np.mean(v)) for k, v in acc.items()}
 
 
 def cpu_baseline(wl, seed, budget_s=25.0):
@@ -191,6 +168,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "persistent", "layered"])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this decode step is not sharded across GPUs "
@@ -199,8 +178,17 @@ def main():
 
     import torch
     from int4_blockwise_gemv_amd import synth
-    wl = synth.WORKLOADS[args.workload]
     assert torch.cuda.is_available()
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+    wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     from int4_blockwise_gemv_amd import vv
     dm, ds, lens = build_inputs(wl, args.seed, args.path)
@@ -228,16 +216,14 @@ def main():
     wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
     total = wb + kvb + lmb
     tag = "7b" if s.hidden == 3584 else "1p5b"
+    kb = kernel_breakdown(ds, s.layers, args.steps, persistent)
+    log(f"kernel means over {args.steps} eager steps (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
     if persistent:
-        kb = kernel_breakdown_persistent(ds, s.layers)
-        log("kernel medians (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
         dom_bytes, dom_ms = wb + kvb, kb["layers"]
         dom_name = "persistent decode-layer kernel (all layers: int4 GEMVs + attention)"
         traffic = read_traffic("persistent_" + tag, ("mega.hip", "gemv_core.h", "vv_internal.h"))
         sum_kern = kb["layers"] + kb["lm_head"]
     else:
-        kb = kernel_breakdown(ds, s.layers)
-        log("kernel means (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in kb.items()))
         dom_bytes = 2 * s.inter * s.hidden // 2 + 2 * s.inter * (s.hidden // 32) * 2
         dom_ms = kb["gateup"]
         dom_name = "gate/up int4 GEMV (+SiLU*up)"

@@ -234,14 +234,15 @@ typedef struct vv_state {
   void* workspace;                 /* device, vv_decode_step_workspace(model, batch, cap) bytes,
                                       zero-filled before first use */
   size_t workspace_bytes;
-  void** events;                   /* optional HOST array of hipEvent_t used to time the kernels of
-                                      an eager vv_decode_step: event i is recorded on the stream
-                                      before kernel i and one more after the last kernel.
-                                      Layered path: prep, then per layer qkv, attention, o,
-                                      gate/up, down, then lm_head (5*n_layers + 3 events).
-                                      Persistent path: one launch per 32 layers, then lm_head
-                                      (ceil(n_layers/32) + 2 events).  NULL disables; graphs
-                                      reject it. */
+  void** events;                   /* optional HOST array of hipEvent_t (created with timing on)
+                                      used to time the operations of an eager vv_decode_step:
+                                      events 2i and 2i+1 receive the start and end times of
+                                      operation i's kernels (hipExtLaunchKernel's kernel
+                                      timestamps, not stream markers).  Layered path: prep, then
+                                      per layer qkv, attention (+ split merge), o, gate/up, down,
+                                      then lm_head: 2*(5*n_layers + 2) events.  Persistent path:
+                                      all layers (counter reset + the single-launch kernels),
+                                      then lm_head: 4 events.  NULL disables; graphs reject it. */
   int n_events;                    /* entries in events */
   int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_PERSISTENT */
 } vv_state;

@@ -31,14 +31,13 @@ __global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restri
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
-hipError_t fill_zero(void* p, size_t bytes, hipStream_t st) {
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev) {
   if (bytes == 0) return hipSuccess;
   const size_t n16 = bytes / 16;
   const size_t ntail = bytes - n16 * 16;
   int grid = (int)std::min<size_t>(4096, (n16 + 255) / 256);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(256), 0, st, (uint4*)p, n16,
-                     (uint8_t*)p + n16 * 16, ntail);
+  VV_LAUNCH(k_fill_zero, dim3(grid), dim3(256), st, ev, (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
   return hipGetLastError();
 }
 

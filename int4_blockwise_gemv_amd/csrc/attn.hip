@@ -327,13 +327,14 @@ void attn_set_workspace(AttnParams& p, void* ws) {
   p.cnt = nullptr;
 }
 
-hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st) {
+hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st, KEv ev) {
   const int grid = p.B * p.nkv * p.nsplit;
-  if (p.split == 64) hipLaunchKernelGGL(k_attn<4>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs);
-  else hipLaunchKernelGGL(k_attn<8>, dim3(grid), dim3(kThreads), 0, st, p, rope_cs);
+  const KEv e1 = p.nsplit == 1 ? ev : ev.first();
+  if (p.split == 64) VV_LAUNCH(k_attn<4>, dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+  else VV_LAUNCH(k_attn<8>, dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(p.B * p.nq), dim3(256), 0, st, p, p.split);
+  VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(256), st, ev.last(), p, p.split);
   return hipGetLastError();
 }
 

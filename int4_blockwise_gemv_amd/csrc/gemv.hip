@@ -32,52 +32,67 @@ constexpr int kWavesSmallM = 4;   // most waves (groups) per workgroup for M <= 
 constexpr int kWavesLargeM = 4;   // for M > 2 (LDS holds M activation slices)
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
 
-// Operands of the epilogue, loaded by wave 0 of every workgroup before the weight stream so the
-// workgroup that finishes a tile does not wait on them.
+// Operands of the epilogue.  Every wave loads them before its weight stream, from clamped
+// in-bounds addresses, so no load sits behind a branch: a conditional load whose result merges
+// with a default value makes the compiler wait for it (and for every load issued before it) on
+// the spot, which serialises the stream.  Values that do not apply are zeroed at use.
 template <int MT>
 struct EpiPre {
-  float rs[MT];     // 1/sqrt(mean(h^2) + eps) of the input rows (or 1)
-  float bias;       // bias of this lane's row (EPI_STORE)
-  float gam;        // gamma of this lane's row (EPI_RESID)
+  float rsp[MT];    // lane l: per-tile sum of squares l of the input rows (rstd source), raw
+  float rs[MT];     // 1/sqrt(mean(h^2) + eps) of the input rows (or 1), after epi_finish
+  uint32_t b16;     // raw fp16 bias (EPI_STORE) or gamma (EPI_RESID) of this lane's row
+  float bias;       // bias of this lane's row (EPI_STORE), after epi_finish
+  float gam;        // gamma of this lane's row (EPI_RESID), after epi_finish
   float h[MT];      // residual of this lane's row (EPI_RESID)
 };
 
 // row of lane `lane` of tile `tile` in the output vector (EPI_SILU: lanes 0-31 gate, 32-63 up
 // of the same 32 rows)
-__device__ __forceinline__ int out_row(const GemvParams& p, int tile, int lane) {
-  return p.epi == EPI_SILU ? tile * 32 + (lane & 31) : tile * kTileRows + lane;
+template <int EPI>
+__device__ __forceinline__ int out_row(int tile, int lane) {
+  return EPI == EPI_SILU ? tile * 32 + (lane & 31) : tile * kTileRows + lane;
 }
 
-template <int MT>
-__device__ __forceinline__ void epi_prefetch(const GemvParams& p, int tile, int lane, EpiPre<MT>& e,
-                                             float (&rsp)[MT]) {
-  const int n = out_row(p, tile, lane);
-  const bool ok = n < p.N;
+// gemv_launch makes rs_parts, bias and gamma readable (pointing at x when absent) and records
+// which are real in rs_mask / has_bias / has_gamma, so these loads need no branch; the values are
+// selected and converted only in epi_finish, after the barrier, so nothing waits on them early.
+template <int MT, int EPI>
+__device__ __forceinline__ void epi_prefetch(const GemvParams& p, int tile, int lane, EpiPre<MT>& e) {
+  const int nc = min(out_row<EPI>(tile, lane), p.N - 1);
+  if (EPI != EPI_RESID) {
+    const int np = max(p.rs_nparts, 1);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      e.rsp[m] = p.rs_parts[min(m, p.M - 1) * np * p.rs_mask + min(lane, np - 1) * p.rs_mask];
+  }
+  if (EPI == EPI_STORE) e.b16 = p.bias[nc * p.has_bias];
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) e.h[m] = p.h[(size_t)min(m, p.M - 1) * p.N + nc];
+    e.b16 = p.gamma[nc * p.has_gamma];
+  }
+}
+
+template <int MT, int EPI>
+__device__ __forceinline__ void epi_finish(const GemvParams& p, int tile, int lane, EpiPre<MT>& e) {
+  const bool ok = out_row<EPI>(tile, lane) < p.N;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    rsp[m] = 0.f;
-    e.h[m] = 0.f;
-    if (m < p.M && p.rs_parts && lane < p.rs_nparts) rsp[m] = p.rs_parts[m * p.rs_nparts + lane];
-    if (m < p.M && p.epi == EPI_RESID && ok) e.h[m] = p.h[(size_t)m * p.N + n];
+    const float part = (EPI != EPI_RESID && lane < p.rs_nparts) ? e.rsp[m] : 0.f;
+    e.rs[m] = (EPI != EPI_RESID && p.rs_mask) ? 1.0f / sqrtf(wave_sum(part) * p.rs_inv_n + p.eps) : 1.f;
   }
-  e.bias = (p.epi == EPI_STORE && ok && p.bias) ? h2f(p.bias[n]) : 0.f;
-  e.gam = (p.epi == EPI_RESID && ok && p.gamma) ? h2f(p.gamma[n]) : 0.f;
-}
-
-// rstd from the per-tile sums of squares (lane l holds part l; fixed reduction tree)
-template <int MT>
-__device__ __forceinline__ void epi_finish_rs(const GemvParams& p, EpiPre<MT>& e, const float (&rsp)[MT]) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m) e.rs[m] = p.rs_parts ? 1.0f / sqrtf(wave_sum(rsp[m]) * p.rs_inv_n + p.eps) : 1.f;
+  const float v = h2f((uint16_t)e.b16);
+  e.bias = (EPI == EPI_STORE && p.has_bias && ok) ? v : 0.f;
+  e.gam = (EPI == EPI_RESID && p.has_gamma) ? v : 0.f;
 }
 
 // Epilogue for one tile's finished row sums (one wave, lane = row within the tile).
-template <int MT>
+template <int MT, int EPI>
 __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], const EpiPre<MT>& e, int lane) {
   const int M = p.M;
-  const int n = out_row(p, tile, lane);
+  const int n = out_row<EPI>(tile, lane);
   const bool ok = n < p.N;
-  if (p.epi == EPI_STORE) {
+  if (EPI == EPI_STORE) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
@@ -87,7 +102,7 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
         else reinterpret_cast<float*>(p.y)[(size_t)m * p.ldy + n] = v;
       }
     }
-  } else if (p.epi == EPI_RESID) {
+  } else if (EPI == EPI_RESID) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
@@ -97,7 +112,7 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
         hn = e.h[m] + tot[m];
         p.h[i] = hn;
         if (p.trace) p.trace[i] = hn;
-        if (p.gamma) {
+        if (p.has_gamma) {
           const float gv = e.gam * hn;
           if (p.g_out) p.g_out[i] = f2h(gv);
           if (p.gf_out) p.gf_out[i] = gv;
@@ -119,8 +134,11 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
 
 template <int MT> struct WavesFor { static constexpr int value = MT <= 2 ? kWavesSmallM : kWavesLargeM; };
 
-// WMAX waves at most; the launch uses p.wpg = blockDim.x / 64 of them (one 8-block group each)
-template <int MT>
+// WMAX waves at most; the launch uses p.wpg = blockDim.x / 64 of them (one 8-block group each).
+// From the first load to the barrier the code is branch-free: every load address is clamped
+// into the operand (a group past the end of K re-reads the last block and gets scale 0, rows
+// past M re-read row M-1 and are never stored), so all loads of a wave are in flight together.
+template <int MT, int EPI>
 __global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                                                   const uint4* __restrict__ sw,
                                                                   const uint16_t* __restrict__ x) {
@@ -141,88 +159,79 @@ __global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p,
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
   const int e0 = kg * W * kBatch * kBlock;          // first K element of this workgroup
-  const int ne = min(K - e0, W * kBatch * kBlock);
 
   // activation slice first (its loads return before the weights), 8 bytes per thread per row
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int e = 4 * (int)threadIdx.x;
-    if (m < M && e < ne)
-      *reinterpret_cast<uint2*>(&xs[m][e]) = *reinterpret_cast<const uint2*>(x + (size_t)m * K + e0 + e);
-  }
   static_assert(kItemK <= 4 * 64 * WMAX, "one 8-byte activation load per thread covers the slice");
+  uint2 xr[MT];
+  {
+    const int ec = min(e0 + 4 * (int)threadIdx.x, K - 4);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xr[m] = *reinterpret_cast<const uint2*>(x + (size_t)min(m, M - 1) * K + ec);
+  }
+  EpiPre<MT> ep;
+  epi_prefetch<MT, EPI>(p, tile, lane, ep);
+
   // this wave's group: 8 blocks and their 8 scales
   const int grp = kg * W + w;
   const int b0 = grp * kBatch;
   const int nblk = min(max(nb - b0, 0), kBatch);
-  const u32x4* qp = reinterpret_cast<const u32x4*>(qw) + ((size_t)tile * nb + b0) * kTileRows + lane;
+  const u32x4* qt = reinterpret_cast<const u32x4*>(qw) + (size_t)tile * nb * kTileRows + lane;
+  // scales first: block 0 needs them, and loads complete in order
+  const u32x4 sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sw) +
+                                              ((size_t)tile * ng + min(grp, ng - 1)) * kTileRows + lane);
   u32x4 wv[kBatch];
-  u32x4 sv = u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i)
-    if (i < nblk) wv[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
-  if (nblk > 0) sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sw) + ((size_t)tile * ng + grp) * kTileRows + lane);
-
-  EpiPre<MT> ep;
-  float rsp[MT];
-  if (w == 0) epi_prefetch<MT>(p, tile, lane, ep, rsp);
+  for (int i = 0; i < kBatch; ++i) wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + i, nb - 1) * kTileRows);
+  // keep the LDS write of the activations behind the weight loads (its wait would hold them back)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[m][4 * threadIdx.x]) = xr[m];
   __syncthreads();
 
   const uint32_t m64 = vconst(0x54005400u);
+  const int xb0 = w * kBatch * kBlock;              // this wave's first element in the slice
+  float corr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + min(lane, 4 * kBatch - 1) * 8]);
+    corr[m] = quad_sum(corr_quarter(xv));           // lane 4i+q: quarter q of block i
+  }
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-  if (nblk > 0) {
-    const int xb0 = w * kBatch * kBlock;            // this wave's first element in the slice
-    float corr[MT];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
+    const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      u32x4 xv = u32x4{0, 0, 0, 0};
-      if (m < M && lane < 4 * nblk) xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + lane * 8]);
-      corr[m] = quad_sum(corr_quarter(xv));           // lane 4i+q: quarter q of block i
-    }
+      const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
+      float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (i < nblk) {
-        const float sc = pick_scale(sv, i);
-        const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m < M) {
-            const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
-            float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const u32x4 xv = xb[k];
-              const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-              t = dot8_pairs(d[k], x4, t, m64);
-            }
-            acc[m] = fmaf(sc, t, acc[m]);
-          }
-        }
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 xv = xb[k];
+        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+        t = dot8_pairs(d[k], x4, t, m64);
       }
+      acc[m] = fmaf(sc, t, acc[m]);
     }
   }
 
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (m < M) red[w][m][lane] = acc[m];
+  for (int m = 0; m < MT; ++m) red[w][m][lane] = acc[m];
   __syncthreads();
   if (w != 0) return;
-  epi_finish_rs<MT>(p, ep, rsp);
+  epi_finish<MT, EPI>(p, tile, lane, ep);
 
   float tot[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    tot[m] = 0.f;
-    if (m < M) {
-      float t = 0.f;
-      for (int v = 0; v < W; ++v) t += red[v][m][lane];
-      tot[m] = t;
-    }
+    float t = 0.f;
+    for (int v = 0; v < W; ++v) t += red[v][m][lane];
+    tot[m] = t;
   }
   if (p.wpt == 1) {
-    epilogue<MT>(p, tile, tot, ep, lane);
+    epilogue<MT, EPI>(p, tile, tot, ep, lane);
     return;
   }
   // publish this workgroup's partial, then count arrivals at the tile
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p,
                              (size_t)MT * kTileRows);
   }
   if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
-  epilogue<MT>(p, tile, tot, ep, lane);
+  epilogue<MT, EPI>(p, tile, tot, ep, lane);
 }
 
 int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
@@ -290,15 +299,35 @@ void gemv_set_workspace(GemvParams& p, void* ws) {
   p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up(part, 256));
 }
 
-hipError_t gemv_launch(const GemvParams& p, hipStream_t st) {
+namespace {
+template <int EPI>
+void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t st, KEv ev) {
+  const dim3 g(p.grid), b(64 * p.wpg);
+  switch (mt_of(p.M)) {
+    case 1: VV_LAUNCH((k_gemv<1, EPI>), g, b, st, ev, p, q, s, p.x); break;
+    case 2: VV_LAUNCH((k_gemv<2, EPI>), g, b, st, ev, p, q, s, p.x); break;
+    case 4: VV_LAUNCH((k_gemv<4, EPI>), g, b, st, ev, p, q, s, p.x); break;
+    case 8: VV_LAUNCH((k_gemv<8, EPI>), g, b, st, ev, p, q, s, p.x); break;
+    default: VV_LAUNCH((k_gemv<16, EPI>), g, b, st, ev, p, q, s, p.x); break;
+  }
+}
+}  // namespace
+
+hipError_t gemv_launch(const GemvParams& p0, hipStream_t st, KEv ev) {
+  GemvParams p = p0;
+  const uint16_t* any = p.x;            // readable stand-in for absent optional operands
+  p.rs_mask = p.rs_parts ? 1 : 0;
+  if (!p.rs_parts) { p.rs_parts = reinterpret_cast<const float*>(any); p.rs_nparts = 0; }
+  p.has_bias = p.bias ? 1 : 0;
+  if (!p.bias) p.bias = any;
+  p.has_gamma = p.gamma ? 1 : 0;
+  if (!p.gamma) p.gamma = any;
   const uint4* q = reinterpret_cast<const uint4*>(p.q);
   const uint4* s = reinterpret_cast<const uint4*>(p.s);
-  switch (mt_of(p.M)) {
-    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
-    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
-    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
-    case 8: hipLaunchKernelGGL(k_gemv<8>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
-    default: hipLaunchKernelGGL(k_gemv<16>, dim3(p.grid), dim3(64 * p.wpg), 0, st, p, q, s, p.x); break;
+  switch (p.epi) {
+    case EPI_STORE: launch_epi<EPI_STORE>(p, q, s, st, ev); break;
+    case EPI_RESID: launch_epi<EPI_RESID>(p, q, s, st, ev); break;
+    default: launch_epi<EPI_SILU>(p, q, s, st, ev); break;
   }
   return hipGetLastError();
 }

@@ -165,13 +165,13 @@ void lm_set_workspace(LmParams& p, void* ws) {
   p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up((size_t)p.B * p.grid * sizeof(uint64_t), 256));
 }
 
-hipError_t lm_launch(const LmParams& p, hipStream_t st) {
+hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev) {
   const int cpl = (int)cdiv(p.H / 8, 64);
   const u32x4* W = reinterpret_cast<const u32x4*>(p.W);
 #define VV_LM_CASE(C)                                                                   \
   case C:                                                                               \
-    if (p.B == 1) hipLaunchKernelGGL((k_lmhead<C, 1>), dim3(p.grid), dim3(256), 0, st, p, W); \
-    else hipLaunchKernelGGL((k_lmhead<C, 2>), dim3(p.grid), dim3(256), 0, st, p, W);          \
+    if (p.B == 1) VV_LAUNCH((k_lmhead<C, 1>), dim3(p.grid), dim3(256), st, ev, p, W);       \
+    else VV_LAUNCH((k_lmhead<C, 2>), dim3(p.grid), dim3(256), st, ev, p, W);                \
     break;
   switch (cpl) {
     VV_LM_CASE(1) VV_LM_CASE(2) VV_LM_CASE(3) VV_LM_CASE(4) VV_LM_CASE(5) VV_LM_CASE(6) VV_LM_CASE(7)

@@ -738,7 +738,7 @@ size_t persistent_workspace_bytes(const vv_model* m, int batch, int cap) {
   return mlayout(mdims(m, batch, cap)).total;
 }
 
-int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, void** events, int* ev) {
+int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, KEv ev) {
   const MDims d = mdims(m, s->batch, s->cap);
   const MLayout y = mlayout(d);
   VV_REQUIRE((int64_t)cdiv(s->cap, kAS) <= 1024, VV_ERR_RANGE,
@@ -774,9 +774,8 @@ int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream
   p.ao = reinterpret_cast<uint16_t*>(ws + y.ao); p.act = reinterpret_cast<uint16_t*>(ws + y.act);
   p.xq_l = y.xq_l; p.xm_l = y.xm_l; p.ao_l = y.ao_l; p.act_l = y.act_l;
 
-  if (events) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(events[(*ev)++]), st));
   // every counter starts each step at zero (a fill kernel: capture-safe, unlike a memset node)
-  VV_HIP(fill_zero(ws + y.cnt, y.cnt_bytes, st));
+  VV_HIP(fill_zero(ws + y.cnt, y.cnt_bytes, st, ev.first()));
   for (int l0 = 0; l0 < d.L; l0 += kMaxL) {
     p.l0 = l0;
     p.l1 = std::min(d.L, l0 + kMaxL);
@@ -792,8 +791,8 @@ int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream
     // RMSNorm_1 weight of the first layer of the next launch (read by this launch's last D items)
     p.g1_next = p.l1 < d.L ? m->layers[p.l1].g1 : nullptr;
     p.total = (l0 == 0 ? 1 : 0) + (p.l1 - l0) * p.T;
-    if (events && l0 > 0) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(events[(*ev)++]), st));
-    hipLaunchKernelGGL(k_decode_flow<1>, dim3(p.total), dim3(kThr), 0, st, p);
+    const KEv e = p.l1 == d.L ? ev.last() : KEv{};
+    VV_LAUNCH(k_decode_flow<1>, dim3(p.total), dim3(kThr), st, e, p);
     VV_HIP(hipGetLastError());
   }
   return VV_OK;

@@ -156,13 +156,13 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
              need);
   VV_REQUIRE((reinterpret_cast<uintptr_t>(s->workspace) & 255) == 0, VV_ERR_RANGE,
              "%s: workspace must be 256-byte aligned", fn);
-  const int nev = use_persistent(m, s) ? (int)cdiv(m->n_layers, 32) + 2 : 5 * m->n_layers + 3;
+  const int nev = use_persistent(m, s) ? 2 * 2 : 2 * (5 * m->n_layers + 2);
   VV_REQUIRE(!s->events || s->n_events >= nev, VV_ERR_RANGE, "%s: events needs at least %d entries", fn, nev);
   return VV_OK;
 }
 
 int enqueue_lm(const vv_model* m, const vv_state* s, const float* gf32, const float* sumsq, char* ws_lm,
-               hipStream_t st) {
+               hipStream_t st, KEv ev) {
   LmParams p{};
   p.W = m->lm_head; p.V = m->vocab; p.H = m->hidden; p.B = s->batch;
   p.x = gf32; p.x_f16 = 0;
@@ -170,25 +170,26 @@ int enqueue_lm(const vv_model* m, const vv_state* s, const float* gf32, const fl
   p.logits = s->logits; p.token = s->token;
   lm_plan(p);
   lm_set_workspace(p, ws_lm);
-  VV_HIP(lm_launch(p, st));
+  VV_HIP(lm_launch(p, st, ev));
   return VV_OK;
+}
+
+// event pair i of the state's timing events (both null when timing is off)
+KEv event_pair(const vv_state* s, int i) {
+  if (!s->events) return KEv{};
+  return KEv{reinterpret_cast<hipEvent_t>(s->events[2 * i]), reinterpret_cast<hipEvent_t>(s->events[2 * i + 1])};
 }
 
 int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
   char* ws = static_cast<char*>(s->workspace);
   char* pws = ws + layered_bytes(m, s->batch, s->cap);
   const Layout lay = layout_of(dims_of(m, s->batch, s->cap));
-  int ev = 0;
-  int rc = persistent_enqueue(m, s, pws, st, s->events, &ev);
+  int rc = persistent_enqueue(m, s, pws, st, event_pair(s, 0));
   if (rc) return rc;
   const float* gf32;
   const float* sumsq;
   persistent_lm_inputs(m, s, pws, &gf32, &sumsq);
-  if (s->events) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st));
-  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st);
-  if (rc) return rc;
-  if (s->events) VV_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st));
-  return VV_OK;
+  return enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st, event_pair(s, 1));
 }
 
 int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
@@ -206,16 +207,10 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   float* rope = reinterpret_cast<float*>(ws + lay.rope);
   const int B = d.B, H = d.H;
   const float inv_h = 1.0f / (float)H;
-  int ev = 0;
-  auto mark = [&]() -> hipError_t {
-    if (!s->events) return hipSuccess;
-    return hipEventRecord(reinterpret_cast<hipEvent_t>(s->events[ev++]), st);
-  };
-
-  VV_HIP(mark());
-  hipLaunchKernelGGL(k_step_prep, dim3(B * d.ntH), dim3(64), 0, st, s->input_embeds, H, d.ntH,
-                     d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
-                     s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
+  int op = 0;   // timing event pair of the next operation
+  VV_LAUNCH(k_step_prep, dim3(B * d.ntH), dim3(64), st, event_pair(s, op++), s->input_embeds, H, d.ntH,
+            d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
+            s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
   VV_HIP(hipGetLastError());
 
   const size_t layer_kv = (size_t)B * d.nkv * (size_t)s->cap * kHeadDim;
@@ -230,8 +225,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
       gemv_set_workspace(p, ws + lay.ws_qkv);
-      VV_HIP(mark());
-      VV_HIP(gemv_launch(p, st));
+      VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
     {  // attention with RoPE and KV append
       AttnParams a{};
@@ -242,8 +236,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       a.kc = s->k_cache + (size_t)l * layer_kv; a.vc = s->v_cache + (size_t)l * layer_kv;
       a.scale = 1.0f / sqrtf((float)kHeadDim);
       a.out = o; a.out_f16 = 1;
-      VV_HIP(mark());
-      VV_HIP(attn_launch_with_rope(a, rope, st));
+      VV_HIP(attn_launch_with_rope(a, rope, st, event_pair(s, op++)));
     }
     {  // o projection + residual; writes fp16(g2 * h) and sum(h^2) for the MLP
       GemvParams p{};
@@ -253,8 +246,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.sumsq_out = sumsq;
       gemv_plan(p);
       gemv_set_workspace(p, ws + lay.ws_o);
-      VV_HIP(mark());
-      VV_HIP(gemv_launch(p, st));
+      VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
     {  // gate/up (32 gate + 32 up rows per tile) + SiLU(gate) * up, RMSNorm_2 folded in
       GemvParams p{};
@@ -265,8 +257,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
       gemv_set_workspace(p, ws + lay.ws_gu);
-      VV_HIP(mark());
-      VV_HIP(gemv_launch(p, st));
+      VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
     {  // down projection + residual; feeds the next layer (or the lm_head)
       const bool last = l == d.L - 1;
@@ -282,16 +273,11 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * B * H : nullptr;
       gemv_plan(p);
       gemv_set_workspace(p, ws + lay.ws_down);
-      VV_HIP(mark());
-      VV_HIP(gemv_launch(p, st));
+      VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
   }
   // final RMSNorm folded into the lm_head; greedy argmax
-  VV_HIP(mark());
-  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st);
-  if (rc) return rc;
-  VV_HIP(mark());
-  return VV_OK;
+  return enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st, event_pair(s, op++));
 }
 
 }  // namespace

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -185,6 +186,23 @@ __device__ __forceinline__ void reset_counter(unsigned* c) {
 // ---------------------------------------------------------------------------------------------
 enum EpiKind { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2 };
 
+// Optional timing events of a launch: hipExtLaunchKernel stores the kernel's own start and end
+// times in them (the dispatch timestamps, not the time the stream reaches a marker).  An
+// operation of several kernels puts `start` on its first launch and `stop` on its last.
+struct KEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+  KEv first() const { return KEv{start, nullptr}; }
+  KEv last() const { return KEv{nullptr, stop}; }
+};
+#define VV_LAUNCH(kern, grid, block, st, ev, ...)                                                     \
+  do {                                                                                                \
+    const ::vv::KEv vv_ev_ = (ev); /* evaluated once */                                               \
+    if (vv_ev_.start || vv_ev_.stop)                                                                  \
+      hipExtLaunchKernelGGL(kern, grid, block, 0, st, vv_ev_.start, vv_ev_.stop, 0, __VA_ARGS__);    \
+    else                                                                                              \
+      hipLaunchKernelGGL(kern, grid, block, 0, st, __VA_ARGS__);                                      \
+  } while (0)
+
 struct GemvParams {
   const uint8_t* q;          // tiled nibbles
   const uint16_t* s;         // tiled scales
@@ -200,6 +218,7 @@ struct GemvParams {
   void* y; int y_f16; int ldy;
   // rstd source (EPI_STORE / EPI_SILU), optional
   const float* rs_parts; int rs_nparts; float rs_inv_n; float eps;
+  int rs_mask, has_bias, has_gamma;   // set by gemv_launch (which points absent operands at x)
   // EPI_RESID
   float* h;                  // fp32 [M][N]
   const uint16_t* gamma;     // fp16 [N]
@@ -214,7 +233,7 @@ struct GemvParams {
 void gemv_plan(GemvParams& p);                       // fills kb/wpg/wpt/grid
 size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
-hipError_t gemv_launch(const GemvParams& p, hipStream_t st);
+hipError_t gemv_launch(const GemvParams& p, hipStream_t st, KEv ev = {});
 
 struct AttnParams {
   int B, nq, nkv, cap, split, nsplit;
@@ -235,7 +254,7 @@ size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit);
 void attn_set_workspace(AttnParams& p, void* ws);
 hipError_t attn_launch(const AttnParams& p, hipStream_t st);
 // step flavour: rope_cs = [B][64][2] (cos, sin) of the new positions
-hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st);
+hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st, KEv ev = {});
 
 struct LmParams {
   const uint16_t* W; int V, H, B;
@@ -248,15 +267,15 @@ struct LmParams {
 void lm_plan(LmParams& p);
 size_t lm_workspace_bytes(int B, int V, int H);
 void lm_set_workspace(LmParams& p, void* ws);
-hipError_t lm_launch(const LmParams& p, hipStream_t st);
+hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev = {});
 
-hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev = {});
 
 // persistent (single-launch) decode step; its workspace region starts with a sticky status word
 bool persistent_supported(const vv_model* m, int batch);
 int persistent_grid();   // resident workgroups on the current device (queried once per device)
 size_t persistent_workspace_bytes(const vv_model* m, int batch, int cap);
-int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, void** events, int* ev);
+int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, KEv ev);
 void persistent_lm_inputs(const vv_model* m, const vv_state* s, char* ws, const float** gf32, const float** sumsq);
 
 }  // namespace vv

@@ -155,10 +155,10 @@ def test_decode_step_validation():
     evs = (C.c_void_p * 4)()
     ev = C.cast(evs, C.POINTER(C.c_void_p))
     lay, per = vvmod.VV_PATH_LAYERED, vvmod.VV_PATH_PERSISTENT
-    # layered: 5 L + 3 events; persistent: ceil(L/32) + 2
+    # a start/stop pair per operation: layered 2 (5 L + 2); persistent 4
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=4, path=lay)), None) == \
         vvmod.VV_ERR_RANGE
-    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=2, path=per)), None) == \
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=3, path=per)), None) == \
         vvmod.VV_ERR_RANGE
     # unknown path; persistent path with a batch it does not take, or without layers
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, path=7)), None) == vvmod.VV_ERR_RANGE
@@ -171,8 +171,9 @@ def test_decode_step_validation():
     assert L.vv_decode_status(None, C.byref(s), C.byref(st), None) == vvmod.VV_ERR_NULL
     assert L.vv_decode_status(C.byref(m), C.byref(s), None, None) == vvmod.VV_ERR_NULL
     h = C.c_void_p()
-    assert L.vv_decode_graph_create(C.byref(m), C.byref(_state(need, events=C.cast(evs, C.POINTER(C.c_void_p)),
-                                                              n_events=8)), None, C.byref(h)) == vvmod.VV_ERR_UNSUPPORTED
+    evs14 = (C.c_void_p * 14)()   # enough pairs for the one-layer model: 2 (5 + 2)
+    assert L.vv_decode_graph_create(C.byref(m), C.byref(_state(need, events=C.cast(evs14, C.POINTER(C.c_void_p)),
+                                                              n_events=14)), None, C.byref(h)) == vvmod.VV_ERR_UNSUPPORTED
     assert L.vv_decode_graph_create(C.byref(_model_struct(head_dim=64)), C.byref(s), None,
                                     C.byref(h)) == vvmod.VV_ERR_SHAPE
     assert h.value is None

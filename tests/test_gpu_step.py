@@ -235,3 +235,32 @@ def test_step_1p5b_full_depth_layerwise(cuda, path):
     logits, _, _ = O.lm_head_argmax(m.lm, f)
     assert rel_err(host(case.ds.logits)[0], logits[0]) <= TOL
     _check_tokens(host(case.ds.token), logits)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_step_kernel_timing_events(path):
+    """Timing events: one start/stop pair per operation, each holding its kernels' own times."""
+    import ctypes as C
+    import torch
+    case = Case(TINY, 7, range(2), [33], 40, path=path)
+    n_ops = 2 if path == "persistent" else 5 * 2 + 2
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    arr = (C.c_void_p * len(evs))(*[C.c_void_p(e.cuda_event) for e in evs])
+    case.ds.struct.events = C.cast(arr, C.POINTER(C.c_void_p))
+    case.ds.struct.n_events = len(evs)
+    try:
+        case.run()
+    finally:
+        case.ds.struct.events = None
+        case.ds.struct.n_events = 0
+    t = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_ops)]
+    assert all(np.isfinite(v) and 0.0 < v < 100.0 for v in t), t
+    # operations run in stream order: each starts after the previous one ended
+    for i in range(1, n_ops):
+        assert evs[2 * i - 1].elapsed_time(evs[2 * i]) >= -1e-3, i
+    ref_logits, _, _, _, _, _ = case.oracle()
+    logits = host(case.ds.logits)
+    assert rel_err(logits, ref_logits) < TOL
