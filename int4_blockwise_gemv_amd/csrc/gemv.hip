@@ -256,6 +256,11 @@ __global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p,
 
 int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
+// Batches of at least kMfmaMinM rows go to the matrix-core kernel (gemv_mfma.hip), which always
+// computes 16 rows: its partials are sized for 16.
+constexpr int kMfmaMinM = 5;
+int part_rows(int M) { return M >= kMfmaMinM ? 16 : mt_of(M); }
+
 struct Plan { int kb, wpg, wpt, grid; };
 
 // One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave.
@@ -285,7 +290,7 @@ void gemv_plan(GemvParams& p) {
 
 size_t gemv_workspace_bytes(int M, int ntiles, int nb) {
   const Plan pl = make_plan(M, ntiles, nb);
-  const int MT = mt_of(M);
+  const int MT = part_rows(M);
   const size_t part = (size_t)ntiles * pl.wpt * MT * kTileRows * sizeof(float);
   const size_t cnt = (size_t)ntiles * sizeof(unsigned);
   return align_up(part, 256) + align_up(cnt, 256);
@@ -293,7 +298,7 @@ size_t gemv_workspace_bytes(int M, int ntiles, int nb) {
 
 void gemv_set_workspace(GemvParams& p, void* ws) {
   const Plan pl = make_plan(p.M, p.ntiles, p.K / kBlock);
-  const int MT = mt_of(p.M);
+  const int MT = part_rows(p.M);
   const size_t part = (size_t)p.ntiles * pl.wpt * MT * kTileRows * sizeof(float);
   p.part = reinterpret_cast<float*>(ws);
   p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up(part, 256));
@@ -314,6 +319,7 @@ void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t
 }  // namespace
 
 hipError_t gemv_launch(const GemvParams& p0, hipStream_t st, KEv ev) {
+  if (p0.M >= kMfmaMinM) return gemv_mfma_launch(p0, st, ev);
   GemvParams p = p0;
   const uint16_t* any = p.x;            // readable stand-in for absent optional operands
   p.rs_mask = p.rs_parts ? 1 : 0;

@@ -234,6 +234,7 @@ void gemv_plan(GemvParams& p);                       // fills kb/wpg/wpt/grid
 size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
 hipError_t gemv_launch(const GemvParams& p, hipStream_t st, KEv ev = {});
+hipError_t gemv_mfma_launch(const GemvParams& p, hipStream_t st, KEv ev);   // 5..16 rows (gemv_launch picks it)
 
 struct AttnParams {
   int B, nq, nkv, cap, split, nsplit;

@@ -152,7 +152,7 @@ def test_gemv_projection_shapes(cuda, shape, mode):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("shape", [(100, 96), (1, 32), (130, 288), (1536, 1536), (256, 8960)])
 def test_gemv_batched_ragged_with_bias(cuda, shape, M):
     N, K = shape
@@ -181,6 +181,21 @@ def test_gemv_one_hot_columns_exact(cuda):
     y = _gemv_gpu(q, s, N, K, x)
     for i, k in enumerate(ks):
         assert np.array_equal(y[i], deq[:, k])
+
+
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", PROJ_SHAPES)
+def test_gemv_batch16_projection_shapes(cuda, shape, mode):
+    """16 rows (the matrix-core kernel) at every projection shape of both model widths."""
+    N, K = shape
+    W = synth.master_weight(3, 0, synth.T_Q, N, K)
+    x = synth.fp16_normal(3, 16, synth.T_X, (16, K))
+    ref = O.gemv(*O.pack(W, mode), x)
+    q, s = _pack_gpu(W, mode, tiled=True)
+    y = _gemv_gpu(q, s, N, K, x)
+    err = rel_err(y, ref)
+    print(f"gemv16 {shape} {mode}: max rel err {err:.2e}")
+    assert err <= TOL
 
 
 def test_gemv_deterministic(cuda):

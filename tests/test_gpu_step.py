@@ -103,6 +103,24 @@ def test_step_tiny_batched_layered(cuda):
     _compare(case, case.oracle())
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_step_tiny_batch_matrix_cores(cuda, B):
+    """Batches of 5..16 sequences take the matrix-core GEMV; ragged positions."""
+    pos = [(7 * b * b + 3 * b) % 90 for b in range(B)]
+    case = Case(TINY, 9, range(2), pos, 96, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
+def test_step_1p5b_width_batch16_ragged(cuda):
+    """Two layers at 1.5B width, 16 sequences of lengths spread over 64..1500 (the batched shape
+    at reduced depth and context)."""
+    pos = [64 + (97 * b) % 1437 for b in range(16)]
+    case = Case(synth.QWEN2_1P5B, 0, [0, 27], pos, 1501, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
 def test_step_persistent_rejects_batch3(cuda):
     from int4_blockwise_gemv_amd import vv
     with pytest.raises(vv.VVError) as e:
