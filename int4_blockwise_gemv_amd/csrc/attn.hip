@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   constexpr int S = kWaves * 4 * NP;
   __shared__ __align__(16) float qs[kMaxG][kD];
   __shared__ float sc[kMaxG][S];
-  __shared__ __align__(16) float red[kWaves][4][kMaxG][kD];   // [wave][position group][head][dim]
+  __shared__ __align__(16) float red[kWaves][kMaxG][kD];      // [wave][head][dim]
   __shared__ __align__(16) uint16_t knew[kD], vnew[kD];
   __shared__ float mh[kMaxG], lh[kMaxG];
 
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
   __syncthreads();
 
-  // ---- P.V: lane holds 8 dims of one position per pass; its sums over its NP positions go to LDS
-  // as they are (no cross-lane shuffles), the 16 (wave, position group) partials are added below
+  // ---- P.V: lane holds 8 dims of one position per pass; the wave's 4 position groups (rows of 16
+  // lanes) are summed lane-wise with permlane swaps, and one row writes the wave's partial ---------
 #pragma unroll 1
   for (int hh = 0; hh < g; ++hh) {
     float acc[8];
@@ -206,9 +206,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       acc[4] = fma_mix_lo(pj, v.z, acc[4]); acc[5] = fma_mix_hi(pj, v.z, acc[5]);
       acc[6] = fma_mix_lo(pj, v.w, acc[6]); acc[7] = fma_mix_hi(pj, v.w, acc[7]);
     }
-    float* dst = &red[w][pg][hh][8 * sl];
-    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = rows_lanewise_sum(acc[t]);
+    if (pg == 0) {
+      float* dst = &red[w][hh][8 * sl];
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
   }
   __syncthreads();
 
@@ -219,9 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
     const int hh = i >> 7, d = i & 127;
     float o = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o += red[ww][q][hh][d];
+    for (int ww = 0; ww < kWaves; ++ww) o += red[ww][hh][d];
     if (single) {
       const size_t oi = ((size_t)G.b * p.nq + (size_t)G.kvh * g + hh) * kD + d;
       if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o / lh[hh]);

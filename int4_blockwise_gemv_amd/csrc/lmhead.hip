@@ -14,6 +14,7 @@ namespace vv {
 namespace {
 
 constexpr int kRowsPerIter = 2;
+constexpr int kLmMfmaMinB = 3;          // batches from 3 rows take the matrix cores
 constexpr int kMaxChunksPerLane = 8;   // H <= 8 * 64 * 8 = 4096
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
@@ -143,9 +144,181 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
   if (tid == 0) reset_counter(p.cnt);
 }
 
+// ---- batches of kLmMfmaMinB..16 rows: fp16 matrix cores ----------------------------------------
+// A operand: 16 vocabulary rows x 32 k straight from the row-major table; B: the activation as two
+// fp16 parts (x = hi + lo, ~22 bits), so the input keeps fp32 precision and each product is
+// exact.  The k order inside a 128-element sub-chunk is permuted the same way on both operands
+// (lane group s takes 32 contiguous k, one MFMA step per 8), which lets each lane load 64
+// contiguous bytes of its row.  A workgroup of 4 waves owns 64 * rgw consecutive rows (wave w
+// takes row groups w, w + 4, ...) and walks H in chunks of kLmKC, staging the chunk of all 16
+// activation rows in LDS.
+typedef _Float16 lm_half8 __attribute__((ext_vector_type(8)));
+typedef float lm_f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kLmKC = 256;        // k per staged chunk
+constexpr int kLmMaxRGW = 8;      // row groups (16 rows) per wave at most
+constexpr int kLmXS = kLmKC + 8;  // padded LDS row
+
+__global__ __launch_bounds__(256) void k_lmhead_mfma(LmParams p, const u32x4* __restrict__ W) {
+  __shared__ __align__(16) uint16_t xh[16][kLmXS], xl[16][kLmXS];
+  __shared__ float rs_s[16];
+  __shared__ uint64_t best_w[4][16];
+  __shared__ unsigned s_last;
+  const int H = p.H, V = p.V, B = p.B;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wg = blockIdx.x;
+  const int rgw = p.rows_per_wg / 64;                // row groups per wave
+  const int rg0 = wg * 4 * rgw;                      // first row group of the workgroup
+  const int li = lane & 15, ls = lane >> 4;
+
+  // rstd of each batch row (wave 0; lane n adds part n)
+  if (w == 0) {
+    for (int j = 0; j < 16; ++j) {
+      float r = 1.f;
+      if (p.rs_parts && j < B) {
+        const float v = lane < p.rs_nparts ? p.rs_parts[(size_t)j * p.rs_nparts + lane] : 0.f;
+        r = 1.0f / sqrtf(wave_sum(v) * p.rs_inv_n + p.eps);
+      }
+      if (lane == 0) rs_s[j] = r;
+    }
+  }
+
+  lm_f32x4 acc[kLmMaxRGW];
+#pragma unroll
+  for (int j = 0; j < kLmMaxRGW; ++j) acc[j] = lm_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < H; c0 += kLmKC) {
+    __syncthreads();   // the previous chunk is consumed
+    {  // thread t: row t / 16, elements 16 (t % 16) .. + 15 of the chunk
+      const int m = tid >> 4, k = (tid & 15) * 16;
+      const int mc = min(m, B - 1);
+      float v[16];
+      if (p.x_f16) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (size_t)mc * H + c0 + k;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(src), b = *reinterpret_cast<const u32x4*>(src + 8);
+        const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { v[2 * i] = (float)as_h2(d[i]).x; v[2 * i + 1] = (float)as_h2(d[i]).y; }
+      } else {
+        const float* src = reinterpret_cast<const float*>(p.x) + (size_t)mc * H + c0 + k;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 f = *reinterpret_cast<const float4*>(src + 4 * i);
+          v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+        }
+      }
+      uint16_t hi[16], lo[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = m < B ? v[i] : 0.f;
+        const _Float16 h = (_Float16)x;
+        hi[i] = __builtin_bit_cast(uint16_t, h);
+        lo[i] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4 a, b;
+        a.x = hi[8 * i] | ((uint32_t)hi[8 * i + 1] << 16); a.y = hi[8 * i + 2] | ((uint32_t)hi[8 * i + 3] << 16);
+        a.z = hi[8 * i + 4] | ((uint32_t)hi[8 * i + 5] << 16); a.w = hi[8 * i + 6] | ((uint32_t)hi[8 * i + 7] << 16);
+        b.x = lo[8 * i] | ((uint32_t)lo[8 * i + 1] << 16); b.y = lo[8 * i + 2] | ((uint32_t)lo[8 * i + 3] << 16);
+        b.z = lo[8 * i + 4] | ((uint32_t)lo[8 * i + 5] << 16); b.w = lo[8 * i + 6] | ((uint32_t)lo[8 * i + 7] << 16);
+        *reinterpret_cast<u32x4*>(&xh[m][k + 8 * i]) = a;
+        *reinterpret_cast<u32x4*>(&xl[m][k + 8 * i]) = b;
+      }
+    }
+    __syncthreads();
+    // B operands of this lane for the chunk: batch row li, k = 128 u + 32 ls + 8 e
+    for (int j = 0; j < rgw; ++j) {
+      const int row = min((rg0 + w + 4 * j) * 16 + li, V - 1);
+      const u32x4* wr = W + ((size_t)row * H + c0) / 8 + 4 * ls;
+      u32x4 a[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * u + e] = __builtin_nontemporal_load(wr + 16 * u + e);
+      lm_f32x4 c = acc[0];
+#pragma unroll
+      for (int jj = 0; jj < kLmMaxRGW; ++jj) if (jj == j) c = acc[jj];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 128 * u + 32 * ls + 8 * e;
+          const lm_half8 bh = __builtin_bit_cast(lm_half8, *reinterpret_cast<const u32x4*>(&xh[li][k]));
+          const lm_half8 bl = __builtin_bit_cast(lm_half8, *reinterpret_cast<const u32x4*>(&xl[li][k]));
+          const lm_half8 av = __builtin_bit_cast(lm_half8, a[4 * u + e]);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, c, 0, 0, 0);
+        }
+#pragma unroll
+      for (int jj = 0; jj < kLmMaxRGW; ++jj) if (jj == j) acc[jj] = c;
+    }
+  }
+
+  // lane l: rows 16 g + 4 (l / 16) + r of its row groups g, batch row l % 16
+  const int b = li;
+  const float rsb = rs_s[b];
+  uint64_t best = 0;
+#pragma unroll
+  for (int j = 0; j < kLmMaxRGW; ++j) {
+    if (j >= rgw) break;
+    const int rbase = (rg0 + w + 4 * j) * 16 + 4 * ls;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = rbase + r;
+      const float v = acc[j][r] * rsb;
+      if (row < V && b < B) {
+        if (p.logits) p.logits[(size_t)b * V + row] = v;
+        const uint64_t k = make_key(v, (uint32_t)row);
+        best = k > best ? k : best;
+      }
+    }
+  }
+  // lanes b, b + 16, b + 32, b + 48 hold batch row b
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const uint64_t v = __shfl_xor(best, o, 64);
+    best = v > best ? v : best;
+  }
+  if (lane < 16) best_w[w][lane] = best;
+  __syncthreads();
+  if (tid < B) {
+    uint64_t k = best_w[0][tid];
+    for (int i = 1; i < 4; ++i) k = best_w[i][tid] > k ? best_w[i][tid] : k;
+    publish_u64(&p.keys[(size_t)tid * gridDim.x + wg], k);
+  }
+  wait_published();
+  __syncthreads();
+  if (tid == 0) s_last = arrive(p.cnt) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int bb = w; bb < B; bb += 4) {
+    uint64_t k = 0;
+    for (int i = lane; i < (int)gridDim.x; i += 64) {
+      const uint64_t v = collect_u64(p.keys + (size_t)bb * gridDim.x + i);
+      k = v > k ? v : k;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t v = __shfl_xor(k, o, 64);
+      k = v > k ? v : k;
+    }
+    if (lane == 0) p.token[bb] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
+  }
+  if (tid == 0) reset_counter(p.cnt);
+}
+
+bool lm_use_mfma(const LmParams& p) { return p.B >= kLmMfmaMinB && p.H % kLmKC == 0; }
+
 }  // namespace
 
 void lm_plan(LmParams& p) {
+  if (lm_use_mfma(p)) {   // 64 rows per row-group layer; about 512 workgroups
+    const int64_t ngroups = cdiv(p.V, 16);
+    const int rgw = (int)std::min<int64_t>(kLmMaxRGW, std::max<int64_t>(1, cdiv(ngroups, 4 * 512)));
+    p.rows_per_wg = 64 * rgw;
+    p.grid = (int)cdiv(p.V, p.rows_per_wg);
+    return;
+  }
   int grid = (int)cdiv(p.V, 64);            // at least 16 rows per wave
   grid = grid > 1024 ? 1024 : (grid < 1 ? 1 : grid);
   p.rows_per_wg = (int)cdiv(p.V, grid);
@@ -168,6 +341,10 @@ void lm_set_workspace(LmParams& p, void* ws) {
 hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev) {
   const int cpl = (int)cdiv(p.H / 8, 64);
   const u32x4* W = reinterpret_cast<const u32x4*>(p.W);
+  if (lm_use_mfma(p)) {
+    VV_LAUNCH(k_lmhead_mfma, dim3(p.grid), dim3(256), st, ev, p, W);
+    return hipGetLastError();
+  }
 #define VV_LM_CASE(C)                                                                   \
   case C:                                                                               \
     if (p.B == 1) VV_LAUNCH((k_lmhead<C, 1>), dim3(p.grid), dim3(256), st, ev, p, W);       \

@@ -114,7 +114,7 @@ def _check_tokens(tok, ref_logits):
 
 
 @pytest.mark.parametrize("H", [1536, 3584])
-@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("B", [1, 3, 8, 16])
 def test_lm_head_full_vocab(cuda, H, B):
     W = synth.fp16_normal(0, 0, synth.T_LM, (151936, H), std=0.02)
     x = synth.fp16_normal(0, 1, synth.T_EMB, (B, H)).astype(np.float32)
@@ -143,3 +143,31 @@ def test_lm_head_fp16_activation_and_odd_sizes(cuda):
     logits, tok = _lm_gpu(W, x)
     assert rel_err(logits, ref) <= TOL
     _check_tokens(tok, ref)
+
+
+def test_lm_head_batch16_keeps_fp32_input_precision(cuda):
+    """Batches of 3..16 run on the matrix cores with the fp32 activation split into two fp16
+    parts: the logits stay within fp32 accumulation error of the fp64 result (far inside the
+    2e-3 budget), including inputs that fp16 alone would round."""
+    H, V, B = 1536, 4096, 16
+    W = synth.fp16_normal(4, 0, synth.T_LM, (V, H), std=0.02)
+    x = synth.fp16_normal(4, 1, synth.T_EMB, (B, H)).astype(np.float32)
+    x = x * np.float32(1.0 + 1.0 / 3000.0)          # not representable in fp16
+    ref, _, _ = O.lm_head_argmax(W, x)
+    logits, tok = _lm_gpu(W, x)
+    err = rel_err(logits, ref)
+    print(f"batch-16 lm_head rel err {err:.2e}")
+    assert err <= 2e-5
+    _check_tokens(tok, ref)
+
+
+def test_lm_head_batched_ties_and_fp16_input(cuda):
+    """Matrix-core path: equal rows tie to the smallest index in every batch row; fp16 input."""
+    H, V, B = 512, 1001, 4
+    W = synth.fp16_normal(5, 0, synth.T_LM, (V, H), std=0.02)
+    x = np.abs(synth.fp16_normal(5, 0, synth.T_EMB, (B, H)))
+    W[[999, 17, 640]] = np.float16(0.5)
+    logits, tok = _lm_gpu(W, x)
+    assert list(tok) == [17] * B
+    ref, _, _ = O.lm_head_argmax(W, x.astype(np.float32))
+    assert rel_err(logits, ref) <= TOL
