@@ -186,17 +186,19 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8, cap <= 131072.
  *
  * Two implementations compute the same step (vv_state.path):
- *   VV_PATH_PERSISTENT  all layers in one launch of a persistent kernel (at most 32 layers per
- *                       launch), then the lm_head: batch 1..2, n_layers >= 1, H <= 4096.  Its
- *                       workgroups hand results to each other through counters in the
- *                       workspace, so it needs every workgroup of its grid resident at once
- *                       (the grid is sized from the occupancy of the current device) and must
- *                       not share the GPU with another persistent launch.  Each wait is bounded:
- *                       a wait that gives up sets a sticky nonzero status word instead of hanging
- *                       (vv_decode_status reads it; clear it with vv_workspace_init).
- *   VV_PATH_LAYERED     one launch per stage (1 + 5 L + 1 kernels): any batch up to max_batch.
- *   VV_PATH_AUTO        the layered path (measured faster on MI355X: the persistent kernel's
- *                       per-item hand-offs through memory cost more than the launches it saves).
+ *   VV_PATH_PERSISTENT  all layers in one launch of a single-launch dataflow kernel (at most 32
+ *                       layers per launch; its workgroups are the work items in dependency order
+ *                       and hand results on through counters in the workspace), then the
+ *                       lm_head: batch 1, n_layers >= 1, H <= 4096.  An item waits only for
+ *                       items dispatched before it, so it needs no particular residency.  Each
+ *                       wait is bounded: a wait that gives up sets a sticky nonzero status word
+ *                       instead of hanging (vv_decode_status reads it; clear it with
+ *                       vv_workspace_init).
+ *   VV_PATH_LAYERED     one launch per stage (1 + 5 L + 1 kernels, plus a split merge per layer
+ *                       when the cache is split): any batch up to max_batch.
+ *   VV_PATH_AUTO        the layered path (measured faster on MI355X: 1.77 ms against 3.8 ms for
+ *                       the 7B-shaped step; the persistent kernel's waiting items hold the slots
+ *                       that the weight streams of later items need).
  * Results of the two paths agree to rounding (the K-splits differ), and each is deterministic.
  * ------------------------------------------------------------------------------------------- */
 enum { VV_PATH_AUTO = 0, VV_PATH_LAYERED = 1, VV_PATH_PERSISTENT = 2 };
@@ -245,6 +247,22 @@ typedef struct vv_state {
                                       then lm_head: 4 events.  NULL disables; graphs reject it. */
   int n_events;                    /* entries in events */
   int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_PERSISTENT */
+  /* Closed-loop greedy decoding (optional).  With feedback_table set, each step ends with a
+   * small kernel that, for every sequence not yet done, records token[b] at history[b][pos[b]]
+   * and then either marks the sequence done (token[b] is one of stop_ids) or gathers
+   * input_embeds[b] = feedback_table[token[b]] and advances pos[b] by one (while pos[b] + 1 <
+   * cap).  The next step, or the next replay of a captured graph, then decodes the following
+   * token with no host round trip ("vibevoice-asr-bitnet-onnx" page, decoding note: greedy
+   * decode, the lm_head tied to the fp16 embedding table, stop tokens 151645 / 151643).
+   * input_embeds and pos are then written by the step, so they must be writable device
+   * buffers.  A done sequence keeps its input and position: its later steps recompute the same
+   * slot and token. */
+  const uint16_t* feedback_table;  /* device fp16 [vocab][hidden] or NULL (no feedback) */
+  int32_t* history;                /* device int32 [B][cap] or NULL */
+  int32_t* done;                   /* device int32 [B] or NULL; set to 1 by a stop token (the
+                                      caller zeroes it before the first step) */
+  int32_t stop_ids[4];             /* stop tokens, n_stop of them */
+  int n_stop;                      /* 0..4 */
 } vv_state;
 
 size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap);

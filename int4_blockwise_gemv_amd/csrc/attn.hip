@@ -265,13 +265,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int S) {
   const int s_beg = half * per, s_end = min(n, s_beg + per);
   const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
   const size_t stride = (size_t)kMaxG * kPS;
-  for (int s = tid; s < n; s += 256) {
+  // every load first, from clamped (valid) records: this half's first kChunk values of dim d, then
+  // the (m, l) of split tid (splits past 256 are rare: a loop takes them afterwards)
+  float v[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) v[u] = rec0[(size_t)min(s_beg + u, n - 1) * stride + 4 + d];
+  const int s0 = min(tid, n - 1);
+  const float m0 = rec0[(size_t)s0 * stride], l0 = rec0[(size_t)s0 * stride + 1];
+  if (tid < n) { ms_[tid] = m0; ls_[tid] = l0; }
+  for (int s = tid + 256; s < n; s += 256) {
     ms_[s] = rec0[s * stride];
     ls_[s] = rec0[s * stride + 1];
   }
-  float v[kChunk];
-#pragma unroll
-  for (int u = 0; u < kChunk; ++u) v[u] = s_beg + u < s_end ? rec0[(s_beg + u) * stride + 4 + d] : 0.f;
   __syncthreads();
   if (tid < 64) {
     float M = -INFINITY;

@@ -1,7 +1,7 @@
 // Decode-step launcher and its hipGraph wrapper.
 //
 // Two implementations of the same step share the entry points: the persistent kernel of
-// mega.hip (one launch for all layers, then the lm_head; used for batch 1..2) and the layered
+// mega.hip (one launch for all layers, then the lm_head; batch 1) and the layered
 // path below (one launch per stage; any batch up to 16).  vv_state.path picks one.
 //
 // decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts):
@@ -54,6 +54,37 @@ __global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ e
     rope[((size_t)b * 64 + lane) * 2] = (float)c;
     rope[((size_t)b * 64 + lane) * 2 + 1] = (float)s;
   }
+}
+
+// Greedy feedback for closed-loop decoding (one workgroup per sequence): record the token, stop
+// on a stop id, else gather the token's embedding row as the next input and advance the position.
+struct StopIds { int32_t id[4]; int n; };
+
+__global__ __launch_bounds__(256) void k_feedback(const int32_t* __restrict__ token, const uint16_t* __restrict__ table,
+                                                  int V, int H, uint16_t* __restrict__ emb, int32_t* __restrict__ pos,
+                                                  int cap, int32_t* __restrict__ history, int32_t* __restrict__ done,
+                                                  StopIds stop) {
+  __shared__ int s_adv, s_tok;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int tok = token[b];
+    int P = pos[b];
+    P = P < 0 ? 0 : (P >= cap ? cap - 1 : P);
+    const bool active = done == nullptr || done[b] == 0;
+    bool stopped = false;
+    for (int i = 0; i < stop.n; ++i) stopped |= tok == stop.id[i];
+    if (active && history) history[(size_t)b * cap + P] = tok;
+    if (active && stopped && done) done[b] = 1;
+    const bool adv = active && !stopped && P + 1 < cap && tok >= 0 && tok < V;
+    if (adv) pos[b] = P + 1;
+    s_adv = adv;
+    s_tok = tok;
+  }
+  __syncthreads();
+  if (!s_adv) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(table + (size_t)s_tok * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(emb + (size_t)b * H);
+  for (int i = threadIdx.x; i < H / 8; i += blockDim.x) dst[i] = src[i];
 }
 
 struct Layout {
@@ -150,7 +181,10 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(s->path == VV_PATH_AUTO || s->path == VV_PATH_LAYERED || s->path == VV_PATH_PERSISTENT, VV_ERR_RANGE,
              "%s: unknown path %d", fn, s->path);
   VV_REQUIRE(s->path != VV_PATH_PERSISTENT || persistent_supported(m, s->batch), VV_ERR_UNSUPPORTED,
-             "%s: the persistent path needs n_layers >= 1, batch <= 2, hidden <= 4096", fn);
+             "%s: the persistent path needs n_layers >= 1, batch 1, hidden <= 4096", fn);
+  VV_REQUIRE(s->n_stop >= 0 && s->n_stop <= 4, VV_ERR_RANGE, "%s: n_stop %d not in 0..4", fn, s->n_stop);
+  VV_REQUIRE(!s->feedback_table || (reinterpret_cast<uintptr_t>(s->feedback_table) & 15) == 0, VV_ERR_RANGE,
+             "%s: feedback_table must be 16-byte aligned", fn);
   const size_t need = step_bytes(m, s->batch, s->cap);
   VV_REQUIRE(s->workspace && s->workspace_bytes >= need, VV_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
              need);
@@ -180,6 +214,19 @@ KEv event_pair(const vv_state* s, int i) {
   return KEv{reinterpret_cast<hipEvent_t>(s->events[2 * i]), reinterpret_cast<hipEvent_t>(s->events[2 * i + 1])};
 }
 
+// closed-loop feedback after the argmax (when requested)
+int enqueue_feedback(const vv_model* m, const vv_state* s, hipStream_t st) {
+  if (!s->feedback_table) return VV_OK;
+  StopIds stop{};
+  stop.n = s->n_stop;
+  for (int i = 0; i < s->n_stop; ++i) stop.id[i] = s->stop_ids[i];
+  hipLaunchKernelGGL(k_feedback, dim3(s->batch), dim3(256), 0, st, s->token, s->feedback_table, m->vocab, m->hidden,
+                     const_cast<uint16_t*>(s->input_embeds), const_cast<int32_t*>(s->pos), s->cap, s->history, s->done,
+                     stop);
+  VV_HIP(hipGetLastError());
+  return VV_OK;
+}
+
 int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
   char* ws = static_cast<char*>(s->workspace);
   char* pws = ws + layered_bytes(m, s->batch, s->cap);
@@ -189,7 +236,9 @@ int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
   const float* gf32;
   const float* sumsq;
   persistent_lm_inputs(m, s, pws, &gf32, &sumsq);
-  return enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st, event_pair(s, 1));
+  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st, event_pair(s, 1));
+  if (rc) return rc;
+  return enqueue_feedback(m, s, st);
 }
 
 int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
@@ -276,8 +325,10 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
   }
-  // final RMSNorm folded into the lm_head; greedy argmax
-  return enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st, event_pair(s, op++));
+  // final RMSNorm folded into the lm_head; greedy argmax; closed-loop feedback
+  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st, event_pair(s, op++));
+  if (rc) return rc;
+  return enqueue_feedback(m, s, st);
 }
 
 }  // namespace

@@ -141,6 +141,24 @@ class DeviceState:
                                   self.token.data_ptr(), self.trace.data_ptr() if trace else None,
                                   self.ws.data_ptr(), nbytes, None, 0, vv.PATH[path])
 
+    def enable_feedback(self, stop_ids=(151645, 151643), table=None):
+        """Closed-loop greedy decoding: every step gathers the embedding of its argmax token from
+        `table` (default: the model's lm_head, the tied fp16 table) as the next input, advances the
+        positions and records the tokens in `history` [B][cap] (position-indexed); a stop token
+        marks its sequence in `done`."""
+        import torch
+        assert 0 <= len(stop_ids) <= 4
+        tab = table if table is not None else self.model.lm
+        self.history = torch.full((self.batch, self.cap), -1, dtype=torch.int32, device=self.emb.device)
+        self.done = torch.zeros(self.batch, dtype=torch.int32, device=self.emb.device)
+        self._feedback_table = tab
+        self.struct.feedback_table = tab.data_ptr()
+        self.struct.history = self.history.data_ptr()
+        self.struct.done = self.done.data_ptr()
+        for i, t in enumerate(stop_ids):
+            self.struct.stop_ids[i] = int(t)
+        self.struct.n_stop = len(stop_ids)
+
     def load_cache_layer(self, idx: int, K: np.ndarray, V: np.ndarray):
         import torch
         self.k[idx].copy_(torch.from_numpy(K))

@@ -46,7 +46,9 @@ class vv_state(C.Structure):
     _fields_ = [("batch", C.c_int), ("cap", C.c_int), ("input_embeds", C.c_void_p), ("pos", C.c_void_p),
                 ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("logits", C.c_void_p), ("token", C.c_void_p),
                 ("h_trace", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int), ("path", C.c_int)]
+                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int), ("path", C.c_int),
+                ("feedback_table", C.c_void_p), ("history", C.c_void_p), ("done", C.c_void_p),
+                ("stop_ids", C.c_int32 * 4), ("n_stop", C.c_int)]
 
 
 _I64, _SZ, _P, _I, _F = C.c_int64, C.c_size_t, C.c_void_p, C.c_int, C.c_float
