@@ -54,8 +54,9 @@ __device__ __forceinline__ Geo geo(const AttnParams& p, int S) {
   return g;
 }
 
-// NP passes of 4 positions per wave: split S = 4 waves * 4 * NP positions
-template <int NP>
+// NP passes of 4 positions per wave: split S = 4 waves * 4 * NP positions.  STEP: the decode-step
+// flavour (q/k/v from the projection output, RoPE, KV append); else the stand-alone flavour.
+template <int NP, bool STEP>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __restrict__ rope_cs) {
   constexpr int S = kWaves * 4 * NP;
   __shared__ __align__(16) float qs[kMaxG][kD];
@@ -68,30 +69,26 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   const Geo G = geo(p, S);
   if (G.npos == 0) return;                 // past the sequence: the merge skips this split
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool step = p.qkv != nullptr;
+  constexpr bool step = STEP;
 
-  // ---- q first (it is needed first and is small), then every K/V row of the split ----------------
+  // ---- q first (small, needed first), then every K/V row of the split; no load is behind a branch
   // step: thread t < 16 g rotates dims 4c..4c+3 with 64+4c..64+4c+3 of head t/16 (c = t%16);
-  //       the next 16 threads rotate the new k, the 16 after them take the new v
+  //       the next 16 threads rotate the new k, the 16 after them take the new v (the other
+  //       threads read head 0 and ignore it)
   // stand-alone: thread t < 32 g takes dims 4(t%32)..+3 of head t/32
   float4 qa = make_float4(0.f, 0.f, 0.f, 0.f), qb = qa, ca = make_float4(1.f, 0.f, 1.f, 0.f), cb = ca;
   const int c16 = tid & 15;
   if (step) {
     const float* row = p.qkv + (size_t)G.b * p.ldqkv;
-    const float* src = nullptr;
-    if (tid < 16 * g) src = row + (size_t)(G.kvh * g + (tid >> 4)) * kD;
-    else if (tid < 16 * g + 16) src = row + (size_t)p.nq * kD + (size_t)G.kvh * kD;
-    else if (tid < 16 * g + 32) src = row + (size_t)(p.nq + p.nkv) * kD + (size_t)G.kvh * kD;
-    if (src) {
-      qa = *reinterpret_cast<const float4*>(src + 4 * c16);
-      qb = *reinterpret_cast<const float4*>(src + 64 + 4 * c16);
-      if (p.rope_theta > 0.f && tid < 16 * g + 16) {
-        ca = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2);
-        cb = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2 + 4);
-      }
-    }
-  } else if (tid < 32 * g) {
-    const size_t qi = ((size_t)G.b * p.nq + (size_t)G.kvh * g + (tid >> 5)) * kD + 4 * (tid & 31);
+    const int off = tid < 16 * g ? (G.kvh * g + (tid >> 4)) * kD
+                  : tid < 16 * g + 16 ? (p.nq + G.kvh) * kD
+                  : tid < 16 * g + 32 ? (p.nq + p.nkv + G.kvh) * kD : 0;
+    qa = *reinterpret_cast<const float4*>(row + off + 4 * c16);
+    qb = *reinterpret_cast<const float4*>(row + off + 64 + 4 * c16);
+    ca = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2);
+    cb = *reinterpret_cast<const float4*>(rope_cs + ((size_t)G.b * 64 + 4 * c16) * 2 + 4);
+  } else {
+    const size_t qi = ((size_t)G.b * p.nq + (size_t)G.kvh * g + min(tid >> 5, g - 1)) * kD + 4 * (tid & 31);
     if (p.q_f16) {
       const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.q) + qi);
       const h2_t h0 = as_h2(h.x), h1 = as_h2(h.y);
@@ -114,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   // ---- q (rotated) and the new k/v into LDS; the new position's cache slot ----------------------
   if (step) {
     // pair (j, j+64), j = 4c + i: (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin); v is not rotated
-    const bool rot = tid < 16 * g + 16;
+    const bool rot = p.rope_theta > 0.f && tid < 16 * g + 16;
     const float c4[4] = {ca.x, ca.z, cb.x, cb.z}, s4[4] = {ca.y, ca.w, cb.y, cb.w};
     const float x1[4] = {qa.x, qa.y, qa.z, qa.w}, x2[4] = {qb.x, qb.y, qb.z, qb.w};
     float r1[4], r2[4];
@@ -337,8 +334,14 @@ void attn_set_workspace(AttnParams& p, void* ws) {
 hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st, KEv ev) {
   const int grid = p.B * p.nkv * p.nsplit;
   const KEv e1 = p.nsplit == 1 ? ev : ev.first();
-  if (p.split == 64) VV_LAUNCH(k_attn<4>, dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
-  else VV_LAUNCH(k_attn<8>, dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+  const bool step = p.qkv != nullptr;
+  if (p.split == 64) {
+    if (step) VV_LAUNCH((k_attn<4, true>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+    else VV_LAUNCH((k_attn<4, false>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+  } else {
+    if (step) VV_LAUNCH((k_attn<8, true>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+    else VV_LAUNCH((k_attn<8, false>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(256), st, ev.last(), p, p.split);

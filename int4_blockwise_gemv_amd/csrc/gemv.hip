@@ -3,7 +3,7 @@
 // Decomposition: a wave owns one 64-row tile and one group of 8 consecutive blocks (lane i
 // accumulates row 64t+i, so each 16-byte block load of the wave is one contiguous 1 KiB run, and
 // the group's 8 fp16 scales are one more 16-byte load); a workgroup takes `wpg` consecutive
-// groups of one tile (up to 16), and a tile's groups are spread over `wpt` workgroups.  All nine
+// groups of one tile (up to 8), and a tile's groups are spread over `wpt` workgroups.  All nine
 // loads of a wave are in flight at once: short waves keep the HBM busiest.
 //
 // Activations: before any weight load, the workgroup's slice of x (256 elements per wave, per row)
@@ -28,8 +28,12 @@
 namespace vv {
 namespace {
 
-constexpr int kWavesSmallM = 4;   // most waves (groups) per workgroup for M <= 2 (wider was slower)
+constexpr int kWavesSmallM = 8;   // most waves (groups) per workgroup for M <= 2
 constexpr int kWavesLargeM = 4;   // for M > 2 (LDS holds M activation slices)
+// M <= 2 takes 8-wave workgroups only when that still leaves >= kWideMinWgs workgroups (two per
+// CU): fewer workgroups per tile shorten the cross-workgroup reduction of the large GEMVs, while
+// the small ones need the parallelism (7B shape: gate/up and down 8 waves, q|k|v and o 4).
+constexpr int kWideMinWgs = 512;
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
 
 // Operands of the epilogue.  Every wave loads them before its weight stream, from clamped
@@ -132,17 +136,16 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
   }
 }
 
-template <int MT> struct WavesFor { static constexpr int value = MT <= 2 ? kWavesSmallM : kWavesLargeM; };
-
-// WMAX waves at most; the launch uses p.wpg = blockDim.x / 64 of them (one 8-block group each).
+// WMAX waves at most (4 or 8: separate instances, so the 4-wave launches keep the register and
+// LDS budget of a 256-thread workgroup); the launch uses p.wpg = blockDim.x / 64 of them (one
+// 8-block group each).
 // From the first load to the barrier the code is branch-free: every load address is clamped
 // into the operand (a group past the end of K re-reads the last block and gets scale 0, rows
 // past M re-read row M-1 and are never stored), so all loads of a wave are in flight together.
-template <int MT, int EPI>
-__global__ __launch_bounds__(64 * WavesFor<MT>::value) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
+template <int MT, int EPI, int WMAX>
+__global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                                                   const uint4* __restrict__ sw,
                                                                   const uint16_t* __restrict__ x) {
-  constexpr int WMAX = WavesFor<MT>::value;
   constexpr int kItemK = WMAX * kBatch * kBlock;  // K elements per workgroup at most
   __shared__ __align__(16) uint16_t xs[MT][kItemK];
   __shared__ float red[WMAX][MT][kTileRows];
@@ -264,12 +267,12 @@ int part_rows(int M) { return M >= kMfmaMinM ? 16 : mt_of(M); }
 struct Plan { int kb, wpg, wpt, grid; };
 
 // One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave.
-// Batch <= 2: up to 16 waves (groups) per workgroup, the groups of a tile spread evenly over
-// wpt = ceil(groups / 16) workgroups; a tile of <= 16 groups is one workgroup and needs no
-// cross-workgroup reduction.  Larger batches: 4 waves per workgroup (LDS holds M slices).
+// The groups of a tile are spread evenly over wpt = ceil(groups / wmax) workgroups of at most
+// wmax waves (8 or 4, see kWideMinWgs; 4 for batches > 2, whose LDS holds M slices); a tile of
+// <= wmax groups is one workgroup and needs no cross-workgroup reduction.
 Plan make_plan(int M, int ntiles, int nb) {
   const int ng = (int)cdiv(nb, kBatch);
-  const int wmax = M <= 2 ? kWavesSmallM : kWavesLargeM;
+  const int wmax = M <= 2 && (int64_t)ntiles * cdiv(ng, kWavesSmallM) >= kWideMinWgs ? kWavesSmallM : kWavesLargeM;
   Plan pl;
   pl.kb = kBatch;
   pl.wpt = (int)cdiv(ng, wmax);
@@ -308,12 +311,19 @@ namespace {
 template <int EPI>
 void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t st, KEv ev) {
   const dim3 g(p.grid), b(64 * p.wpg);
+  const bool wide = p.wpg > kWavesLargeM;   // only batches <= 2 get 8-wave workgroups
   switch (mt_of(p.M)) {
-    case 1: VV_LAUNCH((k_gemv<1, EPI>), g, b, st, ev, p, q, s, p.x); break;
-    case 2: VV_LAUNCH((k_gemv<2, EPI>), g, b, st, ev, p, q, s, p.x); break;
-    case 4: VV_LAUNCH((k_gemv<4, EPI>), g, b, st, ev, p, q, s, p.x); break;
-    case 8: VV_LAUNCH((k_gemv<8, EPI>), g, b, st, ev, p, q, s, p.x); break;
-    default: VV_LAUNCH((k_gemv<16, EPI>), g, b, st, ev, p, q, s, p.x); break;
+    case 1:
+      if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x);
+      break;
+    case 2:
+      if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x);
+      break;
+    case 4: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
+    case 8: VV_LAUNCH((k_gemv<8, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
+    default: VV_LAUNCH((k_gemv<16, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
   }
 }
 }  // namespace
