@@ -211,7 +211,7 @@ def main():
     status = ds.status()
     log(f"{ms * 1e3:.1f} us/step ({1e3 / ms:.1f} steps/s), token {tok}, status {status}")
     if status != 0:
-        raise SystemExit("persistent step reported an in-kernel wait that gave up")
+        raise SystemExit("the persistent step reported an in-device wait that gave up")
 
     wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
     total = wb + kvb + lmb

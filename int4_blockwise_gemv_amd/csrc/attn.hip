@@ -27,6 +27,7 @@ constexpr int kPS = 132;          // partial record: m, l, pad, pad, o[128]
 constexpr int kWaves = 4;         // 256 threads per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSplits = 1024;  // splits per sequence the merge kernel takes
+constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3 for raw (untyped) loads on gfx9
 
 // Geometry of one workgroup's split.
 struct Geo { int b, kvh, bh, sidx, s0, npos, P; bool has_new; };
@@ -60,7 +61,7 @@ template <int NP, bool STEP>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __restrict__ rope_cs) {
   constexpr int S = kWaves * 4 * NP;
   __shared__ __align__(16) float qs[kMaxG][kD];
-  __shared__ float sc[kMaxG][S];
+  __shared__ __align__(16) float sc[kMaxG][S];
   __shared__ __align__(16) float red[kWaves][kMaxG][kD];      // [wave][head][dim]
   __shared__ __align__(16) uint16_t knew[kD], vnew[kD];
   __shared__ float mh[kMaxG], lh[kMaxG];
@@ -100,13 +101,22 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   const size_t kvbase = ((size_t)G.b * p.nkv + G.kvh) * (size_t)p.cap * kD;
   const int sl = lane & 15, pg = lane >> 4;
   const int jw = w * 4 * NP;               // first local position of this wave
-  u32x4 kr[NP], vr[NP];
+  // K: lane (pg, sl) holds dims 8 sl..8 sl+7 of position jw + 4 r + pg (16 lanes per position, for
+  // the score reductions).  V: lane l holds dims 2 l, 2 l + 1 of every position jw + i of the wave
+  // (one 256-byte row per load), so P.V needs no reduction across lanes.  Buffer loads over this
+  // (sequence, KV head)'s cap rows: rows past the capacity read as zero instead of needing a clamp
+  // per position, and the row offsets become immediates.
+  const int kvbytes = p.cap * kD * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kc + kvbase), (short)0, kvbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.vc + kvbase), (short)0, kvbytes, kBufWord3);
+  const int row0 = G.s0 + jw;              // first position of this wave
+  u32x4 kr[NP];
+  uint32_t vr[4 * NP];
 #pragma unroll
-  for (int r = 0; r < NP; ++r) {
-    const int pos = min(G.s0 + jw + 4 * r + pg, p.cap - 1);   // clamped rows are masked below
-    kr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.kc + kvbase + (size_t)pos * kD + 8 * sl));
-    vr[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.vc + kvbase + (size_t)pos * kD + 8 * sl));
-  }
+  for (int r = 0; r < NP; ++r)
+    kr[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (row0 + pg) * 256 + sl * 16 + r * 1024, 0, 0));
+#pragma unroll
+  for (int i = 0; i < 4 * NP; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b32(vrs, row0 * 256 + lane * 4 + i * 256, 0, 0);
 
   // ---- q (rotated) and the new k/v into LDS; the new position's cache slot ----------------------
   if (step) {
@@ -143,28 +153,38 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   if (G.has_new) {  // the new position's row was loaded from the cache before it was written
 #pragma unroll
     for (int r = 0; r < NP; ++r)
-      if (G.s0 + jw + 4 * r + pg == G.P) {
-        kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
-        vr[r] = *reinterpret_cast<const u32x4*>(&vnew[8 * sl]);
-      }
+      if (G.s0 + jw + 4 * r + pg == G.P) kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
+#pragma unroll
+    for (int i = 0; i < 4 * NP; ++i)
+      if (G.s0 + jw + i == G.P) vr[i] = *reinterpret_cast<const uint32_t*>(&vnew[2 * lane]);
   }
   // rows past the sequence get probability 0; zero their V so that whatever the cache holds there
   // (it is never part of the attention) cannot turn 0 * v into a NaN
 #pragma unroll
-  for (int r = 0; r < NP; ++r)
-    if (jw + 4 * r + pg >= G.npos) vr[r] = u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 4 * NP; ++i)
+    if (jw + i >= G.npos) vr[i] = 0u;
 
-  // ---- scores: 16 lanes per position, reduced across the 16 ---------------------------------------
+  // ---- scores: 16 lanes per position, reduced across the 16; two heads per pass (independent
+  // chains hide the LDS and cross-lane latencies when a SIMD runs a single wave) -----------------
 #pragma unroll 1
-  for (int hh = 0; hh < g; ++hh) {
-    float q8[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) q8[t] = qs[hh][8 * sl + t];
+  for (int h0 = 0; h0 < g; h0 += 2) {
+    const int h1 = min(h0 + 1, g - 1);     // a repeated head when g is odd: computed, not stored
+    float q0[8], q1[8];
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl]), b0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl + 4]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl]), b1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl + 4]);
+      q0[0] = a0.x; q0[1] = a0.y; q0[2] = a0.z; q0[3] = a0.w; q0[4] = b0.x; q0[5] = b0.y; q0[6] = b0.z; q0[7] = b0.w;
+      q1[0] = a1.x; q1[1] = a1.y; q1[2] = a1.z; q1[3] = a1.w; q1[4] = b1.x; q1[5] = b1.y; q1[6] = b1.z; q1[7] = b1.w;
+    }
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
-      float a = row16_sum(dot8_mix(q8, kr[r], 0.f));
+      const float s0 = row16_sum(dot8_mix(q0, kr[r], 0.f));
+      const float s1 = row16_sum(dot8_mix(q1, kr[r], 0.f));
       const int j = jw + 4 * r + pg;
-      if (sl == 0) sc[hh][j] = j < G.npos ? a * p.scale : -INFINITY;
+      if (sl == 0) {
+        sc[h0][j] = j < G.npos ? s0 * p.scale : -INFINITY;
+        if (h0 + 1 < g) sc[h1][j] = j < G.npos ? s1 * p.scale : -INFINITY;
+      }
     }
   }
   __syncthreads();
@@ -187,29 +207,28 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
   __syncthreads();
 
-  // ---- P.V: lane holds 8 dims of one position per pass; the wave's 4 position groups (rows of 16
-  // lanes) are summed lane-wise with permlane swaps, and one row writes the wave's partial ---------
+  // ---- P.V: lane l accumulates dims 2 l, 2 l + 1 over the wave's 4 NP positions (weights read
+  // from LDS as broadcasts, four positions per read); two heads per pass ---------------------------
 #pragma unroll 1
-  for (int hh = 0; hh < g; ++hh) {
-    float acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  for (int h0 = 0; h0 < g; h0 += 2) {
+    const int h1 = min(h0 + 1, g - 1);
+    float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
-      const float pj = sc[hh][jw + 4 * r + pg];
-      const u32x4 v = vr[r];
-      acc[0] = fma_mix_lo(pj, v.x, acc[0]); acc[1] = fma_mix_hi(pj, v.x, acc[1]);
-      acc[2] = fma_mix_lo(pj, v.y, acc[2]); acc[3] = fma_mix_hi(pj, v.y, acc[3]);
-      acc[4] = fma_mix_lo(pj, v.z, acc[4]); acc[5] = fma_mix_hi(pj, v.z, acc[5]);
-      acc[6] = fma_mix_lo(pj, v.w, acc[6]); acc[7] = fma_mix_hi(pj, v.w, acc[7]);
-    }
+      const float4 a0 = *reinterpret_cast<const float4*>(&sc[h0][jw + 4 * r]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&sc[h1][jw + 4 * r]);
+      const float q0[4] = {a0.x, a0.y, a0.z, a0.w}, q1[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = rows_lanewise_sum(acc[t]);
-    if (pg == 0) {
-      float* dst = &red[w][hh][8 * sl];
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = vr[4 * r + u];
+        e0 = fma_mix_lo(q0[u], v, e0);
+        o0 = fma_mix_hi(q0[u], v, o0);
+        e1 = fma_mix_lo(q1[u], v, e1);
+        o1 = fma_mix_hi(q1[u], v, o1);
+      }
     }
+    *reinterpret_cast<float2*>(&red[w][h0][2 * lane]) = make_float2(e0, o0);
+    if (h0 + 1 < g) *reinterpret_cast<float2*>(&red[w][h1][2 * lane]) = make_float2(e1, o1);
   }
   __syncthreads();
 
