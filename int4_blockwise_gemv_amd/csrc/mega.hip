@@ -233,23 +233,23 @@ __device__ void gemv_item(const MParams& p, const Item& it, int item, Lds& L) {
   const int tile = it.j / d.ns, sp = it.j % d.ns;
   const int K = d.nb * kBlock;
   const int e0 = sp * kItemK;
-  const int ne = min(K - e0, kItemK);
 
-  // weights first: they do not depend on the phase this item waits for
+  // weights first: they do not depend on the phase this item waits for.  Every load below is
+  // unconditional from a clamped (valid) address: a load behind a branch whose result merges with
+  // a default makes the compiler wait for it, and for every load before it, on the spot.
   const int grp = sp * kW + w;
   const int b0 = grp * kGB;
   const int nblk = min(max(d.nb - b0, 0), kGB);
-  const u32x4* qp = d.q + ((size_t)tile * d.nb + b0) * kTileRows + lane;
+  const int ngr = (d.nb + kGB - 1) / kGB;
+  const u32x4* qt = d.q + (size_t)tile * d.nb * kTileRows + lane;
+  const u32x4 sv = __builtin_nontemporal_load(d.s + ((size_t)tile * ngr + min(grp, ngr - 1)) * kTileRows + lane);
   u32x4 wv[kGB];
-  u32x4 sv = u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < kGB; ++i)
-    if (i < nblk) wv[i] = __builtin_nontemporal_load(qp + (size_t)i * kTileRows);
-  if (nblk > 0) sv = __builtin_nontemporal_load(d.s + ((size_t)tile * ((d.nb + kGB - 1) / kGB) + grp) * kTileRows + lane);
+  for (int i = 0; i < kGB; ++i) wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + i, d.nb - 1) * kTileRows);
 
   wait_dep(p, it, item);
 
-  // activation slice into LDS; epilogue operands (wave 0)
+  // activation slice into LDS, epilogue operands (loaded by every wave, used by wave 0)
   const uint16_t* x;
   switch (it.phase) {
     case PH_Q: x = p.xq + (size_t)l * p.xq_l; break;
@@ -257,68 +257,71 @@ __device__ void gemv_item(const MParams& p, const Item& it, int item, Lds& L) {
     case PH_G: x = p.xm + (size_t)l * p.xm_l; break;
     default:   x = p.act + (size_t)l * p.act_l; break;
   }
+  uint2 xr[MT];
+  {
+    const int ec = min(e0 + 4 * tid, K - 4);
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int e = 4 * tid;
-    if (m < p.B && e < ne)
-      *reinterpret_cast<uint2*>(&xs[m][e]) = *reinterpret_cast<const uint2*>(x + (size_t)m * K + e0 + e);
+    for (int m = 0; m < MT; ++m) xr[m] = *reinterpret_cast<const uint2*>(x + (size_t)min(m, p.B - 1) * K + ec);
   }
   const MLayer& lw = p.lw[l - p.l0];
   const int n64 = tile * kTileRows + lane;
-  float e_ss[MT], e_h[MT], e_b = 0.f, e_gam = 0.f;
+  const bool use_ss = it.phase == PH_Q || it.phase == PH_G;
+  const bool use_h = it.phase == PH_O || it.phase == PH_D;
+  const float* ss_src = it.phase == PH_Q ? p.ssi : p.ssm;
+  const float* h_src = it.phase == PH_D ? p.h1 : p.hin;
+  const int nh = min(n64, p.H - 1);
+  float e_ss[MT], e_h[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) { e_ss[m] = 0.f; e_h[m] = 0.f; }
-  if (w == 0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < p.B) {
-        if ((it.phase == PH_Q || it.phase == PH_G) && lane < p.ntH)
-          e_ss[m] = collect_f32((it.phase == PH_Q ? p.ssi : p.ssm) + (size_t)m * p.ntH + lane);
-        if (it.phase == PH_O) e_h[m] = collect_f32(p.hin + (size_t)m * p.H + n64);
-        if (it.phase == PH_D) e_h[m] = collect_f32(p.h1 + (size_t)m * p.H + n64);
-      }
-    }
-    if (it.phase == PH_Q && lw.bias && n64 < p.nqkv) e_b = h2f(lw.bias[n64]);
-    if (it.phase == PH_O) e_gam = h2f(lw.g2[n64]);
-    if (it.phase == PH_D) {
-      const uint16_t* gsrc = l + 1 == p.L ? p.gf : (l + 1 < p.l1 ? p.lw[l + 1 - p.l0].g1 : p.g1_next);
-      e_gam = h2f(gsrc[n64]);
-    }
+  for (int m = 0; m < MT; ++m) {
+    const int mc = min(m, p.B - 1);
+    e_ss[m] = collect_f32(ss_src + (size_t)mc * p.ntH + min(lane, p.ntH - 1));
+    e_h[m] = collect_f32(h_src + (size_t)mc * p.H + nh);
   }
+  const bool has_bias = it.phase == PH_Q && lw.bias != nullptr;
+  const uint16_t* gsrc = it.phase == PH_O ? lw.g2
+                       : (l + 1 == p.L ? p.gf : (l + 1 < p.l1 ? p.lw[l + 1 - p.l0].g1 : p.g1_next));
+  const uint16_t b16 = (has_bias ? lw.bias : p.gf)[has_bias ? min(n64, p.nqkv - 1) : 0];
+  const uint16_t g16 = gsrc[nh];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[m][4 * tid]) = xr[m];
   __syncthreads();
+  float e_b = 0.f, e_gam = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    e_ss[m] = (use_ss && lane < p.ntH && m < p.B) ? e_ss[m] : 0.f;
+    e_h[m] = (use_h && m < p.B) ? e_h[m] : 0.f;
+  }
+  if (has_bias && n64 < p.nqkv) e_b = h2f(b16);
+  if (use_h) e_gam = h2f(g16);
 
+  // blocks past the group's end get scale 0 (their clamped codes and activations are finite)
   const uint32_t m64 = vconst(0x54005400u);
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-  if (nblk > 0) {
+  {
     const int xb0 = w * kGB * kBlock;
     float corr[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      u32x4 xv = u32x4{0, 0, 0, 0};
-      if (m < p.B && lane < 4 * nblk) xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + lane * 8]);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + min(lane, 4 * kGB - 1) * 8]);
       corr[m] = quad_sum(corr_quarter(xv));
     }
 #pragma unroll
     for (int i = 0; i < kGB; ++i) {
-      if (i < nblk) {
-        const float sc = pick_scale(sv, i);
-        const uint32_t dw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+      const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
+      const uint32_t dw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m < p.B) {
-            const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
-            float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
+        float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const u32x4 xv = xb[k];
-              const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-              t = dot8_pairs(dw[k], x4, t, m64);
-            }
-            acc[m] = fmaf(sc, t, acc[m]);
-          }
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 xv = xb[k];
+          const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+          t = dot8_pairs(dw[k], x4, t, m64);
         }
+        acc[m] = fmaf(sc, t, acc[m]);
       }
     }
   }
