@@ -167,6 +167,9 @@ class Workload:
 QWEN2_1P5B = ModelShape("qwen2-1.5b-shaped", 28, 1536, 12, 2, 128, 8960, 151936)
 QWEN2_7B = ModelShape("qwen2-7b-shaped", 28, 3584, 28, 4, 128, 18944, 151936)
 QWEN2_7B_ABSMAX = ModelShape("qwen2-7b-shaped-absmax", 28, 3584, 28, 4, 128, 18944, 151936, mode="absmax")
+# the Realtime-0.5B decoder shape (20 layers, hidden 896 = 28 blocks per row; Qwen2-0.5B heads and
+# intermediate size), for the lock-step CFG pair (batch 2) and single-sequence decoding
+QWEN2_0P5B = ModelShape("qwen2-0.5b-shaped", 20, 896, 14, 2, 128, 4864, 151936)
 
 WORKLOADS = {
     "single-layer-1536": Workload("single-layer-1536", QWEN2_1P5B, 1, 256, 256, (0,),
@@ -175,6 +178,8 @@ WORKLOADS = {
     "decode-7b-p4000": Workload("decode-7b-p4000", QWEN2_7B, 1, 4000, 4001, tuple(range(5))),
     "decode-7b-absmax-p16384": Workload("decode-7b-absmax-p16384", QWEN2_7B_ABSMAX, 1, 16384, 16385, (0,),
                                         outlier_frac=0.01),
+    "decode-0.5b-cfg-b2": Workload("decode-0.5b-cfg-b2", QWEN2_0P5B, 2, 2048, 2049, (0,),
+                                   notes="lock-step classifier-free-guidance pair: 2 sequences at P = 2048"),
     "decode-1.5b-b16-ragged": Workload("decode-1.5b-b16-ragged", QWEN2_1P5B, 16, 0, 8193, (0,),
                                        ragged=(512, 8192)),
 }

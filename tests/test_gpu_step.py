@@ -172,11 +172,37 @@ def test_step_1p5b_width_two_layers(cuda, path):
     _compare(case, case.oracle())
 
 
+@pytest.mark.parametrize("seed", range(1, 10))
+def test_step_1p5b_width_seeds(cuda, seed):
+    """The other seeds of the 1.5B-shaped workload (two sampled layers each, P = 4096)."""
+    case = Case(synth.QWEN2_1P5B, seed, [seed, 27 - seed], [4096], 4097, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("path", PATHS)
 def test_step_7b_width_one_layer(cuda, path):
     """One layer at full 7B width, P = 4000, full lm_head."""
     case = Case(synth.QWEN2_7B, 0, [5], [4000], 4001, path=path)
+    case.run()
+    _compare(case, case.oracle())
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("seed", range(1, 5))
+def test_step_7b_width_seeds(cuda, seed):
+    """The other seeds of the 7B-shaped workload (one sampled layer each, P = 4000)."""
+    case = Case(synth.QWEN2_7B, seed, [3 * seed], [4000], 4001, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
+@pytest.mark.parametrize("path,pos", [("layered", [2048, 2048]), ("layered", [2048, 1500]), ("persistent", [2048])])
+def test_step_0p5b_cfg_pair(cuda, path, pos):
+    """The Realtime-0.5B shape (hidden 896, 14/2 heads): the lock-step CFG pair (batch 2) and one
+    sequence, two sampled layers, full lm_head (not a multiple of 256 wide: the VALU kernel)."""
+    case = Case(synth.QWEN2_0P5B, 0, [0, 19], pos, 2049, path=path)
     case.run()
     _compare(case, case.oracle())
 
