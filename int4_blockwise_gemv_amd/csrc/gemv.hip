@@ -19,9 +19,18 @@
 // removed once per block by subtracting C_b = 72 * sum_j x_j; the block sum is scaled by the
 // block's fp16 scale in fp32.
 //
-// Split-K: the waves of a workgroup are reduced in LDS; with wpt > 1 the last workgroup to
-// arrive at a tile adds the partials in a fixed order and runs the epilogue, so results do not
-// depend on timing.  With wpt = 1 the workgroup finishes its tile directly.
+// Split-K: the waves of a workgroup are reduced in LDS; with wpt = 1 the workgroup finishes its
+// tile directly.  With wpt > 1 the partials of a tile are added in a fixed order (so results do
+// not depend on timing) by one of two hand-offs:
+//  - small grids (every wave resident at once): the tile's last workgroup (kg = wpt - 1,
+//    dispatched after the others of its tile) is its reader.  The others store their partial with
+//    a tag into a hand-off slot and exit; the reader polls the slots, adds them (then its own
+//    partial), clears them and runs the epilogue: one store and one load on the critical path.
+//    Its writers never wait and are dispatched before it, so the wait ends; it is also bounded,
+//    and a wait that gives up sets the status word (when there is one) and yields NaN.
+//  - large grids: every workgroup publishes its partial and bumps the tile's arrival counter; the
+//    last to arrive adds the partials (a store, an atomic and a load, but no workgroup waits, so
+//    none holds a slot that a later workgroup's weight stream needs).
 #include "vv_internal.h"
 #include "gemv_core.h"
 
@@ -35,6 +44,38 @@ constexpr int kWavesLargeM = 4;   // for M > 2 (LDS holds M activation slices)
 // the small ones need the parallelism (7B shape: gate/up and down 8 waves, q|k|v and o 4).
 constexpr int kWideMinWgs = 512;
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
+constexpr uint64_t kFresh = 1ull << 32;     // tag of a filled hand-off slot (cleared slots are 0)
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up (seconds)
+
+// Sum of the n tagged fp32 values at p[k * stride], k in order, once every tag is set; then clears
+// the slots.  Polls 16 slots at a time (every lane of the wave takes part in the vote).
+__device__ float poll_sum(uint64_t* p, int n, size_t stride, int32_t* status) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    uint64_t v[16];
+    for (uint32_t it = 0;; ++it) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[k] = k0 + k < n ? collect_u64(p + (size_t)(k0 + k) * stride) : kFresh;
+        ok = ok && (v[k] >> 32) == 1u;
+      }
+      if (__all(ok)) break;
+      if (it >= kSpinLimit) {
+        if (status) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_nanf("");
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < n) {
+        s += __uint_as_float((uint32_t)v[k]);
+        publish_u64(p + (size_t)(k0 + k) * stride, 0);
+      }
+  }
+  return s;
+}
 
 // Operands of the epilogue.  Every wave loads them before its weight stream, from clamped
 // in-bounds addresses, so no load sits behind a branch: a conditional load whose result merges
@@ -237,23 +278,41 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
     epilogue<MT, EPI>(p, tile, tot, ep, lane);
     return;
   }
-  // publish this workgroup's partial, then count arrivals at the tile
-  float* my = p.part + ((size_t)tile * p.wpt + kg) * MT * kTileRows;
+  if (!p.poll) {
+    // publish this workgroup's partial, then count arrivals at the tile
+    float* my = p.part + ((size_t)tile * p.wpt + kg) * MT * kTileRows;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (m < M) publish_f32(&my[m * kTileRows + lane], tot[m]);
-  wait_published();
-  unsigned prev = 0;
-  if (lane == 0) prev = arrive(&p.cnt[tile]);
-  prev = __shfl(prev, 0, kWave);
-  if (prev != (unsigned)(p.wpt - 1)) return;
+    for (int m = 0; m < MT; ++m)
+      if (m < M) publish_f32(&my[m * kTileRows + lane], tot[m]);
+    wait_published();
+    unsigned prev = 0;
+    if (lane == 0) prev = arrive(&p.cnt[tile]);
+    prev = __shfl(prev, 0, kWave);
+    if (prev != (unsigned)(p.wpt - 1)) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) continue;
+      tot[m] = collect_sum_f32(p.part + ((size_t)tile * p.wpt * MT + m) * kTileRows + lane, p.wpt,
+                               (size_t)MT * kTileRows);
+    }
+    if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
+    epilogue<MT, EPI>(p, tile, tot, ep, lane);
+    return;
+  }
+  // writers: tagged partial into the tile's slot kg, then done; the reader (kg = wpt - 1) adds them
+  const int nw = p.wpt - 1;
+  uint64_t* sl = p.slots + (size_t)tile * nw * MT * kTileRows;
+  if (kg < nw) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M) publish_u64(&sl[((size_t)kg * MT + m) * kTileRows + lane], kFresh | __float_as_uint(tot[m]));
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= M) continue;
-    tot[m] = collect_sum_f32(p.part + ((size_t)tile * p.wpt * MT + m) * kTileRows + lane, p.wpt,
-                             (size_t)MT * kTileRows);
+    tot[m] = poll_sum(sl + (size_t)m * kTileRows + lane, nw, (size_t)MT * kTileRows, p.status) + tot[m];
   }
-  if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
   epilogue<MT, EPI>(p, tile, tot, ep, lane);
 }
 
@@ -264,7 +323,10 @@ int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16
 constexpr int kMfmaMinM = 5;
 int part_rows(int M) { return M >= kMfmaMinM ? 16 : mt_of(M); }
 
-struct Plan { int kb, wpg, wpt, grid; };
+struct Plan { int kb, wpg, wpt, grid, poll; };
+
+// The polled hand-off needs the whole grid resident: at most 8 waves per CU on 256 CUs.
+constexpr int64_t kPollMaxWaves = 256 * 8;
 
 // One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave.
 // The groups of a tile are spread evenly over wpt = ceil(groups / wmax) workgroups of at most
@@ -278,6 +340,7 @@ Plan make_plan(int M, int ntiles, int nb) {
   pl.wpt = (int)cdiv(ng, wmax);
   pl.wpg = (int)cdiv(ng, pl.wpt);
   pl.grid = (int)(cdiv((int64_t)ntiles * pl.wpt, kNumXcd) * kNumXcd);
+  pl.poll = pl.wpt > 1 && (int64_t)pl.grid * pl.wpg <= kPollMaxWaves;
   return pl;
 }
 
@@ -289,22 +352,36 @@ void gemv_plan(GemvParams& p) {
   p.wpg = pl.wpg;
   p.wpt = pl.wpt;
   p.grid = pl.grid;
+  p.poll = pl.poll;
 }
 
-size_t gemv_workspace_bytes(int M, int ntiles, int nb) {
+// Workspace: hand-off slots of the polled hand-off [tile][wpt - 1][MT][64] (small grids only),
+// then the partials [tile][wpt][MT][64] and arrival counters [tile] of the counter hand-off and
+// the matrix-core kernel.  The regions are separate, so one workspace serves every batch size.
+namespace {
+struct WsParts { size_t slots, part, cnt; };
+WsParts ws_parts(int M, int ntiles, int nb) {
   const Plan pl = make_plan(M, ntiles, nb);
   const int MT = part_rows(M);
-  const size_t part = (size_t)ntiles * pl.wpt * MT * kTileRows * sizeof(float);
-  const size_t cnt = (size_t)ntiles * sizeof(unsigned);
-  return align_up(part, 256) + align_up(cnt, 256);
+  WsParts w;
+  w.slots = pl.poll ? align_up((size_t)ntiles * (pl.wpt - 1) * MT * kTileRows * sizeof(uint64_t), 256) : 0;
+  w.part = align_up((size_t)ntiles * pl.wpt * MT * kTileRows * sizeof(float), 256);
+  w.cnt = align_up((size_t)ntiles * sizeof(unsigned), 256);
+  return w;
+}
+}  // namespace
+
+size_t gemv_workspace_bytes(int M, int ntiles, int nb) {
+  const WsParts w = ws_parts(M, ntiles, nb);
+  return w.slots + w.part + w.cnt;
 }
 
 void gemv_set_workspace(GemvParams& p, void* ws) {
-  const Plan pl = make_plan(p.M, p.ntiles, p.K / kBlock);
-  const int MT = part_rows(p.M);
-  const size_t part = (size_t)p.ntiles * pl.wpt * MT * kTileRows * sizeof(float);
-  p.part = reinterpret_cast<float*>(ws);
-  p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up(part, 256));
+  const WsParts w = ws_parts(p.M, p.ntiles, p.K / kBlock);
+  char* c = static_cast<char*>(ws);
+  p.slots = reinterpret_cast<uint64_t*>(c);
+  p.part = reinterpret_cast<float*>(c + w.slots);
+  p.cnt = reinterpret_cast<unsigned*>(c + w.slots + w.part);
 }
 
 namespace {

@@ -256,6 +256,9 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   float* rope = reinterpret_cast<float*>(ws + lay.rope);
   const int B = d.B, H = d.H;
   const float inv_h = 1.0f / (float)H;
+  // the step's sticky status word (first word of the persistent region): a GEMV hand-off wait
+  // that gives up sets it
+  int32_t* status = reinterpret_cast<int32_t*>(ws + layered_bytes(m, B, s->cap));
   int op = 0;   // timing event pair of the next operation
   VV_LAUNCH(k_step_prep, dim3(B * d.ntH), dim3(64), st, event_pair(s, op++), s->input_embeds, H, d.ntH,
             d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
@@ -273,6 +276,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.epi = EPI_STORE; p.bias = y.qkv_bias; p.y = qkv; p.y_f16 = 0; p.ldy = d.nqkv;
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
+      p.status = status;
       gemv_set_workspace(p, ws + lay.ws_qkv);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
@@ -294,6 +298,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.ntiles = d.ntH;
       p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.sumsq_out = sumsq;
       gemv_plan(p);
+      p.status = status;
       gemv_set_workspace(p, ws + lay.ws_o);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
@@ -305,6 +310,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.epi = EPI_SILU; p.act = act;
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
+      p.status = status;
       gemv_set_workspace(p, ws + lay.ws_gu);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
@@ -321,6 +327,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       p.sumsq_out = sumsq;
       p.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * B * H : nullptr;
       gemv_plan(p);
+      p.status = status;
       gemv_set_workspace(p, ws + lay.ws_down);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }

@@ -209,9 +209,12 @@ struct GemvParams {
   const uint16_t* x;         // fp16 [M][K]
   int M, N, K;               // N valid output rows (EPI_SILU: rows of gate = rows of up)
   int ntiles;                // tiles in the matrix
-  float* part;               // workspace partials
-  unsigned* cnt;             // workspace counters
+  float* part;               // workspace partials (matrix-core kernel)
+  unsigned* cnt;             // workspace counters (matrix-core kernel)
+  uint64_t* slots;           // workspace hand-off slots (VALU kernel): (tag << 32) | fp32 bits
+  int32_t* status;           // sticky status word set when a bounded wait gives up, or null
   int kb, wpg, wpt, grid;    // decomposition (filled by gemv_plan): waves per workgroup, workgroups per tile
+  int poll;                  // split-K hand-off: 1 = polled slots (small grids), 0 = arrival counter
   int epi;
   // EPI_STORE
   const uint16_t* bias;      // fp16 [N] or null
