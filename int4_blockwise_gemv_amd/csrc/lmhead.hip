@@ -6,68 +6,129 @@
 // 16-byte chunks i, i+64, ... of a row: 1 KiB contiguous per load instruction), keeps its slice
 // of the activation in registers, and reduces each row across the wave.  The largest logit is
 // tracked as a 64-bit key (order-preserving float bits, then the complemented index, so ties go
-// to the smallest index); each workgroup publishes its best key and the last one to finish picks
-// the winner in a fixed order.
+// to the smallest index); each workgroup publishes its best key and the grid's last workgroup
+// polls them and picks the winner (the maximum does not depend on the order).
 #include "vv_internal.h"
 
 namespace vv {
 namespace {
 
-constexpr int kRowsPerIter = 2;
+constexpr int kRowsPerIter = 2;   // rows per pass of the two-buffer row stream
 constexpr int kLmMfmaMinB = 3;          // batches from 3 rows take the matrix cores
 constexpr int kMaxChunksPerLane = 8;   // H <= 8 * 64 * 8 = 4096
 
+// key = order-preserving float bits : filled flag : (2^31 - 1 - index).  The flag (set in every
+// published key, cleared slots are 0) does not change the order among published keys.
+constexpr uint64_t kKeyFilled = 1ull << 31;
+constexpr uint32_t kSpinLimit = 1u << 22;
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
-  return ((uint64_t)float_order_key(v) << 32) | (uint64_t)(0xffffffffu - idx);
+  return ((uint64_t)float_order_key(v) << 32) | kKeyFilled | (uint64_t)(0x7fffffffu - idx);
+}
+
+// Argmax over the workgroups' keys.  Every workgroup stores its keys (with the filled flag) and
+// is done: no store waits and no arrival counter, so no workgroup holds its slot for a memory
+// round trip after its rows (an arrival atomic per workgroup, queued behind the weight stream,
+// costs ~12 us over the lm_head's ~1000 workgroups).  The last workgroup of the grid, dispatched
+// after all others, polls the keys of each batch row until every one is filled, takes the
+// maximum (independent of order), clears the slots for the next launch and writes the token.
+// The wait is bounded: one that gives up sets the status word (when there is one) and writes
+// token -1.  All threads of the workgroup call this after publishing their keys.
+__device__ void argmax_finish(const LmParams& p, int B) {
+  if (blockIdx.x != gridDim.x - 1) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = (int)gridDim.x;
+  for (int b = w; b < B; b += 4) {
+    uint64_t* keys = p.keys + (size_t)b * n;
+    uint64_t k = 0;
+    bool gave_up = false;
+    for (int i0 = 0; i0 < n; i0 += 64 * 16) {
+      uint64_t v[16];
+      for (uint32_t it = 0;; ++it) {
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          v[u] = collect_u64(keys + min(i0 + lane + 64 * u, n - 1));
+          ok = ok && (v[u] & kKeyFilled) != 0;
+        }
+        if (__all(ok)) break;
+        if (it >= kSpinLimit) { gave_up = true; break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        k = v[u] > k ? v[u] : k;
+        if (i0 + lane + 64 * u < n) publish_u64(keys + i0 + lane + 64 * u, 0);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t x = __shfl_xor(k, o, 64);
+      k = x > k ? x : k;
+    }
+    if (lane == 0) {
+      if (gave_up && p.status) __hip_atomic_store(p.status, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.token[b] = gave_up ? -1 : (int32_t)(0x7fffffffu - (uint32_t)(k & 0x7fffffffu));
+    }
+  }
 }
 
 template <int CPL, int BT>
 __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restrict__ W) {
   __shared__ uint64_t best_w[4][BT];
-  __shared__ unsigned s_last;
   const int H = p.H, V = p.V;
   const int nch = H / 8;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int wg = blockIdx.x;
   const int r0 = wg * p.rows_per_wg;
   const int r1 = min(V, r0 + p.rows_per_wg);
   const int rpw = (p.rows_per_wg + 3) / 4;
   const int wr0 = r0 + w * rpw;
   const int wr1 = min(r1, wr0 + rpw);
+  const int table_bytes = (int)min<int64_t>((int64_t)V * H * 2, 0x7fffffff);
 
   for (int bb = 0; bb < p.B; bb += BT) {
     const int nbt = min(BT, p.B - bb);
-    // activation slice in registers: chunk c = lane + 64*j holds x[8c .. 8c+7]
-    float xr[BT][CPL][8];
-    float rs[BT];
+    // activation slice in registers, chunk c = lane + 64 j holding x[8c .. 8c+7] scaled by rstd
+    // (so that it stays in fp16 range) and split into fp16 pairs x = hi + lo (~22 bits):
+    // v_dot2_f32_f16 then multiplies both parts by the fp16 weights exactly, accumulating in fp32
+    uint32_t xh[BT][CPL][4], xl[BT][CPL][4];
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
-      rs[t] = 1.f;
+      float rs = 1.f;
       if (t < nbt && p.rs_parts) {  // lane l adds part l (at most 64 parts), fixed reduction tree
         const float v = lane < p.rs_nparts ? p.rs_parts[(size_t)(bb + t) * p.rs_nparts + lane] : 0.f;
-        rs[t] = 1.0f / sqrtf(wave_sum(v) * p.rs_inv_n + p.eps);
+        rs = 1.0f / sqrtf(wave_sum(v) * p.rs_inv_n + p.eps);
       }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
+        float xv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xr[t][j][i] = 0.f;
+        for (int i = 0; i < 8; ++i) xv[i] = 0.f;
         if (t < nbt && c < nch) {
           if (p.x_f16) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + (size_t)(bb + t) * H + 8 * c);
             const uint32_t d4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              xr[t][j][2 * i] = (float)as_h2(d4[i]).x;
-              xr[t][j][2 * i + 1] = (float)as_h2(d4[i]).y;
+              xv[2 * i] = (float)as_h2(d4[i]).x;
+              xv[2 * i + 1] = (float)as_h2(d4[i]).y;
             }
           } else {
             const float* xs = reinterpret_cast<const float*>(p.x) + (size_t)(bb + t) * H + 8 * c;
             const float4 a = *reinterpret_cast<const float4*>(xs);
             const float4 b = *reinterpret_cast<const float4*>(xs + 4);
-            xr[t][j][0] = a.x; xr[t][j][1] = a.y; xr[t][j][2] = a.z; xr[t][j][3] = a.w;
-            xr[t][j][4] = b.x; xr[t][j][5] = b.y; xr[t][j][6] = b.z; xr[t][j][7] = b.w;
+            xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+            xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
           }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = xv[2 * i] * rs, x1 = xv[2 * i + 1] * rs;
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+          xh[t][j][i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          xl[t][j][i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
         }
       }
     }
@@ -75,40 +136,49 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
 #pragma unroll
     for (int t = 0; t < BT; ++t) best[t] = 0;
 
-    for (int r = wr0; r < wr1; r += kRowsPerIter) {
-      u32x4 wv[kRowsPerIter][CPL];
+    // rows stream through two register buffers: the loads of the next row are in flight while
+    // the current one is reduced.  No load sits behind a branch: a row past the wave's range
+    // re-reads its last row, and the loads are buffer loads over the whole table, so a chunk past
+    // H reads the next row's bytes (or zeros past the end of the table) against x = 0.
+    if (wr0 < wr1) {
+      const int row_bytes = H * 2;
+      auto load_row = [&](u32x4 (&buf)[CPL], int row) {
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u32x4*>(W), (short)0, __builtin_amdgcn_readfirstlane(table_bytes), 0x00020000);
+        const int off = min(row, wr1 - 1) * row_bytes + lane * 16;
 #pragma unroll
-      for (int rr = 0; rr < kRowsPerIter; ++rr)
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = lane + 64 * j;
-          wv[rr][j] = u32x4{0, 0, 0, 0};
-          if (r + rr < wr1 && c < nch) wv[rr][j] = __builtin_nontemporal_load(W + (size_t)(r + rr) * nch + c);
-        }
-#pragma unroll
-      for (int rr = 0; rr < kRowsPerIter; ++rr) {
+        for (int j = 0; j < CPL; ++j)
+          buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, j * 1024, 2));
+      };
+      auto reduce_row = [&](const u32x4 (&buf)[CPL], int row) {
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
           if (t >= nbt) continue;
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
-            const uint32_t d4[4] = {wv[rr][j].x, wv[rr][j].y, wv[rr][j].z, wv[rr][j].w};
+            const uint32_t d4[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const h2_t hv = as_h2(d4[i]);
-              a = fmaf((float)hv.x, xr[t][j][2 * i], a);
-              a = fmaf((float)hv.y, xr[t][j][2 * i + 1], a);
+              a = __builtin_amdgcn_fdot2(as_h2(d4[i]), as_h2(xh[t][j][i]), a, false);
+              a = __builtin_amdgcn_fdot2(as_h2(d4[i]), as_h2(xl[t][j][i]), a, false);
             }
           }
-          a = wave_sum(a) * rs[t];
-          const int row = r + rr;
+          a = wave_sum(a);
           if (row < wr1) {
             if (p.logits && lane == 0) p.logits[(size_t)(bb + t) * V + row] = a;
             const uint64_t k = make_key(a, (uint32_t)row);
             best[t] = k > best[t] ? k : best[t];
           }
         }
+      };
+      u32x4 wa[CPL], wb[CPL];
+      load_row(wa, wr0);
+      for (int r = wr0; r < wr1; r += 2) {
+        load_row(wb, r + 1);
+        reduce_row(wa, r);
+        load_row(wa, r + 2);
+        reduce_row(wb, r + 1);
       }
     }
 #pragma unroll
@@ -118,30 +188,11 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
     if (tid < nbt) {
       uint64_t k = best_w[0][tid];
       for (int i = 1; i < 4; ++i) k = best_w[i][tid] > k ? best_w[i][tid] : k;
-      publish_u64(&p.keys[(size_t)(bb + tid) * gridDim.x + wg], k);
+      publish_u64(&p.keys[(size_t)(bb + tid) * gridDim.x + wg], k | kKeyFilled);
     }
     __syncthreads();
   }
-  wait_published();
-  __syncthreads();
-  if (tid == 0) s_last = arrive(p.cnt) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  // one wave per batch row: max over the workgroup keys
-  for (int b = w; b < p.B; b += 4) {
-    uint64_t k = 0;
-    for (int i = lane; i < (int)gridDim.x; i += 64) {
-      const uint64_t v = collect_u64(p.keys + (size_t)b * gridDim.x + i);
-      k = v > k ? v : k;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t v = __shfl_xor(k, o, 64);
-      k = v > k ? v : k;
-    }
-    if (lane == 0) p.token[b] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
-  }
-  if (tid == 0) reset_counter(p.cnt);
+  argmax_finish(p, p.B);
 }
 
 // ---- batches of kLmMfmaMinB..16 rows: fp16 matrix cores ----------------------------------------
@@ -162,7 +213,6 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(LmParams p, const u32x4* __
   __shared__ __align__(16) uint16_t xh[16][kLmXS], xl[16][kLmXS];
   __shared__ float rs_s[16];
   __shared__ uint64_t best_w[4][16];
-  __shared__ unsigned s_last;
   const int H = p.H, V = p.V, B = p.B;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wg = blockIdx.x;
@@ -284,27 +334,9 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(LmParams p, const u32x4* __
   if (tid < B) {
     uint64_t k = best_w[0][tid];
     for (int i = 1; i < 4; ++i) k = best_w[i][tid] > k ? best_w[i][tid] : k;
-    publish_u64(&p.keys[(size_t)tid * gridDim.x + wg], k);
+    publish_u64(&p.keys[(size_t)tid * gridDim.x + wg], k | kKeyFilled);
   }
-  wait_published();
-  __syncthreads();
-  if (tid == 0) s_last = arrive(p.cnt) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  for (int bb = w; bb < B; bb += 4) {
-    uint64_t k = 0;
-    for (int i = lane; i < (int)gridDim.x; i += 64) {
-      const uint64_t v = collect_u64(p.keys + (size_t)bb * gridDim.x + i);
-      k = v > k ? v : k;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t v = __shfl_xor(k, o, 64);
-      k = v > k ? v : k;
-    }
-    if (lane == 0) p.token[bb] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
-  }
-  if (tid == 0) reset_counter(p.cnt);
+  argmax_finish(p, B);
 }
 
 bool lm_use_mfma(const LmParams& p) { return p.B >= kLmMfmaMinB && p.H % kLmKC == 0; }
@@ -326,17 +358,15 @@ void lm_plan(LmParams& p) {
   p.grid = (int)cdiv(p.V, p.rows_per_wg);
 }
 
+// Workspace: one key per (batch row, workgroup).
 size_t lm_workspace_bytes(int B, int V, int H) {
   LmParams p{};
   p.B = B; p.V = V; p.H = H;
   lm_plan(p);
-  return align_up((size_t)B * p.grid * sizeof(uint64_t), 256) + 256;
+  return align_up((size_t)B * p.grid * sizeof(uint64_t), 256);
 }
 
-void lm_set_workspace(LmParams& p, void* ws) {
-  p.keys = reinterpret_cast<uint64_t*>(ws);
-  p.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up((size_t)p.B * p.grid * sizeof(uint64_t), 256));
-}
+void lm_set_workspace(LmParams& p, void* ws) { p.keys = reinterpret_cast<uint64_t*>(ws); }
 
 hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev) {
   const int cpl = (int)cdiv(p.H / 8, 64);

@@ -196,8 +196,9 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
 }
 
 int enqueue_lm(const vv_model* m, const vv_state* s, const float* gf32, const float* sumsq, char* ws_lm,
-               hipStream_t st, KEv ev) {
+               int32_t* status, hipStream_t st, KEv ev) {
   LmParams p{};
+  p.status = status;
   p.W = m->lm_head; p.V = m->vocab; p.H = m->hidden; p.B = s->batch;
   p.x = gf32; p.x_f16 = 0;
   p.rs_parts = sumsq; p.rs_nparts = m->hidden / kTileRows; p.rs_inv_n = 1.0f / (float)m->hidden; p.eps = m->eps;
@@ -236,7 +237,7 @@ int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
   const float* gf32;
   const float* sumsq;
   persistent_lm_inputs(m, s, pws, &gf32, &sumsq);
-  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, st, event_pair(s, 1));
+  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, reinterpret_cast<int32_t*>(pws), st, event_pair(s, 1));
   if (rc) return rc;
   return enqueue_feedback(m, s, st);
 }
@@ -333,7 +334,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     }
   }
   // final RMSNorm folded into the lm_head; greedy argmax; closed-loop feedback
-  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, st, event_pair(s, op++));
+  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, status, st, event_pair(s, op++));
   if (rc) return rc;
   return enqueue_feedback(m, s, st);
 }

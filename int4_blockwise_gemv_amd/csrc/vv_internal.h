@@ -265,7 +265,8 @@ struct LmParams {
   const void* x; int x_f16;
   const float* rs_parts; int rs_nparts; float rs_inv_n; float eps;
   float* logits; int32_t* token;
-  uint64_t* keys; unsigned* cnt;
+  uint64_t* keys;            // workspace: one key per (batch row, workgroup)
+  int32_t* status;           // sticky status word set when a bounded wait gives up, or null
   int grid, rows_per_wg;
 };
 void lm_plan(LmParams& p);
