@@ -20,17 +20,15 @@
 // block's fp16 scale in fp32.
 //
 // Split-K: the waves of a workgroup are reduced in LDS; with wpt = 1 the workgroup finishes its
-// tile directly.  With wpt > 1 the partials of a tile are added in a fixed order (so results do
-// not depend on timing) by one of two hand-offs:
-//  - small grids (every wave resident at once): the tile's last workgroup (kg = wpt - 1,
-//    dispatched after the others of its tile) is its reader.  The others store their partial with
-//    a tag into a hand-off slot and exit; the reader polls the slots, adds them (then its own
-//    partial), clears them and runs the epilogue: one store and one load on the critical path.
-//    Its writers never wait and are dispatched before it, so the wait ends; it is also bounded,
-//    and a wait that gives up sets the status word (when there is one) and yields NaN.
-//  - large grids: every workgroup publishes its partial and bumps the tile's arrival counter; the
-//    last to arrive adds the partials (a store, an atomic and a load, but no workgroup waits, so
-//    none holds a slot that a later workgroup's weight stream needs).
+// tile directly.  With wpt > 1 a tile's last K-chunk workgroup (kg = wpt - 1) is its reader and
+// the others are writers: a writer stores its partial with a tag into a hand-off slot and exits
+// (no store wait, no atomic, so it gives its slot back at once); the reader computes its own
+// chunk, polls the slots, adds them in a fixed order (then its own partial, so results do not
+// depend on timing), clears them and runs the epilogue.  The tiles are dealt to the XCDs in
+// contiguous blocks, and each XCD's dispatch sequence is all writers of its tiles first, then
+// all readers: a reader waits only for writers dispatched before it on its own XCD (so the wait
+// always ends), and by the time it is dispatched they have mostly finished.  The wait is also
+// bounded: one that gives up sets the status word (when there is one) and yields NaN.
 #include "vv_internal.h"
 #include "gemv_core.h"
 
@@ -48,16 +46,19 @@ constexpr uint64_t kFresh = 1ull << 32;     // tag of a filled hand-off slot (cl
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up (seconds)
 
 // Sum of the n tagged fp32 values at p[k * stride], k in order, once every tag is set; then clears
-// the slots.  Polls 16 slots at a time (every lane of the wave takes part in the vote).
+// the slots.  Polls kPollBatch slots at a time (every lane of the wave takes part in the vote):
+// 10 covers the 9 writers of the 7B down projection in one round trip and still fits in the
+// registers the weight stream needs (a batch of 16 costs the M <= 2 kernels two waves per SIMD).
+constexpr int kPollBatch = 10;
 __device__ float poll_sum(uint64_t* p, int n, size_t stride, int32_t* status) {
   float s = 0.f;
-  for (int k0 = 0; k0 < n; k0 += 16) {
-    uint64_t v[16];
+  for (int k0 = 0; k0 < n; k0 += kPollBatch) {
+    uint64_t v[kPollBatch];
     for (uint32_t it = 0;; ++it) {
       bool ok = true;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        v[k] = k0 + k < n ? collect_u64(p + (size_t)(k0 + k) * stride) : kFresh;
+      for (int k = 0; k < kPollBatch; ++k) {
+        v[k] = collect_u64(p + (size_t)min(k0 + k, n - 1) * stride);
         ok = ok && (v[k] >> 32) == 1u;
       }
       if (__all(ok)) break;
@@ -68,13 +69,30 @@ __device__ float poll_sum(uint64_t* p, int n, size_t stride, int32_t* status) {
       __builtin_amdgcn_s_sleep(2);
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < kPollBatch; ++k)
       if (k0 + k < n) {
         s += __uint_as_float((uint32_t)v[k]);
         publish_u64(p + (size_t)(k0 + k) * stride, 0);
       }
   }
   return s;
+}
+
+// Role of this workgroup in the split-K decomposition (see the top of the file): XCD x = wg % 8
+// takes tiles [x tpx, (x + 1) tpx) and runs, in dispatch order, their (wpt - 1) writers (tile-major)
+// and then their readers.  Returns false for padding workgroups.
+__device__ __forceinline__ bool split_role(int ntiles, int wpt, int& tile, int& kg) {
+  const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+  const int tpx = (ntiles + kNumXcd - 1) / kNumXcd;
+  const int nwr = tpx * (wpt - 1);
+  if (i < nwr) {
+    tile = x * tpx + i / (wpt - 1);
+    kg = i % (wpt - 1);
+  } else {
+    tile = x * tpx + (i - nwr);
+    kg = wpt - 1;
+  }
+  return tile < ntiles && i < tpx * wpt;
 }
 
 // Operands of the epilogue.  Every wave loads them before its weight stream, from clamped
@@ -195,11 +213,8 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   const int nb = K / kBlock;
   const int ng = (nb + kBatch - 1) / kBatch;
   const int M = p.M;
-  const uint32_t nwg = (uint32_t)p.ntiles * p.wpt;
-  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (L >= nwg) return;
-  const int tile = L / p.wpt;
-  const int kg = L % p.wpt;
+  int tile, kg;
+  if (!split_role(p.ntiles, p.wpt, tile, kg)) return;
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
   const int e0 = kg * W * kBatch * kBlock;          // first K element of this workgroup
@@ -278,27 +293,6 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
     epilogue<MT, EPI>(p, tile, tot, ep, lane);
     return;
   }
-  if (!p.poll) {
-    // publish this workgroup's partial, then count arrivals at the tile
-    float* my = p.part + ((size_t)tile * p.wpt + kg) * MT * kTileRows;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (m < M) publish_f32(&my[m * kTileRows + lane], tot[m]);
-    wait_published();
-    unsigned prev = 0;
-    if (lane == 0) prev = arrive(&p.cnt[tile]);
-    prev = __shfl(prev, 0, kWave);
-    if (prev != (unsigned)(p.wpt - 1)) return;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= M) continue;
-      tot[m] = collect_sum_f32(p.part + ((size_t)tile * p.wpt * MT + m) * kTileRows + lane, p.wpt,
-                               (size_t)MT * kTileRows);
-    }
-    if (lane == 0) reset_counter(&p.cnt[tile]);  // ready for the next launch
-    epilogue<MT, EPI>(p, tile, tot, ep, lane);
-    return;
-  }
   // writers: tagged partial into the tile's slot kg, then done; the reader (kg = wpt - 1) adds them
   const int nw = p.wpt - 1;
   uint64_t* sl = p.slots + (size_t)tile * nw * MT * kTileRows;
@@ -323,10 +317,7 @@ int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16
 constexpr int kMfmaMinM = 5;
 int part_rows(int M) { return M >= kMfmaMinM ? 16 : mt_of(M); }
 
-struct Plan { int kb, wpg, wpt, grid, poll; };
-
-// The polled hand-off needs the whole grid resident: at most 8 waves per CU on 256 CUs.
-constexpr int64_t kPollMaxWaves = 256 * 8;
+struct Plan { int kb, wpg, wpt, grid; };
 
 // One 8-block group (one batch: 8 weight loads + 1 scale load, all in flight at once) per wave.
 // The groups of a tile are spread evenly over wpt = ceil(groups / wmax) workgroups of at most
@@ -339,8 +330,7 @@ Plan make_plan(int M, int ntiles, int nb) {
   pl.kb = kBatch;
   pl.wpt = (int)cdiv(ng, wmax);
   pl.wpg = (int)cdiv(ng, pl.wpt);
-  pl.grid = (int)(cdiv((int64_t)ntiles * pl.wpt, kNumXcd) * kNumXcd);
-  pl.poll = pl.wpt > 1 && (int64_t)pl.grid * pl.wpg <= kPollMaxWaves;
+  pl.grid = (int)(cdiv(ntiles, kNumXcd) * kNumXcd * pl.wpt);
   return pl;
 }
 
@@ -352,19 +342,18 @@ void gemv_plan(GemvParams& p) {
   p.wpg = pl.wpg;
   p.wpt = pl.wpt;
   p.grid = pl.grid;
-  p.poll = pl.poll;
 }
 
-// Workspace: hand-off slots of the polled hand-off [tile][wpt - 1][MT][64] (small grids only),
-// then the partials [tile][wpt][MT][64] and arrival counters [tile] of the counter hand-off and
-// the matrix-core kernel.  The regions are separate, so one workspace serves every batch size.
+// Workspace: hand-off slots of the VALU kernel [tile][wpt - 1][MT][64], then the partials
+// [tile][wpt][16][64] and arrival counters [tile] of the matrix-core kernel.  The regions are
+// separate, so one workspace serves every batch size.
 namespace {
 struct WsParts { size_t slots, part, cnt; };
 WsParts ws_parts(int M, int ntiles, int nb) {
   const Plan pl = make_plan(M, ntiles, nb);
   const int MT = part_rows(M);
   WsParts w;
-  w.slots = pl.poll ? align_up((size_t)ntiles * (pl.wpt - 1) * MT * kTileRows * sizeof(uint64_t), 256) : 0;
+  w.slots = align_up((size_t)ntiles * (pl.wpt - 1) * MT * kTileRows * sizeof(uint64_t), 256);
   w.part = align_up((size_t)ntiles * pl.wpt * MT * kTileRows * sizeof(float), 256);
   w.cnt = align_up((size_t)ntiles * sizeof(unsigned), 256);
   return w;

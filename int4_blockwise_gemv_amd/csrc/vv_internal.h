@@ -214,7 +214,6 @@ struct GemvParams {
   uint64_t* slots;           // workspace hand-off slots (VALU kernel): (tag << 32) | fp32 bits
   int32_t* status;           // sticky status word set when a bounded wait gives up, or null
   int kb, wpg, wpt, grid;    // decomposition (filled by gemv_plan): waves per workgroup, workgroups per tile
-  int poll;                  // split-K hand-off: 1 = polled slots (small grids), 0 = arrival counter
   int epi;
   // EPI_STORE
   const uint16_t* bias;      // fp16 [N] or null
