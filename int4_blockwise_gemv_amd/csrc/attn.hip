@@ -16,6 +16,8 @@
 // Decode-step flavour: q/k/v come from the fused projection output; the workgroup rotates q
 // (and, for the split that holds the new position, k) with RoPE, writes fp16 k and v into the
 // cache slot of the new position and attends over pos+1 positions.
+#include <algorithm>
+
 #include "vv_internal.h"
 
 namespace vv {
@@ -254,13 +256,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
 }
 
-// One workgroup per (sequence, query head): thread (half, d) holds dim d of the splits of its
-// half.  All record loads are issued at once; the split weights e_s = exp(m_s - M) are computed
-// once in LDS.  o = sum_s e_s o_s / sum_s e_s l_s, splits in a fixed order.
-__global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int S) {
-  constexpr int kChunk = 32;
+// One workgroup per (sequence, query head) of 128 * parts threads: thread (part, d) holds dim d of
+// the splits of its part (a contiguous run).  All record loads are issued at once (parts are sized
+// so that a part holds at most kMergeChunk splits of the longest sequence); the split weights
+// e_s = exp(m_s - M) are computed once in LDS.  o = sum_s e_s o_s / sum_s e_s l_s, splits in a
+// fixed order within each part, then the parts in order.
+constexpr int kMergeChunk = 40;
+constexpr int kMergeMaxParts = 8;
+__global__ __launch_bounds__(128 * kMergeMaxParts) void k_attn_merge(AttnParams p, int S) {
   __shared__ float ms_[kMaxSplits], ls_[kMaxSplits], ws_[kMaxSplits];
-  __shared__ float part[2][kD];
+  __shared__ float part[kMergeMaxParts][kD];
   __shared__ float Ls;
   const int g = p.nq / p.nkv;
   const int bq = blockIdx.x;                 // b * nq + head
@@ -276,20 +281,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int S) {
     len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
   }
   const int n = (len + S - 1) / S;           // splits that hold positions
-  const int tid = threadIdx.x, d = tid & 127, half = tid >> 7;
-  const int per = (n + 1) >> 1;
-  const int s_beg = half * per, s_end = min(n, s_beg + per);
+  const int nthr = blockDim.x, parts = nthr / kD;
+  const int tid = threadIdx.x, d = tid & (kD - 1), pt = tid / kD;
+  const int per = (n + parts - 1) / parts;
+  const int s_beg = pt * per, s_end = min(n, s_beg + per);
   const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
   const size_t stride = (size_t)kMaxG * kPS;
-  // every load first, from clamped (valid) records: this half's first kChunk values of dim d, then
-  // the (m, l) of split tid (splits past 256 are rare: a loop takes them afterwards)
-  float v[kChunk];
+  // every load first, from clamped (valid) records: this part's first kMergeChunk values of dim d,
+  // then the (m, l) of split tid (a loop takes splits past the thread count afterwards)
+  float v[kMergeChunk];
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u) v[u] = rec0[(size_t)min(s_beg + u, n - 1) * stride + 4 + d];
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = rec0[(size_t)min(s_beg + u, n - 1) * stride + 4 + d];
   const int s0 = min(tid, n - 1);
   const float m0 = rec0[(size_t)s0 * stride], l0 = rec0[(size_t)s0 * stride + 1];
   if (tid < n) { ms_[tid] = m0; ls_[tid] = l0; }
-  for (int s = tid + 256; s < n; s += 256) {
+  for (int s = tid + nthr; s < n; s += nthr) {
     ms_[s] = rec0[s * stride];
     ls_[s] = rec0[s * stride + 1];
   }
@@ -310,23 +316,31 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int S) {
   __syncthreads();
   float O = 0.f;
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u)
+  for (int u = 0; u < kMergeChunk; ++u)
     if (s_beg + u < s_end) O = fmaf(ws_[s_beg + u], v[u], O);
-  for (int c0 = s_beg + kChunk; c0 < s_end; c0 += kChunk) {
+  for (int c0 = s_beg + kMergeChunk; c0 < s_end; c0 += kMergeChunk) {
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = c0 + u < s_end ? rec0[(c0 + u) * stride + 4 + d] : 0.f;
+    for (int u = 0; u < kMergeChunk; ++u) v[u] = c0 + u < s_end ? rec0[(c0 + u) * stride + 4 + d] : 0.f;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u)
+    for (int u = 0; u < kMergeChunk; ++u)
       if (c0 + u < s_end) O = fmaf(ws_[c0 + u], v[u], O);
   }
-  part[half][d] = O;
+  part[pt][d] = O;
   __syncthreads();
-  if (half == 0) {
-    const float o = (part[0][d] + part[1][d]) / Ls;
+  if (pt == 0) {
+    float t = 0.f;
+    for (int i = 0; i < parts; ++i) t += part[i][d];
+    const float o = t / Ls;
     const size_t oi = ((size_t)b * p.nq + h) * kD + d;
     if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
     else reinterpret_cast<float*>(p.out)[oi] = o;
   }
+}
+
+// threads of the merge workgroup: enough parts that each holds at most kMergeChunk splits
+int merge_threads(int nsplit) {
+  const int parts = (int)std::min<int64_t>(kMergeMaxParts, std::max<int64_t>(2, cdiv(nsplit, kMergeChunk)));
+  return parts * kD;
 }
 
 }  // namespace
@@ -363,7 +377,7 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(256), st, ev.last(), p, p.split);
+  VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(merge_threads(p.nsplit)), st, ev.last(), p, p.split);
   return hipGetLastError();
 }
 
