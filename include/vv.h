@@ -23,9 +23,9 @@
  *     launched nothing.  Device faults surface at the caller's next synchronisation.
  *   - Workspaces: calls that take `ws`/`ws_bytes` need a device buffer of at least the size their
  *     *_workspace() query returns, ZERO-FILLED before its first use (vv_workspace_init does this);
- *     every completed call leaves its counters and hand-off slots cleared again, so a workspace can be reused
- *     by later calls on the same stream without re-initialisation.  Two calls that run
- *     concurrently must not share a workspace.
+ *     every completed call leaves its counters and hand-off slots cleared again, so a workspace
+ *     can be reused by later calls on the same stream without re-initialisation.  Two calls that
+ *     run concurrently must not share a workspace.
  *   - Return value: VV_OK or a negative vv_status; vv_last_error() gives a thread-local message.
  */
 #ifndef VV_H
