@@ -21,6 +21,7 @@ Sources (pages, cited by title and section):
     lm_head/embeddings stay fp16;
   - graph contracts: decoder_step(input_embeds[1,1,H], position_ids[1,1],
     past K/V [28,1,kv,P,128]) -> logits[1,1,V], present K/V [...,P+1,128];
+    decoder_init (the prompt's S tokens) -> logits and present K/V [...,S,128];
   - decoding note: greedy argmax, stop tokens 151645 / 151643.
 * "VibeVoice-1.5B -- Current Status", Architecture section: the backbone is
   Qwen2.5-1.5B (hidden 1536, 28 layers, 12 heads, 2 KV heads, q/k/v bias,
@@ -372,12 +373,15 @@ def decode_step(m: OModel, input_embeds, pos, Kcaches, Vcaches, trace: Optional[
     return logits, tok, gap, h
 
 
-def full_forward(m: OModel, embeds, K0=None, V0=None):
-    """Independent full causal forward over T tokens (for the incremental == full check).
+def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None):
+    """Independent full causal forward over T tokens (for the incremental == full check, and the
+    decoder_init / prefill contract of the bitnet-onnx page's graph contracts).
 
     embeds [T, H] fp16 values; optional prefix caches K0/V0 [L, nkv, P0, d] fp16 that the
     T tokens attend to (positions 0..P0-1), new tokens at positions P0..P0+T-1.  The new
-    keys/values are rounded to fp16 before use, as the decode step stores them.
+    keys/values are rounded to fp16 before use, as the decode step stores them.  With kv_out
+    (a sequence of (K, V) fp16 arrays [nkv, cap, d], one pair per layer), the new keys/values
+    are also stored at their positions there (the present K/V of the contract).
     Returns logits [T, V] of every position.
     """
     x = np.asarray(embeds, dtype=np.float16).astype(np.float64)
@@ -393,6 +397,10 @@ def full_forward(m: OModel, embeds, K0=None, V0=None):
         v = gemv(*L.v, a, L.bv).reshape(T, nkv, d)
         k = k.astype(np.float16).astype(np.float64)
         v = v.astype(np.float16).astype(np.float64)
+        if kv_out is not None:
+            Kc, Vc = kv_out[li]
+            Kc[:, P0:P0 + T] = k.transpose(1, 0, 2).astype(np.float16)
+            Vc[:, P0:P0 + T] = v.transpose(1, 0, 2).astype(np.float16)
         if P0:
             kall = np.concatenate([np.asarray(K0[li], np.float64).transpose(1, 0, 2), k], axis=0)
             vall = np.concatenate([np.asarray(V0[li], np.float64).transpose(1, 0, 2), v], axis=0)
@@ -412,6 +420,16 @@ def full_forward(m: OModel, embeds, K0=None, V0=None):
         x = x + gemv(*L.down, silu(gemv(*L.gate, mm)) * gemv(*L.up, mm))
     f = rmsnorm(x, m.gf, m.eps)
     return f @ np.asarray(m.lm, np.float64).T
+
+
+def prefill(m: OModel, embeds, Kc, Vc):
+    """decoder_init (bitnet-onnx page, graph contracts): the T prompt embeddings at positions
+    0..T-1 of an empty cache -> present K/V of those positions (written into Kc[l], Vc[l],
+    fp16 [nkv, cap, d]) and the logits of the last position, which greedy decoding needs to
+    pick the first generated token.  Returns (logits [V], token, top-2 gap)."""
+    logits = full_forward(m, embeds, kv_out=list(zip(Kc, Vc)))
+    tok, gap = argmax_with_gap(logits[-1])
+    return logits[-1], tok, gap
 
 
 # ---------------------------------------------------------------------------

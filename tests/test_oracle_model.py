@@ -139,6 +139,32 @@ def test_incremental_decode_equals_full_forward():
         assert tok[0] == int(np.argmax(full[t]))
 
 
+def test_prefill_equals_token_by_token_decode():
+    """The prefill (decoder_init) oracle == T decode steps from an empty cache: the same present
+    K/V at every position and the same logits at the last one (two independent formulations)."""
+    shape = synth.TinyShape(layers=2, hidden=256, n_q=4, n_kv=2, head_dim=64, inter=384, vocab=500)
+    m = oracle_model(shape, seed=3)
+    T, cap = 5, 8
+    L = shape.layers
+    emb = synth.fp16_normal(4, 0, synth.T_EMB, (T, shape.hidden))
+    Kp = [np.zeros((shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
+    Vp = [np.zeros((shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
+    logits, tok, gap = O.prefill(m, emb, Kp, Vp)
+    Kc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
+    Vc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
+    for t in range(T):
+        step_logits, step_tok, _, _ = O.decode_step(m, emb[t:t + 1], np.array([t]), Kc, Vc)
+    assert np.allclose(logits, step_logits[0], rtol=1e-12, atol=1e-12)
+    assert tok == int(step_tok[0])
+    for li in range(L):
+        # fp16 stores of the same float64 values: allow a rounding-boundary flip of one ulp
+        a = Kp[li].astype(np.float64)
+        b = Kc[li][0].astype(np.float64)
+        assert np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3)) <= 2 ** -10
+        assert np.array_equal(Kp[li][:, T:], Kc[li][0][:, T:])   # untouched positions stay zero
+        assert np.max(np.abs(Vp[li].astype(np.float64) - Vc[li][0].astype(np.float64))) <= 2 ** -10 * 8
+
+
 def test_batched_step_equals_per_sequence_steps():
     """Sequences in a batch are independent (ragged positions)."""
     shape = synth.TinyShape(layers=1, hidden=128, n_q=2, n_kv=1, head_dim=64, inter=128, vocab=200)
