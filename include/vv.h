@@ -283,6 +283,26 @@ int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, v
 int vv_decode_graph_launch(vv_graph* g, void* stream);
 int vv_decode_graph_destroy(vv_graph* g);
 
+/* ---------------------------------------------------------------------------------------------
+ * Prefill (bitnet-onnx page, graph contracts: decoder_init runs the prompt and returns logits and
+ * the present K/V that decoder_step continues from), batch 1.
+ *   input_embeds: device fp16 [S][H], the prompt's S embeddings at positions 0..S-1.
+ *   k_cache/v_cache: device fp16 [L][1][nkv][cap][head_dim] (the vv_state layout with batch 1);
+ *     positions 0..S-1 of every layer are written (fp16 k after RoPE, fp16 v), the rest untouched.
+ *     A decode step with pos = S then continues the sequence.
+ *   logits: device fp32 [V] of the last position, or NULL; token: device int32 [1], its greedy
+ *     argmax (smallest index on ties).
+ *   ws: vv_prefill_workspace(m, S, cap) bytes, 256-byte aligned (no zero-fill needed beyond the
+ *     usual first-use rule).  Needs 1 <= S <= cap <= 131072 and the vv_decode_step shape rules.
+ * Computes in the decode step's precisions: int4 weights x fp16 activations with fp32 sums
+ * (matrix cores), fp32 residual stream, RMSNorm and softmax; causal attention over the fp16
+ * cache.
+ * ------------------------------------------------------------------------------------------- */
+size_t vv_prefill_workspace(const vv_model* m, int S, int cap);
+int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t* k_cache,
+               uint16_t* v_cache, int cap, float* logits, int32_t* token, void* ws,
+               size_t ws_bytes, void* stream);
+
 /* Zero-fills a workspace (one fill kernel, capture-safe) */
 int vv_workspace_init(void* ws, size_t ws_bytes, void* stream);
 

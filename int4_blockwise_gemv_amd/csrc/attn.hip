@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       qa = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + qi);
     }
   }
-  const size_t kvbase = ((size_t)G.b * p.nkv + G.kvh) * (size_t)p.cap * kD;
+  const size_t kvbase = ((size_t)(p.kv_shared ? 0 : G.b) * p.nkv + G.kvh) * (size_t)p.cap * kD;
   const int sl = lane & 15, pg = lane >> 4;
   const int jw = w * 4 * NP;               // first local position of this wave
   // K: lane (pg, sl) holds dims 8 sl..8 sl+7 of position jw + 4 r + pg (16 lanes per position, for

@@ -1,6 +1,6 @@
-// Device arithmetic of the int4 block-32 dot product, shared by the stand-alone GEMV and the
-// persistent decode-step kernel (MatMulNBits block layout, "vibevoice-asr-bitnet-onnx" page,
-// quantisation section: code q = t + 8 in a nibble, one fp16 scale per 32-element block).
+// Device arithmetic of the int4 block-32 dot product, shared by the GEMV kernels, the persistent
+// decode-step kernel and the prefill GEMM (MatMulNBits block layout, "vibevoice-asr-bitnet-onnx"
+// page, quantisation section: code q = t + 8 in a nibble, one fp16 scale per 32-element block).
 #pragma once
 
 #include "vv_internal.h"
@@ -46,5 +46,45 @@ __device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---- matrix-core operands (v_mfma_f32_16x16x32_f16) of the tiled layout --------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// A 16-byte block load of a wave gives lane r the 32 codes of row r of a 64-row tile, as 4 dwords
+// of 8 codes.  The 4 x 4 transpose of (dword, 16-lane group) below moves dword s of row 16 g + i
+// to lane 16 s + i of t[g]: t[g] is then the MFMA operand "8 consecutive k of row 16 g + lane % 16,
+// k-slice lane / 16" for row group g.
+__device__ __forceinline__ void block_to_operands(const u32x4& v, uint32_t (&t)[4]) {
+  uint32_t t0 = v.x, t1 = v.y, t2 = v.z, t3 = v.w;
+  swap32(t0, t2);
+  swap32(t1, t3);
+  swap16(t0, t1);
+  swap16(t2, t3);
+  t[0] = t0; t[1] = t1; t[2] = t2; t[3] = t3;
+}
+
+// 8 codes of one dword (even elements in nibbles 0..3, odd in 4..7) -> 8 fp16 (q - 8), k order:
+// the nibble goes into the mantissa of fp16 64.0 (ulp 1/16, so the value reads 64 + q) and one
+// packed fp16 add subtracts 72, exactly
+__device__ __forceinline__ half8 codes_to_half8(uint32_t d, uint32_t m64) {
+  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
+  const h2_t p0 = as_h2(((d << 4) & 0x00F000F0u) | m64) + off;
+  const h2_t p1 = as_h2((d & 0x00F000F0u) | m64) + off;
+  const h2_t p2 = as_h2(((d >> 4) & 0x00F000F0u) | m64) + off;
+  const h2_t p3 = as_h2(((d >> 8) & 0x00F000F0u) | m64) + off;
+  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
 
 }  // namespace vv

@@ -21,35 +21,11 @@
 namespace vv {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kRows = 16;                    // batch rows of the contraction
 constexpr int kW = 4;                        // waves per workgroup
 constexpr int kBatchM = 8;                   // blocks per wave (one scale group)
 constexpr int kItemK = kW * kBatchM * kBlock;
 constexpr int kXPad = 8;                     // fp16 of padding per LDS row (spreads the banks)
-
-__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-
-// 8 codes of one dword (even elements in nibbles 0..3, odd in 4..7) -> 8 fp16 (q - 8), k order
-__device__ __forceinline__ half8 codes_to_half8(uint32_t d, uint32_t m64) {
-  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
-  const h2_t p0 = as_h2(((d << 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p1 = as_h2((d & 0x00F000F0u) | m64) + off;
-  const h2_t p2 = as_h2(((d >> 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p3 = as_h2(((d >> 8) & 0x00F000F0u) | m64) + off;
-  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
 
 template <int EPI>
 __device__ __forceinline__ int out_row(int tile, int n) {
@@ -132,12 +108,8 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_mfma(GemvParams p, const uint4
     for (int i = 0; i < kBatchM; ++i) {
       const u32x4 av = *reinterpret_cast<const u32x4*>(xa + i * kBlock);
       const half8 a = __builtin_bit_cast(half8, av);
-      uint32_t t0 = wv[i].x, t1 = wv[i].y, t2 = wv[i].z, t3 = wv[i].w;
-      swap32(t0, t2);
-      swap32(t1, t3);
-      swap16(t0, t1);
-      swap16(t2, t3);
-      const uint32_t tg[4] = {t0, t1, t2, t3};
+      uint32_t tg[4];
+      block_to_operands(wv[i], tg);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, codes_to_half8(tg[g], m64),

@@ -1,0 +1,374 @@
+// Prefill (decoder_init) of one sequence: the S prompt embeddings at positions 0..S-1 of an empty
+// cache -> the present K/V of those positions, written into the decode step's cache layout, and
+// the logits and greedy token of the last position ("vibevoice-asr-bitnet-onnx" page, graph
+// contracts: decoder_init runs the prompt, decoder_step then continues from its cache).  The
+// layer is the decode step's Qwen2 layer (1.5B STATUS page, Architecture) applied to S rows.
+//
+// Per layer: RMSNorm rows -> q|k|v GEMM (+bias) -> RoPE + K/V cache write -> causal attention ->
+// o GEMM (+residual) -> RMSNorm rows -> gate/up GEMM (SiLU * up) -> down GEMM (+residual); then
+// the final RMSNorm of the last row and the lm_head + argmax of the decode step.
+//
+// The GEMMs are int4-dequant contractions on the matrix cores over the decode step's tiled weights:
+// a workgroup owns one 64-row tile and 128 tokens (4 waves x 32); per 32-k block a wave loads the
+// tile's block once (1 KiB, lane = row), turns it into the four 16-row B operands with the
+// permlane transpose, and runs 2 x 4 v_mfma_f32_16x16x32_f16 against 32 tokens of activations
+// (A operands read from the fp16 activation rows); each block's result is scaled by its fp16
+// scale in fp32 (exact products, as in the decode GEMVs).  The attention is the decode step's
+// split-KV kernel with every token as its own "sequence" of length t + 1 over one shared cache,
+// which makes it causal by construction; it runs in chunks of tokens to bound its workspace.
+#include <algorithm>
+
+#include "vv_internal.h"
+#include "gemv_core.h"
+
+namespace vv {
+namespace {
+
+constexpr int kHD = 128;                     // head_dim
+constexpr int kPfWaves = 4;
+constexpr int kPfTokWave = 32;               // tokens per wave: two 16-token MFMA groups
+constexpr int kPfTokWg = kPfWaves * kPfTokWave;
+constexpr int kPfAttnChunk = 512;            // tokens per attention launch
+
+struct PfGemm {
+  const uint8_t* q; const uint16_t* s;       // tiled int4 weights, ntiles tiles of 64 rows
+  const uint16_t* x;                         // fp16 [S][K]
+  int S, K, N, ntiles;                       // N: output rows (EPI_SILU: rows of gate = of up)
+  const uint16_t* bias;                      // EPI_STORE: fp16 [N] or null
+  float* y; int ldy;                         // EPI_STORE: fp32 [S][ldy]
+  float* h;                                  // EPI_RESID: fp32 [S][N], h += W x
+  uint16_t* act;                             // EPI_SILU: fp16 [S][N]
+};
+
+template <int EPI>
+__global__ __launch_bounds__(64 * kPfWaves) void k_pf_gemm(PfGemm p) {
+  const int tile = blockIdx.x;
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int t0 = blockIdx.y * kPfTokWg + w * kPfTokWave;
+  const int K = p.K, nb = K / kBlock, ng = (nb + 7) / 8;
+  const u32x4* qt = reinterpret_cast<const u32x4*>(p.q) + (size_t)tile * nb * kTileRows + lane;
+  const u32x4* st = reinterpret_cast<const u32x4*>(p.s) + (size_t)tile * ng * kTileRows + lane;
+  // A operand rows: token t0 + 16 j + lane % 16 (clamped: tokens past S are computed, not stored),
+  // k-slice lane / 16 of each block
+  const uint16_t* xa[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    xa[j] = p.x + (size_t)min(t0 + 16 * j + (lane & 15), p.S - 1) * K + 8 * (lane >> 4);
+  const uint32_t m64 = vconst(0x54005400u);
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int grp = 0; grp < ng; ++grp) {
+    // the 8 scales of this lane's row, then those of rows 16 g + lane % 16 (the operand rows)
+    const u32x4 sv = st[(size_t)grp * kTileRows];
+    u32x4 s4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int src = 16 * g + (lane & 15);
+      s4[g] = u32x4{(uint32_t)__shfl((int)sv.x, src, kWave), (uint32_t)__shfl((int)sv.y, src, kWave),
+                    (uint32_t)__shfl((int)sv.z, src, kWave), (uint32_t)__shfl((int)sv.w, src, kWave)};
+    }
+    const int b0 = grp * 8;
+    u32x4 wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + i, nb - 1) * kTileRows);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = b0 + i;
+      if (b >= nb) break;                    // the last group of a K that is not a multiple of 256
+      half8 a[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) a[j] = *reinterpret_cast<const half8*>(xa[j] + (size_t)b * kBlock);
+      uint32_t tg[4];
+      block_to_operands(wv[i], tg);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const half8 bop = codes_to_half8(tg[g], m64);
+        const float sc = pick_scale(s4[g], i);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc[j][g] += sc * d;
+        }
+      }
+    }
+  }
+
+  // lane l holds tokens t0 + 16 j + 4 (l / 16) + r and tile row 16 g + l % 16
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * j + 4 * (lane >> 4) + r;
+      if (t >= p.S) continue;
+      if (EPI == EPI_SILU) {                 // rows 0..31 of the tile are gate rows, 32..63 the up rows
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int n = tile * 32 + 16 * g + (lane & 15);
+          if (n < p.N) p.act[(size_t)t * p.N + n] = f2h(silu(acc[j][g][r]) * acc[j][g + 2][r]);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = tile * kTileRows + 16 * g + (lane & 15);
+          if (n >= p.N) continue;
+          if (EPI == EPI_STORE) p.y[(size_t)t * p.ldy + n] = acc[j][g][r] + (p.bias ? h2f(p.bias[n]) : 0.f);
+          else p.h[(size_t)t * p.N + n] += acc[j][g][r];
+        }
+      }
+    }
+}
+
+// RMSNorm of row t: out = fp16(gamma * h * rstd), rstd = 1/sqrt(mean(h^2) + eps).  With emb set
+// the row is first taken from the fp16 input embeddings into h.  With outf set (the final norm of
+// the last row) the result is written in fp32 instead.
+__global__ __launch_bounds__(256) void k_pf_norm(const uint16_t* __restrict__ emb, float* __restrict__ h, int row0,
+                                                 int H, const uint16_t* __restrict__ gamma, float eps,
+                                                 uint16_t* __restrict__ out, float* __restrict__ outf) {
+  __shared__ float red[4];
+  const int t = row0 + blockIdx.x;
+  float* hr = h + (size_t)t * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    float v;
+    if (emb) {
+      v = h2f(emb[(size_t)t * H + i]);
+      hr[i] = v;
+    } else {
+      v = hr[i];
+    }
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float rstd = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const float v = h2f(gamma[i]) * hr[i] * rstd;
+    if (outf) outf[i] = v;
+    else out[(size_t)t * H + i] = f2h(v);
+  }
+}
+
+// RoPE of token t at position t (NeoX rotate-half pairs (j, j + 64), angles in fp64 as in the
+// decode step): q -> qr fp32 [S][nq][128]; k, v -> fp16 into the cache slot t; lens[t] = t + 1.
+__global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qkv, int nq, int nkv, int cap,
+                                                    double theta, float* __restrict__ qr, uint16_t* __restrict__ kc,
+                                                    uint16_t* __restrict__ vc, int32_t* __restrict__ lens) {
+  __shared__ float cs[64][2];
+  const int t = blockIdx.x;
+  const int ld = (nq + 2 * nkv) * kHD;
+  const float* row = qkv + (size_t)t * ld;
+  if (threadIdx.x < 64) {
+    float c = 1.f, s = 0.f;
+    if (theta > 0.0) {
+      const double inv = pow(theta, -(double)(2 * threadIdx.x) / (double)kHD);
+      double sd, cd;
+      sincos((double)t * inv, &sd, &cd);
+      c = (float)cd;
+      s = (float)sd;
+    }
+    cs[threadIdx.x][0] = c;
+    cs[threadIdx.x][1] = s;
+  }
+  if (threadIdx.x == 0) lens[t] = t + 1;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < (nq + nkv) * 64; idx += 256) {
+    const int hh = idx >> 6, j = idx & 63;
+    const float x1 = row[hh * kHD + j], x2 = row[hh * kHD + j + 64];
+    const float c = cs[j][0], s = cs[j][1];
+    const float r1 = x1 * c - x2 * s, r2 = x2 * c + x1 * s;
+    if (hh < nq) {
+      qr[((size_t)t * nq + hh) * kHD + j] = r1;
+      qr[((size_t)t * nq + hh) * kHD + j + 64] = r2;
+    } else {
+      uint16_t* dst = kc + ((size_t)(hh - nq) * cap + t) * kHD;
+      dst[j] = f2h(r1);
+      dst[j + 64] = f2h(r2);
+    }
+  }
+  for (int idx = threadIdx.x; idx < nkv * kHD; idx += 256) {
+    const int kvh = idx / kHD, d = idx % kHD;
+    vc[((size_t)kvh * cap + t) * kHD + d] = f2h(row[(nq + nkv) * kHD + idx]);
+  }
+}
+
+struct PfDims { int L, H, I, nq, nkv, V, S, cap, nqkv; };
+
+struct PfLayout { size_t h, x, act, qkv, qr, o, lens, gf, attn, lm, total; };
+
+AttnParams pf_attn_params(const PfDims& d) {
+  AttnParams a{};
+  a.B = std::min(d.S, kPfAttnChunk);
+  a.nq = d.nq; a.nkv = d.nkv; a.cap = d.cap;
+  attn_plan(a);
+  return a;
+}
+
+PfLayout pf_layout(const PfDims& d) {
+  PfLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
+  const size_t S = d.S;
+  l.h = take(S * d.H * 4);
+  l.x = take(S * d.H * 2);
+  l.act = take(S * d.I * 2);
+  l.qkv = take(S * d.nqkv * 4);
+  l.qr = take(S * d.nq * kHD * 4);
+  l.o = take(S * d.nq * kHD * 2);
+  l.lens = take(S * 4);
+  l.gf = take((size_t)d.H * 4);
+  const AttnParams a = pf_attn_params(d);
+  l.attn = take(attn_workspace_bytes(a.B, d.nq, d.nkv, a.nsplit));
+  l.lm = take(lm_workspace_bytes(1, d.V, d.H));
+  l.total = off;
+  return l;
+}
+
+PfDims pf_dims(const vv_model* m, int S, int cap) {
+  PfDims d;
+  d.L = m->n_layers; d.H = m->hidden; d.I = m->inter; d.nq = m->n_q; d.nkv = m->n_kv; d.V = m->vocab;
+  d.S = S; d.cap = cap;
+  d.nqkv = (m->n_q + 2 * m->n_kv) * kHD;
+  return d;
+}
+
+template <int EPI>
+hipError_t pf_gemm(const PfGemm& p, hipStream_t st) {
+  const dim3 grid(p.ntiles, (unsigned)cdiv(p.S, kPfTokWg)), block(64 * kPfWaves);
+  hipLaunchKernelGGL(k_pf_gemm<EPI>, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace vv
+
+using namespace vv;
+
+extern "C" {
+
+size_t vv_prefill_workspace(const vv_model* m, int S, int cap) {
+  if (!m || S < 1 || cap < S || m->hidden < 64 || m->inter < 64 || m->n_kv < 1 || m->n_q < 1 || m->n_q % m->n_kv)
+    return 0;
+  return pf_layout(pf_dims(m, S, cap)).total;
+}
+
+int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t* k_cache, uint16_t* v_cache, int cap,
+               float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  VV_REQUIRE(m && input_embeds && token, VV_ERR_NULL, "vv_prefill: model, input_embeds or token is NULL");
+  VV_REQUIRE(m->head_dim == kHD, VV_ERR_SHAPE, "vv_prefill: head_dim %d != 128", m->head_dim);
+  VV_REQUIRE(m->hidden >= 64 && m->hidden % 64 == 0 && m->hidden <= 4096, VV_ERR_SHAPE,
+             "vv_prefill: hidden %d must be a multiple of 64 in [64, 4096]", m->hidden);
+  VV_REQUIRE(m->inter >= 64 && m->inter % 64 == 0, VV_ERR_SHAPE, "vv_prefill: inter %d must be a multiple of 64",
+             m->inter);
+  VV_REQUIRE(m->n_q >= 1 && m->n_kv >= 1 && m->n_q % m->n_kv == 0 && m->n_q / m->n_kv <= 8, VV_ERR_SHAPE,
+             "vv_prefill: n_q %% n_kv must be 0 with n_q/n_kv <= 8");
+  VV_REQUIRE(m->n_layers >= 0 && m->n_layers <= 4096 && (m->n_layers == 0 || m->layers), VV_ERR_RANGE,
+             "vv_prefill: bad layer list");
+  VV_REQUIRE(m->gf && m->lm_head && m->vocab >= 1, VV_ERR_NULL, "vv_prefill: gf or lm_head is NULL");
+  VV_REQUIRE(S >= 1 && cap >= S && cap <= 131072, VV_ERR_RANGE, "vv_prefill: need 1 <= S <= cap <= 131072");
+  VV_REQUIRE(m->n_layers == 0 || (k_cache && v_cache), VV_ERR_NULL, "vv_prefill: KV cache is NULL");
+  VV_REQUIRE(((reinterpret_cast<uintptr_t>(input_embeds) | reinterpret_cast<uintptr_t>(k_cache) |
+               reinterpret_cast<uintptr_t>(v_cache)) & 15) == 0,
+             VV_ERR_RANGE, "vv_prefill: input_embeds and the caches must be 16-byte aligned");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const vv_layer& y = m->layers[l];
+    VV_REQUIRE(y.qkv_q && y.qkv_s && y.o_q && y.o_s && y.gu_q && y.gu_s && y.down_q && y.down_s && y.g1 && y.g2,
+               VV_ERR_NULL, "vv_prefill: layer %d has a NULL weight pointer", l);
+  }
+  const PfDims d = pf_dims(m, S, cap);
+  const PfLayout lay = pf_layout(d);
+  VV_REQUIRE(ws && ws_bytes >= lay.total, VV_ERR_WORKSPACE, "vv_prefill: workspace needs %zu bytes", lay.total);
+  VV_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255) == 0, VV_ERR_RANGE, "vv_prefill: workspace must be 256-byte aligned");
+
+  hipStream_t st = as_stream(stream);
+  char* w = static_cast<char*>(ws);
+  float* h = reinterpret_cast<float*>(w + lay.h);
+  uint16_t* x = reinterpret_cast<uint16_t*>(w + lay.x);
+  uint16_t* act = reinterpret_cast<uint16_t*>(w + lay.act);
+  float* qkv = reinterpret_cast<float*>(w + lay.qkv);
+  float* qr = reinterpret_cast<float*>(w + lay.qr);
+  uint16_t* o = reinterpret_cast<uint16_t*>(w + lay.o);
+  int32_t* lens = reinterpret_cast<int32_t*>(w + lay.lens);
+  float* gf = reinterpret_cast<float*>(w + lay.gf);
+  const size_t layer_kv = (size_t)d.nkv * cap * kHD;
+
+  if (d.L == 0) {
+    hipLaunchKernelGGL(k_pf_norm, dim3(1), dim3(256), 0, st, input_embeds, h, S - 1, d.H, m->gf, m->eps,
+                       (uint16_t*)nullptr, gf);
+    VV_HIP(hipGetLastError());
+  }
+  for (int l = 0; l < d.L; ++l) {
+    const vv_layer& y = m->layers[l];
+    // RMSNorm_1 (the first layer also takes the embeddings into the residual stream)
+    hipLaunchKernelGGL(k_pf_norm, dim3(S), dim3(256), 0, st, l == 0 ? input_embeds : nullptr, h, 0, d.H, y.g1,
+                       m->eps, x, (float*)nullptr);
+    VV_HIP(hipGetLastError());
+    {  // q|k|v (+bias)
+      PfGemm p{};
+      p.q = y.qkv_q; p.s = y.qkv_s; p.x = x; p.S = S; p.K = d.H; p.N = d.nqkv;
+      p.ntiles = (int)cdiv(d.nqkv, kTileRows);
+      p.bias = y.qkv_bias; p.y = qkv; p.ldy = d.nqkv;
+      VV_HIP(pf_gemm<EPI_STORE>(p, st));
+    }
+    uint16_t* kc = k_cache + (size_t)l * layer_kv;
+    uint16_t* vc = v_cache + (size_t)l * layer_kv;
+    hipLaunchKernelGGL(k_pf_rope_kv, dim3(S), dim3(256), 0, st, qkv, d.nq, d.nkv, cap, (double)m->rope_theta, qr,
+                       kc, vc, lens);
+    VV_HIP(hipGetLastError());
+    for (int c0 = 0; c0 < S; c0 += kPfAttnChunk) {   // causal attention: token t attends to 0..t
+      AttnParams a = pf_attn_params(d);
+      a.B = std::min(kPfAttnChunk, S - c0);
+      attn_set_workspace(a, w + lay.attn);
+      a.q = qr + (size_t)c0 * d.nq * kHD; a.q_f16 = 0;
+      a.lens = lens + c0;
+      a.kc = kc; a.vc = vc; a.kv_shared = 1;
+      a.scale = 1.0f / sqrtf((float)kHD);
+      a.out = o + (size_t)c0 * d.nq * kHD; a.out_f16 = 1;
+      VV_HIP(attn_launch(a, st));
+    }
+    {  // o (+residual)
+      PfGemm p{};
+      p.q = y.o_q; p.s = y.o_s; p.x = o; p.S = S; p.K = d.nq * kHD; p.N = d.H;
+      p.ntiles = d.H / kTileRows;
+      p.h = h;
+      VV_HIP(pf_gemm<EPI_RESID>(p, st));
+    }
+    hipLaunchKernelGGL(k_pf_norm, dim3(S), dim3(256), 0, st, (const uint16_t*)nullptr, h, 0, d.H, y.g2, m->eps, x,
+                       (float*)nullptr);
+    VV_HIP(hipGetLastError());
+    {  // gate/up (SiLU * up)
+      PfGemm p{};
+      p.q = y.gu_q; p.s = y.gu_s; p.x = x; p.S = S; p.K = d.H; p.N = d.I;
+      p.ntiles = 2 * d.I / kTileRows;
+      p.act = act;
+      VV_HIP(pf_gemm<EPI_SILU>(p, st));
+    }
+    {  // down (+residual)
+      PfGemm p{};
+      p.q = y.down_q; p.s = y.down_s; p.x = act; p.S = S; p.K = d.I; p.N = d.H;
+      p.ntiles = d.H / kTileRows;
+      p.h = h;
+      VV_HIP(pf_gemm<EPI_RESID>(p, st));
+    }
+  }
+  if (d.L > 0) {  // final RMSNorm of the last row, in fp32
+    hipLaunchKernelGGL(k_pf_norm, dim3(1), dim3(256), 0, st, (const uint16_t*)nullptr, h, S - 1, d.H, m->gf, m->eps,
+                       (uint16_t*)nullptr, gf);
+    VV_HIP(hipGetLastError());
+  }
+  LmParams lp{};
+  lp.W = m->lm_head; lp.V = d.V; lp.H = d.H; lp.B = 1;
+  lp.x = gf; lp.x_f16 = 0;
+  lp.logits = logits; lp.token = token;
+  lm_plan(lp);
+  lm_set_workspace(lp, w + lay.lm);
+  VV_HIP(lm_launch(lp, st));
+  return VV_OK;
+}
+
+}  // extern "C"

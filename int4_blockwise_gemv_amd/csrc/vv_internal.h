@@ -247,7 +247,8 @@ struct AttnParams {
   // stand-alone flavour
   const void* q; int q_f16;
   const int32_t* lens;
-  uint16_t* kc; uint16_t* vc;   // [B][nkv][cap][128]
+  uint16_t* kc; uint16_t* vc;   // [B][nkv][cap][128], or one [nkv][cap][128] cache for all B
+  int kv_shared;                // 1: every sequence b reads the same cache (prefill: b = token)
   float scale;
   void* out; int out_f16;       // [B][nq][128]
   float* part; float* part2; unsigned* cnt;

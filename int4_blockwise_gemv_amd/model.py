@@ -164,6 +164,20 @@ class DeviceState:
         self.k[idx].copy_(torch.from_numpy(K))
         self.v[idx].copy_(torch.from_numpy(V))
 
+    def prefill(self, embeds, stream=None):
+        """decoder_init of sequence 0 (batch-1 states): the prompt embeddings `embeds` (torch fp16
+        [S][H] on the device) fill cache positions 0..S-1 of every layer; the last position's
+        logits go to logits[0] and its greedy token to token[0].  The next decode step continues
+        at pos = S (set by the caller)."""
+        import torch
+        assert self.batch == 1, "prefill runs one sequence"
+        S = int(embeds.shape[0])
+        need = vv.prefill_workspace(self.model.struct, S, self.cap)
+        if getattr(self, "_pf_ws", None) is None or self._pf_ws.numel() < need:
+            self._pf_ws = torch.zeros(need, dtype=torch.uint8, device=self.emb.device)
+        vv.prefill(self.model.struct, embeds, S, self.k, self.v, self.cap, self.logits, self.token, self._pf_ws,
+                   stream)
+
     def step(self, stream=None):
         vv.decode_step(self.model.struct, self.struct, stream)
 

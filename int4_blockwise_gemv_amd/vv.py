@@ -73,6 +73,8 @@ _SIGS = {
     "vv_decode_graph_create": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P, C.POINTER(_P)]),
     "vv_decode_graph_launch": (_I, [_P, _P]),
     "vv_decode_graph_destroy": (_I, [_P]),
+    "vv_prefill_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
+    "vv_prefill": (_I, [C.POINTER(vv_model), _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "vv_workspace_init": (_I, [_P, _SZ, _P]),
     "vv_status_string": (C.c_char_p, [_I]),
     "vv_last_error": (C.c_char_p, []),
@@ -214,6 +216,15 @@ def decode_status(model: vv_model, state: vv_state, stream=None) -> int:
     out = C.c_int32(-1)
     _check(lib().vv_decode_status(C.byref(model), C.byref(state), C.byref(out), _stream(stream)), "vv_decode_status")
     return int(out.value)
+
+
+def prefill_workspace(model: vv_model, S: int, cap: int) -> int:
+    return lib().vv_prefill_workspace(C.byref(model), S, cap)
+
+
+def prefill(model: vv_model, input_embeds, S: int, k_cache, v_cache, cap: int, logits, token, ws, stream=None):
+    _check(lib().vv_prefill(C.byref(model), _ptr(input_embeds), S, _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits),
+                            _ptr(token), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "vv_prefill")
 
 
 class DecodeGraph:

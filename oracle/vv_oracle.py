@@ -373,7 +373,7 @@ def decode_step(m: OModel, input_embeds, pos, Kcaches, Vcaches, trace: Optional[
     return logits, tok, gap, h
 
 
-def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None):
+def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None, last_only: bool = False):
     """Independent full causal forward over T tokens (for the incremental == full check, and the
     decoder_init / prefill contract of the bitnet-onnx page's graph contracts).
 
@@ -382,7 +382,7 @@ def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None):
     keys/values are rounded to fp16 before use, as the decode step stores them.  With kv_out
     (a sequence of (K, V) fp16 arrays [nkv, cap, d], one pair per layer), the new keys/values
     are also stored at their positions there (the present K/V of the contract).
-    Returns logits [T, V] of every position.
+    Returns logits [T, V] of every position (with last_only, [1, V] of the last one).
     """
     x = np.asarray(embeds, dtype=np.float16).astype(np.float64)
     T, H = x.shape
@@ -418,7 +418,7 @@ def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None):
         x = x + gemv(*L.o, o.reshape(T, nq * d))
         mm = rmsnorm(x, L.g2, m.eps)
         x = x + gemv(*L.down, silu(gemv(*L.gate, mm)) * gemv(*L.up, mm))
-    f = rmsnorm(x, m.gf, m.eps)
+    f = rmsnorm(x[-1:] if last_only else x, m.gf, m.eps)
     return f @ np.asarray(m.lm, np.float64).T
 
 
@@ -427,7 +427,7 @@ def prefill(m: OModel, embeds, Kc, Vc):
     0..T-1 of an empty cache -> present K/V of those positions (written into Kc[l], Vc[l],
     fp16 [nkv, cap, d]) and the logits of the last position, which greedy decoding needs to
     pick the first generated token.  Returns (logits [V], token, top-2 gap)."""
-    logits = full_forward(m, embeds, kv_out=list(zip(Kc, Vc)))
+    logits = full_forward(m, embeds, kv_out=list(zip(Kc, Vc)), last_only=True)
     tok, gap = argmax_with_gap(logits[-1])
     return logits[-1], tok, gap
 
