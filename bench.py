@@ -16,6 +16,10 @@ Also reported:
                traffic: from committed rocprofv3 counters when they match the kernel source.
   cpu_baseline the fp64 oracle's decode step timed on a bounded sample of the same workload
                (one layer + a vocabulary slice, scaled to a full step).
+
+python bench.py --prefill S [--workload ...] times the prefill (decoder_init) of an S-token prompt
+of the workload's model instead and prints its own line (tokens/s; matrix TFLOP/s against the
+fp16 matrix-core peak).
 """
 from __future__ import annotations
 
@@ -159,6 +163,72 @@ def cpu_baseline(wl, seed, budget_s=25.0):
                       f"({t_layer:.2f} s/layer, {t_lm:.2f} s lm_head)"}
 
 
+def prefill_flops(shape, S):
+    """Matrix flops of one prefill: every projection over S tokens, causal attention (QK^T and P.V
+    over the S (S + 1) / 2 visible pairs), and the lm_head of the last position."""
+    proj = sum(2 * S * n * k for _, n, k in shape.proj_shapes()) * shape.layers
+    attn = 2 * 2 * shape.n_q * shape.head_dim * (S * (S + 1) // 2) * shape.layers
+    lm = 2 * shape.vocab * shape.hidden
+    return proj, attn, lm
+
+
+def prefill_bench(wl, args):
+    """Prefill of an S-token prompt of the workload's model (batch 1): K calls timed back to back
+    with events on the launch stream, inputs resident.  One JSON line."""
+    import torch
+    from int4_blockwise_gemv_amd import synth
+    from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
+    s, S = wl.shape, args.prefill
+    cap = max(S, wl.cap)
+    t0 = time.time()
+    dm = DeviceModel(s, args.seed, max_batch=1, progress=lambda m: None)
+    ds = DeviceState(dm, 1, cap)
+    emb = synth.fp16_normal(args.seed, synth.GLOBAL_LAYER, synth.T_X, (S, s.hidden))
+    x = torch.from_numpy(emb.view(np.int16)).cuda().view(torch.float16)
+    torch.cuda.synchronize()
+    log(f"packed {s.layers} layers + lm_head, prompt of {S} tokens resident ({time.time() - t0:.1f}s)")
+    steps = max(1, min(args.steps, 20))
+    warm = max(1, min(args.warmup, 3))
+    for _ in range(warm):
+        ds.prefill(x)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        ds.prefill(x)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    proj, attn, lm = prefill_flops(s, S)
+    tflops = (proj + attn + lm) / (ms * 1e-3) / 1e12
+    log(f"prefill of {S} tokens: {ms:.2f} ms ({S / ms * 1e3:.0f} tokens/s, {tflops:.0f} TFLOP/s), "
+        f"token {int(ds.token[0])}")
+    out = {
+        "metric": "prefill tokens/s (decoder_init of one prompt)",
+        "value": S / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate (matrix cores)",
+        "data": "synthetic (seeded N(0,0.02) fp32 masters ternarised on the GPU, fp16 N(0,1) prompt embeddings)",
+        "config": {"workload": f"prefill-{s.name}-s{S}", "layers": s.layers, "hidden": s.hidden, "inter": s.inter,
+                   "n_q": s.n_q, "n_kv": s.n_kv, "vocab": s.vocab, "batch": 1, "prompt": S, "quant": s.mode,
+                   "seed": args.seed},
+        "roofline": {"bound": "mfma", "kernel": "whole prefill (projection GEMMs carry "
+                     f"{100 * proj / (proj + attn + lm):.0f}% of the flops)",
+                     "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": None,
+                     "flops_per_prefill": proj + attn + lm},
+        "token": int(ds.token[0]),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +240,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "persistent", "layered"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="S",
+                    help="time the prefill (decoder_init) of an S-token prompt instead of the decode step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this decode step is not sharded across GPUs "
@@ -190,6 +262,8 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.prefill:
+        return prefill_bench(wl, args)
     from int4_blockwise_gemv_amd import vv
     dm, ds, lens = build_inputs(wl, args.seed, args.path)
     s = wl.shape
