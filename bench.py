@@ -44,11 +44,12 @@ def log(msg):
     sys.stderr.flush()
 
 
-def algorithmic_bytes(shape, batch, lens):
-    """Bytes one step must read: packed nibbles + fp16 scales + fp16 lm_head + fp16 K/V over P+1."""
+def algorithmic_bytes(shape, batch, lens, kv_bytes=2):
+    """Bytes one step must read: packed nibbles + fp16 scales + fp16 lm_head + K/V over P+1
+    (kv_bytes per element: 2 for fp16 caches, 4 for the fp32-KV variant)."""
     per_layer_w = sum(n * k // 2 + n * (k // 32) * 2 for _, n, k in shape.proj_shapes())
     w = per_layer_w * shape.layers
-    kv = sum(int(L) + 1 for L in lens) * shape.n_kv * shape.head_dim * 2 * 2 * shape.layers
+    kv = sum(int(L) + 1 for L in lens) * shape.n_kv * shape.head_dim * 2 * kv_bytes * shape.layers
     lm = shape.vocab * shape.hidden * 2
     return w, kv, lm
 
@@ -79,7 +80,7 @@ def read_traffic(kernel_tag, files):
         return None
 
 
-def build_inputs(wl, seed, path="auto"):
+def build_inputs(wl, seed, path="auto", kv="f16"):
     import torch
     from int4_blockwise_gemv_amd import synth
     from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
@@ -88,9 +89,11 @@ def build_inputs(wl, seed, path="auto"):
     t0 = time.time()
     dm = DeviceModel(s, seed, max_batch=wl.batch, progress=lambda m: None)
     log(f"packed {s.layers} layers + lm_head on the GPU in {time.time() - t0:.1f}s")
-    ds = DeviceState(dm, wl.batch, wl.cap, path=path)
+    ds = DeviceState(dm, wl.batch, wl.cap, path=path, kv=kv)
     for li in range(s.layers):
         K, V = synth.layer_cache(wl, seed, li, lens)
+        if kv == "f32":
+            K, V = K.astype(np.float32), V.astype(np.float32)
         ds.load_cache_layer(li, K, V)
     g = synth.model_globals(s, seed, wl.batch, with_lm=False)
     ds.emb.copy_(torch.from_numpy(g["emb"].view(np.int16)).view(torch.float16).cuda())
@@ -240,6 +243,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "persistent", "layered"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
+    ap.add_argument("--kv", default="f16", choices=["f16", "f32"],
+                    help="KV cache precision (f32: the fp32-KV variant, layered path)")
     ap.add_argument("--prefill", type=int, default=0, metavar="S",
                     help="time the prefill (decoder_init) of an S-token prompt instead of the decode step")
     args = ap.parse_args()
@@ -265,7 +270,7 @@ def main():
     if args.prefill:
         return prefill_bench(wl, args)
     from int4_blockwise_gemv_amd import vv
-    dm, ds, lens = build_inputs(wl, args.seed, args.path)
+    dm, ds, lens = build_inputs(wl, args.seed, args.path, args.kv)
     s = wl.shape
     persistent = args.path == "persistent"
 
@@ -287,7 +292,7 @@ def main():
     if status != 0:
         raise SystemExit("the persistent step reported an in-device wait that gave up")
 
-    wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens)
+    wb, kvb, lmb = algorithmic_bytes(s, wl.batch, lens, 4 if args.kv == "f32" else 2)
     total = wb + kvb + lmb
     tag = "7b" if s.hidden == 3584 else "1p5b"
     kb = kernel_breakdown(ds, s.layers, args.steps, persistent)
@@ -326,7 +331,7 @@ def main():
         "config": {"workload": wl.name, "layers": s.layers, "hidden": s.hidden, "inter": s.inter,
                    "n_q": s.n_q, "n_kv": s.n_kv, "head_dim": s.head_dim, "vocab": s.vocab, "batch": wl.batch,
                    "past": int(lens.max()), "quant": s.mode, "seed": args.seed,
-                   "path": "persistent" if persistent else "layered"},
+                   "path": "persistent" if persistent else "layered", "kv": args.kv},
         "hbm": {"algorithmic_bytes_per_step": total, "weights": wb, "kv": kvb, "lm_head": lmb,
                 "GB_per_s": total / (ms * 1e-3) / 1e9,
                 "frac_of_8TBps": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},

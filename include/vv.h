@@ -229,8 +229,9 @@ typedef struct vv_state {
   int cap;                         /* cache capacity in positions */
   const uint16_t* input_embeds;    /* device fp16 [B][H] */
   const int32_t* pos;              /* device int32 [B]; 0 <= pos[b] < cap (clamped on device) */
-  uint16_t* k_cache;               /* device fp16 [L][B][nkv][cap][head_dim] */
-  uint16_t* v_cache;
+  void* k_cache;                   /* device [L][B][nkv][cap][head_dim], fp16 (fp32 when
+                                      kv_dtype is VV_F32) */
+  void* v_cache;
   float* logits;                   /* device fp32 [B][V] or NULL */
   int32_t* token;                  /* device int32 [B] */
   float* h_trace;                  /* device fp32 [L+1][B][H] residual stream before each layer
@@ -265,6 +266,10 @@ typedef struct vv_state {
                                       caller zeroes it before the first step) */
   int32_t stop_ids[4];             /* stop tokens, n_stop of them */
   int n_stop;                      /* 0..4 */
+  /* KV precision: 0 or VV_F16 = fp16 caches; VV_F32 = fp32 caches (the fp32 KV + attention
+   * variant that the ASR-ONNX card reports as its accuracy fix: k, v are stored unrounded, at
+   * twice the cache bytes).  Layered path only. */
+  int kv_dtype;
 } vv_state;
 
 size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap);
@@ -287,8 +292,9 @@ int vv_decode_graph_destroy(vv_graph* g);
  * Prefill (bitnet-onnx page, graph contracts: decoder_init runs the prompt and returns logits and
  * the present K/V that decoder_step continues from), batch 1.
  *   input_embeds: device fp16 [S][H], the prompt's S embeddings at positions 0..S-1.
- *   k_cache/v_cache: device fp16 [L][1][nkv][cap][head_dim] (the vv_state layout with batch 1);
- *     positions 0..S-1 of every layer are written (fp16 k after RoPE, fp16 v), the rest untouched.
+ *   k_cache/v_cache: device [L][1][nkv][cap][head_dim] (the vv_state layout with batch 1), fp16
+ *     or, with kv_dtype VV_F32, fp32; positions 0..S-1 of every layer are written (k after RoPE,
+ *     v), the rest untouched.
  *     A decode step with pos = S then continues the sequence.
  *   logits: device fp32 [V] of the last position, or NULL; token: device int32 [1], its greedy
  *     argmax (smallest index on ties).
@@ -299,8 +305,8 @@ int vv_decode_graph_destroy(vv_graph* g);
  * cache.
  * ------------------------------------------------------------------------------------------- */
 size_t vv_prefill_workspace(const vv_model* m, int S, int cap);
-int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t* k_cache,
-               uint16_t* v_cache, int cap, float* logits, int32_t* token, void* ws,
+int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_cache,
+               void* v_cache, int cap, int kv_dtype, float* logits, int32_t* token, void* ws,
                size_t ws_bytes, void* stream);
 
 /* Zero-fills a workspace (one fill kernel, capture-safe) */

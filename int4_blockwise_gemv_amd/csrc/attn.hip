@@ -57,15 +57,45 @@ __device__ __forceinline__ Geo geo(const AttnParams& p, int S) {
   return g;
 }
 
+// K of one lane: 8 dims of one position, fp16 (one 16-byte load) or fp32 (two); V of one lane:
+// 2 dims of one position, fp16 (4 bytes) or fp32 (8 bytes)
+template <bool KV32> struct KvLane;
+template <> struct KvLane<false> { typedef u32x4 K; typedef uint32_t V; };
+template <> struct KvLane<true> { struct K { u32x4 a, b; }; typedef uint2 V; };
+
+// q . k over the lane's 8 dims, in dim order (fp16 k read exactly by v_fma_mix_f32)
+__device__ __forceinline__ float dot8_kv(const float* q, const u32x4& k, float c) { return dot8_mix(q, k, c); }
+__device__ __forceinline__ float dot8_kv(const float* q, const KvLane<true>::K& k, float c) {
+  const uint32_t d[8] = {k.a.x, k.a.y, k.a.z, k.a.w, k.b.x, k.b.y, k.b.z, k.b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = fmaf(q[i], __uint_as_float(d[i]), c);
+  return c;
+}
+// p * v for the lane's 2 dims
+__device__ __forceinline__ void pv_kv(float pj, uint32_t v, float& e, float& o) {
+  e = fma_mix_lo(pj, v, e);
+  o = fma_mix_hi(pj, v, o);
+}
+__device__ __forceinline__ void pv_kv(float pj, uint2 v, float& e, float& o) {
+  e = fmaf(pj, __uint_as_float(v.x), e);
+  o = fmaf(pj, __uint_as_float(v.y), o);
+}
+
 // NP passes of 4 positions per wave: split S = 4 waves * 4 * NP positions.  STEP: the decode-step
 // flavour (q/k/v from the projection output, RoPE, KV append); else the stand-alone flavour.
-template <int NP, bool STEP>
+// KV32: the cache holds fp32 K/V (the fp32-KV variant: twice the bytes, no fp16 rounding of k, v).
+template <int NP, bool STEP, bool KV32>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __restrict__ rope_cs) {
   constexpr int S = kWaves * 4 * NP;
+  constexpr int kEsz = KV32 ? 4 : 2;       // bytes per cache element
+  constexpr int kRow = kD * kEsz;          // bytes per cache row
+  typedef typename KvLane<KV32>::K KT;
+  typedef typename KvLane<KV32>::V VT;
   __shared__ __align__(16) float qs[kMaxG][kD];
   __shared__ __align__(16) float sc[kMaxG][S];
   __shared__ __align__(16) float red[kWaves][kMaxG][kD];      // [wave][head][dim]
-  __shared__ __align__(16) uint16_t knew[kD], vnew[kD];
+  __shared__ __align__(16) uint16_t knew[KV32 ? 8 : kD], vnew[KV32 ? 8 : kD];
+  __shared__ __align__(16) float knew32[KV32 ? kD : 4], vnew32[KV32 ? kD : 4];
   __shared__ float mh[kMaxG], lh[kMaxG];
 
   const int g = p.nq / p.nkv;
@@ -108,17 +138,30 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   // (one 256-byte row per load), so P.V needs no reduction across lanes.  Buffer loads over this
   // (sequence, KV head)'s cap rows: rows past the capacity read as zero instead of needing a clamp
   // per position, and the row offsets become immediates.
-  const int kvbytes = p.cap * kD * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kc + kvbase), (short)0, kvbytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.vc + kvbase), (short)0, kvbytes, kBufWord3);
+  const int kvbytes = p.cap * kRow;
+  char* kbase = reinterpret_cast<char*>(p.kc) + kvbase * kEsz;
+  char* vbase = reinterpret_cast<char*>(p.vc) + kvbase * kEsz;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(kbase, (short)0, kvbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(vbase, (short)0, kvbytes, kBufWord3);
   const int row0 = G.s0 + jw;              // first position of this wave
-  u32x4 kr[NP];
-  uint32_t vr[4 * NP];
+  KT kr[NP];
+  VT vr[4 * NP];
 #pragma unroll
-  for (int r = 0; r < NP; ++r)
-    kr[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (row0 + pg) * 256 + sl * 16 + r * 1024, 0, 0));
+  for (int r = 0; r < NP; ++r) {
+    const int off = (row0 + pg) * kRow + sl * 8 * kEsz + r * 4 * kRow;
+    if constexpr (KV32) {
+      kr[r].a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      kr[r].b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0));
+    } else {
+      kr[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+    }
+  }
 #pragma unroll
-  for (int i = 0; i < 4 * NP; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b32(vrs, row0 * 256 + lane * 4 + i * 256, 0, 0);
+  for (int i = 0; i < 4 * NP; ++i) {
+    const int off = row0 * kRow + lane * 2 * kEsz + i * kRow;
+    if constexpr (KV32) vr[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0));
+    else vr[i] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
+  }
 
   // ---- q (rotated) and the new k/v into LDS; the new position's cache slot ----------------------
   if (step) {
@@ -137,15 +180,29 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       *reinterpret_cast<float4*>(&qs[hh][4 * c16]) = make_float4(r1[0], r1[1], r1[2], r1[3]);
       *reinterpret_cast<float4*>(&qs[hh][64 + 4 * c16]) = make_float4(r2[0], r2[1], r2[2], r2[3]);
     } else if (G.has_new && tid < 16 * g + 32) {
-      uint16_t* dst = tid < 16 * g + 16 ? knew : vnew;
-      uint16_t* cache = (tid < 16 * g + 16 ? p.kc : p.vc) + kvbase + (size_t)G.P * kD;
+      const bool isk = tid < 16 * g + 16;
+      char* cb = (isk ? kbase : vbase) + (size_t)G.P * kRow;
+      if constexpr (KV32) {
+        float* dst = isk ? knew32 : vnew32;
+        float* cache = reinterpret_cast<float*>(cb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t a = f2h(r1[i]), bb = f2h(r2[i]);
-        dst[4 * c16 + i] = a;
-        dst[64 + 4 * c16 + i] = bb;
-        cache[4 * c16 + i] = a;
-        cache[64 + 4 * c16 + i] = bb;
+        for (int i = 0; i < 4; ++i) {
+          dst[4 * c16 + i] = r1[i];
+          dst[64 + 4 * c16 + i] = r2[i];
+          cache[4 * c16 + i] = r1[i];
+          cache[64 + 4 * c16 + i] = r2[i];
+        }
+      } else {
+        uint16_t* dst = isk ? knew : vnew;
+        uint16_t* cache = reinterpret_cast<uint16_t*>(cb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t a = f2h(r1[i]), bb = f2h(r2[i]);
+          dst[4 * c16 + i] = a;
+          dst[64 + 4 * c16 + i] = bb;
+          cache[4 * c16 + i] = a;
+          cache[64 + 4 * c16 + i] = bb;
+        }
       }
     }
   } else if (tid < 32 * g) {
@@ -155,16 +212,26 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   if (G.has_new) {  // the new position's row was loaded from the cache before it was written
 #pragma unroll
     for (int r = 0; r < NP; ++r)
-      if (G.s0 + jw + 4 * r + pg == G.P) kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
+      if (G.s0 + jw + 4 * r + pg == G.P) {
+        if constexpr (KV32) {
+          kr[r].a = *reinterpret_cast<const u32x4*>(&knew32[8 * sl]);
+          kr[r].b = *reinterpret_cast<const u32x4*>(&knew32[8 * sl + 4]);
+        } else {
+          kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
+        }
+      }
 #pragma unroll
     for (int i = 0; i < 4 * NP; ++i)
-      if (G.s0 + jw + i == G.P) vr[i] = *reinterpret_cast<const uint32_t*>(&vnew[2 * lane]);
+      if (G.s0 + jw + i == G.P) {
+        if constexpr (KV32) vr[i] = *reinterpret_cast<const uint2*>(&vnew32[2 * lane]);
+        else vr[i] = *reinterpret_cast<const uint32_t*>(&vnew[2 * lane]);
+      }
   }
   // rows past the sequence get probability 0; zero their V so that whatever the cache holds there
   // (it is never part of the attention) cannot turn 0 * v into a NaN
 #pragma unroll
   for (int i = 0; i < 4 * NP; ++i)
-    if (jw + i >= G.npos) vr[i] = 0u;
+    if (jw + i >= G.npos) vr[i] = VT{};
 
   // ---- scores: 16 lanes per position, reduced across the 16; two heads per pass (independent
   // chains hide the LDS and cross-lane latencies when a SIMD runs a single wave) -----------------
@@ -180,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
     }
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
-      const float s0 = row16_sum(dot8_mix(q0, kr[r], 0.f));
-      const float s1 = row16_sum(dot8_mix(q1, kr[r], 0.f));
+      const float s0 = row16_sum(dot8_kv(q0, kr[r], 0.f));
+      const float s1 = row16_sum(dot8_kv(q1, kr[r], 0.f));
       const int j = jw + 4 * r + pg;
       if (sl == 0) {
         sc[h0][j] = j < G.npos ? s0 * p.scale : -INFINITY;
@@ -222,11 +289,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       const float q0[4] = {a0.x, a0.y, a0.z, a0.w}, q1[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t v = vr[4 * r + u];
-        e0 = fma_mix_lo(q0[u], v, e0);
-        o0 = fma_mix_hi(q0[u], v, o0);
-        e1 = fma_mix_lo(q1[u], v, e1);
-        o1 = fma_mix_hi(q1[u], v, o1);
+        pv_kv(q0[u], vr[4 * r + u], e0, o0);
+        pv_kv(q1[u], vr[4 * r + u], e1, o1);
       }
     }
     *reinterpret_cast<float2*>(&red[w][h0][2 * lane]) = make_float2(e0, o0);
@@ -368,13 +432,15 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
   const int grid = p.B * p.nkv * p.nsplit;
   const KEv e1 = p.nsplit == 1 ? ev : ev.first();
   const bool step = p.qkv != nullptr;
+#define VV_ATTN_CASE(NP, KV32)                                                                      \
+  if (step) VV_LAUNCH((k_attn<NP, true, KV32>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);     \
+  else VV_LAUNCH((k_attn<NP, false, KV32>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
   if (p.split == 64) {
-    if (step) VV_LAUNCH((k_attn<4, true>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
-    else VV_LAUNCH((k_attn<4, false>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+    if (p.kv_f32) { VV_ATTN_CASE(4, true) } else { VV_ATTN_CASE(4, false) }
   } else {
-    if (step) VV_LAUNCH((k_attn<8, true>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
-    else VV_LAUNCH((k_attn<8, false>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+    if (p.kv_f32) { VV_ATTN_CASE(8, true) } else { VV_ATTN_CASE(8, false) }
   }
+#undef VV_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(merge_threads(p.nsplit)), st, ev.last(), p, p.split);

@@ -750,7 +750,8 @@ int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream
   p.L = d.L; p.B = d.B; p.H = d.H; p.I = d.I; p.nq = d.nq; p.nkv = d.nkv; p.g = d.g; p.cap = d.cap;
   p.nqkv = d.nqkv; p.ntH = d.ntH;
   p.eps = m->eps; p.inv_h = 1.0f / (float)d.H; p.scale = 1.0f / sqrtf((float)kD); p.theta = m->rope_theta;
-  p.emb = s->input_embeds; p.pos = s->pos; p.kc = s->k_cache; p.vc = s->v_cache;
+  p.emb = s->input_embeds; p.pos = s->pos;
+  p.kc = static_cast<uint16_t*>(s->k_cache); p.vc = static_cast<uint16_t*>(s->v_cache);
   p.kv_layer = (size_t)d.B * d.nkv * (size_t)d.cap * kD;
   p.gf = m->gf; p.trace = s->h_trace;
   p.ntq = d.ntq; p.ntg = d.ntg;

@@ -153,11 +153,18 @@ __global__ __launch_bounds__(256) void k_pf_norm(const uint16_t* __restrict__ em
   }
 }
 
+// element i of a cache, fp16 or fp32
+__device__ __forceinline__ void put_kv(void* c, size_t i, float v, bool kv32) {
+  if (kv32) static_cast<float*>(c)[i] = v;
+  else static_cast<uint16_t*>(c)[i] = f2h(v);
+}
+
 // RoPE of token t at position t (NeoX rotate-half pairs (j, j + 64), angles in fp64 as in the
-// decode step): q -> qr fp32 [S][nq][128]; k, v -> fp16 into the cache slot t; lens[t] = t + 1.
+// decode step): q -> qr fp32 [S][nq][128]; k, v -> fp16 (fp32 with kv32) into the cache slot t;
+// lens[t] = t + 1.
 __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qkv, int nq, int nkv, int cap,
-                                                    double theta, float* __restrict__ qr, uint16_t* __restrict__ kc,
-                                                    uint16_t* __restrict__ vc, int32_t* __restrict__ lens) {
+                                                    double theta, float* __restrict__ qr, void* __restrict__ kc,
+                                                    void* __restrict__ vc, int kv32, int32_t* __restrict__ lens) {
   __shared__ float cs[64][2];
   const int t = blockIdx.x;
   const int ld = (nq + 2 * nkv) * kHD;
@@ -185,14 +192,14 @@ __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qk
       qr[((size_t)t * nq + hh) * kHD + j] = r1;
       qr[((size_t)t * nq + hh) * kHD + j + 64] = r2;
     } else {
-      uint16_t* dst = kc + ((size_t)(hh - nq) * cap + t) * kHD;
-      dst[j] = f2h(r1);
-      dst[j + 64] = f2h(r2);
+      const size_t i0 = ((size_t)(hh - nq) * cap + t) * kHD;
+      put_kv(kc, i0 + j, r1, kv32);
+      put_kv(kc, i0 + j + 64, r2, kv32);
     }
   }
   for (int idx = threadIdx.x; idx < nkv * kHD; idx += 256) {
     const int kvh = idx / kHD, d = idx % kHD;
-    vc[((size_t)kvh * cap + t) * kHD + d] = f2h(row[(nq + nkv) * kHD + idx]);
+    put_kv(vc, ((size_t)kvh * cap + t) * kHD + d, row[(nq + nkv) * kHD + idx], kv32);
   }
 }
 
@@ -256,8 +263,8 @@ size_t vv_prefill_workspace(const vv_model* m, int S, int cap) {
   return pf_layout(pf_dims(m, S, cap)).total;
 }
 
-int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t* k_cache, uint16_t* v_cache, int cap,
-               float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_cache, void* v_cache, int cap,
+               int kv_dtype, float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   VV_REQUIRE(m && input_embeds && token, VV_ERR_NULL, "vv_prefill: model, input_embeds or token is NULL");
   VV_REQUIRE(m->head_dim == kHD, VV_ERR_SHAPE, "vv_prefill: head_dim %d != 128", m->head_dim);
@@ -271,6 +278,8 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t*
              "vv_prefill: bad layer list");
   VV_REQUIRE(m->gf && m->lm_head && m->vocab >= 1, VV_ERR_NULL, "vv_prefill: gf or lm_head is NULL");
   VV_REQUIRE(S >= 1 && cap >= S && cap <= 131072, VV_ERR_RANGE, "vv_prefill: need 1 <= S <= cap <= 131072");
+  VV_REQUIRE(kv_dtype == 0 || kv_dtype == VV_F16 || kv_dtype == VV_F32, VV_ERR_DTYPE,
+             "vv_prefill: kv_dtype %d is not VV_F16 or VV_F32", kv_dtype);
   VV_REQUIRE(m->n_layers == 0 || (k_cache && v_cache), VV_ERR_NULL, "vv_prefill: KV cache is NULL");
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(input_embeds) | reinterpret_cast<uintptr_t>(k_cache) |
                reinterpret_cast<uintptr_t>(v_cache)) & 15) == 0,
@@ -295,7 +304,8 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t*
   uint16_t* o = reinterpret_cast<uint16_t*>(w + lay.o);
   int32_t* lens = reinterpret_cast<int32_t*>(w + lay.lens);
   float* gf = reinterpret_cast<float*>(w + lay.gf);
-  const size_t layer_kv = (size_t)d.nkv * cap * kHD;
+  const bool kv32 = kv_dtype == VV_F32;
+  const size_t layer_kv_bytes = (size_t)d.nkv * cap * kHD * (kv32 ? 4 : 2);
 
   if (d.L == 0) {
     hipLaunchKernelGGL(k_pf_norm, dim3(1), dim3(256), 0, st, input_embeds, h, S - 1, d.H, m->gf, m->eps,
@@ -315,10 +325,10 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t*
       p.bias = y.qkv_bias; p.y = qkv; p.ldy = d.nqkv;
       VV_HIP(pf_gemm<EPI_STORE>(p, st));
     }
-    uint16_t* kc = k_cache + (size_t)l * layer_kv;
-    uint16_t* vc = v_cache + (size_t)l * layer_kv;
+    void* kc = static_cast<char*>(k_cache) + (size_t)l * layer_kv_bytes;
+    void* vc = static_cast<char*>(v_cache) + (size_t)l * layer_kv_bytes;
     hipLaunchKernelGGL(k_pf_rope_kv, dim3(S), dim3(256), 0, st, qkv, d.nq, d.nkv, cap, (double)m->rope_theta, qr,
-                       kc, vc, lens);
+                       kc, vc, (int)kv32, lens);
     VV_HIP(hipGetLastError());
     for (int c0 = 0; c0 < S; c0 += kPfAttnChunk) {   // causal attention: token t attends to 0..t
       AttnParams a = pf_attn_params(d);
@@ -326,7 +336,7 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, uint16_t*
       attn_set_workspace(a, w + lay.attn);
       a.q = qr + (size_t)c0 * d.nq * kHD; a.q_f16 = 0;
       a.lens = lens + c0;
-      a.kc = kc; a.vc = vc; a.kv_shared = 1;
+      a.kc = kc; a.vc = vc; a.kv_shared = 1; a.kv_f32 = kv32;
       a.scale = 1.0f / sqrtf((float)kHD);
       a.out = o + (size_t)c0 * d.nq * kHD; a.out_f16 = 1;
       VV_HIP(attn_launch(a, st));

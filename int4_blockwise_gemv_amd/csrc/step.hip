@@ -183,6 +183,10 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(s->path != VV_PATH_PERSISTENT || persistent_supported(m, s->batch), VV_ERR_UNSUPPORTED,
              "%s: the persistent path needs n_layers >= 1, batch 1, hidden <= 4096", fn);
   VV_REQUIRE(s->n_stop >= 0 && s->n_stop <= 4, VV_ERR_RANGE, "%s: n_stop %d not in 0..4", fn, s->n_stop);
+  VV_REQUIRE(s->kv_dtype == 0 || s->kv_dtype == VV_F16 || s->kv_dtype == VV_F32, VV_ERR_DTYPE,
+             "%s: kv_dtype %d is not VV_F16 or VV_F32", fn, s->kv_dtype);
+  VV_REQUIRE(s->kv_dtype != VV_F32 || !use_persistent(m, s), VV_ERR_UNSUPPORTED,
+             "%s: fp32 KV caches need the layered path", fn);
   VV_REQUIRE(!s->feedback_table || (reinterpret_cast<uintptr_t>(s->feedback_table) & 15) == 0, VV_ERR_RANGE,
              "%s: feedback_table must be 16-byte aligned", fn);
   const size_t need = step_bytes(m, s->batch, s->cap);
@@ -266,7 +270,8 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
             s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
   VV_HIP(hipGetLastError());
 
-  const size_t layer_kv = (size_t)B * d.nkv * (size_t)s->cap * kHeadDim;
+  const bool kv32 = s->kv_dtype == VV_F32;
+  const size_t layer_kv_bytes = (size_t)B * d.nkv * (size_t)s->cap * kHeadDim * (kv32 ? 4 : 2);
   for (int l = 0; l < d.L; ++l) {
     const vv_layer& y = m->layers[l];
     {  // fused q|k|v projection, RMSNorm_1 folded in, bias added
@@ -287,7 +292,9 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       attn_plan(a);
       attn_set_workspace(a, ws + lay.ws_attn);
       a.qkv = qkv; a.ldqkv = d.nqkv; a.pos = s->pos; a.rope_theta = m->rope_theta;
-      a.kc = s->k_cache + (size_t)l * layer_kv; a.vc = s->v_cache + (size_t)l * layer_kv;
+      a.kc = static_cast<char*>(s->k_cache) + (size_t)l * layer_kv_bytes;
+      a.vc = static_cast<char*>(s->v_cache) + (size_t)l * layer_kv_bytes;
+      a.kv_f32 = kv32;
       a.scale = 1.0f / sqrtf((float)kHeadDim);
       a.out = o; a.out_f16 = 1;
       VV_HIP(attn_launch_with_rope(a, rope, st, event_pair(s, op++)));

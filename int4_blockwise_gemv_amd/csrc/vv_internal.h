@@ -247,8 +247,10 @@ struct AttnParams {
   // stand-alone flavour
   const void* q; int q_f16;
   const int32_t* lens;
-  uint16_t* kc; uint16_t* vc;   // [B][nkv][cap][128], or one [nkv][cap][128] cache for all B
+  void* kc; void* vc;           // [B][nkv][cap][128] fp16 (fp32 with kv_f32), or one
+                                // [nkv][cap][128] cache for all B (kv_shared)
   int kv_shared;                // 1: every sequence b reads the same cache (prefill: b = token)
+  int kv_f32;                   // 1: the caches hold fp32
   float scale;
   void* out; int out_f16;       // [B][nq][128]
   float* part; float* part2; unsigned* cnt;

@@ -122,12 +122,13 @@ class DeviceState:
     """KV caches, inputs, outputs and workspace of one decode step."""
 
     def __init__(self, model: DeviceModel, batch: int, cap: int, device="cuda", trace: bool = False,
-                 logits: bool = True, path: str = "auto"):
+                 logits: bool = True, path: str = "auto", kv: str = "f16"):
         import torch
         s = model.shape
         self.model, self.batch, self.cap = model, batch, cap
         L = len(model.layers)
-        self.k = torch.zeros((max(1, L), batch, s.n_kv, cap, s.head_dim), dtype=torch.float16, device=device)
+        kv_dtype = {"f16": torch.float16, "f32": torch.float32}[kv]
+        self.k = torch.zeros((max(1, L), batch, s.n_kv, cap, s.head_dim), dtype=kv_dtype, device=device)
         self.v = torch.zeros_like(self.k)
         self.emb = torch.zeros((batch, s.hidden), dtype=torch.float16, device=device)
         self.pos = torch.zeros(batch, dtype=torch.int32, device=device)
@@ -140,6 +141,7 @@ class DeviceState:
                                   self.v.data_ptr(), self.logits.data_ptr() if logits else None,
                                   self.token.data_ptr(), self.trace.data_ptr() if trace else None,
                                   self.ws.data_ptr(), nbytes, None, 0, vv.PATH[path])
+        self.struct.kv_dtype = vv.VV_F32 if kv == "f32" else vv.VV_F16
 
     def enable_feedback(self, stop_ids=(151645, 151643), table=None):
         """Closed-loop greedy decoding: every step gathers the embedding of its argmax token from

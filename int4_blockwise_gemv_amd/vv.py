@@ -48,7 +48,7 @@ class vv_state(C.Structure):
                 ("h_trace", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int), ("path", C.c_int),
                 ("feedback_table", C.c_void_p), ("history", C.c_void_p), ("done", C.c_void_p),
-                ("stop_ids", C.c_int32 * 4), ("n_stop", C.c_int)]
+                ("stop_ids", C.c_int32 * 4), ("n_stop", C.c_int), ("kv_dtype", C.c_int)]
 
 
 _I64, _SZ, _P, _I, _F = C.c_int64, C.c_size_t, C.c_void_p, C.c_int, C.c_float
@@ -74,7 +74,7 @@ _SIGS = {
     "vv_decode_graph_launch": (_I, [_P, _P]),
     "vv_decode_graph_destroy": (_I, [_P]),
     "vv_prefill_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
-    "vv_prefill": (_I, [C.POINTER(vv_model), _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "vv_prefill": (_I, [C.POINTER(vv_model), _P, _I, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "vv_workspace_init": (_I, [_P, _SZ, _P]),
     "vv_status_string": (C.c_char_p, [_I]),
     "vv_last_error": (C.c_char_p, []),
@@ -223,8 +223,9 @@ def prefill_workspace(model: vv_model, S: int, cap: int) -> int:
 
 
 def prefill(model: vv_model, input_embeds, S: int, k_cache, v_cache, cap: int, logits, token, ws, stream=None):
-    _check(lib().vv_prefill(C.byref(model), _ptr(input_embeds), S, _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits),
-                            _ptr(token), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "vv_prefill")
+    _check(lib().vv_prefill(C.byref(model), _ptr(input_embeds), S, _ptr(k_cache), _ptr(v_cache), cap,
+                            _dtype_code(k_cache), _ptr(logits), _ptr(token), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "vv_prefill")
 
 
 class DecodeGraph:

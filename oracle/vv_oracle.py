@@ -339,8 +339,8 @@ def layer_step(L: OLayer, m: OModel, h, pos, Kc, Vc, trace: Optional[dict] = Non
     o = np.empty((B, nq, d), np.float64)
     for b in range(B):
         p = int(pos[b])
-        Kc[b, :, p] = k[b].astype(np.float16)
-        Vc[b, :, p] = v[b].astype(np.float16)
+        Kc[b, :, p] = k[b].astype(Kc.dtype)     # fp16 caches, or fp32 in the fp32-KV variant
+        Vc[b, :, p] = v[b].astype(Vc.dtype)
         o[b] = gqa_decode(q[b], Kc[b], Vc[b], p + 1, 1.0 / math.sqrt(d))
     h = h + gemv(*L.o, o.reshape(B, nq * d))
     mm = rmsnorm(h, L.g2, m.eps)
@@ -373,13 +373,15 @@ def decode_step(m: OModel, input_embeds, pos, Kcaches, Vcaches, trace: Optional[
     return logits, tok, gap, h
 
 
-def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None, last_only: bool = False):
+def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None, last_only: bool = False,
+                 kv_dtype=np.float16):
     """Independent full causal forward over T tokens (for the incremental == full check, and the
     decoder_init / prefill contract of the bitnet-onnx page's graph contracts).
 
     embeds [T, H] fp16 values; optional prefix caches K0/V0 [L, nkv, P0, d] fp16 that the
     T tokens attend to (positions 0..P0-1), new tokens at positions P0..P0+T-1.  The new
-    keys/values are rounded to fp16 before use, as the decode step stores them.  With kv_out
+    keys/values are rounded to kv_dtype (fp16, or fp32 for the fp32-KV variant of the ASR-ONNX
+    card) before use, as the decode step stores them.  With kv_out
     (a sequence of (K, V) fp16 arrays [nkv, cap, d], one pair per layer), the new keys/values
     are also stored at their positions there (the present K/V of the contract).
     Returns logits [T, V] of every position (with last_only, [1, V] of the last one).
@@ -395,12 +397,12 @@ def full_forward(m: OModel, embeds, K0=None, V0=None, kv_out=None, last_only: bo
         q = rope(gemv(*L.q, a, L.bq).reshape(T, nq, d), pos, m.rope_theta)
         k = rope(gemv(*L.k, a, L.bk).reshape(T, nkv, d), pos, m.rope_theta)
         v = gemv(*L.v, a, L.bv).reshape(T, nkv, d)
-        k = k.astype(np.float16).astype(np.float64)
-        v = v.astype(np.float16).astype(np.float64)
+        k = k.astype(kv_dtype).astype(np.float64)
+        v = v.astype(kv_dtype).astype(np.float64)
         if kv_out is not None:
             Kc, Vc = kv_out[li]
-            Kc[:, P0:P0 + T] = k.transpose(1, 0, 2).astype(np.float16)
-            Vc[:, P0:P0 + T] = v.transpose(1, 0, 2).astype(np.float16)
+            Kc[:, P0:P0 + T] = k.transpose(1, 0, 2).astype(kv_dtype)
+            Vc[:, P0:P0 + T] = v.transpose(1, 0, 2).astype(kv_dtype)
         if P0:
             kall = np.concatenate([np.asarray(K0[li], np.float64).transpose(1, 0, 2), k], axis=0)
             vall = np.concatenate([np.asarray(V0[li], np.float64).transpose(1, 0, 2), v], axis=0)
@@ -426,8 +428,10 @@ def prefill(m: OModel, embeds, Kc, Vc):
     """decoder_init (bitnet-onnx page, graph contracts): the T prompt embeddings at positions
     0..T-1 of an empty cache -> present K/V of those positions (written into Kc[l], Vc[l],
     fp16 [nkv, cap, d]) and the logits of the last position, which greedy decoding needs to
-    pick the first generated token.  Returns (logits [V], token, top-2 gap)."""
-    logits = full_forward(m, embeds, kv_out=list(zip(Kc, Vc)), last_only=True)
+    pick the first generated token.  The caches' dtype (fp16, or fp32 for the fp32-KV variant)
+    is the storage precision of k and v.  Returns (logits [V], token, top-2 gap)."""
+    kv_dtype = Kc[0].dtype if len(Kc) else np.float16
+    logits = full_forward(m, embeds, kv_out=list(zip(Kc, Vc)), last_only=True, kv_dtype=kv_dtype)
     tok, gap = argmax_with_gap(logits[-1])
     return logits[-1], tok, gap
 

@@ -22,12 +22,13 @@ def _prompt(shape, seed, S):
 
 
 class PrefillCase:
-    def __init__(self, shape, seed, layer_ids, S, cap):
+    def __init__(self, shape, seed, layer_ids, S, cap, kv="f16"):
         from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
         self.shape, self.seed, self.layer_ids, self.S, self.cap = shape, seed, list(layer_ids), S, cap
+        self.kv_np = np.float32 if kv == "f32" else np.float16
         self.glob = synth.model_globals(shape, seed, 1)
         self.dm = DeviceModel(shape, seed, self.layer_ids, max_batch=1, lm=self.glob["lm"], gf=self.glob["gf"])
-        self.ds = DeviceState(self.dm, 1, cap)
+        self.ds = DeviceState(self.dm, 1, cap, kv=kv)
         self.emb = _prompt(shape, seed, S)
 
     def run(self):
@@ -39,8 +40,8 @@ class PrefillCase:
     def oracle(self):
         m = oracle_model(self.shape, self.seed, self.layer_ids, glob=self.glob)
         s = self.shape
-        Kp = [np.zeros((s.n_kv, self.cap, s.head_dim), np.float16) for _ in self.layer_ids]
-        Vp = [np.zeros((s.n_kv, self.cap, s.head_dim), np.float16) for _ in self.layer_ids]
+        Kp = [np.zeros((s.n_kv, self.cap, s.head_dim), self.kv_np) for _ in self.layer_ids]
+        Vp = [np.zeros((s.n_kv, self.cap, s.head_dim), self.kv_np) for _ in self.layer_ids]
         logits, tok, gap = O.prefill(m, self.emb, Kp, Vp)
         return m, logits, tok, gap, Kp, Vp
 
@@ -119,12 +120,21 @@ def test_prefill_7b_width(cuda):
     _compare(case, case.oracle())
 
 
-def test_prefill_then_decode(cuda):
+@pytest.mark.parametrize("S", [17, 130])
+def test_prefill_tiny_fp32_kv(cuda, S):
+    """The fp32-KV variant: k and v written to fp32 caches unrounded."""
+    case = PrefillCase(TINY, 7, range(2), S, S + 8, kv="f32")
+    case.run()
+    _compare(case, case.oracle())
+
+
+@pytest.mark.parametrize("kv", ["f16", "f32"])
+def test_prefill_then_decode(cuda, kv):
     """decoder_init then decoder_step: decode steps at positions S, S+1, S+2 over the prefilled
     cache equal the oracle's decode steps over its own prefilled cache."""
     import torch
     S, cap = 40, 48
-    case = PrefillCase(TINY, 5, range(2), S, cap)
+    case = PrefillCase(TINY, 5, range(2), S, cap, kv=kv)
     case.run()
     m, _, _, _, Kp, Vp = case.oracle()
     Kc = [k[None].copy() for k in Kp]

@@ -17,7 +17,7 @@ class Case:
     """Seeded inputs of one decode step, on the GPU (packed by the library) and in the oracle."""
 
     def __init__(self, shape, seed, layer_ids, pos, cap, outlier_frac=0.0, trace=False, with_lm=True,
-                 path="auto"):
+                 path="auto", kv="f16"):
         import torch
         from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
         self.shape, self.seed, self.layer_ids = shape, seed, list(layer_ids)
@@ -28,10 +28,12 @@ class Case:
         self.dm = DeviceModel(shape, seed, self.layer_ids, with_lm=with_lm, max_batch=B, lm=self.glob.get("lm"),
                               gf=self.glob["gf"])
         self.path = path
-        self.ds = DeviceState(self.dm, B, cap, trace=trace, logits=with_lm, path=path)
+        self.ds = DeviceState(self.dm, B, cap, trace=trace, logits=with_lm, path=path, kv=kv)
         self.K, self.V = [], []
         for i, li in enumerate(self.layer_ids):
             K, V = synth.layer_cache(self.w, seed, li, self.pos)
+            if kv == "f32":   # the fp32-KV variant: the same past values, stored in fp32
+                K, V = K.astype(np.float32), V.astype(np.float32)
             self.K.append(K)
             self.V.append(V)
             self.ds.load_cache_layer(i, K, V)
@@ -95,6 +97,28 @@ def test_step_tiny(cuda, pos, path):
     case = Case(TINY, 0, range(2), pos, 130, path=path)
     case.run()
     _compare(case, case.oracle())
+
+
+@pytest.mark.parametrize("pos", [[0], [47], [64], [100], [33, 0, 90]])
+def test_step_tiny_fp32_kv(cuda, pos):
+    """The fp32-KV variant: fp32 caches, k and v appended unrounded."""
+    case = Case(TINY, 1, range(2), pos, 130, path="layered", kv="f32")
+    case.run()
+    _compare(case, case.oracle())
+
+
+def test_step_1p5b_width_fp32_kv(cuda):
+    """The fp32-KV variant at 1.5B width over 4096 past positions (two sampled layers)."""
+    case = Case(synth.QWEN2_1P5B, 0, [0, 27], [4096], 4097, path="layered", kv="f32")
+    case.run()
+    _compare(case, case.oracle())
+
+
+def test_step_persistent_rejects_fp32_kv(cuda):
+    from int4_blockwise_gemv_amd import vv
+    case = Case(TINY, 0, range(2), [5], 16, path="persistent", kv="f32")
+    with pytest.raises(vv.VVError):
+        case.ds.step()
 
 
 def test_step_tiny_batched_layered(cuda):

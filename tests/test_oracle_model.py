@@ -4,6 +4,7 @@ incremental-equals-full check the 1.5B STATUS page reports for its ONNX decoder)
 import math
 
 import numpy as np
+import pytest
 
 from oracle import vv_oracle as O
 from int4_blockwise_gemv_amd import synth
@@ -118,18 +119,20 @@ def test_zero_layers_reduce_to_lm_head_argmax():
     assert list(tok) == list(np.argmax(want, axis=1))
 
 
-def test_incremental_decode_equals_full_forward():
-    """T decode steps from a prefix cache == one full causal forward over the same tokens."""
+@pytest.mark.parametrize("kv_dtype", [np.float16, np.float32])
+def test_incremental_decode_equals_full_forward(kv_dtype):
+    """T decode steps from a prefix cache == one full causal forward over the same tokens, with
+    fp16 caches and with the fp32-KV variant."""
     shape = synth.TinyShape(layers=2, hidden=256, n_q=4, n_kv=2, head_dim=64, inter=384, vocab=500)
     m = oracle_model(shape, seed=0)
     T, P0, cap = 4, 3, 8
     L = shape.layers
-    K0 = synth.fp16_normal(0, 0, synth.T_KC, (L, shape.n_kv, P0, shape.head_dim))
-    V0 = synth.fp16_normal(0, 0, synth.T_VC, (L, shape.n_kv, P0, shape.head_dim))
+    K0 = synth.fp16_normal(0, 0, synth.T_KC, (L, shape.n_kv, P0, shape.head_dim)).astype(kv_dtype)
+    V0 = synth.fp16_normal(0, 0, synth.T_VC, (L, shape.n_kv, P0, shape.head_dim)).astype(kv_dtype)
     emb = synth.fp16_normal(9, 0, synth.T_EMB, (T, shape.hidden))
-    full = O.full_forward(m, emb, K0, V0)
-    Kc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
-    Vc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), np.float16) for _ in range(L)]
+    full = O.full_forward(m, emb, K0, V0, kv_dtype=kv_dtype)
+    Kc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), kv_dtype) for _ in range(L)]
+    Vc = [np.zeros((1, shape.n_kv, cap, shape.head_dim), kv_dtype) for _ in range(L)]
     for li in range(L):
         Kc[li][0, :, :P0] = K0[li]
         Vc[li][0, :, :P0] = V0[li]
@@ -163,6 +166,23 @@ def test_prefill_equals_token_by_token_decode():
         assert np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3)) <= 2 ** -10
         assert np.array_equal(Kp[li][:, T:], Kc[li][0][:, T:])   # untouched positions stay zero
         assert np.max(np.abs(Vp[li].astype(np.float64) - Vc[li][0].astype(np.float64))) <= 2 ** -10 * 8
+
+
+def test_fp32_kv_stores_unrounded_keys():
+    """The fp32-KV variant keeps k and v unrounded: its stored keys differ from the fp16 cache's by
+    the fp16 rounding only, and its attention output equals the fp16 cache's within that rounding."""
+    shape = synth.TinyShape(layers=1, hidden=256, n_q=4, n_kv=2, head_dim=64, inter=384, vocab=500)
+    m = oracle_model(shape, seed=2)
+    emb = synth.fp16_normal(5, 0, synth.T_EMB, (3, shape.hidden))
+    K16 = [np.zeros((shape.n_kv, 4, shape.head_dim), np.float16)]
+    V16 = [np.zeros((shape.n_kv, 4, shape.head_dim), np.float16)]
+    K32 = [np.zeros((shape.n_kv, 4, shape.head_dim), np.float32)]
+    V32 = [np.zeros((shape.n_kv, 4, shape.head_dim), np.float32)]
+    l16, _, _ = O.prefill(m, emb, K16, V16)
+    l32, _, _ = O.prefill(m, emb, K32, V32)
+    assert np.array_equal(K32[0].astype(np.float16), K16[0])      # fp16(fp32 value) is the fp16 store
+    assert not np.array_equal(K32[0], K16[0].astype(np.float32))  # and fp32 keeps more bits
+    assert np.allclose(l32, l16, rtol=0, atol=1e-2 * np.max(np.abs(l16)))
 
 
 def test_batched_step_equals_per_sequence_steps():
