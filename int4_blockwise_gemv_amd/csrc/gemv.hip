@@ -42,59 +42,6 @@ constexpr int kWavesLargeM = 4;   // for M > 2 (LDS holds M activation slices)
 // the small ones need the parallelism (7B shape: gate/up and down 8 waves, q|k|v and o 4).
 constexpr int kWideMinWgs = 512;
 constexpr int kBatch = 8;        // blocks per load batch (one scale group)
-constexpr uint64_t kFresh = 1ull << 32;     // tag of a filled hand-off slot (cleared slots are 0)
-constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up (seconds)
-
-// Sum of the n tagged fp32 values at p[k * stride], k in order, once every tag is set; then clears
-// the slots.  Polls kPollBatch slots at a time (every lane of the wave takes part in the vote):
-// 10 covers the 9 writers of the 7B down projection in one round trip and still fits in the
-// registers the weight stream needs (a batch of 16 costs the M <= 2 kernels two waves per SIMD).
-constexpr int kPollBatch = 10;
-__device__ float poll_sum(uint64_t* p, int n, size_t stride, int32_t* status) {
-  float s = 0.f;
-  for (int k0 = 0; k0 < n; k0 += kPollBatch) {
-    uint64_t v[kPollBatch];
-    for (uint32_t it = 0;; ++it) {
-      bool ok = true;
-#pragma unroll
-      for (int k = 0; k < kPollBatch; ++k) {
-        v[k] = collect_u64(p + (size_t)min(k0 + k, n - 1) * stride);
-        ok = ok && (v[k] >> 32) == 1u;
-      }
-      if (__all(ok)) break;
-      if (it >= kSpinLimit) {
-        if (status) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return __builtin_nanf("");
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-#pragma unroll
-    for (int k = 0; k < kPollBatch; ++k)
-      if (k0 + k < n) {
-        s += __uint_as_float((uint32_t)v[k]);
-        publish_u64(p + (size_t)(k0 + k) * stride, 0);
-      }
-  }
-  return s;
-}
-
-// Role of this workgroup in the split-K decomposition (see the top of the file): XCD x = wg % 8
-// takes tiles [x tpx, (x + 1) tpx) and runs, in dispatch order, their (wpt - 1) writers (tile-major)
-// and then their readers.  Returns false for padding workgroups.
-__device__ __forceinline__ bool split_role(int ntiles, int wpt, int& tile, int& kg) {
-  const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
-  const int tpx = (ntiles + kNumXcd - 1) / kNumXcd;
-  const int nwr = tpx * (wpt - 1);
-  if (i < nwr) {
-    tile = x * tpx + i / (wpt - 1);
-    kg = i % (wpt - 1);
-  } else {
-    tile = x * tpx + (i - nwr);
-    kg = wpt - 1;
-  }
-  return tile < ntiles && i < tpx * wpt;
-}
-
 // Operands of the epilogue.  Every wave loads them before its weight stream, from clamped
 // in-bounds addresses, so no load sits behind a branch: a conditional load whose result merges
 // with a default value makes the compiler wait for it (and for every load issued before it) on

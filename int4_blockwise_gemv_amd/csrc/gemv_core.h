@@ -47,6 +47,63 @@ __device__ __forceinline__ float pick_scale(const u32x4& s, int j) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---- split-K hand-off without atomics (the VALU GEMV) ---------------------------------------------
+// A writer stores its partial as a 64-bit (tag, fp32 bits) word into its slot and exits; the reader
+// polls the slots, adds them in a fixed order and clears them.
+constexpr uint64_t kFresh = 1ull << 32;     // tag of a filled hand-off slot (cleared slots are 0)
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up (seconds)
+
+// Sum of the n tagged fp32 values at p[k * stride], k in order, once every tag is set; then clears
+// the slots.  Polls kPollBatch slots at a time (every lane of the wave takes part in the vote):
+// 10 covers the 9 writers of the 7B down projection in one round trip and still fits in the
+// registers the weight stream needs (a batch of 16 costs the M <= 2 kernels two waves per SIMD).
+constexpr int kPollBatch = 10;
+__device__ __forceinline__ float poll_sum(uint64_t* p, int n, size_t stride, int32_t* status) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < n; k0 += kPollBatch) {
+    uint64_t v[kPollBatch];
+    for (uint32_t it = 0;; ++it) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < kPollBatch; ++k) {
+        v[k] = collect_u64(p + (size_t)min(k0 + k, n - 1) * stride);
+        ok = ok && (v[k] >> 32) == 1u;
+      }
+      if (__all(ok)) break;
+      if (it >= kSpinLimit) {
+        if (status) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_nanf("");
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int k = 0; k < kPollBatch; ++k)
+      if (k0 + k < n) {
+        s += __uint_as_float((uint32_t)v[k]);
+        publish_u64(p + (size_t)(k0 + k) * stride, 0);
+      }
+  }
+  return s;
+}
+
+// Role of this workgroup in a split-K decomposition of ntiles tiles into wpt K-chunks: XCD x =
+// wg % 8 takes tiles [x tpx, (x + 1) tpx) and runs, in dispatch order, their (wpt - 1) writers
+// (tile-major) and then their readers (kg = wpt - 1).  A reader waits only for writers dispatched
+// before it on its own XCD.  Needs a grid of 8 tpx wpt workgroups; returns false for padding.
+__device__ __forceinline__ bool split_role(int ntiles, int wpt, int& tile, int& kg) {
+  const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+  const int tpx = (ntiles + kNumXcd - 1) / kNumXcd;
+  const int nwr = tpx * (wpt - 1);
+  if (i < nwr) {
+    tile = x * tpx + i / (wpt - 1);
+    kg = i % (wpt - 1);
+  } else {
+    tile = x * tpx + (i - nwr);
+    kg = wpt - 1;
+  }
+  return tile < ntiles && i < tpx * wpt;
+}
+
 // ---- matrix-core operands (v_mfma_f32_16x16x32_f16) of the tiled layout --------------------------
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
