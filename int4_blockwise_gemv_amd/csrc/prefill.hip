@@ -203,6 +203,160 @@ __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qk
   }
 }
 
+// ---- causal attention of the prompt on the matrix cores (fp16 caches) -----------------------------
+// A workgroup takes one query head and 64 consecutive queries (4 waves x 16) and walks the keys
+// 0 .. (its last query) in blocks of 32 with an online softmax, all in fp32:
+//   S = Q K^T: A = q (16 queries x 32 dims, fp16 hi + lo parts of the scaled fp32 q, so the product
+//     keeps fp32 precision), B = K^T (32 dims x 16 keys, the fp16 cache: exact) -> 2 x 4 x 2
+//     v_mfma_f32_16x16x32_f16 per block; causal mask key > query;
+//   O += P V: A = P (16 queries x 32 keys, fp16 hi + lo of the fp32 probabilities, through LDS
+//     to change from the result layout to the operand layout), B = V (32 keys x 16 dims, staged
+//     transposed in LDS) -> 8 x 2 MFMAs per block.
+// The block's K rows and transposed V go through LDS once per workgroup; each wave skips the
+// blocks that lie entirely after its queries.
+constexpr int kFaQ = 64;                     // queries per workgroup
+constexpr int kFaK = 32;                     // keys per block
+constexpr int kFaKP = kFaK + 8;              // padded LDS rows
+constexpr int kFaDP = kHD + 8;
+
+__device__ __forceinline__ void split_hi_lo(const float* v, half8& hi, half8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 h = (_Float16)v[i];
+    hi[i] = h;
+    lo[i] = (_Float16)(v[i] - (float)h);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pf_flash(const float* __restrict__ qr, const uint16_t* __restrict__ kc,
+                                                  const uint16_t* __restrict__ vc, int S, int nq, int nkv, int cap,
+                                                  float scale, uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t Ks[kFaK][kFaDP];          // [key][dim]
+  __shared__ __align__(16) uint16_t Vt[kHD][kFaKP];           // [dim][key]
+  __shared__ __align__(16) uint16_t Ps[4][2][16][kFaKP];      // [wave][hi, lo][query][key]
+  const int h = blockIdx.y, kvh = h / (nq / nkv);
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int qb = blockIdx.x * kFaQ, q0 = qb + 16 * w;
+  const uint16_t* kbase = kc + (size_t)kvh * cap * kHD;
+  const uint16_t* vbase = vc + (size_t)kvh * cap * kHD;
+
+  // A operands of q: query q0 + lane % 16, dims 32 ks + 8 (lane / 16) .. + 7, scaled, hi + lo
+  half8 qh[4], ql[4];
+  {
+    const float* qrow = qr + ((size_t)min(q0 + (lane & 15), S - 1) * nq + h) * kHD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * ks);
+      const float4 b = *reinterpret_cast<const float4*>(qrow + 32 * ks + 4);
+      const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                          b.x * scale, b.y * scale, b.z * scale, b.w * scale};
+      split_hi_lo(v, qh[ks], ql[ks]);
+    }
+  }
+  float m_i[4], l_i[4];
+  f32x4 O[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_i[r] = -INFINITY; l_i[r] = 0.f; }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kend = min(S, qb + kFaQ);        // keys the workgroup's last query sees
+  // staging: thread t takes key row t / 8, dims 16 (t % 8) .. + 15 of K and of V
+  const int sr = tid >> 3, sd = (tid & 7) * 16;
+  for (int kb = 0; kb < kend; kb += kFaK) {
+    {
+      const size_t row = (size_t)min(kb + sr, S - 1) * kHD + sd;
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kbase + row);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kbase + row + 8);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(vbase + row);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(vbase + row + 8);
+      __syncthreads();                       // the previous block's operands are consumed
+      *reinterpret_cast<u32x4*>(&Ks[sr][sd]) = k0;
+      *reinterpret_cast<u32x4*>(&Ks[sr][sd + 8]) = k1;
+      const uint32_t vd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        Vt[sd + 2 * i][sr] = (uint16_t)(vd[i] & 0xffffu);
+        Vt[sd + 2 * i + 1][sr] = (uint16_t)(vd[i] >> 16);
+      }
+      __syncthreads();
+    }
+    if (kb > q0 + 15) continue;              // every query of this wave is before the block
+
+    // scores of queries 4 (lane / 16) + r against keys kb + 16 nb + lane % 16
+    f32x4 sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const half8 b = *reinterpret_cast<const half8*>(&Ks[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], b, acc, 0, 0, 0);
+      }
+      sc[nb] = acc;
+    }
+    // causal mask, online softmax (each row lives in the 16 lanes of one lane group)
+    float p[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + 4 * (lane >> 4) + r;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int key = kb + 16 * nb + (lane & 15);
+        const float v = (key <= q && key < S) ? sc[nb][r] : -INFINITY;
+        sc[nb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = row16_max(mx);
+      const float m_new = fmaxf(m_i[r], mx);  // finite: key 0 is in the first block of every row
+      const float alpha = expf(m_i[r] - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        p[nb][r] = expf(sc[nb][r] - m_new);
+        rs += p[nb][r];
+      }
+      rs = row16_sum(rs);
+      l_i[r] = l_i[r] * alpha + rs;
+      m_i[r] = m_new;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) O[n][r] *= alpha;
+    }
+    // P (result layout) -> LDS -> A operand layout (query lane % 16, keys 8 (lane / 16) .. + 7)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const _Float16 hi = (_Float16)p[nb][r];
+        const _Float16 lo = (_Float16)(p[nb][r] - (float)hi);
+        Ps[w][0][4 * (lane >> 4) + r][16 * nb + (lane & 15)] = __builtin_bit_cast(uint16_t, hi);
+        Ps[w][1][4 * (lane >> 4) + r][16 * nb + (lane & 15)] = __builtin_bit_cast(uint16_t, lo);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const half8 ph = *reinterpret_cast<const half8*>(&Ps[w][0][lane & 15][8 * (lane >> 4)]);
+    const half8 pl = *reinterpret_cast<const half8*>(&Ps[w][1][lane & 15][8 * (lane >> 4)]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const half8 b = *reinterpret_cast<const half8*>(&Vt[16 * n + (lane & 15)][8 * (lane >> 4)]);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, b, O[n], 0, 0, 0);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, b, O[n], 0, 0, 0);
+    }
+  }
+  // O / l -> out[query][h][dims 16 n + lane % 16] (fp16)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = q0 + 4 * (lane >> 4) + r;
+    if (q >= S) continue;
+    const float inv = 1.0f / l_i[r];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) out[((size_t)q * nq + h) * kHD + 16 * n + (lane & 15)] = f2h(O[n][r] * inv);
+  }
+}
+
 struct PfDims { int L, H, I, nq, nkv, V, S, cap, nqkv; };
 
 struct PfLayout { size_t h, x, act, qkv, qr, o, lens, gf, attn, lm, total; };
@@ -330,7 +484,13 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_c
     hipLaunchKernelGGL(k_pf_rope_kv, dim3(S), dim3(256), 0, st, qkv, d.nq, d.nkv, cap, (double)m->rope_theta, qr,
                        kc, vc, (int)kv32, lens);
     VV_HIP(hipGetLastError());
-    for (int c0 = 0; c0 < S; c0 += kPfAttnChunk) {   // causal attention: token t attends to 0..t
+    if (!kv32) {   // causal attention on the matrix cores: token t attends to 0..t
+      hipLaunchKernelGGL(k_pf_flash, dim3((unsigned)cdiv(S, kFaQ), d.nq), dim3(256), 0, st, qr,
+                         static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), S, d.nq, d.nkv, cap,
+                         1.0f / sqrtf((float)kHD), o);
+      VV_HIP(hipGetLastError());
+    }
+    for (int c0 = 0; kv32 && c0 < S; c0 += kPfAttnChunk) {   // fp32 caches: the split-KV kernel
       AttnParams a = pf_attn_params(d);
       a.B = std::min(kPfAttnChunk, S - c0);
       attn_set_workspace(a, w + lay.attn);
