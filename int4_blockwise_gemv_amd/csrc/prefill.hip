@@ -25,9 +25,9 @@ namespace vv {
 namespace {
 
 constexpr int kHD = 128;                     // head_dim
-constexpr int kPfWaves = 4;
-constexpr int kPfTokWave = 32;               // tokens per wave: two 16-token MFMA groups
-constexpr int kPfTokWg = kPfWaves * kPfTokWave;
+constexpr int kPfWaves = 8;                  // GEMM: tiles per workgroup, one per wave
+constexpr int kPfTok = 64;                   // GEMM: tokens per workgroup, four 16-token MFMA groups
+constexpr int kPfStage = kPfTok * 256 * 2;   // GEMM: activation bytes of one group of 8 blocks
 constexpr int kPfAttnChunk = 512;            // tokens per attention launch
 
 struct PfGemm {
@@ -40,30 +40,84 @@ struct PfGemm {
   uint16_t* act;                             // EPI_SILU: fp16 [S][N]
 };
 
+// 8 codes of one dword -> 8 fp16 (q - 8) * s, k order (the magic-exponent form of the decode GEMVs,
+// then one packed multiply by the block scale s2 = (s, s)): exact for ternary codes (q - 8 in
+// {-1, 0, 1}); for general int4 codes the product rounds once to fp16 (relative error <= 2^-11).
+__device__ __forceinline__ half8 codes_to_half8_scaled(uint32_t d, uint32_t m64, h2_t s2) {
+  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
+  const h2_t p0 = (as_h2(((d << 4) & 0x00F000F0u) | m64) + off) * s2;
+  const h2_t p1 = (as_h2((d & 0x00F000F0u) | m64) + off) * s2;
+  const h2_t p2 = (as_h2(((d >> 4) & 0x00F000F0u) | m64) + off) * s2;
+  const h2_t p3 = (as_h2(((d >> 8) & 0x00F000F0u) | m64) + off) * s2;
+  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// (s, s) for the fp16 scale of block i (0..7) out of a lane's 4 scale dwords
+__device__ __forceinline__ h2_t scale_pair(const u32x4& s, int i) {
+  const uint32_t d = (i >> 1) == 0 ? s.x : (i >> 1) == 1 ? s.y : (i >> 1) == 2 ? s.z : s.w;
+  return as_h2(__builtin_amdgcn_perm(d, d, (i & 1) ? 0x03020302u : 0x01000100u));
+}
+
 template <int EPI>
 __global__ __launch_bounds__(64 * kPfWaves) void k_pf_gemm(PfGemm p) {
-  const int tile = blockIdx.x;
+  __shared__ __align__(16) uint8_t As[2][kPfStage];
+  // workgroup -> (tile group, token block): XCD x takes tile groups x, x + 8, ... and runs every
+  // token block of one tile group back to back, so its tiles' weights come from HBM once and
+  // from the XCD's L2 after that
+  const int ntb = (p.S + kPfTok - 1) / kPfTok, ntg = (p.ntiles + kPfWaves - 1) / kPfWaves;
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  const int tb = seq % ntb, tgrp = 8 * (seq / ntb) + xcd;
+  if (tgrp >= ntg) return;                   // padding of the grid to whole rounds of 8
   const int w = wave_id(), lane = threadIdx.x & 63;
-  const int t0 = blockIdx.y * kPfTokWg + w * kPfTokWave;
+  const int tile_u = tgrp * kPfWaves + w;
+  const int tile = min(tile_u, p.ntiles - 1); // a wave past the last tile recomputes it, stores nothing
+  const int t0 = tb * kPfTok;
   const int K = p.K, nb = K / kBlock, ng = (nb + 7) / 8;
   const u32x4* qt = reinterpret_cast<const u32x4*>(p.q) + (size_t)tile * nb * kTileRows + lane;
   const u32x4* st = reinterpret_cast<const u32x4*>(p.s) + (size_t)tile * ng * kTileRows + lane;
-  // A operand rows: token t0 + 16 j + lane % 16 (clamped: tokens past S are computed, not stored),
-  // k-slice lane / 16 of each block
-  const uint16_t* xa[2];
+  // A staging, operand order: 1 KiB chunk 4 i + j of a stage holds block i (of 8) of token group j
+  // (16 tokens), lane l's 16 B = token 16 j + l % 16, k 32 i + 8 (l / 16) .. + 7.  Wave w fills
+  // chunks 8 u + w (u = 0..3): block 2 u + w / 4, token group w % 4.  Token rows past S are
+  // clamped (computed, not stored); blocks past K are clamped (their MFMAs are skipped).
+  const uint16_t* xs = p.x + (size_t)min(t0 + 16 * (w & 3) + (lane & 15), p.S - 1) * K + 8 * (lane >> 4);
+  auto load_stage = [&](int grp, u32x4 (&r)[4]) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    xa[j] = p.x + (size_t)min(t0 + 16 * j + (lane & 15), p.S - 1) * K + 8 * (lane >> 4);
+    for (int u = 0; u < 4; ++u) {
+      const int blk = min(grp * 8 + 2 * u + (w >> 2), nb - 1);
+      r[u] = *reinterpret_cast<const u32x4*>(xs + (size_t)blk * kBlock);
+    }
+  };
+  auto store_stage = [&](int buf, const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(&As[buf][(8 * u + w) * 1024 + lane * 16]) = r[u];
+  };
+  // a group's weights: 8 blocks of the tile (lane = row) and the 8 scales of the lane's row
+  auto load_w = [&](int grp, u32x4 (&wv)[8], u32x4& sv) {
+    sv = st[(size_t)grp * kTileRows];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = qt[(size_t)min(grp * 8 + i, nb - 1) * kTileRows];
+  };
+
   const uint32_t m64 = vconst(0x54005400u);
-  f32x4 acc[2][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  u32x4 ar[4], wv[8], sv;
+  load_stage(0, ar);
+  load_w(0, wv, sv);
+  store_stage(0, ar);
+  __syncthreads();
   for (int grp = 0; grp < ng; ++grp) {
-    // the 8 scales of this lane's row, then those of rows 16 g + lane % 16 (the operand rows)
-    const u32x4 sv = st[(size_t)grp * kTileRows];
+    const int cur = grp & 1, nxt = min(grp + 1, ng - 1);
+    // the next group's operands are in flight while this group computes (the last group reloads
+    // its own, unused, so that no load sits under a branch)
+    u32x4 wn[8], sn;
+    load_stage(nxt, ar);
+    load_w(nxt, wn, sn);
+    // the scales of the operand rows 16 g + lane % 16
     u32x4 s4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -71,35 +125,34 @@ __global__ __launch_bounds__(64 * kPfWaves) void k_pf_gemm(PfGemm p) {
       s4[g] = u32x4{(uint32_t)__shfl((int)sv.x, src, kWave), (uint32_t)__shfl((int)sv.y, src, kWave),
                     (uint32_t)__shfl((int)sv.z, src, kWave), (uint32_t)__shfl((int)sv.w, src, kWave)};
     }
-    const int b0 = grp * 8;
-    u32x4 wv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + i, nb - 1) * kTileRows);
+    const uint8_t* as = As[cur] + lane * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int b = b0 + i;
-      if (b >= nb) break;                    // the last group of a K that is not a multiple of 256
-      half8 a[2];
+      if (grp * 8 + i >= nb) break;          // the last group of a K that is not a multiple of 256
+      half8 a[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) a[j] = *reinterpret_cast<const half8*>(xa[j] + (size_t)b * kBlock);
-      uint32_t tg[4];
-      block_to_operands(wv[i], tg);
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const half8*>(as + (4 * i + j) * 1024);
+      uint32_t tq[4];
+      block_to_operands(wv[i], tq);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const half8 bop = codes_to_half8(tg[g], m64);
-        const float sc = pick_scale(s4[g], i);
+        const half8 bop = codes_to_half8_scaled(tq[g], m64, scale_pair(s4[g], i));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          acc[j][g] += sc * d;
-        }
+        for (int j = 0; j < 4; ++j) acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, acc[j][g], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = wn[i];
+    sv = sn;
+    // every wave finished reading stage buffer cur ^ 1 before the previous barrier
+    store_stage(cur ^ 1, ar);
+    __syncthreads();
   }
+  if (tile_u >= p.ntiles) return;
 
   // lane l holds tokens t0 + 16 j + 4 (l / 16) + r and tile row 16 g + l % 16
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 16 * j + 4 * (lane >> 4) + r;
@@ -399,7 +452,8 @@ PfDims pf_dims(const vv_model* m, int S, int cap) {
 
 template <int EPI>
 hipError_t pf_gemm(const PfGemm& p, hipStream_t st) {
-  const dim3 grid(p.ntiles, (unsigned)cdiv(p.S, kPfTokWg)), block(64 * kPfWaves);
+  const int ntg = cdiv(p.ntiles, kPfWaves);
+  const dim3 grid((unsigned)(8 * cdiv(ntg, 8) * cdiv(p.S, kPfTok))), block(64 * kPfWaves);
   hipLaunchKernelGGL(k_pf_gemm<EPI>, grid, block, 0, st, p);
   return hipGetLastError();
 }
