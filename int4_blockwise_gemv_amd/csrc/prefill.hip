@@ -257,16 +257,21 @@ __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qk
 }
 
 // ---- causal attention of the prompt on the matrix cores (fp16 caches) -----------------------------
-// A workgroup takes one query head and 64 consecutive queries (4 waves x 16) and walks the keys
-// 0 .. (its last query) in blocks of 32 with an online softmax, all in fp32:
-//   S = Q K^T: A = q (16 queries x 32 dims, fp16 hi + lo parts of the scaled fp32 q, so the product
-//     keeps fp32 precision), B = K^T (32 dims x 16 keys, the fp16 cache: exact) -> 2 x 4 x 2
-//     v_mfma_f32_16x16x32_f16 per block; causal mask key > query;
-//   O += P V: A = P (16 queries x 32 keys, fp16 hi + lo of the fp32 probabilities, through LDS
-//     to change from the result layout to the operand layout), B = V (32 keys x 16 dims, staged
-//     transposed in LDS) -> 8 x 2 MFMAs per block.
-// The block's K rows and transposed V go through LDS once per workgroup; each wave skips the
-// blocks that lie entirely after its queries.
+// A workgroup takes one query head and a block of 64 consecutive queries (4 waves x 16) and walks the keys
+// 0 .. (its last query) in blocks of 32 with an online softmax in base 2 (q carries log2 e), fp32.
+// The products are taken transposed so that every lane owns one query:
+//   S^T = K Q^T: A = K (16 keys x 32 dims, the fp16 cache: exact), B = Q^T (the fp16 hi + lo parts
+//     of the scaled fp32 q, so the product keeps fp32 precision) -> lane l holds query l % 16 and
+//     keys 16 nb + 4 (l / 16) + r of the block;
+//   O^T += V^T P^T: B = P^T straight from those registers (fp16 hi + lo of the fp32 weights); the
+//     k order of this product is the lane groups' key order, so V is staged transposed with its
+//     keys permuted to match (lane group g's 8 keys contiguous) -> lane l holds query l % 16 and
+//     dims 16 n + 4 (l / 16) + r.
+// The max, the rescale factor and the running sum are then per lane; the max is exchanged across
+// the 4 lane groups with two lane shuffles.  K and V blocks are staged in double-buffered LDS,
+// one barrier per block, the next block's loads in flight during the current one; a wave skips
+// the blocks that lie entirely after its queries.  A workgroup takes two query blocks, the
+// (nqb - 1 - x)-th and the x-th, so that every workgroup walks about the same number of keys.
 constexpr int kFaQ = 64;                     // queries per workgroup
 constexpr int kFaK = 32;                     // keys per block
 constexpr int kFaKP = kFaK + 8;              // padded LDS rows
@@ -281,132 +286,150 @@ __device__ __forceinline__ void split_hi_lo(const float* v, half8& hi, half8& lo
   }
 }
 
-__global__ __launch_bounds__(256) void k_pf_flash(const float* __restrict__ qr, const uint16_t* __restrict__ kc,
-                                                  const uint16_t* __restrict__ vc, int S, int nq, int nkv, int cap,
-                                                  float scale, uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint16_t Ks[kFaK][kFaDP];          // [key][dim]
-  __shared__ __align__(16) uint16_t Vt[kHD][kFaKP];           // [dim][key]
-  __shared__ __align__(16) uint16_t Ps[4][2][16][kFaKP];      // [wave][hi, lo][query][key]
+// max and sum over the 4 lane groups (lanes l % 16 equal)
+__device__ __forceinline__ float groups_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  return fmaxf(v, __shfl_xor(v, 32, kWave));
+}
+__device__ __forceinline__ float groups_sum(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  return v + __shfl_xor(v, 32, kWave);
+}
+
+__global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ qr, const uint16_t* __restrict__ kc,
+                                                     const uint16_t* __restrict__ vc, int S, int nq, int nkv, int cap,
+                                                     float scale, uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t Ks[2][kFaK][kFaDP];       // [buffer][key][dim]
+  __shared__ __align__(16) uint16_t Vt[2][kHD][kFaKP];        // [buffer][dim][permuted key]
   const int h = blockIdx.y, kvh = h / (nq / nkv);
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
-  const int qb = blockIdx.x * kFaQ, q0 = qb + 16 * w;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, grp = lane >> 4;
   const uint16_t* kbase = kc + (size_t)kvh * cap * kHD;
   const uint16_t* vbase = vc + (size_t)kvh * cap * kHD;
+  // staging: thread -> key pair sp (rows 2 sp, 2 sp + 1) and 8-dim chunk sc; four consecutive
+  // lanes read 64 contiguous bytes of a row.  V goes to LDS transposed, as dwords holding the
+  // pair's two keys of one dimension, at the permuted key position of key 2 sp.
+  const int sp = lane >> 2, sc = 4 * w + (lane & 3);
+  const int kp = 2 * sp;
+  const int vpos = 8 * ((kp & 15) >> 2) + 4 * (kp >> 4) + (kp & 3);
+  auto load_blk = [&](int kb, u32x4 (&r)[4]) {
+    const size_t r0 = (size_t)min(kb + kp, S - 1) * kHD + 8 * sc;
+    const size_t r1 = (size_t)min(kb + kp + 1, S - 1) * kHD + 8 * sc;
+    r[0] = *reinterpret_cast<const u32x4*>(kbase + r0);
+    r[1] = *reinterpret_cast<const u32x4*>(kbase + r1);
+    r[2] = *reinterpret_cast<const u32x4*>(vbase + r0);
+    r[3] = *reinterpret_cast<const u32x4*>(vbase + r1);
+  };
+  auto stage = [&](int buf, const u32x4 (&r)[4]) {
+    *reinterpret_cast<u32x4*>(&Ks[buf][kp][8 * sc]) = r[0];
+    *reinterpret_cast<u32x4*>(&Ks[buf][kp + 1][8 * sc]) = r[1];
+    const uint32_t a[4] = {r[2].x, r[2].y, r[2].z, r[2].w}, b[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)              // (V[2 sp][d], V[2 sp + 1][d]) for d = 8 sc + i
+      *reinterpret_cast<uint32_t*>(&Vt[buf][8 * sc + i][vpos]) =
+          __builtin_amdgcn_perm(b[i >> 1], a[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+  };
 
-  // A operands of q: query q0 + lane % 16, dims 32 ks + 8 (lane / 16) .. + 7, scaled, hi + lo
-  half8 qh[4], ql[4];
-  {
-    const float* qrow = qr + ((size_t)min(q0 + (lane & 15), S - 1) * nq + h) * kHD + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * ks);
-      const float4 b = *reinterpret_cast<const float4*>(qrow + 32 * ks + 4);
-      const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
-                          b.x * scale, b.y * scale, b.z * scale, b.w * scale};
-      split_hi_lo(v, qh[ks], ql[ks]);
-    }
-  }
-  float m_i[4], l_i[4];
-  f32x4 O[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { m_i[r] = -INFINITY; l_i[r] = 0.f; }
-#pragma unroll
-  for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the workgroup takes query block nqb - 1 - x and then query block x: every workgroup walks
+  // about the same number of keys
+  const int nqb = (S + kFaQ - 1) / kFaQ;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qblk = pass == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (pass == 1 && qblk >= nqb - 1 - (int)blockIdx.x) break;   // the middle block of an odd count
+    const int qb = qblk * kFaQ;
+    const int q0 = qb + 16 * w, q = q0 + (lane & 15);
 
-  const int kend = min(S, qb + kFaQ);        // keys the workgroup's last query sees
-  // staging: thread t takes key row t / 8, dims 16 (t % 8) .. + 15 of K and of V
-  const int sr = tid >> 3, sd = (tid & 7) * 16;
-  for (int kb = 0; kb < kend; kb += kFaK) {
+    // B operands of q: query q, dims 32 ks + 8 (lane / 16) .. + 7, scaled, hi + lo
+    half8 qh[4], ql[4];
     {
-      const size_t row = (size_t)min(kb + sr, S - 1) * kHD + sd;
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kbase + row);
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kbase + row + 8);
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(vbase + row);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(vbase + row + 8);
-      __syncthreads();                       // the previous block's operands are consumed
-      *reinterpret_cast<u32x4*>(&Ks[sr][sd]) = k0;
-      *reinterpret_cast<u32x4*>(&Ks[sr][sd + 8]) = k1;
-      const uint32_t vd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Vt[sd + 2 * i][sr] = (uint16_t)(vd[i] & 0xffffu);
-        Vt[sd + 2 * i + 1][sr] = (uint16_t)(vd[i] >> 16);
-      }
-      __syncthreads();
-    }
-    if (kb > q0 + 15) continue;              // every query of this wave is before the block
-
-    // scores of queries 4 (lane / 16) + r against keys kb + 16 nb + lane % 16
-    f32x4 sc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* qrow = qr + ((size_t)min(q, S - 1) * nq + h) * kHD + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const half8 b = *reinterpret_cast<const half8*>(&Ks[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], b, acc, 0, 0, 0);
+        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * ks);
+        const float4 b = *reinterpret_cast<const float4*>(qrow + 32 * ks + 4);
+        const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                            b.x * scale, b.y * scale, b.z * scale, b.w * scale};
+        split_hi_lo(v, qh[ks], ql[ks]);
       }
-      sc[nb] = acc;
     }
-    // causal mask, online softmax (each row lives in the 16 lanes of one lane group)
-    float p[2][4];
+    float m_i = -INFINITY, l_part = 0.f;     // running max of query q; this lane's share of its sum
+    f32x4 O[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = q0 + 4 * (lane >> 4) + r;
-      float mx = -INFINITY;
+    for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int kend = min(S, qb + kFaQ);      // keys the block's last query sees
+    u32x4 kv[4];
+    load_blk(0, kv);
+    stage(0, kv);                            // every wave finished the previous pass before its last barrier
+    __syncthreads();
+    load_blk(kFaK, kv);
+    int buf = 0;
+    for (int kb = 0; kb < kend; kb += kFaK, buf ^= 1) {
+      if (kb <= q0 + 15) {                   // else every query of this wave is before the block
+        // scores (base 2): sT[nb][r] = query q . key kb + 16 nb + 4 grp + r
+        f32x4 sT[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int key = kb + 16 * nb + (lane & 15);
-        const float v = (key <= q && key < S) ? sc[nb][r] : -INFINITY;
-        sc[nb][r] = v;
-        mx = fmaxf(mx, v);
+        for (int nb = 0; nb < 2; ++nb) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const half8 kop = *reinterpret_cast<const half8*>(&Ks[buf][16 * nb + (lane & 15)][32 * ks + 8 * grp]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qh[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, ql[ks], acc, 0, 0, 0);
+          }
+          sT[nb] = acc;
+        }
+        if (kb + kFaK - 1 > q0 || kb + kFaK > S) {   // causal mask (and the end of the prompt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = kb + 16 * nb + 4 * grp + r;
+              if (key > q || key >= S) sT[nb][r] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sT[0][0], sT[0][1]), fmaxf(sT[0][2], sT[0][3])),
+                         fmaxf(fmaxf(sT[1][0], sT[1][1]), fmaxf(sT[1][2], sT[1][3])));
+        // finite: key 0 is in the first block of every query
+        const float m_new = fmaxf(m_i, groups_max(mx));
+        const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);   // v_exp_f32 (2^-126 and below flush to 0)
+        m_i = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) O[n] *= alpha;
+        half8 ph, pl;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(sT[nb][r] - m_new);
+            l_part += pv;
+            const _Float16 hi = (_Float16)pv;
+            ph[4 * nb + r] = hi;
+            pl[4 * nb + r] = (_Float16)(pv - (float)hi);
+          }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const half8 vop = *reinterpret_cast<const half8*>(&Vt[buf][16 * n + (lane & 15)][8 * grp]);
+          O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, ph, O[n], 0, 0, 0);
+          O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pl, O[n], 0, 0, 0);
+        }
       }
-      mx = row16_max(mx);
-      const float m_new = fmaxf(m_i[r], mx);  // finite: key 0 is in the first block of every row
-      const float alpha = expf(m_i[r] - m_new);
-      float rs = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        p[nb][r] = expf(sc[nb][r] - m_new);
-        rs += p[nb][r];
-      }
-      rs = row16_sum(rs);
-      l_i[r] = l_i[r] * alpha + rs;
-      m_i[r] = m_new;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) O[n][r] *= alpha;
+      // the other buffer was last read before the previous barrier
+      stage(buf ^ 1, kv);
+      __syncthreads();
+      load_blk(kb + 2 * kFaK, kv);           // rows clamp to the prompt: always in bounds
     }
-    // P (result layout) -> LDS -> A operand layout (query lane % 16, keys 8 (lane / 16) .. + 7)
+    // O^T / l -> out[q][h][dims 16 n + 4 grp .. + 3] (fp16, 8 bytes per lane and n)
+    const float inv = 1.0f / groups_sum(l_part);
+    if (q < S) {
+      uint16_t* orow = out + ((size_t)q * nq + h) * kHD + 4 * grp;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const _Float16 hi = (_Float16)p[nb][r];
-        const _Float16 lo = (_Float16)(p[nb][r] - (float)hi);
-        Ps[w][0][4 * (lane >> 4) + r][16 * nb + (lane & 15)] = __builtin_bit_cast(uint16_t, hi);
-        Ps[w][1][4 * (lane >> 4) + r][16 * nb + (lane & 15)] = __builtin_bit_cast(uint16_t, lo);
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t lo = (uint32_t)f2h(O[n][0] * inv) | ((uint32_t)f2h(O[n][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f2h(O[n][2] * inv) | ((uint32_t)f2h(O[n][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * n) = make_uint2(lo, hi);
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const half8 ph = *reinterpret_cast<const half8*>(&Ps[w][0][lane & 15][8 * (lane >> 4)]);
-    const half8 pl = *reinterpret_cast<const half8*>(&Ps[w][1][lane & 15][8 * (lane >> 4)]);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const half8 b = *reinterpret_cast<const half8*>(&Vt[16 * n + (lane & 15)][8 * (lane >> 4)]);
-      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, b, O[n], 0, 0, 0);
-      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, b, O[n], 0, 0, 0);
     }
-  }
-  // O / l -> out[query][h][dims 16 n + lane % 16] (fp16)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int q = q0 + 4 * (lane >> 4) + r;
-    if (q >= S) continue;
-    const float inv = 1.0f / l_i[r];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) out[((size_t)q * nq + h) * kHD + 16 * n + (lane & 15)] = f2h(O[n][r] * inv);
   }
 }
 
@@ -539,9 +562,9 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_c
                        kc, vc, (int)kv32, lens);
     VV_HIP(hipGetLastError());
     if (!kv32) {   // causal attention on the matrix cores: token t attends to 0..t
-      hipLaunchKernelGGL(k_pf_flash, dim3((unsigned)cdiv(S, kFaQ), d.nq), dim3(256), 0, st, qr,
+      hipLaunchKernelGGL(k_pf_flash, dim3((unsigned)cdiv(cdiv(S, kFaQ), 2), d.nq), dim3(256), 0, st, qr,
                          static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), S, d.nq, d.nkv, cap,
-                         1.0f / sqrtf((float)kHD), o);
+                         (float)(1.4426950408889634 / std::sqrt((double)kHD)), o);
       VV_HIP(hipGetLastError());
     }
     for (int c0 = 0; kv32 && c0 < S; c0 += kPfAttnChunk) {   // fp32 caches: the split-KV kernel

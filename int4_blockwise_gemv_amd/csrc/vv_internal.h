@@ -79,15 +79,13 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f<0x140>(v));
   return v;
 }
-// lane-wise sum over the 4 rows of the wave (every lane l gets sum_r v[16r + l%16]):
-// v_permlane16_swap exchanges the odd rows of its first operand with the even rows of its
-// second, so with both operands = v the two results add up to (r0+r1, r0+r1, r2+r3, r2+r3);
-// v_permlane32_swap then does the same with the two halves.  Fixed order, no LDS traffic.
+// lane-wise sum over the 4 rows of the wave (every lane l gets sum_r v[16r + l%16]) as
+// (r0 + r1) + (r2 + r3) in every lane (the two partial sums commute), by two lane shuffles.  (A
+// v_permlane16_swap with the same value in both operands would do it without LDS, but the
+// compiler has been seen to take its two results for one.)
 __device__ __forceinline__ float rows_lanewise_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
 }
 // sum / max over the whole wave (uniform result)
 __device__ __forceinline__ float wave_sum(float v) {
