@@ -25,10 +25,11 @@ namespace vv {
 namespace {
 
 constexpr int kHD = 128;                     // head_dim
-constexpr int kPfWaves = 8;                  // GEMM: tiles per workgroup, one per wave
-constexpr int kPfTok = 64;                   // GEMM: tokens per workgroup, four 16-token MFMA groups
-constexpr int kPfStage = kPfTok * 256 * 2;   // GEMM: activation bytes of one group of 8 blocks
-constexpr int kPfAttnChunk = 512;            // tokens per attention launch
+constexpr int kPfAttnChunk = 512;
+#ifndef PF_GEMM_TG
+#define PF_GEMM_TG 4
+#define PF_GEMM_NW 4
+#endif            // tokens per attention launch
 
 struct PfGemm {
   const uint8_t* q; const uint16_t* s;       // tiled int4 weights, ntiles tiles of 64 rows
@@ -58,92 +59,97 @@ __device__ __forceinline__ h2_t scale_pair(const u32x4& s, int i) {
   return as_h2(__builtin_amdgcn_perm(d, d, (i & 1) ? 0x03020302u : 0x01000100u));
 }
 
-template <int EPI>
-__global__ __launch_bounds__(64 * kPfWaves) void k_pf_gemm(PfGemm p) {
-  __shared__ __align__(16) uint8_t As[2][kPfStage];
+// One workgroup = NW waves x (its own 64-row tile) x the same 16 TG tokens.
+template <int EPI, int TG, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_pf_gemm(PfGemm p) {   // two waves per SIMD
+  constexpr int kTok = 16 * TG;              // tokens per workgroup
+  constexpr int kChunks = 8 * TG;            // 1 KiB chunks per stage: 8 blocks x TG token groups
+  constexpr int kPerWave = kChunks / NW;     // chunks each wave stages
+  static_assert(kChunks % NW == 0, "stage chunks split evenly over the waves");
+  __shared__ __align__(16) uint8_t As[2][kChunks * 1024];
   // workgroup -> (tile group, token block): XCD x takes tile groups x, x + 8, ... and runs every
   // token block of one tile group back to back, so its tiles' weights come from HBM once and
   // from the XCD's L2 after that
-  const int ntb = (p.S + kPfTok - 1) / kPfTok, ntg = (p.ntiles + kPfWaves - 1) / kPfWaves;
+  const int ntb = (p.S + kTok - 1) / kTok, ntg = (p.ntiles + NW - 1) / NW;
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
   const int tb = seq % ntb, tgrp = 8 * (seq / ntb) + xcd;
   if (tgrp >= ntg) return;                   // padding of the grid to whole rounds of 8
   const int w = wave_id(), lane = threadIdx.x & 63;
-  const int tile_u = tgrp * kPfWaves + w;
+  const int tile_u = tgrp * NW + w;
   const int tile = min(tile_u, p.ntiles - 1); // a wave past the last tile recomputes it, stores nothing
-  const int t0 = tb * kPfTok;
+  const int t0 = tb * kTok;
   const int K = p.K, nb = K / kBlock, ng = (nb + 7) / 8;
   const u32x4* qt = reinterpret_cast<const u32x4*>(p.q) + (size_t)tile * nb * kTileRows + lane;
-  const u32x4* st = reinterpret_cast<const u32x4*>(p.s) + (size_t)tile * ng * kTileRows + lane;
-  // A staging, operand order: 1 KiB chunk 4 i + j of a stage holds block i (of 8) of token group j
+  const u32x4* st = reinterpret_cast<const u32x4*>(p.s) + (size_t)tile * ng * kTileRows + (lane & 15);
+  // A staging, operand order: 1 KiB chunk TG i + j of a stage holds block i (of 8) of token group j
   // (16 tokens), lane l's 16 B = token 16 j + l % 16, k 32 i + 8 (l / 16) .. + 7.  Wave w fills
-  // chunks 8 u + w (u = 0..3): block 2 u + w / 4, token group w % 4.  Token rows past S are
-  // clamped (computed, not stored); blocks past K are clamped (their MFMAs are skipped).
-  const uint16_t* xs = p.x + (size_t)min(t0 + 16 * (w & 3) + (lane & 15), p.S - 1) * K + 8 * (lane >> 4);
-  auto load_stage = [&](int grp, u32x4 (&r)[4]) {
+  // chunks NW u + w.  Token rows past S are clamped (computed, not stored); blocks past K are
+  // clamped (their MFMAs are skipped).
+  const uint16_t* xs[kPerWave];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int blk = min(grp * 8 + 2 * u + (w >> 2), nb - 1);
-      r[u] = *reinterpret_cast<const u32x4*>(xs + (size_t)blk * kBlock);
+  for (int u = 0; u < kPerWave; ++u) {
+    const int c = NW * u + w, j = c % TG;
+    xs[u] = p.x + (size_t)min(t0 + 16 * j + (lane & 15), p.S - 1) * K + 8 * (lane >> 4);
+  }
+  auto load_stage = [&](int grp, u32x4 (&r)[kPerWave]) {
+#pragma unroll
+    for (int u = 0; u < kPerWave; ++u) {
+      const int blk = min(grp * 8 + (NW * u + w) / TG, nb - 1);
+      r[u] = *reinterpret_cast<const u32x4*>(xs[u] + (size_t)blk * kBlock);
     }
   };
-  auto store_stage = [&](int buf, const u32x4 (&r)[4]) {
+  auto store_stage = [&](int buf, const u32x4 (&r)[kPerWave]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(&As[buf][(8 * u + w) * 1024 + lane * 16]) = r[u];
+    for (int u = 0; u < kPerWave; ++u) *reinterpret_cast<u32x4*>(&As[buf][(NW * u + w) * 1024 + lane * 16]) = r[u];
   };
-  // a group's weights: 8 blocks of the tile (lane = row) and the 8 scales of the lane's row
-  auto load_w = [&](int grp, u32x4 (&wv)[8], u32x4& sv) {
-    sv = st[(size_t)grp * kTileRows];
+  // a group's weights: 8 blocks of the tile (lane = row), and the 8 scales of each operand row
+  // 16 g + lane % 16 (the scale rows are read straight in operand order, 4 x 16 B per lane)
+  auto load_w = [&](int grp, u32x4 (&wv)[8], u32x4 (&sv)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sv[g] = st[(size_t)grp * kTileRows + 16 * g];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wv[i] = qt[(size_t)min(grp * 8 + i, nb - 1) * kTileRows];
   };
 
   const uint32_t m64 = vconst(0x54005400u);
-  f32x4 acc[4][4];
+  f32x4 acc[TG][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < TG; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[4], wv[8], sv;
+  u32x4 ar[kPerWave], wv[8], s4[4];
   load_stage(0, ar);
-  load_w(0, wv, sv);
+  load_w(0, wv, s4);
   store_stage(0, ar);
   __syncthreads();
   for (int grp = 0; grp < ng; ++grp) {
     const int cur = grp & 1, nxt = min(grp + 1, ng - 1);
     // the next group's operands are in flight while this group computes (the last group reloads
     // its own, unused, so that no load sits under a branch)
-    u32x4 wn[8], sn;
+    u32x4 wn[8], sn[4];
     load_stage(nxt, ar);
     load_w(nxt, wn, sn);
-    // the scales of the operand rows 16 g + lane % 16
-    u32x4 s4[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int src = 16 * g + (lane & 15);
-      s4[g] = u32x4{(uint32_t)__shfl((int)sv.x, src, kWave), (uint32_t)__shfl((int)sv.y, src, kWave),
-                    (uint32_t)__shfl((int)sv.z, src, kWave), (uint32_t)__shfl((int)sv.w, src, kWave)};
-    }
     const uint8_t* as = As[cur] + lane * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (grp * 8 + i >= nb) break;          // the last group of a K that is not a multiple of 256
-      half8 a[4];
+      half8 a[TG];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const half8*>(as + (4 * i + j) * 1024);
+      for (int j = 0; j < TG; ++j) a[j] = *reinterpret_cast<const half8*>(as + (TG * i + j) * 1024);
       uint32_t tq[4];
       block_to_operands(wv[i], tq);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const half8 bop = codes_to_half8_scaled(tq[g], m64, scale_pair(s4[g], i));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, acc[j][g], 0, 0, 0);
+        for (int j = 0; j < TG; ++j) acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, acc[j][g], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) wv[i] = wn[i];
-    sv = sn;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) s4[g] = sn[g];
     // every wave finished reading stage buffer cur ^ 1 before the previous barrier
     store_stage(cur ^ 1, ar);
     __syncthreads();
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void k_pf_gemm(PfGemm p) {
 
   // lane l holds tokens t0 + 16 j + 4 (l / 16) + r and tile row 16 g + l % 16
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < TG; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 16 * j + 4 * (lane >> 4) + r;
@@ -473,12 +479,17 @@ PfDims pf_dims(const vv_model* m, int S, int cap) {
   return d;
 }
 
+// TG token groups of 16 and NW tiles (one per wave) per workgroup
+template <int EPI, int TG, int NW>
+hipError_t pf_gemm_launch(const PfGemm& p, hipStream_t st) {
+  const int ntg = (int)cdiv(p.ntiles, NW);
+  const dim3 grid((unsigned)(8 * cdiv(ntg, 8) * cdiv(p.S, 16 * TG))), block(64 * NW);
+  hipLaunchKernelGGL((k_pf_gemm<EPI, TG, NW>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
 template <int EPI>
 hipError_t pf_gemm(const PfGemm& p, hipStream_t st) {
-  const int ntg = cdiv(p.ntiles, kPfWaves);
-  const dim3 grid((unsigned)(8 * cdiv(ntg, 8) * cdiv(p.S, kPfTok))), block(64 * kPfWaves);
-  hipLaunchKernelGGL(k_pf_gemm<EPI>, grid, block, 0, st, p);
-  return hipGetLastError();
+  return pf_gemm_launch<EPI, PF_GEMM_TG, PF_GEMM_NW>(p, st);
 }
 
 }  // namespace
