@@ -9,13 +9,13 @@
 // the final RMSNorm of the last row and the lm_head + argmax of the decode step.
 //
 // The GEMMs are int4-dequant contractions on the matrix cores over the decode step's tiled weights:
-// a workgroup owns one 64-row tile and 128 tokens (4 waves x 32); per 32-k block a wave loads the
-// tile's block once (1 KiB, lane = row), turns it into the four 16-row B operands with the
-// permlane transpose, and runs 2 x 4 v_mfma_f32_16x16x32_f16 against 32 tokens of activations
-// (A operands read from the fp16 activation rows); each block's result is scaled by its fp16
-// scale in fp32 (exact products, as in the decode GEMVs).  The attention is the decode step's
-// split-KV kernel with every token as its own "sequence" of length t + 1 over one shared cache,
-// which makes it causal by construction; it runs in chunks of tokens to bound its workspace.
+// each wave of a workgroup owns one 64-row tile, all waves share the workgroup's tokens, staged in
+// LDS; per 32-k block a wave turns its tile's block (1 KiB, lane = row) into the four 16-row B
+// operands with the permlane transpose, scales the dequantised codes by the block's fp16 scale and
+// runs v_mfma_f32_16x16x32_f16 against every 16-token group.  The attention of fp16 caches is a
+// matrix-core kernel with an online softmax; with fp32 caches it is the decode step's split-KV
+// kernel with every token as its own "sequence" of length t + 1 over one shared cache, which
+// makes it causal by construction, run in chunks of tokens to bound its workspace.
 #include <algorithm>
 
 #include "vv_internal.h"
