@@ -161,3 +161,17 @@ def test_prefill_deterministic(cuda):
     case.ds.v.zero_()
     case.run()
     assert np.array_equal(host(case.ds.k), k1) and np.array_equal(host(case.ds.logits), l1)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_7b_full_prompt(cuda):
+    """The benchmarked prompt length at 7B width: one layer, S = 2048 (32 query blocks of the causal
+    attention, 32 token blocks of the GEMMs), every position's K/V and the last logits against the
+    oracle."""
+    import time
+    case = PrefillCase(synth.QWEN2_7B, 0, [3], 2048, 2048)
+    case.run()
+    t = time.time()
+    ref = case.oracle()
+    print(f"oracle prefill {time.time() - t:.1f} s")
+    _compare(case, ref)
