@@ -23,6 +23,9 @@
 namespace vv {
 namespace {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 constexpr int kD = 128;           // head_dim
 constexpr int kMaxG = 8;          // query heads per KV head
 constexpr int kPS = 132;          // partial record: m, l, pad, pad, o[128]
@@ -97,6 +100,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   __shared__ __align__(16) uint16_t knew[KV32 ? 8 : kD], vnew[KV32 ? 8 : kD];
   __shared__ __align__(16) float knew32[KV32 ? kD : 4], vnew32[KV32 ? kD : 4];
   __shared__ float mh[kMaxG], lh[kMaxG];
+  // fp16 caches: q of the group as the scores' MFMA B operand, fp16 hi + lo parts, heads g..15 zero
+  __shared__ __align__(16) _Float16 qhi[KV32 ? 1 : 16][kD], qlo[KV32 ? 1 : 16][kD];
 
   const int g = p.nq / p.nkv;
   const Geo G = geo(p, S);
@@ -144,15 +149,19 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(kbase, (short)0, kvbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(vbase, (short)0, kvbytes, kBufWord3);
   const int row0 = G.s0 + jw;              // first position of this wave
+  // fp16 caches: load r = 4 nb + ks holds dims 32 ks + 8 (lane / 16) .. + 7 of position
+  // jw + 16 nb + lane % 16, the A operand (16 positions x 32 dims) of the scores' MFMAs
+  const int kpos = lane & 15, kdim = 8 * (lane >> 4);
   KT kr[NP];
   VT vr[4 * NP];
 #pragma unroll
   for (int r = 0; r < NP; ++r) {
-    const int off = (row0 + pg) * kRow + sl * 8 * kEsz + r * 4 * kRow;
     if constexpr (KV32) {
+      const int off = (row0 + pg) * kRow + sl * 8 * kEsz + r * 4 * kRow;
       kr[r].a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
       kr[r].b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0));
     } else {
+      const int off = (row0 + 16 * (r >> 2) + kpos) * kRow + (32 * (r & 3) + kdim) * kEsz;
       kr[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
     }
   }
@@ -179,6 +188,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       const int hh = tid >> 4;
       *reinterpret_cast<float4*>(&qs[hh][4 * c16]) = make_float4(r1[0], r1[1], r1[2], r1[3]);
       *reinterpret_cast<float4*>(&qs[hh][64 + 4 * c16]) = make_float4(r2[0], r2[1], r2[2], r2[3]);
+      if constexpr (!KV32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const _Float16 a = (_Float16)r1[i], b = (_Float16)r2[i];
+          qhi[hh][4 * c16 + i] = a;
+          qlo[hh][4 * c16 + i] = (_Float16)(r1[i] - (float)a);
+          qhi[hh][64 + 4 * c16 + i] = b;
+          qlo[hh][64 + 4 * c16 + i] = (_Float16)(r2[i] - (float)b);
+        }
+      }
     } else if (G.has_new && tid < 16 * g + 32) {
       const bool isk = tid < 16 * g + 16;
       char* cb = (isk ? kbase : vbase) + (size_t)G.P * kRow;
@@ -207,19 +226,35 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
     }
   } else if (tid < 32 * g) {
     *reinterpret_cast<float4*>(&qs[tid >> 5][4 * (tid & 31)]) = qa;
+    if constexpr (!KV32) {
+      const float v[4] = {qa.x, qa.y, qa.z, qa.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 a = (_Float16)v[i];
+        qhi[tid >> 5][4 * (tid & 31) + i] = a;
+        qlo[tid >> 5][4 * (tid & 31) + i] = (_Float16)(v[i] - (float)a);
+      }
+    }
+  }
+  if constexpr (!KV32) {                     // heads g..15 of the operand are zero
+    for (int i = tid; i < (16 - g) * kD; i += kThreads) {
+      qhi[g + i / kD][i % kD] = (_Float16)0.f;
+      qlo[g + i / kD][i % kD] = (_Float16)0.f;
+    }
   }
   __syncthreads();
   if (G.has_new) {  // the new position's row was loaded from the cache before it was written
 #pragma unroll
-    for (int r = 0; r < NP; ++r)
-      if (G.s0 + jw + 4 * r + pg == G.P) {
-        if constexpr (KV32) {
+    for (int r = 0; r < NP; ++r) {
+      if constexpr (KV32) {
+        if (G.s0 + jw + 4 * r + pg == G.P) {
           kr[r].a = *reinterpret_cast<const u32x4*>(&knew32[8 * sl]);
           kr[r].b = *reinterpret_cast<const u32x4*>(&knew32[8 * sl + 4]);
-        } else {
-          kr[r] = *reinterpret_cast<const u32x4*>(&knew[8 * sl]);
         }
+      } else {
+        if (G.s0 + jw + 16 * (r >> 2) + kpos == G.P) kr[r] = *reinterpret_cast<const u32x4*>(&knew[32 * (r & 3) + kdim]);
       }
+    }
 #pragma unroll
     for (int i = 0; i < 4 * NP; ++i)
       if (G.s0 + jw + i == G.P) {
@@ -233,26 +268,56 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   for (int i = 0; i < 4 * NP; ++i)
     if (jw + i >= G.npos) vr[i] = VT{};
 
-  // ---- scores: 16 lanes per position, reduced across the 16; two heads per pass (independent
-  // chains hide the LDS and cross-lane latencies when a SIMD runs a single wave) -----------------
-#pragma unroll 1
-  for (int h0 = 0; h0 < g; h0 += 2) {
-    const int h1 = min(h0 + 1, g - 1);     // a repeated head when g is odd: computed, not stored
-    float q0[8], q1[8];
-    {
-      const float4 a0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl]), b0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl + 4]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl]), b1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl + 4]);
-      q0[0] = a0.x; q0[1] = a0.y; q0[2] = a0.z; q0[3] = a0.w; q0[4] = b0.x; q0[5] = b0.y; q0[6] = b0.z; q0[7] = b0.w;
-      q1[0] = a1.x; q1[1] = a1.y; q1[2] = a1.z; q1[3] = a1.w; q1[4] = b1.x; q1[5] = b1.y; q1[6] = b1.z; q1[7] = b1.w;
+  // ---- scores ----------------------------------------------------------------------------------
+  if constexpr (!KV32) {
+    // matrix cores: D (16 positions x 16 heads) = K (16 x 32 dims) . q^T (32 dims x 16 heads) over 4
+    // dim steps, q as fp16 hi + lo (the fp16 K is exact, so the products keep fp32 precision);
+    // lane l gets positions jw + 16 nb + 4 (l / 16) + r of head l % 16
+    f16x8 bh[4], bl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bh[ks] = *reinterpret_cast<const f16x8*>(&qhi[kpos][32 * ks + kdim]);
+      bl[ks] = *reinterpret_cast<const f16x8*>(&qlo[kpos][32 * ks + kdim]);
     }
 #pragma unroll
-    for (int r = 0; r < NP; ++r) {
-      const float s0 = row16_sum(dot8_kv(q0, kr[r], 0.f));
-      const float s1 = row16_sum(dot8_kv(q1, kr[r], 0.f));
-      const int j = jw + 4 * r + pg;
-      if (sl == 0) {
-        sc[h0][j] = j < G.npos ? s0 * p.scale : -INFINITY;
-        if (h0 + 1 < g) sc[h1][j] = j < G.npos ? s1 * p.scale : -INFINITY;
+    for (int nb = 0; nb < NP / 4; ++nb) {
+      f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 a = __builtin_bit_cast(f16x8, kr[4 * nb + ks]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl[ks], acc, 0, 0, 0);
+      }
+      if (kpos < g) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jw + 16 * nb + 4 * (lane >> 4) + r;
+          sc[kpos][j] = j < G.npos ? acc[r] * p.scale : -INFINITY;
+        }
+      }
+    }
+  } else {
+    // fp32 caches: 16 lanes per position, reduced across the 16; two heads per pass (independent
+    // chains hide the LDS and cross-lane latencies when a SIMD runs a single wave)
+#pragma unroll 1
+    for (int h0 = 0; h0 < g; h0 += 2) {
+      const int h1 = min(h0 + 1, g - 1);     // a repeated head when g is odd: computed, not stored
+      float q0[8], q1[8];
+      {
+        const float4 a0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl]), b0 = *reinterpret_cast<const float4*>(&qs[h0][8 * sl + 4]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl]), b1 = *reinterpret_cast<const float4*>(&qs[h1][8 * sl + 4]);
+        q0[0] = a0.x; q0[1] = a0.y; q0[2] = a0.z; q0[3] = a0.w; q0[4] = b0.x; q0[5] = b0.y; q0[6] = b0.z; q0[7] = b0.w;
+        q1[0] = a1.x; q1[1] = a1.y; q1[2] = a1.z; q1[3] = a1.w; q1[4] = b1.x; q1[5] = b1.y; q1[6] = b1.z; q1[7] = b1.w;
+      }
+#pragma unroll
+      for (int r = 0; r < NP; ++r) {
+        const float s0 = row16_sum(dot8_kv(q0, kr[r], 0.f));
+        const float s1 = row16_sum(dot8_kv(q1, kr[r], 0.f));
+        const int j = jw + 4 * r + pg;
+        if (sl == 0) {
+          sc[h0][j] = j < G.npos ? s0 * p.scale : -INFINITY;
+          if (h0 + 1 < g) sc[h1][j] = j < G.npos ? s1 * p.scale : -INFINITY;
+        }
       }
     }
   }
