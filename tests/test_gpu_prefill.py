@@ -175,3 +175,12 @@ def test_prefill_7b_full_prompt(cuda):
     ref = case.oracle()
     print(f"oracle prefill {time.time() - t:.1f} s")
     _compare(case, ref)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_0p5b_width(cuda):
+    """Two layers at the 0.5B width (H 896 = 28 blocks: the GEMMs over K = H end on a partial group of
+    4 blocks; 14/2 heads, I 4864)."""
+    case = PrefillCase(synth.QWEN2_0P5B, 2, [0, 19], 300, 320)
+    case.run()
+    _compare(case, case.oracle())
