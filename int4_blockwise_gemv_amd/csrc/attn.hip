@@ -6,10 +6,11 @@
 //
 // Work unit: (sequence b, KV head, split of S = 64 or 128 positions), one workgroup of 4 waves
 // serving all g = nq/nkv query heads of the group.  The group's q (a few KiB) is loaded first and
-// staged in LDS; then every K and V row of the split is loaded at once (lane = 8 dims of one
-// position, 16 lanes per 256-byte row, so each wave load is 1 KiB contiguous): 8 to 16 KiB in
-// flight per wave, and B * nkv * ceil(cap / S) workgroups.  Each split writes
-// (max, sum, unnormalised output) per head; a second small kernel, one workgroup per query head,
+// staged in LDS; then every K and V row of the split is loaded at once: 8 to 16 KiB in flight
+// per wave, and B * nkv * ceil(cap / S) workgroups.  With fp16 caches the scores run on the
+// matrix cores (K rows loaded straight into the MFMA operand layout, q as fp16 hi + lo parts);
+// with fp32 caches 16 lanes share a position and reduce their partial dot products.  Each split
+// writes (max, sum, unnormalised output) per head; a second small kernel, one workgroup per query head,
 // merges the splits (online-softmax rescaling, fixed order).  The kernel boundary is the
 // hand-off, so no workgroup waits on another.  Splits past the sequence exit at once.
 //
