@@ -467,6 +467,49 @@ __global__ __launch_bounds__(128 * kMergeMaxParts) void k_attn_merge(AttnParams 
   }
 }
 
+// At most 64 splits: one wave per (sequence, query head, 64-dim half), no LDS and no barrier.
+// Lane s loads the (m, l) of split s and lane d the 64 splits' values of its dim, all at once;
+// M and L come from wave reductions and each split's weight e_s = exp(m_s - M) reaches every lane
+// by readlane.  o = sum_s e_s o_s / sum_s e_s l_s, splits in order.
+constexpr int kMergeWaveMax = 64;
+__global__ __launch_bounds__(64) void k_attn_merge_wave(AttnParams p, int S) {
+  const int g = p.nq / p.nkv;
+  const int bq = blockIdx.x >> 1;            // b * nq + head
+  const int b = bq / p.nq, h = bq % p.nq;
+  const int kvh = h / g, hh = h % g;
+  const int bh = b * p.nkv + kvh;
+  int len;
+  if (p.qkv) {
+    const int P = p.pos[b];
+    len = (P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P)) + 1;
+  } else {
+    const int l = p.lens[b];
+    len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
+  }
+  const int n = (len + S - 1) / S;           // splits that hold positions (1..64)
+  const int lane = threadIdx.x, d = 64 * (blockIdx.x & 1) + lane;
+  const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
+  const size_t stride = (size_t)kMaxG * kPS;
+  float v[kMergeWaveMax];
+#pragma unroll
+  for (int u = 0; u < kMergeWaveMax; ++u) v[u] = rec0[(size_t)min(u, n - 1) * stride + 4 + d];
+  const int sl = min(lane, n - 1);
+  const float ms = rec0[(size_t)sl * stride], ls = rec0[(size_t)sl * stride + 1];
+  const float M = wave_max(lane < n ? ms : -INFINITY);
+  const float e = lane < n ? expf(ms - M) : 0.f;
+  const float L = wave_sum(e * ls);
+  float O = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMergeWaveMax; ++u) {
+    const float eu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), u));
+    O = fmaf(eu, v[u], O);                   // e_u = 0 past the last split
+  }
+  const float o = O / L;
+  const size_t oi = ((size_t)b * p.nq + h) * kD + d;
+  if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
+  else reinterpret_cast<float*>(p.out)[oi] = o;
+}
+
 // threads of the merge workgroup: enough parts that each holds at most kMergeChunk splits
 int merge_threads(int nsplit) {
   const int parts = (int)std::min<int64_t>(kMergeMaxParts, std::max<int64_t>(2, cdiv(nsplit, kMergeChunk)));
@@ -509,7 +552,10 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
 #undef VV_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(merge_threads(p.nsplit)), st, ev.last(), p, p.split);
+  if (p.nsplit <= kMergeWaveMax)
+    VV_LAUNCH(k_attn_merge_wave, dim3(p.B * p.nq * 2), dim3(64), st, ev.last(), p, p.split);
+  else
+    VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(merge_threads(p.nsplit)), st, ev.last(), p, p.split);
   return hipGetLastError();
 }
 
