@@ -386,93 +386,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
 }
 
-// One workgroup per (sequence, query head) of 128 * parts threads: thread (part, d) holds dim d of
-// the splits of its part (a contiguous run).  All record loads are issued at once (parts are sized
-// so that a part holds at most kMergeChunk splits of the longest sequence); the split weights
-// e_s = exp(m_s - M) are computed once in LDS.  o = sum_s e_s o_s / sum_s e_s l_s, splits in a
-// fixed order within each part, then the parts in order.
-constexpr int kMergeChunk = 40;
-constexpr int kMergeMaxParts = 8;
-__global__ __launch_bounds__(128 * kMergeMaxParts) void k_attn_merge(AttnParams p, int S) {
-  __shared__ float ms_[kMaxSplits], ls_[kMaxSplits], ws_[kMaxSplits];
-  __shared__ float part[kMergeMaxParts][kD];
-  __shared__ float Ls;
-  const int g = p.nq / p.nkv;
-  const int bq = blockIdx.x;                 // b * nq + head
-  const int b = bq / p.nq, h = bq % p.nq;
-  const int kvh = h / g, hh = h % g;
-  const int bh = b * p.nkv + kvh;
-  int len;
-  if (p.qkv) {
-    const int P = p.pos[b];
-    len = (P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P)) + 1;
-  } else {
-    const int l = p.lens[b];
-    len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
-  }
-  const int n = (len + S - 1) / S;           // splits that hold positions
-  const int nthr = blockDim.x, parts = nthr / kD;
-  const int tid = threadIdx.x, d = tid & (kD - 1), pt = tid / kD;
-  const int per = (n + parts - 1) / parts;
-  const int s_beg = pt * per, s_end = min(n, s_beg + per);
-  const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
-  const size_t stride = (size_t)kMaxG * kPS;
-  // every load first, from clamped (valid) records: this part's first kMergeChunk values of dim d,
-  // then the (m, l) of split tid (a loop takes splits past the thread count afterwards)
-  float v[kMergeChunk];
-#pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u) v[u] = rec0[(size_t)min(s_beg + u, n - 1) * stride + 4 + d];
-  const int s0 = min(tid, n - 1);
-  const float m0 = rec0[(size_t)s0 * stride], l0 = rec0[(size_t)s0 * stride + 1];
-  if (tid < n) { ms_[tid] = m0; ls_[tid] = l0; }
-  for (int s = tid + nthr; s < n; s += nthr) {
-    ms_[s] = rec0[s * stride];
-    ls_[s] = rec0[s * stride + 1];
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float M = -INFINITY;
-    for (int s = tid; s < n; s += 64) M = fmaxf(M, ms_[s]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int s = tid; s < n; s += 64) {
-      const float e = expf(ms_[s] - M);
-      ws_[s] = e;
-      L = fmaf(e, ls_[s], L);
-    }
-    L = wave_sum(L);
-    if (tid == 0) Ls = L;
-  }
-  __syncthreads();
-  float O = 0.f;
-#pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u)
-    if (s_beg + u < s_end) O = fmaf(ws_[s_beg + u], v[u], O);
-  for (int c0 = s_beg + kMergeChunk; c0 < s_end; c0 += kMergeChunk) {
-#pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) v[u] = c0 + u < s_end ? rec0[(c0 + u) * stride + 4 + d] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u)
-      if (c0 + u < s_end) O = fmaf(ws_[c0 + u], v[u], O);
-  }
-  part[pt][d] = O;
-  __syncthreads();
-  if (pt == 0) {
-    float t = 0.f;
-    for (int i = 0; i < parts; ++i) t += part[i][d];
-    const float o = t / Ls;
-    const size_t oi = ((size_t)b * p.nq + h) * kD + d;
-    if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
-    else reinterpret_cast<float*>(p.out)[oi] = o;
-  }
-}
-
-// At most 64 splits: one wave per (sequence, query head, 64-dim half), no LDS and no barrier.
-// Lane s loads the (m, l) of split s and lane d the 64 splits' values of its dim, all at once;
-// M and L come from wave reductions and each split's weight e_s = exp(m_s - M) reaches every lane
-// by readlane.  o = sum_s e_s o_s / sum_s e_s l_s, splits in order.
-constexpr int kMergeWaveMax = 64;
-__global__ __launch_bounds__(64) void k_attn_merge_wave(AttnParams p, int S) {
+// One workgroup per (sequence, query head, 64-dim half) of W = ceil(nsplit / 64) waves; wave w
+// takes splits 64 w .. 64 w + 63.  Lane s of a wave loads the (m, l) of its split s and lane d the
+// wave's 64 split values of dim d, all at once; the wave's max and weighted sum come from wave
+// reductions and the split weights e_s = exp(m_s - M_w) reach every lane by readlane, so a single
+// wave needs no LDS and no barrier.  With W > 1 the waves' (M_w, L_w, O_w) are combined by wave 0
+// through LDS after one barrier.  o = sum_s e_s o_s / sum_s e_s l_s, splits in order within a
+// wave, then the waves in order.
+constexpr int kMergeWaves = kMaxSplits / 64;
+__global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(AttnParams p, int S) {
+  __shared__ float pm[kMergeWaves], pl[kMergeWaves], po[kMergeWaves][64];
   const int g = p.nq / p.nkv;
   const int bq = blockIdx.x >> 1;            // b * nq + head
   const int b = bq / p.nq, h = bq % p.nq;
@@ -486,43 +409,57 @@ __global__ __launch_bounds__(64) void k_attn_merge_wave(AttnParams p, int S) {
     const int l = p.lens[b];
     len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
   }
-  const int n = (len + S - 1) / S;           // splits that hold positions (1..64)
-  const int lane = threadIdx.x, d = 64 * (blockIdx.x & 1) + lane;
+  const int n = (len + S - 1) / S;           // splits that hold positions
+  const int W = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d = 64 * (blockIdx.x & 1) + lane;
+  const int s0 = 64 * w, ns = min(max(n - s0, 0), 64);   // this wave's splits
   const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
   const size_t stride = (size_t)kMaxG * kPS;
-  float v[kMergeWaveMax];
+  float v[64];
 #pragma unroll
-  for (int u = 0; u < kMergeWaveMax; ++u) v[u] = rec0[(size_t)min(u, n - 1) * stride + 4 + d];
-  const int sl = min(lane, n - 1);
+  for (int u = 0; u < 64; ++u) v[u] = rec0[(size_t)min(s0 + u, n - 1) * stride + 4 + d];
+  const int sl = min(s0 + lane, n - 1);
   const float ms = rec0[(size_t)sl * stride], ls = rec0[(size_t)sl * stride + 1];
-  const float M = wave_max(lane < n ? ms : -INFINITY);
-  const float e = lane < n ? expf(ms - M) : 0.f;
-  const float L = wave_sum(e * ls);
-  float O = 0.f;
+  const bool mine = lane < ns;
+  const float Mw = wave_max(mine ? ms : -INFINITY);
+  const float e = mine ? expf(ms - Mw) : 0.f;
+  const float Lw = wave_sum(e * ls);
+  float Ow = 0.f;
 #pragma unroll
-  for (int u = 0; u < kMergeWaveMax; ++u) {
+  for (int u = 0; u < 64; ++u) {
     const float eu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), u));
-    O = fmaf(eu, v[u], O);                   // e_u = 0 past the last split
+    Ow = fmaf(eu, v[u], Ow);                 // e_u = 0 past the wave's last split
   }
-  const float o = O / L;
   const size_t oi = ((size_t)b * p.nq + h) * kD + d;
-  if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(o);
-  else reinterpret_cast<float*>(p.out)[oi] = o;
-}
-
-// threads of the merge workgroup: enough parts that each holds at most kMergeChunk splits
-int merge_threads(int nsplit) {
-  const int parts = (int)std::min<int64_t>(kMergeMaxParts, std::max<int64_t>(2, cdiv(nsplit, kMergeChunk)));
-  return parts * kD;
+  if (W == 1) {
+    if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(Ow / Lw);
+    else reinterpret_cast<float*>(p.out)[oi] = Ow / Lw;
+    return;
+  }
+  if (lane == 0) { pm[w] = Mw; pl[w] = Lw; }
+  po[w][lane] = Ow;
+  __syncthreads();
+  if (w != 0) return;
+  float M = -INFINITY;
+  for (int ww = 0; ww < W; ++ww) M = fmaxf(M, pm[ww]);      // finite: wave 0 holds split 0
+  float O = 0.f, L = 0.f;
+  for (int ww = 0; ww < W; ++ww) {
+    const float f = pm[ww] == -INFINITY ? 0.f : expf(pm[ww] - M);   // a wave past the sequence: 0
+    O = fmaf(f, po[ww][lane], O);
+    L = fmaf(f, pl[ww], L);
+  }
+  if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(O / L);
+  else reinterpret_cast<float*>(p.out)[oi] = O / L;
 }
 
 }  // namespace
 
-// Split size 64 positions, or 128 when that would give more than ~2048 workgroups; at most
-// 1024 splits per sequence (cap <= 131072).
+// Split size 64 positions, or 128 when that would give more than ~2048 workgroups or more than
+// the merge's 1024 splits per sequence (so cap <= 131072 always fits).
 void attn_plan(AttnParams& p) {
-  const int64_t wgs64 = (int64_t)p.B * p.nkv * cdiv(p.cap, 64);
-  p.split = wgs64 > 2048 ? 128 : 64;
+  const int64_t n64 = cdiv(p.cap, 64);
+  const int64_t wgs64 = (int64_t)p.B * p.nkv * n64;
+  p.split = wgs64 > 2048 || n64 > kMaxSplits ? 128 : 64;
   p.nsplit = (int)cdiv(p.cap, p.split);
 }
 
@@ -552,10 +489,7 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
 #undef VV_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  if (p.nsplit <= kMergeWaveMax)
-    VV_LAUNCH(k_attn_merge_wave, dim3(p.B * p.nq * 2), dim3(64), st, ev.last(), p, p.split);
-  else
-    VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq), dim3(merge_threads(p.nsplit)), st, ev.last(), p, p.split);
+  VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq * 2), dim3(64 * cdiv(p.nsplit, 64)), st, ev.last(), p, p.split);
   return hipGetLastError();
 }
 

@@ -109,6 +109,18 @@ def test_gqa_validation():
     assert L.vv_gqa_decode(d, 2, d, d, d, 1, 12, 2, 256, 128, 0.1, d, 2, d, 8, None) == vvmod.VV_ERR_WORKSPACE
 
 
+def test_gqa_split_plan_bounds():
+    """The split-KV partials take (8 heads x 132 floats) per split; a sequence never gets more than
+    1024 splits (the merge's limit): one KV head at the largest capacity switches to 128-position
+    splits even though its workgroup count alone would keep 64."""
+    rec = 8 * 132 * 4
+    align = lambda n: (n + 255) // 256 * 256
+    assert vvmod.gqa_workspace(1, 8, 1, 131072) == align(1024 * rec)          # 128-position splits
+    assert vvmod.gqa_workspace(1, 8, 1, 65536) == align(1024 * rec)           # 64-position splits
+    assert vvmod.gqa_workspace(1, 8, 4, 4000) == align(4 * 63 * rec)          # 64-position splits
+    assert vvmod.gqa_workspace(16, 12, 2, 8192) == align(16 * 2 * 64 * rec)   # > 2048 workgroups: 128
+
+
 def test_lm_head_validation():
     L = _lib()
     d = P(64)
