@@ -58,6 +58,8 @@ def test_gqa_tiny_brute_shape(cuda):
     (8, 8, 64, [64, 31]),             # group of 1
     (16, 2, 300, [300]),              # group of 8
     (8, 8, 17000, [17000, 5]),        # > 2048 workgroups at 64 positions: 128-position splits
+    (8, 1, 65536, [65536, 3]),        # 1024 splits of 64 positions: the merge's 16 waves
+    (8, 1, 131072, [131072]),         # largest capacity, one KV head: 1024 splits of 128
 ])
 def test_gqa_shapes_and_ragged(cuda, nq, nkv, cap, lens):
     B = len(lens)
