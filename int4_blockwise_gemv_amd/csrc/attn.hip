@@ -325,7 +325,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   __syncthreads();
 
   // ---- split-local softmax statistics, one wave per head -----------------------------------------
-  for (int hh = w; hh < g; hh += kWaves) {
+#pragma unroll
+  for (int it = 0; it < kMaxG / kWaves; ++it) {       // unrolled: one wave per SIMD, registers spare
+    const int hh = w + it * kWaves;
+    if (hh >= g) break;
     float m = -INFINITY;
 #pragma unroll
     for (int j = lane; j < S; j += 64) m = fmaxf(m, sc[hh][j]);
@@ -344,8 +347,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
 
   // ---- P.V: lane l accumulates dims 2 l, 2 l + 1 over the wave's 4 NP positions (weights read
   // from LDS as broadcasts, four positions per read); two heads per pass ---------------------------
-#pragma unroll 1
-  for (int h0 = 0; h0 < g; h0 += 2) {
+#pragma unroll
+  for (int h0 = 0; h0 < kMaxG; h0 += 2) {             // unrolled: the LDS reads of later pairs overlap
+    if (h0 >= g) break;
     const int h1 = min(h0 + 1, g - 1);
     float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
 #pragma unroll
@@ -367,7 +371,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   // ---- the split's output: final when it is the only split, else a record for the merge ----------
   const bool single = p.nsplit == 1;
   float* rec = p.part + ((size_t)G.bh * p.nsplit + G.sidx) * kMaxG * kPS;
-  for (int i = tid; i < g * kD; i += kThreads) {
+#pragma unroll
+  for (int it = 0; it < kMaxG * kD / kThreads; ++it) {
+    const int i = tid + it * kThreads;
+    if (i >= g * kD) break;
     const int hh = i >> 7, d = i & 127;
     float o = 0.f;
 #pragma unroll
