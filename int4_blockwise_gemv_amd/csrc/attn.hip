@@ -28,8 +28,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;           // head_dim
-constexpr int kMaxG = 8;          // query heads per KV head
-constexpr int kPS = 132;          // partial record: m, l, pad, pad, o[128]
+constexpr int kMaxG = kAttnMaxG;  // query heads per KV head
+constexpr int kPS = kAttnRec;     // partial record: m, l, pad, pad, o[128]
 constexpr int kWaves = 4;         // 256 threads per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSplits = 1024;  // splits per sequence the merge kernel takes
@@ -408,35 +408,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(AttnParams p, i
   const int b = bq / p.nq, h = bq % p.nq;
   const int kvh = h / g, hh = h % g;
   const int bh = b * p.nkv + kvh;
-  int len;
-  if (p.qkv) {
-    const int P = p.pos[b];
-    len = (P < 0 ? 0 : (P >= p.cap ? p.cap - 1 : P)) + 1;
-  } else {
-    const int l = p.lens[b];
-    len = l < 1 ? 1 : (l > p.cap ? p.cap : l);
-  }
-  const int n = (len + S - 1) / S;           // splits that hold positions
+  const int n = attn_splits(p.qkv ? p.pos : nullptr, p.lens, b, p.cap, S);
   const int W = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = 64 * (blockIdx.x & 1) + lane;
-  const int s0 = 64 * w, ns = min(max(n - s0, 0), 64);   // this wave's splits
   const float* rec0 = p.part + ((size_t)bh * p.nsplit * kMaxG + hh) * kPS;
-  const size_t stride = (size_t)kMaxG * kPS;
-  float v[64];
-#pragma unroll
-  for (int u = 0; u < 64; ++u) v[u] = rec0[(size_t)min(s0 + u, n - 1) * stride + 4 + d];
-  const int sl = min(s0 + lane, n - 1);
-  const float ms = rec0[(size_t)sl * stride], ls = rec0[(size_t)sl * stride + 1];
-  const bool mine = lane < ns;
-  const float Mw = wave_max(mine ? ms : -INFINITY);
-  const float e = mine ? expf(ms - Mw) : 0.f;
-  const float Lw = wave_sum(e * ls);
-  float Ow = 0.f;
-#pragma unroll
-  for (int u = 0; u < 64; ++u) {
-    const float eu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), u));
-    Ow = fmaf(eu, v[u], Ow);                 // e_u = 0 past the wave's last split
-  }
+  float Mw, Lw;
+  const float Ow = merge_wave64(rec0, (size_t)kMaxG * kPS, 64 * w, n, d, Mw, Lw);
   const size_t oi = ((size_t)b * p.nq + h) * kD + d;
   if (W == 1) {
     if (p.out_f16) reinterpret_cast<uint16_t*>(p.out)[oi] = f2h(Ow / Lw);
@@ -483,7 +460,7 @@ void attn_set_workspace(AttnParams& p, void* ws) {
 
 hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipStream_t st, KEv ev) {
   const int grid = p.B * p.nkv * p.nsplit;
-  const KEv e1 = p.nsplit == 1 ? ev : ev.first();
+  const KEv e1 = p.nsplit == 1 || p.skip_merge ? ev : ev.first();
   const bool step = p.qkv != nullptr;
 #define VV_ATTN_CASE(NP, KV32)                                                                      \
   if (step) VV_LAUNCH((k_attn<NP, true, KV32>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);     \
@@ -495,7 +472,7 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
   }
 #undef VV_ATTN_CASE
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
+  if (e != hipSuccess || p.nsplit == 1 || p.skip_merge) return e;
   VV_LAUNCH(k_attn_merge, dim3(p.B * p.nq * 2), dim3(64 * cdiv(p.nsplit, 64)), st, ev.last(), p, p.split);
   return hipGetLastError();
 }

@@ -148,29 +148,54 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
 // From the first load to the barrier the code is branch-free: every load address is clamped
 // into the operand (a group past the end of K re-reads the last block and gets scale 0, rows
 // past M re-read row M-1 and are never stored), so all loads of a wave are in flight together.
-template <int MT, int EPI, int WMAX>
+// Fused split-KV merge (the leading p.mrg_blocks workgroups of an XT launch): wave w of workgroup
+// i merges item i W + w = (query head, 64-dim half) of batch row 0 over at most 64 splits and stores
+// each dim as a tagged word (tag << 32) | fp16 bits of the normalised output.
+__device__ void fused_merge(const GemvParams& p) {
+  const int W = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int item = blockIdx.x * W + w;
+  if (item >= 2 * p.mrg_nq) return;
+  const int h = item >> 1, d = 64 * (item & 1) + lane;
+  const int g = p.mrg_nq / p.mrg_nkv, kvh = h / g, hh = h % g;
+  const int n = attn_splits(p.mrg_pos, nullptr, 0, p.mrg_cap, p.mrg_split);
+  const float* rec0 = p.mrg_part + ((size_t)kvh * p.mrg_nsplit * kAttnMaxG + hh) * kAttnRec;
+  float Mw, Lw;
+  const float Ow = merge_wave64(rec0, (size_t)kAttnMaxG * kAttnRec, 0, n, d, Mw, Lw);
+  const uint32_t tag = p.epoch[0] * p.tag_mul + p.tag_add;
+  publish_u64(p.xtag + (size_t)h * 128 + d, ((uint64_t)tag << 32) | f2h(Ow / Lw));
+}
+
+template <int MT, int EPI, int WMAX, bool XT>
 __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                                                   const uint4* __restrict__ sw,
                                                                   const uint16_t* __restrict__ x) {
   constexpr int kItemK = WMAX * kBatch * kBlock;  // K elements per workgroup at most
   __shared__ __align__(16) uint16_t xs[MT][kItemK];
   __shared__ float red[WMAX][MT][kTileRows];
+  static_assert(!XT || MT == 1, "the fused merge serves batch 1");
+  if constexpr (XT) {
+    if ((int)blockIdx.x < p.mrg_blocks) {
+      fused_merge(p);
+      return;
+    }
+  }
   const int W = p.wpg;
   const int K = p.K;
   const int nb = K / kBlock;
   const int ng = (nb + kBatch - 1) / kBatch;
   const int M = p.M;
   int tile, kg;
-  if (!split_role(p.ntiles, p.wpt, tile, kg)) return;
+  if (!split_role(p.ntiles, p.wpt, tile, kg, XT ? (int)blockIdx.x - p.mrg_blocks : (int)blockIdx.x)) return;
   const int w = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
   const int e0 = kg * W * kBatch * kBlock;          // first K element of this workgroup
 
-  // activation slice first (its loads return before the weights), 8 bytes per thread per row
+  // activation slice first (its loads return before the weights), 8 bytes per thread per row;
+  // with XT it is polled after the weight loads instead (it is still being merged)
   static_assert(kItemK <= 4 * 64 * WMAX, "one 8-byte activation load per thread covers the slice");
   uint2 xr[MT];
-  {
-    const int ec = min(e0 + 4 * (int)threadIdx.x, K - 4);
+  const int ec = min(e0 + 4 * (int)threadIdx.x, K - 4);
+  if constexpr (!XT) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) xr[m] = *reinterpret_cast<const uint2*>(x + (size_t)min(m, M - 1) * K + ec);
   }
@@ -190,6 +215,29 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   for (int i = 0; i < kBatch; ++i) wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + i, nb - 1) * kTileRows);
   // keep the LDS write of the activations behind the weight loads (its wait would hold them back)
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XT) {
+    // the merged attention output of this step and layer: 4 tagged words per thread (bounded wait)
+    const uint32_t tag = p.epoch[0] * p.tag_mul + p.tag_add;
+    uint64_t t[4];
+    for (uint32_t it = 0;; ++it) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        t[k] = collect_u64(p.xtag + ec + k);
+        ok = ok && (uint32_t)(t[k] >> 32) == tag;
+      }
+      if (__all(ok)) break;
+      if (it >= kSpinLimit) {
+        if (p.status) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t[k] = 0x7e00u;     // fp16 NaN
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    xr[0] = make_uint2((uint32_t)(t[0] & 0xffffu) | ((uint32_t)(t[1] & 0xffffu) << 16),
+                       (uint32_t)(t[2] & 0xffffu) | ((uint32_t)(t[3] & 0xffffu) << 16));
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[m][4 * threadIdx.x]) = xr[m];
   __syncthreads();
@@ -323,20 +371,27 @@ void gemv_set_workspace(GemvParams& p, void* ws) {
 namespace {
 template <int EPI>
 void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t st, KEv ev) {
-  const dim3 g(p.grid), b(64 * p.wpg);
+  const dim3 g(p.grid + p.mrg_blocks), b(64 * p.wpg);
   const bool wide = p.wpg > kWavesLargeM;   // only batches <= 2 get 8-wave workgroups
   switch (mt_of(p.M)) {
     case 1:
-      if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM>), g, b, st, ev, p, q, s, p.x);
-      else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x);
+      if constexpr (EPI == EPI_RESID) {      // the o projection may take the fused merge
+        if (p.mrg_blocks) {
+          if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, true>), g, b, st, ev, p, q, s, p.x);
+          else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, true>), g, b, st, ev, p, q, s, p.x);
+          break;
+        }
+      }
+      if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, false>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x);
       break;
     case 2:
-      if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM>), g, b, st, ev, p, q, s, p.x);
-      else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x);
+      if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM, false>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x);
       break;
-    case 4: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
-    case 8: VV_LAUNCH((k_gemv<8, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
-    default: VV_LAUNCH((k_gemv<16, EPI, kWavesLargeM>), g, b, st, ev, p, q, s, p.x); break;
+    case 4: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
+    case 8: VV_LAUNCH((k_gemv<8, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
+    default: VV_LAUNCH((k_gemv<16, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
   }
 }
 }  // namespace

@@ -90,8 +90,10 @@ __device__ __forceinline__ float poll_sum(uint64_t* p, int n, size_t stride, int
 // wg % 8 takes tiles [x tpx, (x + 1) tpx) and runs, in dispatch order, their (wpt - 1) writers
 // (tile-major) and then their readers (kg = wpt - 1).  A reader waits only for writers dispatched
 // before it on its own XCD.  Needs a grid of 8 tpx wpt workgroups; returns false for padding.
-__device__ __forceinline__ bool split_role(int ntiles, int wpt, int& tile, int& kg) {
-  const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+// bid: the workgroup's index in that grid (blockIdx.x less a multiple of 8 of leading workgroups
+// with another role, so that bid % 8 is still the XCD).
+__device__ __forceinline__ bool split_role(int ntiles, int wpt, int& tile, int& kg, int bid) {
+  const int x = bid % kNumXcd, i = bid / kNumXcd;
   const int tpx = (ntiles + kNumXcd - 1) / kNumXcd;
   const int nwr = tpx * (wpt - 1);
   if (i < nwr) {

@@ -26,14 +26,16 @@ namespace {
 constexpr int kHeadDim = 128;
 
 // h = fp32(input_embeds); g = fp16(gamma * h) (or gf = gamma * h in fp32 when there are no
-// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs.
+// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs; the
+// step counter advances.
 __global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ emb, int H, int ntiles,
                                                   const uint16_t* __restrict__ gamma, float* __restrict__ h,
                                                   uint16_t* __restrict__ g, float* __restrict__ gf,
                                                   float* __restrict__ sumsq, float* __restrict__ trace,
                                                   const int32_t* __restrict__ pos, int cap, double theta,
-                                                  float* __restrict__ rope) {
+                                                  float* __restrict__ rope, uint32_t* __restrict__ epoch) {
   const int t = blockIdx.x % ntiles, b = blockIdx.x / ntiles;
+  if (blockIdx.x == 0 && threadIdx.x == 0) epoch[0] += 1;   // a new step: fresh tags for this step's words
   const int lane = threadIdx.x;
   const int n = t * 64 + lane;
   const size_t i = (size_t)b * H + n;
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void k_feedback(const int32_t* __restrict__ to
 }
 
 struct Layout {
-  size_t h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, total;
+  size_t h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, otag, epoch, total;
 };
 
 struct Dims {
@@ -126,6 +128,8 @@ Layout layout_of(const Dims& d) {
   attn_plan(ap);
   l.ws_attn = take(attn_workspace_bytes(d.B, d.nq, d.nkv, ap.nsplit));
   l.ws_lm = take(lm_workspace_bytes(d.B, d.V, d.H));
+  l.otag = take((size_t)d.nq * kHeadDim * sizeof(uint64_t));   // fused merge -> o projection (batch 1)
+  l.epoch = take(sizeof(uint32_t));                              // step counter (tags of otag)
   l.total = off;
   return l;
 }
@@ -267,7 +271,8 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   int op = 0;   // timing event pair of the next operation
   VV_LAUNCH(k_step_prep, dim3(B * d.ntH), dim3(64), st, event_pair(s, op++), s->input_embeds, H, d.ntH,
             d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
-            s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
+            s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope,
+            reinterpret_cast<uint32_t*>(ws + lay.epoch));
   VV_HIP(hipGetLastError());
 
   const bool kv32 = s->kv_dtype == VV_F32;
@@ -286,11 +291,15 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_set_workspace(p, ws + lay.ws_qkv);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
+    // batch 1 over fp16 caches with at most 64 splits: the o projection's launch also merges the
+    // attention's split records (its leading workgroups), so the merge needs no launch of its own
+    AttnParams a{};
+    a.B = B; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
+    attn_plan(a);
+    const bool fuse_merge = B == 1 && !kv32 && a.nsplit > 1 && a.nsplit <= 64;
     {  // attention with RoPE and KV append
-      AttnParams a{};
-      a.B = B; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
-      attn_plan(a);
       attn_set_workspace(a, ws + lay.ws_attn);
+      a.skip_merge = fuse_merge;
       a.qkv = qkv; a.ldqkv = d.nqkv; a.pos = s->pos; a.rope_theta = m->rope_theta;
       a.kc = static_cast<char*>(s->k_cache) + (size_t)l * layer_kv_bytes;
       a.vc = static_cast<char*>(s->v_cache) + (size_t)l * layer_kv_bytes;
@@ -308,6 +317,14 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_plan(p);
       p.status = status;
       gemv_set_workspace(p, ws + lay.ws_o);
+      if (fuse_merge) {   // one wave per (query head, 64-dim half), whole rounds of 8 workgroups
+        p.mrg_blocks = (int)(cdiv(cdiv(2 * d.nq, p.wpg), 8) * 8);
+        p.mrg_part = a.part; p.mrg_pos = s->pos; p.mrg_nsplit = a.nsplit; p.mrg_split = a.split;
+        p.mrg_cap = s->cap; p.mrg_nq = d.nq; p.mrg_nkv = d.nkv;
+        p.xtag = reinterpret_cast<uint64_t*>(ws + lay.otag);
+        p.epoch = reinterpret_cast<const uint32_t*>(ws + lay.epoch);
+        p.tag_mul = (uint32_t)d.L + 1; p.tag_add = (uint32_t)l + 1;
+      }
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
     {  // gate/up (32 gate + 32 up rows per tile) + SiLU(gate) * up, RMSNorm_2 folded in

@@ -158,6 +158,51 @@ __device__ __forceinline__ void wait_published() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// ---- split-KV merge of one wave ------------------------------------------------------------------
+// Split records of the decode attention: per (sequence, KV head, split) and query head of the group,
+// kAttnRec floats = m, l, 2 pad, o[128] (m the split's max score, l = sum e^{s-m}, o = sum e^{s-m} v).
+constexpr int kAttnMaxG = 8;                 // query heads per KV head
+constexpr int kAttnRec = 132;
+// The wave merges splits s0 .. s0 + 63 (those below n) of one query head for dim d of this lane:
+// lane s loads split s0 + s's (m, l) and every lane the 64 splits' values of its dim, all at once;
+// Mw and Lw come from wave reductions and each split's weight e_s = exp(m_s - Mw) reaches every lane
+// by readlane.  Returns Ow = sum_s e_s o_s[d] (splits in order), with Lw = sum_s e_s l_s; a wave with
+// no split gets Mw = -inf, Lw = Ow = 0.  rec0: the head's record of split 0; stride: floats from one
+// split's record to the next.
+__device__ __forceinline__ float merge_wave64(const float* rec0, size_t stride, int s0, int n, int d, float& Mw,
+                                              float& Lw) {
+  const int lane = threadIdx.x & 63;
+  const int ns = min(max(n - s0, 0), 64);
+  float v[64];
+#pragma unroll
+  for (int u = 0; u < 64; ++u) v[u] = rec0[(size_t)min(s0 + u, n - 1) * stride + 4 + d];
+  const int sl = min(s0 + lane, n - 1);
+  const float ms = rec0[(size_t)sl * stride], ls = rec0[(size_t)sl * stride + 1];
+  const bool mine = lane < ns;
+  Mw = wave_max(mine ? ms : -INFINITY);
+  const float e = mine ? expf(ms - Mw) : 0.f;
+  Lw = wave_sum(e * ls);
+  float Ow = 0.f;
+#pragma unroll
+  for (int u = 0; u < 64; ++u) {
+    const float eu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), u));
+    Ow = fmaf(eu, v[u], Ow);                 // e_u = 0 past the wave's last split
+  }
+  return Ow;
+}
+// number of splits that hold positions for sequence b (the step flavour reads pos, else lens)
+__device__ __forceinline__ int attn_splits(const int32_t* pos, const int32_t* lens, int b, int cap, int S) {
+  int len;
+  if (pos) {
+    const int P = pos[b];
+    len = (P < 0 ? 0 : (P >= cap ? cap - 1 : P)) + 1;
+  } else {
+    const int l = lens[b];
+    len = l < 1 ? 1 : (l > cap ? cap : l);
+  }
+  return (len + S - 1) / S;
+}
 // sum_{k < n} p[k * stride] in k order, with the loads issued 16 at a time (a runtime-length
 // loop of agent-scope loads would wait for each one before issuing the next)
 __device__ __forceinline__ float collect_sum_f32(const float* p, int n, size_t stride) {
@@ -228,6 +273,13 @@ struct GemvParams {
   float* trace;              // fp32 [M][N] copy of h or null
   // EPI_SILU
   uint16_t* act;             // fp16 [M][N]
+  // fused split-KV merge (batch 1, at most 64 splits): the first mrg_blocks workgroups merge the
+  // attention records into tagged activation words xtag[k] = (tag << 32) | fp32 bits, which the
+  // GEMV workgroups poll instead of reading x; tag = epoch[0] * tag_mul + tag_add (the step's
+  // epoch, so that no word needs clearing)
+  int mrg_blocks;            // 0: no fused merge
+  const float* mrg_part; const int32_t* mrg_pos; int mrg_nsplit, mrg_split, mrg_cap, mrg_nq, mrg_nkv;
+  uint64_t* xtag; const uint32_t* epoch; uint32_t tag_mul, tag_add;
 };
 
 void gemv_plan(GemvParams& p);                       // fills kb/wpg/wpt/grid
@@ -252,6 +304,7 @@ struct AttnParams {
   float scale;
   void* out; int out_f16;       // [B][nq][128]
   float* part; float* part2; unsigned* cnt;
+  int skip_merge;               // 1: the split records are merged elsewhere (a fused consumer)
 };
 void attn_plan(AttnParams& p);
 size_t attn_workspace_bytes(int B, int nq, int nkv, int nsplit);
