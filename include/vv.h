@@ -23,7 +23,8 @@
  *     launched nothing.  Device faults surface at the caller's next synchronisation.
  *   - Workspaces: calls that take `ws`/`ws_bytes` need a device buffer of at least the size their
  *     *_workspace() query returns, ZERO-FILLED before its first use (vv_workspace_init does this);
- *     every completed call leaves its counters and hand-off slots cleared again, so a workspace
+ *     every completed call leaves its counters and hand-off slots cleared again (the decode
+ *     step also keeps a step counter there, whose tagged words need no clearing), so a workspace
  *     can be reused by later calls on the same stream without re-initialisation.  Two calls that
  *     run concurrently must not share a workspace.
  *   - Return value: VV_OK or a negative vv_status; vv_last_error() gives a thread-local message.
@@ -195,9 +196,11 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  *                       instead of hanging (vv_decode_status reads it; clear it with
  *                       vv_workspace_init).
  *   VV_PATH_LAYERED     one launch per stage (1 + 5 L + 1 kernels, plus a split merge per layer
- *                       when the cache is split): any batch up to max_batch.  Its split-K GEMV
- *                       hand-offs and the lm_head argmax also wait on other workgroups; those
- *                       waits are bounded the same way and set the same status word.
+ *                       when the cache is split, except at batch 1 over fp16 caches with at most
+ *                       64 splits, where the o projection's launch does the merge): any batch up
+ *                       to max_batch.  Its split-K GEMV hand-offs, the fused merge and the lm_head
+ *                       argmax also wait on other workgroups; those waits are bounded the same way
+ *                       and set the same status word.
  *   VV_PATH_AUTO        the layered path (measured faster on MI355X: 1.62 ms against 3.8 ms for
  *                       the 7B-shaped step; the persistent kernel's waiting items hold the slots
  *                       that the weight streams of later items need).
