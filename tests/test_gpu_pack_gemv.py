@@ -152,6 +152,23 @@ def test_gemv_projection_shapes(cuda, shape, mode):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", [(37888, 3584), (40000, 3616)])
+def test_gemv_two_groups_per_wave(cuda, shape, mode):
+    """Batch-1 grids with more 8-block groups than the chip holds waves at once take two groups per
+    wave: the 7B gate|up row count, and a ragged one (rows past a whole tile; K = 113 blocks, so the
+    last wave holds one group and a group past K)."""
+    N, K = shape
+    W = synth.master_weight(4, 0, synth.T_Q, N, K)
+    x = synth.fp16_normal(4, 0, synth.T_X, (1, K))
+    ref = O.gemv(*O.pack(W, mode), x)
+    q, s = _pack_gpu(W, mode, tiled=True)
+    y = _gemv_gpu(q, s, N, K, x)
+    err = rel_err(y, ref)
+    print(f"gemv {shape} {mode}: max rel err {err:.2e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("shape", [(100, 96), (1, 32), (130, 288), (1536, 1536), (256, 8960)])
 def test_gemv_batched_ragged_with_bias(cuda, shape, M):
