@@ -41,15 +41,21 @@ struct PfGemm {
   uint16_t* act;                             // EPI_SILU: fp16 [S][N]
 };
 
-// 8 codes of one dword -> 8 fp16 (q - 8) * s, k order (the magic-exponent form of the decode GEMVs,
-// then one packed multiply by the block scale s2 = (s, s)): exact for ternary codes (q - 8 in
-// {-1, 0, 1}); for general int4 codes the product rounds once to fp16 (relative error <= 2^-11).
+// 8 codes of one dword -> 8 fp16 (q - 8) * s, in the order of the decode GEMVs' codes_to_half8, then
+// one packed multiply by the block scale s2 = (s, s): exact for ternary codes (q - 8 in {-1, 0, 1});
+// for general int4 codes the product rounds once to fp16 (relative error <= 2^-11).  The nibble in
+// bits 0..3 of a 16-bit half goes into the mantissa of fp16 1024 (ulp 1: 1024 + q, less 1032) and
+// the one in bits 4..7 into that of fp16 64 (ulp 1/16: 64 + q, less 72), so one shift by 8 serves
+// the upper two nibbles; every step is exact.
 __device__ __forceinline__ half8 codes_to_half8_scaled(uint32_t d, uint32_t m64, h2_t s2) {
-  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
-  const h2_t p0 = (as_h2(((d << 4) & 0x00F000F0u) | m64) + off) * s2;
-  const h2_t p1 = (as_h2((d & 0x00F000F0u) | m64) + off) * s2;
-  const h2_t p2 = (as_h2(((d >> 4) & 0x00F000F0u) | m64) + off) * s2;
-  const h2_t p3 = (as_h2(((d >> 8) & 0x00F000F0u) | m64) + off) * s2;
+  const uint32_t m1024 = 0x64006400u;        // (1024, 1024)
+  const h2_t off_lo = as_h2(0xE408E408u);    // (-1032, -1032)
+  const h2_t off_hi = as_h2(0xD480D480u);    // (-72, -72)
+  const uint32_t d8 = d >> 8;
+  const h2_t p0 = (as_h2((d & 0x000F000Fu) | m1024) + off_lo) * s2;
+  const h2_t p1 = (as_h2((d & 0x00F000F0u) | m64) + off_hi) * s2;
+  const h2_t p2 = (as_h2((d8 & 0x000F000Fu) | m1024) + off_lo) * s2;
+  const h2_t p3 = (as_h2((d8 & 0x00F000F0u) | m64) + off_hi) * s2;
   return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
