@@ -9,8 +9,9 @@
 // on the Qwen2 layer of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA,
 // SiLU-gated MLP, residual adds.  One step is 1 + 5 L + 1 kernels:
 //   prep (embeddings -> residual stream, RoPE table)
-//   per layer: QKV GEMV (RMSNorm folded in) | attention (+RoPE, KV append, split merge)
-//              | o GEMV + residual | gate/up GEMV + SiLU*up | down GEMV + residual
+//   per layer: QKV GEMV (RMSNorm folded in) | attention (+RoPE, KV append) and its split merge
+//              (a kernel of its own, or at batch 1 over fp16 caches the leading workgroups of the
+//              o GEMV's launch) | o GEMV + residual | gate/up GEMV + SiLU*up | down GEMV + residual
 //   lm_head + argmax (final RMSNorm folded in).
 // RMSNorm is folded into the GEMVs: the producer of h writes fp16(gamma * h) and per-tile sums of
 // h^2; the consumer scales its row sums by rstd = 1/sqrt(mean(h^2) + eps).  Positions are read
