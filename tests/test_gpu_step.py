@@ -256,6 +256,31 @@ def test_graph_replay_equals_eager_and_determinism(cuda, path, pos):
         g.close()
 
 
+def test_graph_replay_fused_merge(cuda):
+    """Batch 1 over fp16 caches with several splits (cap 300: 5 splits) takes the merge inside the o
+    projection's launch, whose hand-off words carry the step counter: graph replays interleaved with
+    eager steps, a dozen steps in all, give bit-identical results."""
+    import torch
+    case = Case(TINY, 8, range(2), [250], 300, trace=True, path="layered")
+    case.run()
+    ref = [host(case.ds.logits).copy(), host(case.ds.token).copy(), host(case.ds.trace).copy()]
+    assert case.ds.status() == 0
+    g = case.ds.graph()
+    try:
+        for r in range(6):
+            g.launch()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+            assert np.array_equal(host(case.ds.token), ref[1]), r
+            assert np.array_equal(host(case.ds.trace), ref[2]), r
+            case.run()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+    finally:
+        g.close()
+    assert case.ds.status() == 0
+    _compare(case, case.oracle())
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_graph_follows_device_positions(cuda, path):
     """One captured graph serves successive positions: replays at pos, pos+1 == eager steps."""
