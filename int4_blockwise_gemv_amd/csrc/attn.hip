@@ -25,6 +25,7 @@ namespace vv {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;           // head_dim
@@ -88,14 +89,17 @@ __device__ __forceinline__ void pv_kv(float pj, uint2 v, float& e, float& o) {
 // NP passes of 4 positions per wave: split S = 4 waves * 4 * NP positions.  STEP: the decode-step
 // flavour (q/k/v from the projection output, RoPE, KV append); else the stand-alone flavour.
 // KV32: the cache holds fp32 K/V (the fp32-KV variant: twice the bytes, no fp16 rounding of k, v).
-template <int NP, bool STEP, bool KV32>
+// PVM: P.V on the matrix cores (fp16 caches; more LDS, so the host takes it for grids that are
+// resident at once anyway).
+template <int NP, bool STEP, bool KV32, bool PVM>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __restrict__ rope_cs) {
+  static_assert(!PVM || !KV32, "the matrix-core P.V reads fp16 V");
   constexpr int S = kWaves * 4 * NP;
   constexpr int kEsz = KV32 ? 4 : 2;       // bytes per cache element
   constexpr int kRow = kD * kEsz;          // bytes per cache row
   typedef typename KvLane<KV32>::K KT;
   typedef typename KvLane<KV32>::V VT;
-  __shared__ __align__(16) float qs[kMaxG][kD];
+  __shared__ __align__(16) float qs[KV32 ? kMaxG : 1][kD];   // fp32 q (fp32 caches' VALU scores)
   __shared__ __align__(16) float sc[kMaxG][S];
   __shared__ __align__(16) float red[kWaves][kMaxG][kD];      // [wave][head][dim]
   __shared__ __align__(16) uint16_t knew[KV32 ? 8 : kD], vnew[KV32 ? 8 : kD];
@@ -103,6 +107,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   __shared__ float mh[kMaxG], lh[kMaxG];
   // fp16 caches: q of the group as the scores' MFMA B operand, fp16 hi + lo parts, heads g..15 zero
   __shared__ __align__(16) _Float16 qhi[KV32 ? 1 : 16][kD], qlo[KV32 ? 1 : 16][kD];
+  // PVM: each wave's V transposed ([dim][position], padded rows) for the P.V MFMAs
+  constexpr int kVP = 4 * NP + 4;
+  __shared__ __align__(16) uint16_t vt[PVM ? kWaves : 1][PVM ? kD : 1][PVM ? kVP : 2];
 
   const int g = p.nq / p.nkv;
   const Geo G = geo(p, S);
@@ -187,17 +194,23 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
     }
     if (tid < 16 * g) {
       const int hh = tid >> 4;
-      *reinterpret_cast<float4*>(&qs[hh][4 * c16]) = make_float4(r1[0], r1[1], r1[2], r1[3]);
-      *reinterpret_cast<float4*>(&qs[hh][64 + 4 * c16]) = make_float4(r2[0], r2[1], r2[2], r2[3]);
-      if constexpr (!KV32) {
+      if constexpr (KV32) {
+        *reinterpret_cast<float4*>(&qs[hh][4 * c16]) = make_float4(r1[0], r1[1], r1[2], r1[3]);
+        *reinterpret_cast<float4*>(&qs[hh][64 + 4 * c16]) = make_float4(r2[0], r2[1], r2[2], r2[3]);
+      }
+      if constexpr (!KV32) {                 // 4 dims of hi and of lo per 8-byte store
+        f16x4 h1, l1, h2, l2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const _Float16 a = (_Float16)r1[i], b = (_Float16)r2[i];
-          qhi[hh][4 * c16 + i] = a;
-          qlo[hh][4 * c16 + i] = (_Float16)(r1[i] - (float)a);
-          qhi[hh][64 + 4 * c16 + i] = b;
-          qlo[hh][64 + 4 * c16 + i] = (_Float16)(r2[i] - (float)b);
+          h1[i] = (_Float16)r1[i];
+          l1[i] = (_Float16)(r1[i] - (float)h1[i]);
+          h2[i] = (_Float16)r2[i];
+          l2[i] = (_Float16)(r2[i] - (float)h2[i]);
         }
+        *reinterpret_cast<f16x4*>(&qhi[hh][4 * c16]) = h1;
+        *reinterpret_cast<f16x4*>(&qlo[hh][4 * c16]) = l1;
+        *reinterpret_cast<f16x4*>(&qhi[hh][64 + 4 * c16]) = h2;
+        *reinterpret_cast<f16x4*>(&qlo[hh][64 + 4 * c16]) = l2;
       }
     } else if (G.has_new && tid < 16 * g + 32) {
       const bool isk = tid < 16 * g + 16;
@@ -226,21 +239,23 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
       }
     }
   } else if (tid < 32 * g) {
-    *reinterpret_cast<float4*>(&qs[tid >> 5][4 * (tid & 31)]) = qa;
+    if constexpr (KV32) *reinterpret_cast<float4*>(&qs[tid >> 5][4 * (tid & 31)]) = qa;
     if constexpr (!KV32) {
       const float v[4] = {qa.x, qa.y, qa.z, qa.w};
+      f16x4 hv, lv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const _Float16 a = (_Float16)v[i];
-        qhi[tid >> 5][4 * (tid & 31) + i] = a;
-        qlo[tid >> 5][4 * (tid & 31) + i] = (_Float16)(v[i] - (float)a);
+        hv[i] = (_Float16)v[i];
+        lv[i] = (_Float16)(v[i] - (float)hv[i]);
       }
+      *reinterpret_cast<f16x4*>(&qhi[tid >> 5][4 * (tid & 31)]) = hv;
+      *reinterpret_cast<f16x4*>(&qlo[tid >> 5][4 * (tid & 31)]) = lv;
     }
   }
-  if constexpr (!KV32) {                     // heads g..15 of the operand are zero
-    for (int i = tid; i < (16 - g) * kD; i += kThreads) {
-      qhi[g + i / kD][i % kD] = (_Float16)0.f;
-      qlo[g + i / kD][i % kD] = (_Float16)0.f;
+  if constexpr (!KV32) {                     // heads g..15 of the operand are zero (16-byte stores)
+    for (int i = tid; i < (16 - g) * (kD / 8); i += kThreads) {
+      *reinterpret_cast<u32x4*>(&qhi[g + i / (kD / 8)][8 * (i % (kD / 8))]) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&qlo[g + i / (kD / 8)][8 * (i % (kD / 8))]) = u32x4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();
@@ -345,26 +360,70 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnParams p, const float* __
   }
   __syncthreads();
 
-  // ---- P.V: lane l accumulates dims 2 l, 2 l + 1 over the wave's 4 NP positions (weights read
-  // from LDS as broadcasts, four positions per read); two heads per pass ---------------------------
+  if constexpr (PVM) {
+    // ---- P.V on the matrix cores: O^T (16 dims x 16 heads) += V^T (16 dims x 16 positions) .
+    // P^T (16 positions x 16 heads) per 16-position block of the wave, v_mfma_f32_16x16x16f16.  V^T:
+    // the lane's two dims of every position go to this wave's LDS tile transposed (a dword holds
+    // one dim at two consecutive positions); P^T: the weights from sc as fp16 hi + lo (heads past
+    // g zero), so the product keeps fp32 precision against the exact fp16 V.
 #pragma unroll
-  for (int h0 = 0; h0 < kMaxG; h0 += 2) {             // unrolled: the LDS reads of later pairs overlap
-    if (h0 >= g) break;
-    const int h1 = min(h0 + 1, g - 1);
-    float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
+    for (int i = 0; i < 4 * NP; i += 2) {
+      const uint32_t a = vr[i], b = vr[i + 1];
+      *reinterpret_cast<uint32_t*>(&vt[w][2 * lane][i]) = __builtin_amdgcn_perm(b, a, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&vt[w][2 * lane + 1][i]) = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int hq = lane & 15, kq = 4 * (lane >> 4);
+    f32x4v acc[8];
 #pragma unroll
-    for (int r = 0; r < NP; ++r) {
-      const float4 a0 = *reinterpret_cast<const float4*>(&sc[h0][jw + 4 * r]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&sc[h1][jw + 4 * r]);
-      const float q0[4] = {a0.x, a0.y, a0.z, a0.w}, q1[4] = {a1.x, a1.y, a1.z, a1.w};
+    for (int n = 0; n < 8; ++n) acc[n] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NP / 4; ++kb) {
+      const float4 pp = hq < g ? *reinterpret_cast<const float4*>(&sc[hq][jw + 16 * kb + kq])
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
+      f16x4 ph, pl;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        pv_kv(q0[u], vr[4 * r + u], e0, o0);
-        pv_kv(q1[u], vr[4 * r + u], e1, o1);
+        ph[u] = (_Float16)pv[u];
+        pl[u] = (_Float16)(pv[u] - (float)ph[u]);
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const f16x4 va = *reinterpret_cast<const f16x4*>(&vt[w][16 * n + hq][16 * kb + kq]);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, acc[n], 0, 0, 0);
       }
     }
-    *reinterpret_cast<float2*>(&red[w][h0][2 * lane]) = make_float2(e0, o0);
-    if (h0 + 1 < g) *reinterpret_cast<float2*>(&red[w][h1][2 * lane]) = make_float2(e1, o1);
+    // lane l holds dims 16 n + 4 (l / 16) + r of head l % 16
+    if (hq < g) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4v*>(&red[w][hq][16 * n + kq]) = acc[n];
+    }
+  } else {
+    // ---- P.V: lane l accumulates dims 2 l, 2 l + 1 over the wave's 4 NP positions
+    // (weights read from LDS as broadcasts, four positions per read); two heads per pass
+#pragma unroll
+    for (int h0 = 0; h0 < kMaxG; h0 += 2) {             // unrolled: the LDS reads of later pairs overlap
+      if (h0 >= g) break;
+      const int h1 = min(h0 + 1, g - 1);
+      float e0 = 0.f, o0 = 0.f, e1 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NP; ++r) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&sc[h0][jw + 4 * r]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&sc[h1][jw + 4 * r]);
+        const float q0[4] = {a0.x, a0.y, a0.z, a0.w}, q1[4] = {a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pv_kv(q0[u], vr[4 * r + u], e0, o0);
+          pv_kv(q1[u], vr[4 * r + u], e1, o1);
+        }
+      }
+      *reinterpret_cast<float2*>(&red[w][h0][2 * lane]) = make_float2(e0, o0);
+      if (h0 + 1 < g) *reinterpret_cast<float2*>(&red[w][h1][2 * lane]) = make_float2(e1, o1);
+    }
   }
   __syncthreads();
 
@@ -462,13 +521,15 @@ hipError_t attn_launch_with_rope(const AttnParams& p, const float* rope_cs, hipS
   const int grid = p.B * p.nkv * p.nsplit;
   const KEv e1 = p.nsplit == 1 || p.skip_merge ? ev : ev.first();
   const bool step = p.qkv != nullptr;
-#define VV_ATTN_CASE(NP, KV32)                                                                      \
-  if (step) VV_LAUNCH((k_attn<NP, true, KV32>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);     \
-  else VV_LAUNCH((k_attn<NP, false, KV32>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
+  // the matrix-core P.V takes more LDS: only for grids resident at once with it (<= 2 per CU)
+  const bool pvm = !p.kv_f32 && grid <= 2 * 256;
+#define VV_ATTN_CASE(NP, KV32, PVM)                                                                      \
+  if (step) VV_LAUNCH((k_attn<NP, true, KV32, PVM>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);     \
+  else VV_LAUNCH((k_attn<NP, false, KV32, PVM>), dim3(grid), dim3(kThreads), st, e1, p, rope_cs);
   if (p.split == 64) {
-    if (p.kv_f32) { VV_ATTN_CASE(4, true) } else { VV_ATTN_CASE(4, false) }
+    if (p.kv_f32) { VV_ATTN_CASE(4, true, false) } else if (pvm) { VV_ATTN_CASE(4, false, true) } else { VV_ATTN_CASE(4, false, false) }
   } else {
-    if (p.kv_f32) { VV_ATTN_CASE(8, true) } else { VV_ATTN_CASE(8, false) }
+    if (p.kv_f32) { VV_ATTN_CASE(8, true, false) } else if (pvm) { VV_ATTN_CASE(8, false, true) } else { VV_ATTN_CASE(8, false, false) }
   }
 #undef VV_ATTN_CASE
   hipError_t e = hipGetLastError();
