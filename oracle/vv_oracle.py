@@ -28,7 +28,7 @@ Sources (pages, cited by title and section):
   embeddings tied to the head); Inference section: KV-incremental decoding
   equals full recomputation.
 
-Readings where the pages are silent (each listed with its reason in the design doc):
+Readings where the pages are silent (the plainest reading the rest of the pages support):
 
 * the stored block scale is mean(|W|) = 1/s (the only reading that puts the
   codes in {7,8,9}); mean(|W|) is per projection tensor, the same value in
