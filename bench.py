@@ -185,7 +185,7 @@ def prefill_bench(wl, args):
     cap = max(S, wl.cap)
     t0 = time.time()
     dm = DeviceModel(s, args.seed, max_batch=1, progress=lambda m: None)
-    ds = DeviceState(dm, 1, cap)
+    ds = DeviceState(dm, 1, cap, kv=args.kv)
     emb = synth.fp16_normal(args.seed, synth.GLOBAL_LAYER, synth.T_X, (S, s.hidden))
     x = torch.from_numpy(emb.view(np.int16)).cuda().view(torch.float16)
     torch.cuda.synchronize()
@@ -221,7 +221,7 @@ def prefill_bench(wl, args):
         "data": "synthetic (seeded N(0,0.02) fp32 masters ternarised on the GPU, fp16 N(0,1) prompt embeddings)",
         "config": {"workload": f"prefill-{s.name}-s{S}", "layers": s.layers, "hidden": s.hidden, "inter": s.inter,
                    "n_q": s.n_q, "n_kv": s.n_kv, "vocab": s.vocab, "batch": 1, "prompt": S, "quant": s.mode,
-                   "seed": args.seed},
+                   "kv": args.kv, "seed": args.seed},
         "roofline": {"bound": "mfma", "kernel": "whole prefill (projection GEMMs carry "
                      f"{100 * proj / (proj + attn + lm):.0f}% of the flops)",
                      "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": None,

@@ -12,10 +12,8 @@
 // each wave of a workgroup owns one 64-row tile, all waves share the workgroup's tokens, staged in
 // LDS; per 32-k block a wave turns its tile's block (1 KiB, lane = row) into the four 16-row B
 // operands with the permlane transpose, scales the dequantised codes by the block's fp16 scale and
-// runs v_mfma_f32_16x16x32_f16 against every 16-token group.  The attention of fp16 caches is a
-// matrix-core kernel with an online softmax; with fp32 caches it is the decode step's split-KV
-// kernel with every token as its own "sequence" of length t + 1 over one shared cache, which
-// makes it causal by construction, run in chunks of tokens to bound its workspace.
+// runs v_mfma_f32_16x16x32_f16 against every 16-token group.  The causal attention is a
+// matrix-core kernel with an online softmax, over fp16 caches or (as fp16 hi + lo parts) fp32 ones.
 #include <algorithm>
 
 #include "vv_internal.h"
@@ -25,7 +23,6 @@ namespace vv {
 namespace {
 
 constexpr int kHD = 128;                     // head_dim
-constexpr int kPfAttnChunk = 512;
 #ifndef PF_GEMM_TG
 #define PF_GEMM_TG 4
 #define PF_GEMM_NW 4
@@ -225,11 +222,10 @@ __device__ __forceinline__ void put_kv(void* c, size_t i, float v, bool kv32) {
 }
 
 // RoPE of token t at position t (NeoX rotate-half pairs (j, j + 64), angles in fp64 as in the
-// decode step): q -> qr fp32 [S][nq][128]; k, v -> fp16 (fp32 with kv32) into the cache slot t;
-// lens[t] = t + 1.
+// decode step): q -> qr fp32 [S][nq][128]; k, v -> fp16 (fp32 with kv32) into the cache slot t.
 __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qkv, int nq, int nkv, int cap,
                                                     double theta, float* __restrict__ qr, void* __restrict__ kc,
-                                                    void* __restrict__ vc, int kv32, int32_t* __restrict__ lens) {
+                                                    void* __restrict__ vc, int kv32) {
   __shared__ float cs[64][2];
   const int t = blockIdx.x;
   const int ld = (nq + 2 * nkv) * kHD;
@@ -246,7 +242,6 @@ __global__ __launch_bounds__(256) void k_pf_rope_kv(const float* __restrict__ qk
     cs[threadIdx.x][0] = c;
     cs[threadIdx.x][1] = s;
   }
-  if (threadIdx.x == 0) lens[t] = t + 1;
   __syncthreads();
   for (int idx = threadIdx.x; idx < (nq + nkv) * 64; idx += 256) {
     const int hh = idx >> 6, j = idx & 63;
@@ -308,37 +303,80 @@ __device__ __forceinline__ float groups_sum(float v) {
   return v + __shfl_xor(v, 32, kWave);
 }
 
-__global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ qr, const uint16_t* __restrict__ kc,
-                                                     const uint16_t* __restrict__ vc, int S, int nq, int nkv, int cap,
+// fp16 hi and lo parts of 8 fp32 values, packed in k order
+__device__ __forceinline__ void split8(const u32x4& a, const u32x4& b, u32x4& hi, u32x4& lo) {
+  const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float f = __uint_as_float(v[i]);
+    const _Float16 t = (_Float16)f;
+    h[i] = __builtin_bit_cast(uint16_t, t);
+    l[i] = __builtin_bit_cast(uint16_t, (_Float16)(f - (float)t));
+  }
+  hi = u32x4{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+  lo = u32x4{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
+}
+
+// KV32: fp32 caches.  K and V are staged as fp16 hi + lo parts (Ks/Vt and Kl/Vl), and each product
+// takes the three terms hi.hi, hi.lo, lo.hi (the lo.lo term is below fp32 rounding).
+template <bool KV32>
+__global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ qr, const void* __restrict__ kc,
+                                                     const void* __restrict__ vc, int S, int nq, int nkv, int cap,
                                                      float scale, uint16_t* __restrict__ out) {
   __shared__ __align__(16) uint16_t Ks[2][kFaK][kFaDP];       // [buffer][key][dim]
   __shared__ __align__(16) uint16_t Vt[2][kHD][kFaKP];        // [buffer][dim][permuted key]
+  __shared__ __align__(16) uint16_t Kl[KV32 ? 2 : 1][KV32 ? kFaK : 1][KV32 ? kFaDP : 8];
+  __shared__ __align__(16) uint16_t Vl[KV32 ? 2 : 1][KV32 ? kHD : 1][KV32 ? kFaKP : 8];
+  constexpr int kEsz = KV32 ? 4 : 2;
+  constexpr int kLd = KV32 ? 4 : 2;          // 16-byte loads per row chunk of 8 dims: K, V of two rows
   const int h = blockIdx.y, kvh = h / (nq / nkv);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, grp = lane >> 4;
-  const uint16_t* kbase = kc + (size_t)kvh * cap * kHD;
-  const uint16_t* vbase = vc + (size_t)kvh * cap * kHD;
+  const char* kbase = static_cast<const char*>(kc) + (size_t)kvh * cap * kHD * kEsz;
+  const char* vbase = static_cast<const char*>(vc) + (size_t)kvh * cap * kHD * kEsz;
   // staging: thread -> key pair sp (rows 2 sp, 2 sp + 1) and 8-dim chunk sc; four consecutive
-  // lanes read 64 contiguous bytes of a row.  V goes to LDS transposed, as dwords holding the
-  // pair's two keys of one dimension, at the permuted key position of key 2 sp.
+  // lanes read 64 (fp32: 128) contiguous bytes of a row.  V goes to LDS transposed, as dwords
+  // holding the pair's two keys of one dimension, at the permuted key position of key 2 sp.
   const int sp = lane >> 2, sc = 4 * w + (lane & 3);
   const int kp = 2 * sp;
   const int vpos = 8 * ((kp & 15) >> 2) + 4 * (kp >> 4) + (kp & 3);
-  auto load_blk = [&](int kb, u32x4 (&r)[4]) {
-    const size_t r0 = (size_t)min(kb + kp, S - 1) * kHD + 8 * sc;
-    const size_t r1 = (size_t)min(kb + kp + 1, S - 1) * kHD + 8 * sc;
-    r[0] = *reinterpret_cast<const u32x4*>(kbase + r0);
-    r[1] = *reinterpret_cast<const u32x4*>(kbase + r1);
-    r[2] = *reinterpret_cast<const u32x4*>(vbase + r0);
-    r[3] = *reinterpret_cast<const u32x4*>(vbase + r1);
+  // r: K row 2 sp, K row 2 sp + 1, V row 2 sp, V row 2 sp + 1 (each 8 dims: 1 or 2 loads)
+  auto load_blk = [&](int kb, u32x4 (&r)[2 * kLd]) {
+    const size_t r0 = ((size_t)min(kb + kp, S - 1) * kHD + 8 * sc) * kEsz;
+    const size_t r1 = ((size_t)min(kb + kp + 1, S - 1) * kHD + 8 * sc) * kEsz;
+    const size_t off[4] = {r0, r1, r0, r1};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const char* base = j < 2 ? kbase : vbase;
+#pragma unroll
+      for (int c = 0; c < kLd / 2; ++c) r[j * (kLd / 2) + c] = *reinterpret_cast<const u32x4*>(base + off[j] + 16 * c);
+    }
   };
-  auto stage = [&](int buf, const u32x4 (&r)[4]) {
-    *reinterpret_cast<u32x4*>(&Ks[buf][kp][8 * sc]) = r[0];
-    *reinterpret_cast<u32x4*>(&Ks[buf][kp + 1][8 * sc]) = r[1];
-    const uint32_t a[4] = {r[2].x, r[2].y, r[2].z, r[2].w}, b[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+  auto put_v = [&](uint16_t (*dst)[kFaKP], const u32x4& a4, const u32x4& b4) {
+    const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i)              // (V[2 sp][d], V[2 sp + 1][d]) for d = 8 sc + i
-      *reinterpret_cast<uint32_t*>(&Vt[buf][8 * sc + i][vpos]) =
+      *reinterpret_cast<uint32_t*>(&dst[8 * sc + i][vpos]) =
           __builtin_amdgcn_perm(b[i >> 1], a[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+  };
+  auto stage = [&](int buf, const u32x4 (&r)[2 * kLd]) {
+    if constexpr (KV32) {
+      u32x4 kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
+      split8(r[0], r[1], kh0, kl0);
+      split8(r[2], r[3], kh1, kl1);
+      split8(r[4], r[5], vh0, vl0);
+      split8(r[6], r[7], vh1, vl1);
+      *reinterpret_cast<u32x4*>(&Ks[buf][kp][8 * sc]) = kh0;
+      *reinterpret_cast<u32x4*>(&Ks[buf][kp + 1][8 * sc]) = kh1;
+      *reinterpret_cast<u32x4*>(&Kl[buf][kp][8 * sc]) = kl0;
+      *reinterpret_cast<u32x4*>(&Kl[buf][kp + 1][8 * sc]) = kl1;
+      put_v(Vt[buf], vh0, vh1);
+      put_v(Vl[buf], vl0, vl1);
+    } else {
+      *reinterpret_cast<u32x4*>(&Ks[buf][kp][8 * sc]) = r[0];
+      *reinterpret_cast<u32x4*>(&Ks[buf][kp + 1][8 * sc]) = r[1];
+      put_v(Vt[buf], r[2], r[3]);
+    }
   };
 
   // the workgroup takes query block nqb - 1 - x and then query block x: every workgroup walks
@@ -369,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ q
     for (int n = 0; n < 8; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int kend = min(S, qb + kFaQ);      // keys the block's last query sees
-    u32x4 kv[4];
+    u32x4 kv[2 * kLd];
     load_blk(0, kv);
     stage(0, kv);                            // every wave finished the previous pass before its last barrier
     __syncthreads();
@@ -387,6 +425,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ q
             const half8 kop = *reinterpret_cast<const half8*>(&Ks[buf][16 * nb + (lane & 15)][32 * ks + 8 * grp]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qh[ks], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, ql[ks], acc, 0, 0, 0);
+            if constexpr (KV32) {
+              const half8 klo = *reinterpret_cast<const half8*>(&Kl[buf][16 * nb + (lane & 15)][32 * ks + 8 * grp]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(klo, qh[ks], acc, 0, 0, 0);
+            }
           }
           sT[nb] = acc;
         }
@@ -424,6 +466,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ q
           const half8 vop = *reinterpret_cast<const half8*>(&Vt[buf][16 * n + (lane & 15)][8 * grp]);
           O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, ph, O[n], 0, 0, 0);
           O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pl, O[n], 0, 0, 0);
+          if constexpr (KV32) {
+            const half8 vlo = *reinterpret_cast<const half8*>(&Vl[buf][16 * n + (lane & 15)][8 * grp]);
+            O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, ph, O[n], 0, 0, 0);
+          }
         }
       }
       // the other buffer was last read before the previous barrier
@@ -447,15 +493,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_flash(const float* __restrict__ q
 
 struct PfDims { int L, H, I, nq, nkv, V, S, cap, nqkv; };
 
-struct PfLayout { size_t h, x, act, qkv, qr, o, lens, gf, attn, lm, total; };
+struct PfLayout { size_t h, x, act, qkv, qr, o, gf, lm, total; };
 
-AttnParams pf_attn_params(const PfDims& d) {
-  AttnParams a{};
-  a.B = std::min(d.S, kPfAttnChunk);
-  a.nq = d.nq; a.nkv = d.nkv; a.cap = d.cap;
-  attn_plan(a);
-  return a;
-}
 
 PfLayout pf_layout(const PfDims& d) {
   PfLayout l{};
@@ -468,10 +507,7 @@ PfLayout pf_layout(const PfDims& d) {
   l.qkv = take(S * d.nqkv * 4);
   l.qr = take(S * d.nq * kHD * 4);
   l.o = take(S * d.nq * kHD * 2);
-  l.lens = take(S * 4);
   l.gf = take((size_t)d.H * 4);
-  const AttnParams a = pf_attn_params(d);
-  l.attn = take(attn_workspace_bytes(a.B, d.nq, d.nkv, a.nsplit));
   l.lm = take(lm_workspace_bytes(1, d.V, d.H));
   l.total = off;
   return l;
@@ -550,7 +586,6 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_c
   float* qkv = reinterpret_cast<float*>(w + lay.qkv);
   float* qr = reinterpret_cast<float*>(w + lay.qr);
   uint16_t* o = reinterpret_cast<uint16_t*>(w + lay.o);
-  int32_t* lens = reinterpret_cast<int32_t*>(w + lay.lens);
   float* gf = reinterpret_cast<float*>(w + lay.gf);
   const bool kv32 = kv_dtype == VV_F32;
   const size_t layer_kv_bytes = (size_t)d.nkv * cap * kHD * (kv32 ? 4 : 2);
@@ -576,24 +611,14 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_c
     void* kc = static_cast<char*>(k_cache) + (size_t)l * layer_kv_bytes;
     void* vc = static_cast<char*>(v_cache) + (size_t)l * layer_kv_bytes;
     hipLaunchKernelGGL(k_pf_rope_kv, dim3(S), dim3(256), 0, st, qkv, d.nq, d.nkv, cap, (double)m->rope_theta, qr,
-                       kc, vc, (int)kv32, lens);
+                       kc, vc, (int)kv32);
     VV_HIP(hipGetLastError());
-    if (!kv32) {   // causal attention on the matrix cores: token t attends to 0..t
-      hipLaunchKernelGGL(k_pf_flash, dim3((unsigned)cdiv(cdiv(S, kFaQ), 2), d.nq), dim3(256), 0, st, qr,
-                         static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), S, d.nq, d.nkv, cap,
-                         (float)(1.4426950408889634 / std::sqrt((double)kHD)), o);
+    {  // causal attention on the matrix cores: token t attends to 0..t
+      const dim3 grid((unsigned)cdiv(cdiv(S, kFaQ), 2), d.nq);
+      const float sc = (float)(1.4426950408889634 / std::sqrt((double)kHD));
+      if (kv32) hipLaunchKernelGGL(k_pf_flash<true>, grid, dim3(256), 0, st, qr, kc, vc, S, d.nq, d.nkv, cap, sc, o);
+      else hipLaunchKernelGGL(k_pf_flash<false>, grid, dim3(256), 0, st, qr, kc, vc, S, d.nq, d.nkv, cap, sc, o);
       VV_HIP(hipGetLastError());
-    }
-    for (int c0 = 0; kv32 && c0 < S; c0 += kPfAttnChunk) {   // fp32 caches: the split-KV kernel
-      AttnParams a = pf_attn_params(d);
-      a.B = std::min(kPfAttnChunk, S - c0);
-      attn_set_workspace(a, w + lay.attn);
-      a.q = qr + (size_t)c0 * d.nq * kHD; a.q_f16 = 0;
-      a.lens = lens + c0;
-      a.kc = kc; a.vc = vc; a.kv_shared = 1; a.kv_f32 = kv32;
-      a.scale = 1.0f / sqrtf((float)kHD);
-      a.out = o + (size_t)c0 * d.nq * kHD; a.out_f16 = 1;
-      VV_HIP(attn_launch(a, st));
     }
     {  // o (+residual)
       PfGemm p{};

@@ -184,3 +184,11 @@ def test_prefill_0p5b_width(cuda):
     case = PrefillCase(synth.QWEN2_0P5B, 2, [0, 19], 300, 320)
     case.run()
     _compare(case, case.oracle())
+
+
+@pytest.mark.timeout(600)
+def test_prefill_1p5b_width_fp32_kv(cuda):
+    """fp32 caches at 1.5B width: the causal attention reads K and V as fp16 hi + lo parts."""
+    case = PrefillCase(synth.QWEN2_1P5B, 1, [0, 27], 300, 364, kv="f32")
+    case.run()
+    _compare(case, case.oracle())
