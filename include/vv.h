@@ -25,8 +25,10 @@
  *     *_workspace() query returns, ZERO-FILLED before its first use (vv_workspace_init does this);
  *     every completed call leaves its counters and hand-off slots cleared again (the decode
  *     step also keeps a step counter there, whose tagged words need no clearing), so a workspace
- *     can be reused by later calls on the same stream without re-initialisation.  Two calls that
- *     run concurrently must not share a workspace.
+ *     can be reused without re-initialisation by later calls of the same entry point with the same
+ *     shape arguments on the same stream (vv_prefill: any prompt length S).  Before a workspace
+ *     serves another entry point or other shapes, zero-fill it again.  Two calls that run
+ *     concurrently must not share a workspace.
  *   - Return value: VV_OK or a negative vv_status; vv_last_error() gives a thread-local message.
  */
 #ifndef VV_H
@@ -116,27 +118,43 @@ int vv_repack_int4_tiled(const uint8_t* packed, const uint16_t* scales, int64_t 
                          int64_t row_group, int64_t group_stride, int64_t row_offset,
                          int64_t dst_rows, uint8_t* tiled, uint16_t* tiled_scales, void* stream);
 
-/* Dequantiser: W[n][k] = (q - 8) * scale as fp32 (exact for both modes: a 4-bit integer times an
- * fp16 value needs at most 15 significant bits).  `layout` says how packed/scales are stored;
- * for VV_LAYOUT_TILED, rows 0..N-1 of tiles 0..ceil(N/64)-1 are read. */
+/* Dequantiser (bitnet-onnx page, MatMulNBits note: symmetric block-32 codes with zero point 8
+ * and one fp16 scale per block, so an element's value is (q - 8) * scale; ternary codes give
+ * exactly -scale, 0, +scale, the values the ternarisation paragraph says fp16 holds exactly).
+ *   W[n][k] = (q - 8) * scale as fp32 (exact for both modes: a 4-bit integer times an fp16 value
+ *   needs at most 15 significant bits).  `layout` says how packed/scales are stored; for
+ *   VV_LAYOUT_TILED, rows 0..N-1 of tiles 0..ceil(N/64)-1 are read.  W: device fp32 [N][K].
+ *   Errors: NULL pointers, K % 32, N < 1, unknown layout. */
 int vv_dequant_int4(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int layout,
                     float* W, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * int4 GEMV (MatMulNBits with float activations; bitnet-onnx page: activations run in float).
- *   y[m][n] = sum_k deq(W)[n][k] * x[m][k] + bias[n]
- *   packed/scales: VV_LAYOUT_TILED with ceil(N/64) tiles; x: device fp16 [M][K]; bias: device
- *   fp16 [N] or NULL; y: device [M][N] of y_dtype (VV_F32 or VV_F16).  M in 1..16.
+ * int4 GEMV (MatMulNBits with float activations; bitnet-onnx page: MatMulNBits note for the
+ * weights, ternarisation paragraph: activations run in float).
+ *   y[m][n] = sum_k deq(W)[n][k] * x[m][k] + bias[n], deq(W) = (q - 8) * scale.
+ *   packed/scales in `layout`: VV_LAYOUT_ROWMAJOR (the MatMulNBits bytes [N][K/32][16] and fp16
+ *   scales [N][K/32], e.g. vv_pack_int4's output) or VV_LAYOUT_TILED (ceil(N/64) tiles, the
+ *   decode step's layout, e.g. vv_pack_int4_tiled's or vv_repack_int4_tiled's output).
+ *   x: device fp16 [M][K]; bias: device fp16 [N] or NULL; y: device [M][N] of y_dtype (VV_F32
+ *   or VV_F16).  M in 1..16, K % 32 == 0.  packed and x 16-byte aligned; scales 16-byte aligned
+ *   (tiled) or 2-byte aligned (row-major).
  *   Accumulation is fp32 (products of fp16 x and exact small integers, block sums scaled once).
- *   ws: vv_gemv_int4_workspace(M, N, K) bytes, zero-filled before first use.
+ *   ws: vv_gemv_int4_workspace(M, N, K, layout) bytes, zero-filled before first use (the
+ *   row-major kernel needs no workspace but takes the query's small size for uniformity).
+ *   Errors: NULL pointers, M/N out of range, K % 32, unknown layout or dtype, misalignment,
+ *   small workspace.  The query returns 0 for arguments the call would reject.
  * ------------------------------------------------------------------------------------------- */
-size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K);
+size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K, int layout);
 int vv_gemv_int4(const uint8_t* packed, const uint16_t* scales, const uint16_t* bias,
-                 const uint16_t* x, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
-                 void* ws, size_t ws_bytes, void* stream);
+                 const uint16_t* x, int64_t M, int64_t N, int64_t K, int layout, void* y,
+                 int y_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * GQA decode attention (GroupQueryAttention over a GPU-resident KV cache).
+ * GQA decode attention: the GroupQueryAttention node of each layer ("VibeVoice-1.5B — Current
+ * Status", Done section: one GroupQueryAttention per layer beside its MatMulNBits projections)
+ * over the KV cache of the decoder_step contract (bitnet-onnx page, graph contracts: past K/V
+ * [L,1,kv,P,128] with 128-wide heads), kept on the GPU ("VibeVoice-ASR — ONNX export for
+ * Vernacula", Highlights: device-resident KV instead of host round trips; fp32 attention math).
  *   q: device [B][nq][head_dim] of q_dtype (VV_F32 / VV_F16);
  *   k_cache, v_cache: device fp16 [B][nkv][cap][head_dim];
  *   lens: device int32 [B]; sequence b attends over positions [0, lens[b]) (1 <= lens[b] <= cap,
@@ -186,27 +204,25 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  *   down: H rows, K = I.
  * H and I must be multiples of 64, head_dim 128, nq % nkv == 0, nq/nkv <= 8, cap <= 131072.
  *
- * Two implementations compute the same step (vv_state.path):
- *   VV_PATH_PERSISTENT  all layers in one launch of a single-launch dataflow kernel (at most 32
- *                       layers per launch; its workgroups are the work items in dependency order
- *                       and hand results on through counters in the workspace), then the
- *                       lm_head: batch 1, n_layers >= 1, H <= 4096.  An item waits only for
- *                       items dispatched before it, so it needs no particular residency.  Each
- *                       wait is bounded: a wait that gives up sets a sticky nonzero status word
- *                       instead of hanging (vv_decode_status reads it; clear it with
- *                       vv_workspace_init).
- *   VV_PATH_LAYERED     one launch per stage (1 + 5 L + 1 kernels, plus a split merge per layer
- *                       when the cache is split, except at batch 1 over fp16 caches with at most
- *                       64 splits, where the o projection's launch does the merge): any batch up
- *                       to max_batch.  Its split-K GEMV hand-offs, the fused merge and the lm_head
- *                       argmax also wait on other workgroups; those waits are bounded the same way
- *                       and set the same status word.
- *   VV_PATH_AUTO        the layered path (measured faster on MI355X: 1.62 ms against 3.8 ms for
- *                       the 7B-shaped step; the persistent kernel's waiting items hold the slots
- *                       that the weight streams of later items need).
- * Results of the two paths agree to rounding (the K-splits differ), and each is deterministic.
+ * Two launch plans compute the same step (vv_state.path):
+ *   VV_PATH_LAYERED  one launch per stage: 1 + 5 L + 1 kernels (plus a split merge per layer
+ *                    when the cache is split, except at batch 1 over fp16 caches with at most 64
+ *                    splits, where the o projection's launch does the merge); any batch up to
+ *                    max_batch, fp16 or fp32 caches.
+ *   VV_PATH_CHAINED  two launches per layer: the attention, then one grid running the split
+ *                    merge, o, gate/up, down and the next layer's q|k|v as consecutive segments
+ *                    whose workgroups start their weight streams before their inputs are ready
+ *                    and wait for them on tagged words (1 + 2 L + 1 kernels); batch 1, fp16
+ *                    caches, n_layers >= 1 and 2..128 attention splits (cap 65..8192 positions),
+ *                    else VV_ERR_UNSUPPORTED.
+ *   VV_PATH_AUTO     the layered path (measured faster for the 7B-shaped step).
+ * Both are deterministic; their results agree to rounding (K-splits and merge order differ).
+ * The split-K GEMV hand-offs, the merges, the chained segments and the lm_head argmax wait on
+ * other workgroups of their own launch, only on workgroups with smaller indices; each wait is
+ * bounded: one that gives up sets a sticky nonzero status word in the workspace instead of
+ * hanging (vv_decode_status reads it; vv_workspace_init clears it).
  * ------------------------------------------------------------------------------------------- */
-enum { VV_PATH_AUTO = 0, VV_PATH_LAYERED = 1, VV_PATH_PERSISTENT = 2 };
+enum { VV_PATH_AUTO = 0, VV_PATH_LAYERED = 1, VV_PATH_CHAINED = 2 };
 
 typedef struct vv_layer {
   const uint8_t* qkv_q;   const uint16_t* qkv_s;    /* device, tiled */
@@ -246,13 +262,14 @@ typedef struct vv_state {
                                       used to time the operations of an eager vv_decode_step:
                                       events 2i and 2i+1 receive the start and end times of
                                       operation i's kernels (hipExtLaunchKernel's kernel
-                                      timestamps, not stream markers).  Layered path: prep, then
-                                      per layer qkv, attention (+ split merge), o, gate/up, down,
-                                      then lm_head: 2*(5*n_layers + 2) events.  Persistent path:
-                                      all layers (counter reset + the single-launch kernels),
-                                      then lm_head: 4 events.  NULL disables; graphs reject it. */
+                                      timestamps, not stream markers).  Layered: prep, then
+                                      per layer qkv, attention (+ split merge), o, gate/up,
+                                      down, then lm_head: 2*(5*n_layers + 2) events.  Chained:
+                                      prep + qkv of layer 0, per layer attention and the chained
+                                      launch, then lm_head: 2*(2*n_layers + 2) events.  NULL
+                                      disables; graphs reject it. */
   int n_events;                    /* entries in events */
-  int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_PERSISTENT */
+  int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_CHAINED */
   /* Closed-loop greedy decoding (optional).  With feedback_table set, each step ends with a
    * small kernel that, for every sequence not yet done, records token[b] at history[b][pos[b]]
    * and then either marks the sequence done (token[b] is one of stop_ids) or gathers
@@ -271,21 +288,32 @@ typedef struct vv_state {
   int n_stop;                      /* 0..4 */
   /* KV precision: 0 or VV_F16 = fp16 caches; VV_F32 = fp32 caches (the fp32 KV + attention
    * variant that the ASR-ONNX card reports as its accuracy fix: k, v are stored unrounded, at
-   * twice the cache bytes).  Layered path only. */
+   * twice the cache bytes). */
   int kv_dtype;
 } vv_state;
 
 size_t vv_decode_step_workspace(const vv_model* m, int batch, int cap);
 int vv_decode_step(const vv_model* m, const vv_state* s, void* stream);
+/* The launch plan vv_decode_step takes for m and s: VV_PATH_LAYERED or VV_PATH_CHAINED (what
+ * VV_PATH_AUTO resolves to), or the negative status vv_decode_step would return.  Host only. */
+int vv_decode_path(const vv_model* m, const vv_state* s);
 
 /* Copies the step's sticky status word to *status (host) and waits for the stream: 0 = every
  * bounded wait of every launch so far was satisfied; nonzero = a wait gave up (results of that
  * step and later ones are invalid until vv_workspace_init clears the workspace). */
 int vv_decode_status(const vv_model* m, const vv_state* s, int32_t* status, void* stream);
 
-/* hipGraph capture of one vv_decode_step (one host->GPU crossing per step).  The graph keeps the
- * device pointers of m and s; pos/input_embeds are read from device memory at replay, so one
- * graph serves every step whose shapes and buffers stay the same. */
+/* hipGraph capture of one vv_decode_step: one host->GPU submission per step instead of one per
+ * kernel ("VibeVoice-ASR — ONNX export for Vernacula", Highlights: per-launch overhead, about
+ * 1950 launches of ~7 us each per step, was the largest share of that runtime's decode time).
+ *   create: validates m and s as vv_decode_step does (events must be NULL), captures the step's
+ *     launches and instantiates the graph; *out receives a library-owned handle.  The graph keeps
+ *     the device pointers of m and s (weights, caches, workspace, inputs, outputs): those buffers
+ *     must stay allocated and unmoved until destroy.  pos/input_embeds are read from device memory
+ *     at replay, so one graph serves every step whose shapes and buffers stay the same.
+ *   launch: replays the step on `stream` (asynchronous); destroy: frees the handle (NULL is a
+ *     no-op).  Errors: the vv_decode_step errors at create, VV_ERR_NULL for a NULL handle at
+ *     launch, VV_ERR_HIP if the runtime fails. */
 typedef struct vv_graph vv_graph;
 int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, vv_graph** out);
 int vv_decode_graph_launch(vv_graph* g, void* stream);
@@ -311,6 +339,13 @@ size_t vv_prefill_workspace(const vv_model* m, int S, int cap);
 int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_cache,
                void* v_cache, int cap, int kv_dtype, float* logits, int32_t* token, void* ws,
                size_t ws_bytes, void* stream);
+
+/* Measuring stick: reads `bytes` (a positive multiple of 32768) of device memory at p (16-byte
+ * aligned) once, as a pure stream of 16-byte loads from the whole chip, and stores nothing (sink:
+ * a device uint32 that is written only on a value practically never met).  The time it takes is
+ * the part's streaming-read ceiling, against which the decode kernels' achieved bandwidth can be
+ * read next to the published 8 TB/s. */
+int vv_stream_read(const void* p, size_t bytes, uint32_t* sink, void* stream);
 
 /* Zero-fills a workspace (one fill kernel, capture-safe) */
 int vv_workspace_init(void* ws, size_t ws_bytes, void* stream);

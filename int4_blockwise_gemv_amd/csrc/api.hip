@@ -41,6 +41,25 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev) {
   return hipGetLastError();
 }
 
+// Streaming read of a buffer (a measuring stick for the HBM-bound kernels): workgroup w reads the
+// 32 KiB pieces w, w + grid, ... with eight 16-byte loads per thread in flight (each load
+// instruction of the workgroup covers 4 KiB contiguous) and folds them into an XOR that is stored
+// only on a value practically never met, so the loads are kept and the writes cost nothing.
+constexpr size_t kStreamPiece = 32768;
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ p, size_t npieces,
+                                                     uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  for (size_t pc = blockIdx.x; pc < npieces; pc += gridDim.x) {
+    const u32x4* b = p + pc * (kStreamPiece / 16) + threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(b + j * 256);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 }  // namespace vv
 
 using namespace vv;
@@ -70,6 +89,20 @@ int vv_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (ws_bytes == 0) return VV_OK;
   VV_REQUIRE(ws != nullptr, VV_ERR_NULL, "vv_workspace_init: ws is NULL");
   VV_HIP(fill_zero(ws, ws_bytes, as_stream(stream)));
+  return VV_OK;
+}
+
+int vv_stream_read(const void* p, size_t bytes, uint32_t* sink, void* stream) {
+  clear_error();
+  VV_REQUIRE(p && sink, VV_ERR_NULL, "vv_stream_read: NULL pointer");
+  VV_REQUIRE(bytes > 0 && bytes % kStreamPiece == 0, VV_ERR_RANGE,
+             "vv_stream_read: bytes = %zu is not a positive multiple of 32768", bytes);
+  VV_REQUIRE((reinterpret_cast<uintptr_t>(p) & 15) == 0, VV_ERR_RANGE, "vv_stream_read: p must be 16-byte aligned");
+  const size_t np = bytes / kStreamPiece;
+  const int grid = (int)std::min<size_t>(np, 2048);
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, as_stream(stream), reinterpret_cast<const u32x4*>(p), np,
+                     sink);
+  VV_HIP(hipGetLastError());
   return VV_OK;
 }
 

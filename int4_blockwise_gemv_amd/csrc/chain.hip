@@ -1,0 +1,337 @@
+// Chained launches of the batch-1 decode step: the GEMV stages of a layer run as segments of one
+// grid, so that each stage's weight stream starts while its predecessor is still finishing.
+//
+// The decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts) on the Qwen2 layer
+// of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA, SiLU-gated MLP, residual
+// adds, with the int4 block-32 MatMulNBits projections of the same page.  At batch 1 a layer is
+// ~140 MB of weights against a handful of dependent stages, and a kernel boundary costs about
+// 2 us of idle HBM (the ramp of the next grid and the tail of the last one), so the step runs as
+//   launch 0:      [prep | q|k|v of layer 0]
+//   per layer l:   attention(l)   (its own launch: RoPE, KV append, split records)
+//                  [merge(l) | o(l) | gate/up(l) | down(l) | q|k|v(l+1)]
+//   then the lm_head + argmax.
+// A segment's workgroups issue their weight loads first and then wait for their inputs, which
+// earlier segments of the same grid publish as 64-bit tagged words: a 32-bit tag (the step
+// counter times a stride, plus the layer and stage) and a payload of one fp32 or two fp16
+// values.  A word is stored once per step with a single atomic store, so a reader that sees the
+// expected tag sees the value, and no word ever needs clearing (a stale word carries an older
+// tag).  Progress: a workgroup only waits for workgroups with smaller indices (earlier segments,
+// and within a segment the split-K writers dispatched before their reader on the same XCD), and
+// each XCD dispatches its workgroups in increasing index, so the smallest unfinished workgroup
+// always runs to completion.  Every wait is bounded: one that gives up sets the step's status
+// word and continues with NaN instead of hanging.
+#include "vv_internal.h"
+#include "gemv_core.h"
+
+namespace vv {
+namespace {
+
+constexpr int kCW = kChainWaves;           // waves per workgroup
+constexpr int kCT = kCW * kWave;           // threads per workgroup
+constexpr int kCItemK = kCW * 8 * kBlock;  // K elements per workgroup at most (8 groups of 8 blocks)
+
+union CLds {
+  struct { uint16_t xs[kCItemK]; float red[kCW][kWave]; } g;
+  struct { float pm[kCW], pl[kCW]; float po[kCW][kWave]; } m;
+};
+
+__device__ __forceinline__ uint64_t tag_f32(uint32_t tag, float v) {
+  return ((uint64_t)tag << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ uint64_t tag_h2(uint32_t tag, uint16_t lo, uint16_t hi) {
+  return ((uint64_t)tag << 32) | lo | ((uint32_t)hi << 16);
+}
+__device__ __forceinline__ bool has_tag(uint64_t v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
+__device__ __forceinline__ void give_up(int32_t* status) {
+  __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every lane of the wave reloads its word until all carry `tag` (bounded); returns the word
+__device__ __forceinline__ uint64_t wait_word(const uint64_t* p, uint64_t v, uint32_t tag, int32_t* status) {
+  for (uint32_t it = 0; !__all(has_tag(v, tag)); ++it) {
+    if (it >= kSpinLimit) {
+      give_up(status);
+      return tag_f32(tag, __builtin_nanf(""));
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = collect_u64(p);
+  }
+  return v;
+}
+
+// ---- prep: embeddings -> residual stream (layer 0's input), RMSNorm_1 numerator, sum(h^2) per
+// tile, the RoPE table of the new position ----------------------------------------------------
+__device__ void seg_prep(const ChainParams& P, int bid, uint32_t ebase) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int t = bid * kCW + w;
+  const uint32_t tag = ebase + P.prep_add;
+  if (t < P.H / kTileRows) {
+    const int n = t * kTileRows + lane;
+    const float hv = h2f(P.emb[n]);
+    publish_u64(P.h + n, tag_f32(tag, hv));
+    if (P.trace0) P.trace0[n] = hv;
+    const uint16_t gv = f2h(h2f(P.g1[n]) * hv);
+    const uint16_t gh = (uint16_t)__shfl_down((int)gv, 1, kWave);
+    if ((lane & 1) == 0) publish_u64(P.xq + n / 2, tag_h2(tag, gv, gh));
+    const float ss = wave_sum(hv * hv);
+    if (lane == 0) publish_u64(P.ssq + t, tag_f32(tag, ss));
+  }
+  if (bid == 0 && w == 0 && P.rope_on) {
+    // angle pos * theta^(-2i/128) (the inverse frequency computed on the host in fp64), reduced in
+    // fp64 to a fraction of a turn in [-1/2, 1/2]; cos and sin of that fraction come from the
+    // hardware's turn-based v_cos_f32 / v_sin_f32 (absolute error ~1e-6 for these arguments)
+    int pp = P.pos[0];
+    pp = pp < 0 ? 0 : (pp >= P.cap ? P.cap - 1 : pp);
+    const double turns = (double)pp * P.inv_freq[lane] * 0.15915494309189535;   // 1 / (2 pi)
+    const float f = (float)(turns - rint(turns));
+    P.rope[lane * 2] = __builtin_amdgcn_cosf(f);
+    P.rope[lane * 2 + 1] = __builtin_amdgcn_sinf(f);
+  }
+}
+
+// ---- merge of the attention's split records: one workgroup per query head; waves 0-3 take dims
+// 0-63 and waves 4-7 dims 64-127, wave w & 3 splits 32 (w & 3) .. + 31 (all 32 record loads of a
+// lane in flight at once); the four quarters of each half meet in LDS ---------------------------
+__device__ void seg_merge(const ChainParams& P, int bid, uint32_t ebase, CLds& L) {
+  const int h = bid;
+  if (h >= P.nq) return;
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int half = w >> 2, qt = w & 3;
+  const int g = P.nq / P.nkv, kvh = h / g, hh = h % g;
+  const int n = attn_splits(P.pos, nullptr, 0, P.cap, P.split);
+  const int d = 64 * half + lane;
+  const float* rec0 = P.part + ((size_t)kvh * P.nsplit * kAttnMaxG + hh) * kAttnRec;
+  const size_t stride = (size_t)kAttnMaxG * kAttnRec;
+  const int s0 = 32 * qt;
+  float v[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) v[u] = rec0[(size_t)min(s0 + u, n - 1) * stride + 4 + d];
+  const int sl = min(s0 + (lane & 31), n - 1);
+  const float ms = rec0[(size_t)sl * stride], ls = rec0[(size_t)sl * stride + 1];
+  const bool mine = lane < 32 && s0 + lane < n;
+  const float Mw = wave_max(mine ? ms : -INFINITY);
+  const float e = mine ? expf(ms - Mw) : 0.f;
+  const float Lw = wave_sum(mine ? e * ls : 0.f);
+  float Ow = 0.f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const float eu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), u));
+    Ow = fmaf(eu, v[u], Ow);              // e_u = 0 past the quarter's last split
+  }
+  if (lane == 0) {
+    L.m.pm[w] = Mw;
+    L.m.pl[w] = Lw;
+  }
+  L.m.po[w][lane] = Ow;
+  __syncthreads();
+  if (qt != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) M = fmaxf(M, L.m.pm[w + k]);    // finite: quarter 0 holds split 0
+  float O = 0.f, Ls = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float pmk = L.m.pm[w + k];
+    const float f = pmk == -INFINITY ? 0.f : expf(pmk - M);   // a quarter past the sequence: 0
+    O = fmaf(f, L.m.po[w + k][lane], O);
+    Ls = fmaf(f, L.m.pl[w + k], Ls);
+  }
+  const uint16_t o16 = f2h(O / Ls);
+  const uint16_t oh = (uint16_t)__shfl_down((int)o16, 1, kWave);
+  const uint32_t tag = ebase + P.mrg_add;
+  if ((lane & 1) == 0) publish_u64(P.xo + ((size_t)h * 128 + d) / 2, tag_h2(tag, o16, oh));
+  if (lane == 0) publish_u64(P.xo_gate + 2 * h + half, tag_f32(tag, 0.f));   // this half is out
+}
+
+// ---- one GEMV segment (batch 1): the decomposition, dequantisation and split-K hand-off of the
+// layered GEMV kernel, with tagged inputs and outputs --------------------------------------------
+template <int EPI>
+__device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t ebase, CLds& L) {
+  const int K = g.K, nb = K / kBlock, ng = (nb + 7) / 8, W = g.wpg;
+  int tile, kg;
+  if (!split_role(g.ntiles, g.wpt, tile, kg, bid)) return;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int e0 = kg * W * 8 * kBlock;
+  const bool active = w < W;
+
+  // epilogue operands, loaded before the weights (their tags are checked where they are used)
+  const int n = EPI == EPI_SILU ? tile * 32 + (lane & 31) : tile * kTileRows + lane;
+  const int nc = min(n, g.N - 1);
+  uint64_t ssv = 0, hv = 0;
+  if (EPI != EPI_RESID) ssv = collect_u64(g.ssin + min(lane, g.ss_n - 1));
+  if (EPI == EPI_RESID) hv = collect_u64(P.h + nc);
+  const uint32_t p16 = EPI == EPI_STORE ? g.bias[nc * g.has_bias] : EPI == EPI_RESID ? g.gamma[nc] : 0u;
+
+  // this wave's group: 8 blocks and their 8 scales (scales first: block 0 needs them).  No load
+  // sits behind a branch (a load whose result merges with a default at a join makes the compiler
+  // wait for every load issued so far): a wave past the workgroup's W groups re-reads the last
+  // block of the group before it, 1 KiB that its neighbour is fetching anyway, and gets scale 0.
+  const int grp = kg * W + min(w, W - 1);
+  const int b0 = active ? grp * 8 : min(grp * 8 + 7, nb - 1);
+  const int bstep = active ? 1 : 0;
+  const int nblk = active ? min(max(nb - b0, 0), 8) : 0;
+  const u32x4* qt = g.q + (size_t)tile * nb * kTileRows + lane;
+  const u32x4 sv = __builtin_nontemporal_load(g.s + ((size_t)tile * ng + min(grp, ng - 1)) * kTileRows + lane);
+  u32x4 wv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + bstep * i, nb - 1) * kTileRows);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The activation slice: two tagged words (four fp16) per thread, loaded once right behind the
+  // weight loads.  Waiting is done by wave 0 alone, on the slice's gate words (one per producer
+  // tile or attention head-half, each stored after its producer's data words), so that the many
+  // workgroups that wait for an earlier segment re-read a few words per round rather than their
+  // whole slice; the other waves wait at the barrier.  A data word still stale after its gate
+  // opened (the gate's store became visible first) is reloaded.
+  const int ec = min(e0 + 4 * tid, K - 4);
+  const uint32_t xtag = ebase + g.xin_add;
+  const uint64_t* xp = g.xin + ec / 2;
+  uint64_t t0 = collect_u64(xp), t1 = collect_u64(xp + 1);
+  if (w == 0) {
+    const int ga = e0 / g.gate_span;
+    const int gn = min((e0 + W * 8 * kBlock + g.gate_span - 1) / g.gate_span, K / g.gate_span) - ga;
+    const uint64_t* gp = g.gate + ga + min(lane, gn - 1);
+    wait_word(gp, collect_u64(gp), xtag, P.status);
+  }
+  __syncthreads();
+  for (uint32_t it = 0; !__all(has_tag(t0, xtag) && has_tag(t1, xtag)); ++it) {
+    if (it >= kSpinLimit) {
+      give_up(P.status);
+      t0 = t1 = 0x7e007e00u;          // fp16 NaN pairs
+      break;
+    }
+    if (it) __builtin_amdgcn_s_sleep(2);
+    t0 = collect_u64(xp);
+    t1 = collect_u64(xp + 1);
+  }
+  *reinterpret_cast<uint2*>(&L.g.xs[4 * tid]) = make_uint2((uint32_t)t0, (uint32_t)t1);
+  __syncthreads();
+
+  float acc = 0.f;
+  {
+    const uint32_t m64 = vconst(0x54005400u);
+    const int xb0 = w * 8 * kBlock;
+    const u32x4 cx = *reinterpret_cast<const u32x4*>(&L.g.xs[xb0 + min(lane, 31) * 8]);
+    const float corr = quad_sum(corr_quarter(cx));   // lane 4i + q: quarter q of block i
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
+      const uint32_t dw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+      const u32x4* xb = reinterpret_cast<const u32x4*>(&L.g.xs[xb0 + i * kBlock]);
+      float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr), 4 * i));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 xv = xb[k];
+        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+        t = dot8_pairs(dw[k], x4, t, m64);
+      }
+      acc = fmaf(sc, t, acc);
+    }
+  }
+  L.g.red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  float tot = 0.f;
+  for (int v = 0; v < W; ++v) tot += L.g.red[v][lane];
+  if (g.wpt > 1) {
+    const int nw = g.wpt - 1;
+    uint64_t* sl = g.slots + (size_t)tile * nw * kTileRows;
+    if (kg < nw) {   // writer: tagged partial into the tile's slot kg, then done
+      publish_u64(&sl[(size_t)kg * kTileRows + lane], kFresh | __float_as_uint(tot));
+      return;
+    }
+    tot = poll_sum(sl + lane, nw, kTileRows, P.status) + tot;
+  }
+
+  const uint32_t otag = ebase + g.out_add;
+  if (EPI == EPI_STORE || EPI == EPI_SILU) {
+    ssv = wait_word(g.ssin + min(lane, g.ss_n - 1), ssv, ebase + g.ss_add, P.status);
+    const float part = lane < g.ss_n ? __uint_as_float((uint32_t)ssv) : 0.f;
+    const float rs = 1.0f / sqrtf(wave_sum(part) * P.inv_h + P.eps);
+    if (EPI == EPI_STORE) {
+      const float bias = g.has_bias ? h2f((uint16_t)p16) : 0.f;
+      if (n < g.N) g.y[n] = tot * rs + bias;
+    } else {   // lanes 0-31: gate rows, 32-63: the same up rows
+      const float gt = tot * rs;
+      const float u = __shfl(tot, (lane & 31) + 32, kWave) * rs;
+      const uint16_t a16 = f2h(silu(gt) * u);
+      const uint16_t ah = (uint16_t)__shfl_down((int)a16, 1, kWave);
+      if (lane < 32 && (lane & 1) == 0 && n < g.N) publish_u64(g.act + n / 2, tag_h2(otag, a16, ah));
+      if (lane == 0) publish_u64(g.act_gate + tile, tag_f32(otag, 0.f));     // this tile's outputs are out
+    }
+  } else {   // EPI_RESID: h += tot; the next norm's numerator and sum(h^2) of the tile
+    hv = wait_word(P.h + nc, hv, ebase + g.hin_add, P.status);
+    const float hn = __uint_as_float((uint32_t)hv) + tot;
+    publish_u64(P.h + n, tag_f32(otag, hn));
+    if (g.trace) g.trace[n] = hn;
+    const float gv = h2f((uint16_t)p16) * hn;
+    if (g.gf) g.gf[n] = gv;
+    const float ss = wave_sum(hn * hn);
+    if (g.sumsq && lane == 0) g.sumsq[tile] = ss;
+    if (g.xgout) {
+      const uint16_t g16 = f2h(gv);
+      const uint16_t gh = (uint16_t)__shfl_down((int)g16, 1, kWave);
+      if ((lane & 1) == 0) publish_u64(g.xgout + n / 2, tag_h2(otag, g16, gh));
+      if (lane == 0) publish_u64(g.ssout + tile, tag_f32(otag, ss));
+    }
+  }
+}
+
+// 8 waves per SIMD (at most 64 VGPRs): the weight streams of the GEMV segments need the
+// occupancy.  The segments sit at fixed positions (FIRST: prep, q|k|v; else merge, o, gate/up,
+// down and, unless nseg == 4, q|k|v), so every segment field is read at a constant offset.
+template <bool FIRST>
+__global__ __launch_bounds__(kCT, 8) void k_chain(ChainParams P) {
+  __shared__ CLds L;
+  const uint32_t ebase = P.epoch[0] * P.tag_mul;
+  int b = blockIdx.x;
+  if (FIRST) {
+    if (b < P.seg[0].blocks) {
+      seg_prep(P, b, ebase);
+      return;
+    }
+    seg_gemv<EPI_STORE>(P, P.seg[1], b - P.seg[0].blocks, ebase, L);
+    return;
+  }
+  if (b < P.seg[0].blocks) {
+    seg_merge(P, b, ebase, L);
+    return;
+  }
+  b -= P.seg[0].blocks;
+  if (b < P.seg[1].blocks) {
+    seg_gemv<EPI_RESID>(P, P.seg[1], b, ebase, L);
+    return;
+  }
+  b -= P.seg[1].blocks;
+  if (b < P.seg[2].blocks) {
+    seg_gemv<EPI_SILU>(P, P.seg[2], b, ebase, L);
+    return;
+  }
+  b -= P.seg[2].blocks;
+  if (b < P.seg[3].blocks) {
+    seg_gemv<EPI_RESID>(P, P.seg[3], b, ebase, L);
+    return;
+  }
+  b -= P.seg[3].blocks;
+  if (P.nseg > 4) seg_gemv<EPI_STORE>(P, P.seg[4], b, ebase, L);
+}
+
+}  // namespace
+
+void chain_gemv_plan(CSeg& g) {
+  const int nb = g.K / kBlock;
+  const int ng = (nb + 7) / 8;
+  g.wpt = (ng + kCW - 1) / kCW;
+  g.wpg = (ng + g.wpt - 1) / g.wpt;
+  g.blocks = (int)(cdiv(g.ntiles, kNumXcd) * kNumXcd * g.wpt);
+}
+
+hipError_t chain_launch(const ChainParams& P, hipStream_t st, KEv ev) {
+  int grid = 0;
+  for (int i = 0; i < P.nseg; ++i) grid += P.seg[i].blocks;
+  if (P.seg[0].kind == SEG_PREP) VV_LAUNCH((k_chain<true>), dim3(grid), dim3(kCT), st, ev, P);
+  else VV_LAUNCH((k_chain<false>), dim3(grid), dim3(kCT), st, ev, P);
+  return hipGetLastError();
+}
+
+}  // namespace vv

@@ -422,25 +422,34 @@ using namespace vv;
 
 extern "C" {
 
-size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K) {
+size_t vv_gemv_int4_workspace(int64_t M, int64_t N, int64_t K, int layout) {
   if (M < 1 || M > 16 || N < 1 || K < kBlock || K % kBlock) return 0;
+  if (layout == VV_LAYOUT_ROWMAJOR) return 256;   // the row-major kernel uses none of it
+  if (layout != VV_LAYOUT_TILED) return 0;
   return gemv_workspace_bytes((int)M, (int)cdiv(N, kTileRows), (int)(K / kBlock));
 }
 
 int vv_gemv_int4(const uint8_t* packed, const uint16_t* scales, const uint16_t* bias, const uint16_t* x, int64_t M,
-                 int64_t N, int64_t K, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+                 int64_t N, int64_t K, int layout, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   VV_REQUIRE(packed && scales && x && y, VV_ERR_NULL, "vv_gemv_int4: NULL pointer");
   VV_REQUIRE(M >= 1 && M <= 16, VV_ERR_RANGE, "vv_gemv_int4: M = %lld not in 1..16", (long long)M);
   VV_REQUIRE(N >= 1 && N <= (1 << 26), VV_ERR_RANGE, "vv_gemv_int4: N = %lld out of range", (long long)N);
   VV_REQUIRE(K >= kBlock && K % kBlock == 0 && K <= (1 << 22), VV_ERR_SHAPE,
              "vv_gemv_int4: K = %lld is not a positive multiple of 32 (<= 4M)", (long long)K);
+  VV_REQUIRE(layout == VV_LAYOUT_ROWMAJOR || layout == VV_LAYOUT_TILED, VV_ERR_DTYPE,
+             "vv_gemv_int4: unknown layout %d", layout);
   VV_REQUIRE(y_dtype == VV_F16 || y_dtype == VV_F32, VV_ERR_DTYPE, "vv_gemv_int4: unknown y dtype %d", y_dtype);
-  VV_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(scales) |
-               reinterpret_cast<uintptr_t>(x)) & 15) == 0,
-             VV_ERR_RANGE, "vv_gemv_int4: packed, scales and x must be 16-byte aligned");
-  const size_t need = vv_gemv_int4_workspace(M, N, K);
+  VV_REQUIRE(((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
+                 (reinterpret_cast<uintptr_t>(scales) & (layout == VV_LAYOUT_TILED ? 15 : 1)) == 0,
+             VV_ERR_RANGE, "vv_gemv_int4: packed and x must be 16-byte aligned (tiled scales too, row-major 2)");
+  const size_t need = vv_gemv_int4_workspace(M, N, K, layout);
   VV_REQUIRE(ws && ws_bytes >= need, VV_ERR_WORKSPACE, "vv_gemv_int4: workspace needs %zu bytes", need);
+  if (layout == VV_LAYOUT_ROWMAJOR) {
+    VV_HIP(gemv_rowmajor_launch(packed, scales, bias, x, (int)M, (int)N, (int)K, y, y_dtype == VV_F16,
+                                as_stream(stream)));
+    return VV_OK;
+  }
   GemvParams p{};
   p.q = packed; p.s = scales; p.x = x;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;

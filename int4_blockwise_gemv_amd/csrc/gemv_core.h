@@ -1,6 +1,6 @@
-// Device arithmetic of the int4 block-32 dot product, shared by the GEMV kernels, the persistent
-// decode-step kernel and the prefill GEMM (MatMulNBits block layout, "vibevoice-asr-bitnet-onnx"
-// page, quantisation section: code q = t + 8 in a nibble, one fp16 scale per 32-element block).
+// Device arithmetic of the int4 block-32 dot product, shared by the GEMV kernels and the prefill
+// GEMM (MatMulNBits block layout, "vibevoice-asr-bitnet-onnx" page, quantisation section: code
+// q = t + 8 in a nibble, one fp16 scale per 32-element block).
 #pragma once
 
 #include "vv_internal.h"

@@ -70,6 +70,9 @@ __device__ void argmax_finish(const LmParams& p, int B) {
       p.token[b] = gave_up ? -1 : (int32_t)(0x7fffffffu - (uint32_t)(k & 0x7fffffffu));
     }
   }
+  // the decode step ends here: advance its counter, so the next step's tagged words get new tags
+  // (nothing in this launch reads it; the next step's kernels run after this one)
+  if (p.epoch && tid == 0) p.epoch[0] += 1;
 }
 
 template <int CPL, int BT>
@@ -150,6 +153,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
         for (int j = 0; j < CPL; ++j)
           buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, j * 1024, 2));
       };
+      // chunks past H hold the next row's weights: they are zeroed, not multiplied by x = 0, so a
+      // non-finite weight of one row never reaches another row's sum (0 * NaN would).  Only the
+      // last chunk of a lane can lie past H.
+      const bool tail_live = lane + 64 * (CPL - 1) < nch;
       auto reduce_row = [&](const u32x4 (&buf)[CPL], int row) {
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
@@ -157,7 +164,9 @@ __global__ __launch_bounds__(256) void k_lmhead(LmParams p, const u32x4* __restr
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
-            const uint32_t d4[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
+            const bool live = j + 1 < CPL || tail_live;
+            const uint32_t d4[4] = {live ? buf[j].x : 0u, live ? buf[j].y : 0u, live ? buf[j].z : 0u,
+                                    live ? buf[j].w : 0u};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               a = __builtin_amdgcn_fdot2(as_h2(d4[i]), as_h2(xh[t][j][i]), a, false);
@@ -359,6 +368,8 @@ void lm_plan(LmParams& p) {
 }
 
 // Workspace: one key per (batch row, workgroup).
+bool lm_table_fits(int64_t V, int64_t H) { return V * H * 2 <= kLmMaxTableBytes; }
+
 size_t lm_workspace_bytes(int B, int V, int H) {
   LmParams p{};
   p.B = B; p.V = V; p.H = H;
@@ -408,6 +419,8 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
   VV_REQUIRE(V >= 1, VV_ERR_RANGE, "vv_lm_head_argmax: V = %d < 1", V);
   VV_REQUIRE(H >= 8 && H % 8 == 0 && H <= 8 * 64 * kMaxChunksPerLane, VV_ERR_SHAPE,
              "vv_lm_head_argmax: H = %d must be a multiple of 8 in [8, 4096]", H);
+  VV_REQUIRE(lm_table_fits(V, H), VV_ERR_RANGE, "vv_lm_head_argmax: a %d x %d fp16 table exceeds %lld bytes", V, H,
+             (long long)kLmMaxTableBytes);
   VV_REQUIRE(x_dtype == VV_F16 || x_dtype == VV_F32, VV_ERR_DTYPE, "vv_lm_head_argmax: unknown x dtype");
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(x)) & 15) == 0, VV_ERR_RANGE,
              "vv_lm_head_argmax: W and x must be 16-byte aligned");

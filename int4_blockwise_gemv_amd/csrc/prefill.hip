@@ -23,10 +23,8 @@ namespace vv {
 namespace {
 
 constexpr int kHD = 128;                     // head_dim
-#ifndef PF_GEMM_TG
-#define PF_GEMM_TG 4
-#define PF_GEMM_NW 4
-#endif            // tokens per attention launch
+constexpr int kPfTG = 4;                     // GEMM token groups of 16 per workgroup (64 tokens)
+constexpr int kPfNW = 4;                     // GEMM waves (64-row tiles) per workgroup
 
 struct PfGemm {
   const uint8_t* q; const uint16_t* s;       // tiled int4 weights, ntiles tiles of 64 rows
@@ -501,6 +499,9 @@ PfLayout pf_layout(const PfDims& d) {
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
   const size_t S = d.S;
+  // the argmax keys first: their offset does not depend on S, so a workspace that served a longer
+  // prompt (whose activations sit further on) still holds cleared keys here for a shorter one
+  l.lm = take(lm_workspace_bytes(1, d.V, d.H));
   l.h = take(S * d.H * 4);
   l.x = take(S * d.H * 2);
   l.act = take(S * d.I * 2);
@@ -508,7 +509,6 @@ PfLayout pf_layout(const PfDims& d) {
   l.qr = take(S * d.nq * kHD * 4);
   l.o = take(S * d.nq * kHD * 2);
   l.gf = take((size_t)d.H * 4);
-  l.lm = take(lm_workspace_bytes(1, d.V, d.H));
   l.total = off;
   return l;
 }
@@ -531,7 +531,7 @@ hipError_t pf_gemm_launch(const PfGemm& p, hipStream_t st) {
 }
 template <int EPI>
 hipError_t pf_gemm(const PfGemm& p, hipStream_t st) {
-  return pf_gemm_launch<EPI, PF_GEMM_TG, PF_GEMM_NW>(p, st);
+  return pf_gemm_launch<EPI, kPfTG, kPfNW>(p, st);
 }
 
 }  // namespace
@@ -561,6 +561,8 @@ int vv_prefill(const vv_model* m, const uint16_t* input_embeds, int S, void* k_c
   VV_REQUIRE(m->n_layers >= 0 && m->n_layers <= 4096 && (m->n_layers == 0 || m->layers), VV_ERR_RANGE,
              "vv_prefill: bad layer list");
   VV_REQUIRE(m->gf && m->lm_head && m->vocab >= 1, VV_ERR_NULL, "vv_prefill: gf or lm_head is NULL");
+  VV_REQUIRE(lm_table_fits(m->vocab, m->hidden), VV_ERR_RANGE, "vv_prefill: the %d x %d lm_head exceeds %lld bytes",
+             m->vocab, m->hidden, (long long)kLmMaxTableBytes);
   VV_REQUIRE(S >= 1 && cap >= S && cap <= 131072, VV_ERR_RANGE, "vv_prefill: need 1 <= S <= cap <= 131072");
   VV_REQUIRE(kv_dtype == 0 || kv_dtype == VV_F16 || kv_dtype == VV_F32, VV_ERR_DTYPE,
              "vv_prefill: kv_dtype %d is not VV_F16 or VV_F32", kv_dtype);

@@ -1,9 +1,5 @@
 // Decode-step launcher and its hipGraph wrapper.
 //
-// Two implementations of the same step share the entry points: the persistent kernel of
-// mega.hip (one launch for all layers, then the lm_head; batch 1) and the layered
-// path below (one launch per stage; any batch up to 16).  vv_state.path picks one.
-//
 // decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts):
 //   input_embeds [B,H], position_ids [B], past K/V -> logits [B,V], present K/V (one more slot)
 // on the Qwen2 layer of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA,
@@ -27,16 +23,14 @@ namespace {
 constexpr int kHeadDim = 128;
 
 // h = fp32(input_embeds); g = fp16(gamma * h) (or gf = gamma * h in fp32 when there are no
-// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs; the
-// step counter advances.
+// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs.
 __global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ emb, int H, int ntiles,
                                                   const uint16_t* __restrict__ gamma, float* __restrict__ h,
                                                   uint16_t* __restrict__ g, float* __restrict__ gf,
                                                   float* __restrict__ sumsq, float* __restrict__ trace,
                                                   const int32_t* __restrict__ pos, int cap, double theta,
-                                                  float* __restrict__ rope, uint32_t* __restrict__ epoch) {
+                                                  float* __restrict__ rope) {
   const int t = blockIdx.x % ntiles, b = blockIdx.x / ntiles;
-  if (blockIdx.x == 0 && threadIdx.x == 0) epoch[0] += 1;   // a new step: fresh tags for this step's words
   const int lane = threadIdx.x;
   const int n = t * 64 + lane;
   const size_t i = (size_t)b * H + n;
@@ -91,7 +85,9 @@ __global__ __launch_bounds__(256) void k_feedback(const int32_t* __restrict__ to
 }
 
 struct Layout {
-  size_t h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, otag, epoch, total;
+  size_t status, h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, otag, epoch;
+  size_t th, txq, tssq, txm, tssm, txo, txd, txog, txdg;   // tagged words of the chained path (batch 1)
+  size_t total;
 };
 
 struct Dims {
@@ -112,6 +108,7 @@ Layout layout_of(const Dims& d) {
   Layout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
+  l.status = take(sizeof(int32_t));   // sticky status word: a bounded wait that gave up sets it
   l.h = take((size_t)d.B * d.H * 4);
   l.g = take((size_t)d.B * d.H * 2);
   l.gf = take((size_t)d.B * d.H * 4);
@@ -131,22 +128,42 @@ Layout layout_of(const Dims& d) {
   l.ws_lm = take(lm_workspace_bytes(d.B, d.V, d.H));
   l.otag = take((size_t)d.nq * kHeadDim * sizeof(uint64_t));   // fused merge -> o projection (batch 1)
   l.epoch = take(sizeof(uint32_t));                              // step counter (tags of otag)
+  l.th = take((size_t)d.H * 8);
+  l.txq = take((size_t)d.H / 2 * 8);
+  l.tssq = take((size_t)d.ntH * 8);
+  l.txm = take((size_t)d.H / 2 * 8);
+  l.tssm = take((size_t)d.ntH * 8);
+  l.txo = take((size_t)d.nq * kHeadDim / 2 * 8);
+  l.txd = take((size_t)d.I / 2 * 8);
+  l.txog = take((size_t)d.nq * 2 * 8);
+  l.txdg = take((size_t)2 * d.ntI * 8);
   l.total = off;
   return l;
 }
 
-// bytes of the layered path's region; the persistent region follows it
-size_t layered_bytes(const vv_model* m, int B, int cap) { return align_up(layout_of(dims_of(m, B, cap)).total, 256); }
+size_t step_bytes(const vv_model* m, int B, int cap) { return align_up(layout_of(dims_of(m, B, cap)).total, 256); }
 
-size_t step_bytes(const vv_model* m, int B, int cap) {
-  return layered_bytes(m, B, cap) + persistent_workspace_bytes(m, B, cap);
+// The chained path (two launches per layer) serves batch 1 over fp16 caches with 2..128
+// attention splits; everything else takes the layered path (five launches per layer).
+bool chain_supported(const vv_model* m, const vv_state* s) {
+  if (s->batch != 1 || s->kv_dtype == VV_F32 || m->n_layers < 1) return false;
+  AttnParams a{};
+  a.B = 1; a.nq = m->n_q; a.nkv = m->n_kv; a.cap = s->cap;
+  attn_plan(a);
+  return a.nsplit >= 2 && a.nsplit <= kChainMaxSplits;
 }
 
-// AUTO takes the layered path: on MI355X it is the faster of the two at present (the persistent
-// kernel's per-item hand-offs cost more than the launches they save); see the path notes in vv.h
-bool use_persistent(const vv_model* m, const vv_state* s) {
+// AUTO takes the layered plan: on MI355X it is the faster of the two for the 7B-shaped step
+bool use_chain(const vv_model* m, const vv_state* s) {
   (void)m;
-  return s->path == VV_PATH_PERSISTENT;
+  return s->path == VV_PATH_CHAINED;
+}
+
+// timed operations of one step (two events each): prep, then per layer q|k|v, attention, o,
+// gate/up, down, then the lm_head; chained: prep + q|k|v of layer 0, per layer attention and the
+// chained launch, then the lm_head
+int step_ops(const vv_model* m, const vv_state* s) {
+  return use_chain(m, s) ? 2 * m->n_layers + 2 : 5 * m->n_layers + 2;
 }
 
 int validate(const vv_model* m, const vv_state* s, const char* fn) {
@@ -160,6 +177,8 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(m->n_q >= 1 && m->n_kv >= 1 && m->n_q % m->n_kv == 0 && m->n_q / m->n_kv <= 8, VV_ERR_SHAPE,
              "%s: n_q %% n_kv must be 0 with n_q/n_kv <= 8", fn);
   VV_REQUIRE(m->vocab >= 1, VV_ERR_RANGE, "%s: vocab < 1", fn);
+  VV_REQUIRE(lm_table_fits(m->vocab, m->hidden), VV_ERR_RANGE, "%s: the %d x %d lm_head exceeds %lld bytes", fn,
+             m->vocab, m->hidden, (long long)kLmMaxTableBytes);
   VV_REQUIRE(m->max_batch >= 1 && m->max_batch <= 16, VV_ERR_RANGE, "%s: max_batch not in 1..16", fn);
   VV_REQUIRE(m->eps >= 0.f, VV_ERR_RANGE, "%s: eps < 0", fn);
   VV_REQUIRE(m->gf && m->lm_head, VV_ERR_NULL, "%s: gf or lm_head is NULL", fn);
@@ -183,15 +202,11 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
   VV_REQUIRE(m->n_layers == 0 || (s->k_cache && s->v_cache), VV_ERR_NULL, "%s: KV cache is NULL", fn);
   VV_REQUIRE(((reinterpret_cast<uintptr_t>(s->k_cache) | reinterpret_cast<uintptr_t>(s->v_cache)) & 15) == 0,
              VV_ERR_RANGE, "%s: KV caches must be 16-byte aligned", fn);
-  VV_REQUIRE(s->path == VV_PATH_AUTO || s->path == VV_PATH_LAYERED || s->path == VV_PATH_PERSISTENT, VV_ERR_RANGE,
+  VV_REQUIRE(s->path == VV_PATH_AUTO || s->path == VV_PATH_LAYERED || s->path == VV_PATH_CHAINED, VV_ERR_RANGE,
              "%s: unknown path %d", fn, s->path);
-  VV_REQUIRE(s->path != VV_PATH_PERSISTENT || persistent_supported(m, s->batch), VV_ERR_UNSUPPORTED,
-             "%s: the persistent path needs n_layers >= 1, batch 1, hidden <= 4096", fn);
   VV_REQUIRE(s->n_stop >= 0 && s->n_stop <= 4, VV_ERR_RANGE, "%s: n_stop %d not in 0..4", fn, s->n_stop);
   VV_REQUIRE(s->kv_dtype == 0 || s->kv_dtype == VV_F16 || s->kv_dtype == VV_F32, VV_ERR_DTYPE,
              "%s: kv_dtype %d is not VV_F16 or VV_F32", fn, s->kv_dtype);
-  VV_REQUIRE(s->kv_dtype != VV_F32 || !use_persistent(m, s), VV_ERR_UNSUPPORTED,
-             "%s: fp32 KV caches need the layered path", fn);
   VV_REQUIRE(!s->feedback_table || (reinterpret_cast<uintptr_t>(s->feedback_table) & 15) == 0, VV_ERR_RANGE,
              "%s: feedback_table must be 16-byte aligned", fn);
   const size_t need = step_bytes(m, s->batch, s->cap);
@@ -199,15 +214,19 @@ int validate(const vv_model* m, const vv_state* s, const char* fn) {
              need);
   VV_REQUIRE((reinterpret_cast<uintptr_t>(s->workspace) & 255) == 0, VV_ERR_RANGE,
              "%s: workspace must be 256-byte aligned", fn);
-  const int nev = use_persistent(m, s) ? 2 * 2 : 2 * (5 * m->n_layers + 2);
+  VV_REQUIRE(s->path != VV_PATH_CHAINED || chain_supported(m, s), VV_ERR_UNSUPPORTED,
+             "%s: the chained path needs batch 1, fp16 caches, >= 1 layer and 2..%d attention splits", fn,
+             kChainMaxSplits);
+  const int nev = 2 * step_ops(m, s);
   VV_REQUIRE(!s->events || s->n_events >= nev, VV_ERR_RANGE, "%s: events needs at least %d entries", fn, nev);
   return VV_OK;
 }
 
 int enqueue_lm(const vv_model* m, const vv_state* s, const float* gf32, const float* sumsq, char* ws_lm,
-               int32_t* status, hipStream_t st, KEv ev) {
+               int32_t* status, uint32_t* epoch, hipStream_t st, KEv ev) {
   LmParams p{};
   p.status = status;
+  p.epoch = epoch;
   p.W = m->lm_head; p.V = m->vocab; p.H = m->hidden; p.B = s->batch;
   p.x = gf32; p.x_f16 = 0;
   p.rs_parts = sumsq; p.rs_nparts = m->hidden / kTileRows; p.rs_inv_n = 1.0f / (float)m->hidden; p.eps = m->eps;
@@ -237,22 +256,137 @@ int enqueue_feedback(const vv_model* m, const vv_state* s, hipStream_t st) {
   return VV_OK;
 }
 
-int enqueue_persistent(const vv_model* m, const vv_state* s, hipStream_t st) {
+// The chained path: [prep | q|k|v(0)], then per layer the attention and [merge | o | gate/up |
+// down | q|k|v(l+1)], then the lm_head.  Tags: stage st of layer l is 1 + 4 l + st (st: 0 the
+// q|k|v input and residual, 1 the attention output, 2 the MLP input and residual, 3 SiLU * up),
+// added to epoch * (4 (L + 1) + 1); the epoch advances at the end of every step.
+int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
+  const Dims d = dims_of(m, 1, s->cap);
+  const Layout lay = layout_of(d);
   char* ws = static_cast<char*>(s->workspace);
-  char* pws = ws + layered_bytes(m, s->batch, s->cap);
-  const Layout lay = layout_of(dims_of(m, s->batch, s->cap));
-  int rc = persistent_enqueue(m, s, pws, st, event_pair(s, 0));
-  if (rc) return rc;
-  const float* gf32;
-  const float* sumsq;
-  persistent_lm_inputs(m, s, pws, &gf32, &sumsq);
-  rc = enqueue_lm(m, s, gf32, sumsq, ws + lay.ws_lm, reinterpret_cast<int32_t*>(pws), st, event_pair(s, 1));
+  auto U64 = [&](size_t off) { return reinterpret_cast<uint64_t*>(ws + off); };
+  float* qkv = reinterpret_cast<float*>(ws + lay.qkv);
+  float* gf = reinterpret_cast<float*>(ws + lay.gf);
+  float* sumsq = reinterpret_cast<float*>(ws + lay.sumsq);
+  float* rope = reinterpret_cast<float*>(ws + lay.rope);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + lay.status);
+  uint32_t* epoch = reinterpret_cast<uint32_t*>(ws + lay.epoch);
+  const int L = d.L, H = d.H;
+  auto tagadd = [](int l, int stage) { return (uint32_t)(1 + 4 * l + stage); };
+  enum { XQ = 0, XO = 1, XM = 2, XD = 3 };
+
+  ChainParams base{};
+  base.h = U64(lay.th); base.H = H; base.eps = m->eps; base.inv_h = 1.0f / (float)H;
+  base.epoch = epoch; base.tag_mul = 4u * (uint32_t)(L + 1) + 1u; base.status = status;
+  base.pos = s->pos; base.cap = s->cap;
+
+  AttnParams a{};
+  a.B = 1; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
+  attn_plan(a);
+  attn_set_workspace(a, ws + lay.ws_attn);
+
+  auto gemv_seg = [&](int kind, const uint8_t* q, const uint16_t* sc, int N, int K, int ntiles, size_t slots) {
+    CSeg g{};
+    g.kind = kind;
+    g.q = reinterpret_cast<const u32x4*>(q); g.s = reinterpret_cast<const u32x4*>(sc);
+    g.N = N; g.K = K; g.ntiles = ntiles;
+    g.slots = U64(slots);
+    g.ss_n = d.ntH;
+    chain_gemv_plan(g);
+    return g;
+  };
+  auto qkv_seg = [&](int l) {
+    const vv_layer& y = m->layers[l];
+    CSeg g = gemv_seg(SEG_QKV, y.qkv_q, y.qkv_s, d.nqkv, H, (int)cdiv(d.nqkv, kTileRows), lay.ws_qkv);
+    g.xin = U64(lay.txq); g.xin_add = tagadd(l, XQ);
+    g.gate = U64(lay.tssq); g.gate_span = kTileRows;
+    g.ssin = U64(lay.tssq); g.ss_add = tagadd(l, XQ);
+    g.has_bias = y.qkv_bias != nullptr;
+    g.bias = y.qkv_bias ? y.qkv_bias : y.g1;      // a readable stand-in when there is no bias
+    g.y = qkv;
+    return g;
+  };
+
+  int op = 0;
+  {  // launch 0: prep + q|k|v of layer 0
+    ChainParams P = base;
+    P.prep_add = tagadd(0, XQ);
+    P.emb = s->input_embeds; P.g1 = m->layers[0].g1;
+    P.xq = U64(lay.txq); P.ssq = U64(lay.tssq); P.trace0 = s->h_trace;
+    P.rope_on = m->rope_theta > 0.f;
+    P.rope = rope;
+    for (int i = 0; i < 64; ++i) P.inv_freq[i] = P.rope_on ? pow((double)m->rope_theta, -(double)(2 * i) / 128.0) : 0.0;
+    CSeg pg{};
+    pg.kind = SEG_PREP;
+    pg.blocks = (int)(cdiv(cdiv(d.ntH, kChainWaves), kNumXcd) * kNumXcd);
+    P.seg[0] = pg;
+    P.seg[1] = qkv_seg(0);
+    P.nseg = 2;
+    VV_HIP(chain_launch(P, st, event_pair(s, op++)));
+  }
+  const size_t layer_kv_bytes = (size_t)d.nkv * (size_t)s->cap * kHeadDim * 2;
+  for (int l = 0; l < L; ++l) {
+    const vv_layer& y = m->layers[l];
+    const bool last = l == L - 1;
+    {  // attention with RoPE and KV append; its split records are merged by the next launch
+      AttnParams ap = a;
+      ap.skip_merge = 1;
+      ap.qkv = qkv; ap.ldqkv = d.nqkv; ap.pos = s->pos; ap.rope_theta = m->rope_theta;
+      ap.kc = static_cast<char*>(s->k_cache) + (size_t)l * layer_kv_bytes;
+      ap.vc = static_cast<char*>(s->v_cache) + (size_t)l * layer_kv_bytes;
+      ap.kv_f32 = 0;
+      ap.scale = 1.0f / sqrtf((float)kHeadDim);
+      ap.out = nullptr; ap.out_f16 = 1;
+      VV_HIP(attn_launch_with_rope(ap, rope, st, event_pair(s, op++)));
+    }
+    ChainParams P = base;
+    int ns = 0;
+    {  // merge of the split records: one workgroup per query head
+      P.part = a.part; P.nsplit = a.nsplit; P.split = a.split; P.nq = d.nq; P.nkv = d.nkv;
+      P.xo = U64(lay.txo); P.xo_gate = U64(lay.txog); P.mrg_add = tagadd(l, XO);
+      CSeg mg{};
+      mg.kind = SEG_MERGE;
+      mg.blocks = (int)(cdiv(d.nq, kNumXcd) * kNumXcd);
+      P.seg[ns++] = mg;
+    }
+    {  // o projection + residual -> the MLP's input
+      CSeg g = gemv_seg(SEG_O, y.o_q, y.o_s, H, d.nq * kHeadDim, d.ntH, lay.ws_o);
+      g.xin = U64(lay.txo); g.xin_add = tagadd(l, XO);
+      g.gate = U64(lay.txog); g.gate_span = 64;
+      g.hin_add = tagadd(l, XQ); g.out_add = tagadd(l, XM);
+      g.gamma = y.g2; g.xgout = U64(lay.txm); g.ssout = U64(lay.tssm);
+      P.seg[ns++] = g;
+    }
+    {  // gate/up + SiLU * up
+      CSeg g = gemv_seg(SEG_GU, y.gu_q, y.gu_s, d.I, H, 2 * d.ntI, lay.ws_gu);
+      g.xin = U64(lay.txm); g.xin_add = tagadd(l, XM);
+      g.gate = U64(lay.tssm); g.gate_span = kTileRows;
+      g.ssin = U64(lay.tssm); g.ss_add = tagadd(l, XM);
+      g.act = U64(lay.txd); g.act_gate = U64(lay.txdg); g.out_add = tagadd(l, XD);
+      P.seg[ns++] = g;
+    }
+    {  // down + residual -> the next layer's input (or the lm_head's)
+      CSeg g = gemv_seg(SEG_DOWN, y.down_q, y.down_s, H, d.I, d.ntH, lay.ws_down);
+      g.xin = U64(lay.txd); g.xin_add = tagadd(l, XD);
+      g.gate = U64(lay.txdg); g.gate_span = 32;      // a gate/up tile yields 32 outputs
+      g.hin_add = tagadd(l, XM); g.out_add = tagadd(l + 1, XQ);
+      g.gamma = last ? m->gf : m->layers[l + 1].g1;
+      if (!last) { g.xgout = U64(lay.txq); g.ssout = U64(lay.tssq); }
+      else { g.gf = gf; g.sumsq = sumsq; }
+      g.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * H : nullptr;
+      P.seg[ns++] = g;
+    }
+    if (!last) P.seg[ns++] = qkv_seg(l + 1);
+    P.nseg = ns;
+    VV_HIP(chain_launch(P, st, event_pair(s, op++)));
+  }
+  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, status, epoch, st, event_pair(s, op++));
   if (rc) return rc;
   return enqueue_feedback(m, s, st);
 }
 
 int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
-  if (use_persistent(m, s)) return enqueue_persistent(m, s, st);
+  if (use_chain(m, s)) return enqueue_chain_step(m, s, st);
   const Dims d = dims_of(m, s->batch, s->cap);
   const Layout lay = layout_of(d);
   char* ws = static_cast<char*>(s->workspace);
@@ -266,14 +400,13 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   float* rope = reinterpret_cast<float*>(ws + lay.rope);
   const int B = d.B, H = d.H;
   const float inv_h = 1.0f / (float)H;
-  // the step's sticky status word (first word of the persistent region): a GEMV hand-off wait
-  // that gives up sets it
-  int32_t* status = reinterpret_cast<int32_t*>(ws + layered_bytes(m, B, s->cap));
+  // the step's sticky status word: a bounded wait (split-K hand-off, fused merge, argmax) that
+  // gives up sets it
+  int32_t* status = reinterpret_cast<int32_t*>(ws + lay.status);
   int op = 0;   // timing event pair of the next operation
   VV_LAUNCH(k_step_prep, dim3(B * d.ntH), dim3(64), st, event_pair(s, op++), s->input_embeds, H, d.ntH,
             d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
-            s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope,
-            reinterpret_cast<uint32_t*>(ws + lay.epoch));
+            s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
   VV_HIP(hipGetLastError());
 
   const bool kv32 = s->kv_dtype == VV_F32;
@@ -359,7 +492,8 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     }
   }
   // final RMSNorm folded into the lm_head; greedy argmax; closed-loop feedback
-  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, status, st, event_pair(s, op++));
+  const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, status, reinterpret_cast<uint32_t*>(ws + lay.epoch), st,
+                            event_pair(s, op++));
   if (rc) return rc;
   return enqueue_feedback(m, s, st);
 }
@@ -387,11 +521,18 @@ int vv_decode_status(const vv_model* m, const vv_state* s, int32_t* status, void
   clear_error();
   VV_REQUIRE(m && s && status, VV_ERR_NULL, "vv_decode_status: NULL argument");
   VV_REQUIRE(s->workspace && s->batch >= 1 && s->cap >= 1, VV_ERR_RANGE, "vv_decode_status: bad state");
-  const char* pws = static_cast<const char*>(s->workspace) + layered_bytes(m, s->batch, s->cap);
+  const char* pws = static_cast<const char*>(s->workspace) + layout_of(dims_of(m, s->batch, s->cap)).status;
   hipStream_t st = as_stream(stream);
   VV_HIP(hipMemcpyAsync(status, pws, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   VV_HIP(hipStreamSynchronize(st));
   return VV_OK;
+}
+
+int vv_decode_path(const vv_model* m, const vv_state* s) {
+  clear_error();
+  const int rc = validate(m, s, "vv_decode_path");
+  if (rc) return rc;
+  return use_chain(m, s) ? VV_PATH_CHAINED : VV_PATH_LAYERED;
 }
 
 int vv_decode_step(const vv_model* m, const vv_state* s, void* stream) {
@@ -409,8 +550,6 @@ int vv_decode_graph_create(const vv_model* m, const vv_state* s, void* stream, v
   if (rc) return rc;
   VV_REQUIRE(s->events == nullptr, VV_ERR_UNSUPPORTED, "vv_decode_graph_create: timing events are eager-only");
   (void)stream;
-  // size the persistent grid before capturing (the occupancy query is not a stream operation)
-  if (use_persistent(m, s)) VV_REQUIRE(persistent_grid() > 0, VV_ERR_HIP, "vv_decode_graph_create: no resident grid");
   hipStream_t cs;
   VV_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
   hipGraph_t graph = nullptr;

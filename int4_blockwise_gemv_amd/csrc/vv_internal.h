@@ -287,6 +287,9 @@ size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
 hipError_t gemv_launch(const GemvParams& p, hipStream_t st, KEv ev = {});
 hipError_t gemv_mfma_launch(const GemvParams& p, hipStream_t st, KEv ev);   // 5..16 rows (gemv_launch picks it)
+// the stand-alone GEMV on the MatMulNBits row-major bytes (no workspace, 1..16 rows)
+hipError_t gemv_rowmajor_launch(const uint8_t* q, const uint16_t* s, const uint16_t* bias, const uint16_t* x, int M,
+                                int N, int K, void* y, int y_f16, hipStream_t st);
 
 struct AttnParams {
   int B, nq, nkv, cap, split, nsplit;
@@ -320,8 +323,13 @@ struct LmParams {
   float* logits; int32_t* token;
   uint64_t* keys;            // workspace: one key per (batch row, workgroup)
   int32_t* status;           // sticky status word set when a bounded wait gives up, or null
+  uint32_t* epoch;           // decode step counter, advanced by the argmax's last workgroup, or null
   int grid, rows_per_wg;
 };
+// The row-stream kernel addresses the table with 32-bit byte offsets from one buffer resource, so
+// every entry point that runs the lm_head rejects a table larger than this (VV_ERR_RANGE).
+constexpr int64_t kLmMaxTableBytes = 0x7fffffff;
+bool lm_table_fits(int64_t V, int64_t H);
 void lm_plan(LmParams& p);
 size_t lm_workspace_bytes(int B, int V, int H);
 void lm_set_workspace(LmParams& p, void* ws);
@@ -329,11 +337,49 @@ hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev = {});
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev = {});
 
-// persistent (single-launch) decode step; its workspace region starts with a sticky status word
-bool persistent_supported(const vv_model* m, int batch);
-int persistent_grid();   // resident workgroups on the current device (queried once per device)
-size_t persistent_workspace_bytes(const vv_model* m, int batch, int cap);
-int persistent_enqueue(const vv_model* m, const vv_state* s, char* ws, hipStream_t st, KEv ev);
-void persistent_lm_inputs(const vv_model* m, const vv_state* s, char* ws, const float** gf32, const float** sumsq);
+// ---- chained launches of the batch-1 step (chain.hip) ------------------------------------------
+// One grid runs several stages as segments (consecutive ranges of workgroups, each a multiple of 8
+// so that a workgroup's index within its segment keeps its XCD).  Cross-segment data are 64-bit
+// tagged words (tag << 32 | one fp32 or two fp16); a tag is epoch * tag_mul + add.
+constexpr int kChainWaves = 8;        // waves per workgroup
+constexpr int kChainMaxSeg = 5;
+constexpr int kChainMaxSplits = 128;  // attention splits the merge segment takes
+enum ChainSegKind { SEG_PREP = 0, SEG_MERGE, SEG_QKV, SEG_O, SEG_GU, SEG_DOWN };
+struct CSeg {
+  int kind, blocks;
+  // GEMV segments (batch 1, tiled weights; wpt workgroups of wpg waves per tile)
+  const u32x4* q; const u32x4* s;
+  int N, K, ntiles, wpt, wpg;
+  uint64_t* slots;                               // split-K hand-off slots [tile][wpt - 1][64]
+  const uint64_t* xin; uint32_t xin_add;         // tagged input pairs [K / 2]
+  const uint64_t* gate; int gate_span;           // a tagged word per gate_span inputs, stored after them
+  const uint64_t* ssin; uint32_t ss_add; int ss_n;   // QKV, GU: tagged sum(h^2) per tile (rstd)
+  uint32_t hin_add;                              // O, DOWN: tag of the residual they add to
+  uint32_t out_add;                              // tag of the words this segment writes
+  const uint16_t* bias; int has_bias; float* y;  // QKV: fp16 bias (readable stand-in if absent), fp32 out
+  const uint16_t* gamma;                         // O, DOWN: weight of the next RMSNorm
+  uint64_t* xgout; uint64_t* ssout;              // O, DOWN: tagged fp16(gamma * h) pairs, sum(h^2) per tile
+  float* trace; float* gf; float* sumsq;         // DOWN: optional plain copies (trace, lm_head inputs)
+  uint64_t* act; uint64_t* act_gate;             // GU: tagged SiLU(gate) * up pairs [N / 2], a gate per tile
+};
+struct ChainParams {
+  int nseg;
+  CSeg seg[kChainMaxSeg];
+  uint64_t* h;                                   // tagged fp32 residual stream [H]
+  int H;
+  float eps, inv_h;
+  const uint32_t* epoch; uint32_t tag_mul;
+  int32_t* status;
+  // SEG_PREP: embeddings -> h, fp16(g1 * h) pairs, sum(h^2) per tile, the RoPE table
+  uint32_t prep_add;
+  const uint16_t* emb; const uint16_t* g1; uint64_t* xq; uint64_t* ssq; float* trace0;
+  const int32_t* pos; int cap; int rope_on; float* rope;
+  double inv_freq[64];                           // theta^(-2i/128), i = 0..63 (host fp64)
+  // SEG_MERGE: attention split records -> tagged fp16 pairs of the attention output [nq * 64]
+  const float* part; int nsplit, split, nq, nkv;
+  uint64_t* xo; uint64_t* xo_gate; uint32_t mrg_add;   // xo_gate: a word per (head, 64-dim half)
+};
+void chain_gemv_plan(CSeg& g);                  // fills wpt / wpg / blocks from ntiles and K
+hipError_t chain_launch(const ChainParams& P, hipStream_t st, KEv ev = {});
 
 }  // namespace vv

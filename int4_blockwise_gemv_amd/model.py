@@ -183,6 +183,10 @@ class DeviceState:
     def step(self, stream=None):
         vv.decode_step(self.model.struct, self.struct, stream)
 
+    def path(self) -> str:
+        """The launch plan of this state's steps ("layered" or "chained")."""
+        return vv.decode_path(self.model.struct, self.struct)
+
     def status(self, stream=None) -> int:
         return vv.decode_status(self.model.struct, self.struct, stream)
 

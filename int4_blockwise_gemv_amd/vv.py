@@ -18,8 +18,8 @@ VV_ERR_WORKSPACE, VV_ERR_UNSUPPORTED, VV_ERR_HIP = -5, -6, -7
 VV_Q_TERNARY, VV_Q_ABSMAX = 0, 1
 VV_F16, VV_F32 = 1, 2
 VV_LAYOUT_ROWMAJOR, VV_LAYOUT_TILED = 0, 1
-VV_PATH_AUTO, VV_PATH_LAYERED, VV_PATH_PERSISTENT = 0, 1, 2
-PATH = {"auto": VV_PATH_AUTO, "layered": VV_PATH_LAYERED, "persistent": VV_PATH_PERSISTENT}
+VV_PATH_AUTO, VV_PATH_LAYERED, VV_PATH_CHAINED = 0, 1, 2
+PATH = {"auto": VV_PATH_AUTO, "layered": VV_PATH_LAYERED, "chained": VV_PATH_CHAINED}
 MODE = {"ternary": VV_Q_TERNARY, "absmax": VV_Q_ABSMAX}
 
 
@@ -61,14 +61,15 @@ _SIGS = {
     "vv_pack_int4_tiled": (_I, [_P, _I64, _I64, _I, _I64, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "vv_repack_int4_tiled": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "vv_dequant_int4": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
-    "vv_gemv_int4_workspace": (_SZ, [_I64, _I64, _I64]),
-    "vv_gemv_int4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "vv_gemv_int4_workspace": (_SZ, [_I64, _I64, _I64, _I]),
+    "vv_gemv_int4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I, _P, _SZ, _P]),
     "vv_gqa_decode_workspace": (_SZ, [_I, _I, _I, _I]),
     "vv_gqa_decode": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _SZ, _P]),
     "vv_lm_head_argmax_workspace": (_SZ, [_I, _I, _I]),
     "vv_lm_head_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "vv_decode_step_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
     "vv_decode_step": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P]),
+    "vv_decode_path": (_I, [C.POINTER(vv_model), C.POINTER(vv_state)]),
     "vv_decode_status": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), C.POINTER(C.c_int32), _P]),
     "vv_decode_graph_create": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P, C.POINTER(_P)]),
     "vv_decode_graph_launch": (_I, [_P, _P]),
@@ -76,6 +77,7 @@ _SIGS = {
     "vv_prefill_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
     "vv_prefill": (_I, [C.POINTER(vv_model), _P, _I, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "vv_workspace_init": (_I, [_P, _SZ, _P]),
+    "vv_stream_read": (_I, [_P, _SZ, _P, _P]),
     "vv_status_string": (C.c_char_p, [_I]),
     "vv_last_error": (C.c_char_p, []),
     "vv_version": (_I, []),
@@ -170,14 +172,15 @@ def dequant_int4(packed, scales, N, K, layout, out, stream=None):
            "vv_dequant_int4")
 
 
-def gemv_workspace(M, N, K):
-    return lib().vv_gemv_int4_workspace(M, N, K)
+def gemv_workspace(M, N, K, layout=VV_LAYOUT_TILED):
+    return lib().vv_gemv_int4_workspace(M, N, K, layout)
 
 
-def gemv_int4(packed, scales, bias, x, N, K, y, ws, stream=None):
+def gemv_int4(packed, scales, bias, x, N, K, y, ws, stream=None, layout=VV_LAYOUT_TILED):
     M = x.shape[0]
-    _check(lib().vv_gemv_int4(_ptr(packed), _ptr(scales), _ptr(bias), _ptr(x), M, N, K, _ptr(y), _dtype_code(y),
-                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "vv_gemv_int4")
+    _check(lib().vv_gemv_int4(_ptr(packed), _ptr(scales), _ptr(bias), _ptr(x), M, N, K, layout, _ptr(y),
+                              _dtype_code(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "vv_gemv_int4")
 
 
 def gqa_workspace(B, nq, nkv, cap):
@@ -203,6 +206,12 @@ def lm_head_argmax(W, x, logits, token, ws, stream=None):
                                    ws.numel() * ws.element_size(), _stream(stream)), "vv_lm_head_argmax")
 
 
+def stream_read(buf, sink, stream=None):
+    """One streaming read of the whole tensor `buf` (its byte size a multiple of 32768)."""
+    _check(lib().vv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "vv_stream_read")
+
+
 def step_workspace(model: vv_model, batch: int, cap: int) -> int:
     return lib().vv_decode_step_workspace(C.byref(model), batch, cap)
 
@@ -211,8 +220,16 @@ def decode_step(model: vv_model, state: vv_state, stream=None):
     _check(lib().vv_decode_step(C.byref(model), C.byref(state), _stream(stream)), "vv_decode_step")
 
 
+def decode_path(model: vv_model, state: vv_state) -> str:
+    """The launch plan a decode step takes for this model and state ("layered" or "chained")."""
+    rc = lib().vv_decode_path(C.byref(model), C.byref(state))
+    if rc < 0:
+        _check(rc, "vv_decode_path")
+    return {VV_PATH_LAYERED: "layered", VV_PATH_CHAINED: "chained"}[rc]
+
+
 def decode_status(model: vv_model, state: vv_state, stream=None) -> int:
-    """Sticky status word of the persistent path (0 = every in-kernel wait was satisfied)."""
+    """Sticky status word of the step (0 = every bounded in-kernel wait was satisfied)."""
     out = C.c_int32(-1)
     _check(lib().vv_decode_status(C.byref(model), C.byref(state), C.byref(out), _stream(stream)), "vv_decode_status")
     return int(out.value)

@@ -1,6 +1,9 @@
 """Helpers for the GPU parity tests (host <-> device copies and the tiled layout on the host)."""
 import numpy as np
 
+# implementations of the decode step that the step tests run (vv_state.path)
+STEP_PATHS = ["layered", "chained"]
+
 
 def dev(a, device="cuda"):
     import torch

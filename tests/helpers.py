@@ -40,3 +40,27 @@ def scaled_identity_proj(n, c_bits, scale_bits):
     codes = np.full((n, n), 8, np.uint8)
     np.fill_diagonal(codes, c_bits)
     return O.pack_nibbles(codes), np.full((n, n // 32), scale_bits, np.uint16)
+
+
+def _pack_layer_job(args):
+    shape, seed, layer = args
+    return layer, oracle_pack_layer(shape, seed, layer)
+
+
+def oracle_packs_parallel(shape, seed, layer_ids, workers=None):
+    """Oracle packing of several layers in worker processes (spawned: they import only numpy, the
+    oracle and the seeded generators, never the GPU).  Returns {layer: packs}."""
+    import os
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    layer_ids = list(layer_ids)
+    if workers is None:
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            ncpu = os.cpu_count() or 1
+        workers = max(1, min(8, ncpu, len(layer_ids)))
+    if workers == 1:
+        return dict(_pack_layer_job((shape, seed, li)) for li in layer_ids)
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        return dict(ex.map(_pack_layer_job, [(shape, seed, li) for li in layer_ids]))

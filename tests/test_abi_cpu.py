@@ -86,14 +86,32 @@ def test_pack_validation():
 def test_gemv_validation():
     L = _lib()
     d = P(64)
-    assert L.vv_gemv_int4(None, d, None, d, 1, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_NULL
-    assert L.vv_gemv_int4(d, d, None, d, 0, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
-    assert L.vv_gemv_int4(d, d, None, d, 17, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
-    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 48, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_SHAPE
-    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, d, 9, d, 1 << 20, None) == vvmod.VV_ERR_DTYPE
-    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, d, 2, d, 4, None) == vvmod.VV_ERR_WORKSPACE
-    assert L.vv_gemv_int4(P(65), d, None, d, 1, 64, 64, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
-    assert vvmod.gemv_workspace(1, 1536, 1536) > 0
+    T, R = vvmod.VV_LAYOUT_TILED, vvmod.VV_LAYOUT_ROWMAJOR
+    for lay in (T, R):
+        assert L.vv_gemv_int4(None, d, None, d, 1, 64, 64, lay, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_NULL
+        assert L.vv_gemv_int4(d, d, None, d, 0, 64, 64, lay, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+        assert L.vv_gemv_int4(d, d, None, d, 17, 64, 64, lay, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+        assert L.vv_gemv_int4(d, d, None, d, 1, 64, 48, lay, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_SHAPE
+        assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, lay, d, 9, d, 1 << 20, None) == vvmod.VV_ERR_DTYPE
+        assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, lay, d, 2, None, 1 << 20, None) == vvmod.VV_ERR_WORKSPACE
+        assert L.vv_gemv_int4(P(65), d, None, d, 1, 64, 64, lay, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+        assert vvmod.gemv_workspace(1, 1536, 1536, lay) > 0
+    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, T, d, 2, d, 4, None) == vvmod.VV_ERR_WORKSPACE
+    # unknown layout; row-major scales need only 2-byte alignment, tiled ones 16
+    assert L.vv_gemv_int4(d, d, None, d, 1, 64, 64, 5, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_DTYPE
+    assert vvmod.gemv_workspace(1, 64, 64, 5) == 0
+    assert L.vv_gemv_int4(d, P(66), None, d, 1, 64, 64, T, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_gemv_int4(d, P(67), None, d, 1, 64, 64, R, d, 2, d, 1 << 20, None) == vvmod.VV_ERR_RANGE
+
+
+def test_stream_read_validation():
+    L = _lib()
+    d = P(64)
+    assert L.vv_stream_read(None, 32768, d, None) == vvmod.VV_ERR_NULL
+    assert L.vv_stream_read(d, 32768, None, None) == vvmod.VV_ERR_NULL
+    assert L.vv_stream_read(d, 0, d, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_stream_read(d, 32768 + 16, d, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_stream_read(P(72), 32768, d, None) == vvmod.VV_ERR_RANGE
 
 
 def test_gqa_validation():
@@ -166,19 +184,19 @@ def test_decode_step_validation():
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, workspace=300)), None) == vvmod.VV_ERR_RANGE
     evs = (C.c_void_p * 4)()
     ev = C.cast(evs, C.POINTER(C.c_void_p))
-    lay, per = vvmod.VV_PATH_LAYERED, vvmod.VV_PATH_PERSISTENT
-    # a start/stop pair per operation: layered 2 (5 L + 2); persistent 4
+    lay = vvmod.VV_PATH_LAYERED
+    # a start/stop pair per operation: 2 (5 L + 2)
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=4, path=lay)), None) == \
         vvmod.VV_ERR_RANGE
-    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, events=ev, n_events=3, path=per)), None) == \
-        vvmod.VV_ERR_RANGE
-    # unknown path; persistent path with a batch it does not take, or without layers
+    # unknown path; the chained path with a batch, a cache or a KV precision it does not serve
     assert L.vv_decode_step(C.byref(m), C.byref(_state(need, path=7)), None) == vvmod.VV_ERR_RANGE
+    ch = vvmod.VV_PATH_CHAINED
     need3 = vvmod.step_workspace(m, 3, 64)
-    assert L.vv_decode_step(C.byref(m), C.byref(_state(need3, batch=3, path=per)), None) == vvmod.VV_ERR_UNSUPPORTED
-    m0 = _model_struct(n_layers=0)
-    assert L.vv_decode_step(C.byref(m0), C.byref(_state(vvmod.step_workspace(m0, 1, 64), path=per)), None) == \
-        vvmod.VV_ERR_UNSUPPORTED
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need3, batch=3, path=ch)), None) == vvmod.VV_ERR_UNSUPPORTED
+    assert L.vv_decode_step(C.byref(m), C.byref(_state(need, path=ch)), None) == vvmod.VV_ERR_UNSUPPORTED  # 1 split
+    st32 = _state(vvmod.step_workspace(m, 1, 128), cap=128, path=ch)   # 2 splits, but fp32 caches
+    st32.kv_dtype = vvmod.VV_F32
+    assert L.vv_decode_step(C.byref(m), C.byref(st32), None) == vvmod.VV_ERR_UNSUPPORTED
     st = C.c_int32(0)
     assert L.vv_decode_status(None, C.byref(s), C.byref(st), None) == vvmod.VV_ERR_NULL
     assert L.vv_decode_status(C.byref(m), C.byref(s), None, None) == vvmod.VV_ERR_NULL

@@ -173,3 +173,23 @@ def test_lm_head_batched_ties_and_fp16_input(cuda):
     assert list(tok) == [17] * B
     ref, _, _ = O.lm_head_argmax(W, x.astype(np.float32))
     assert rel_err(logits, ref) <= TOL
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_lm_head_nan_rows_never_win(cuda, B):
+    """NaN logits (rows of NaN weights, one of them where the true maximum would be) never win:
+    the token is the argmax over the finite logits (VALU path at B = 1, matrix cores at B = 3)."""
+    H, V = 256, 3000
+    W = synth.fp16_normal(6, 0, synth.T_LM, (V, H), std=0.02)
+    x = synth.fp16_normal(6, 1, synth.T_EMB, (B, H)).astype(np.float32)
+    ref, _, _ = O.lm_head_argmax(W, x)
+    best = [int(np.argmax(ref[b])) for b in range(B)]
+    nan_rows = sorted(set(best + [0, 5, 2999]))
+    W[nan_rows] = np.float16(np.nan)
+    ref[:, nan_rows] = -np.inf
+    logits, tok = _lm_gpu(W, x)
+    assert np.isnan(logits[:, nan_rows]).all()
+    keep = np.setdiff1d(np.arange(V), nan_rows)
+    assert rel_err(logits[:, keep], ref[:, keep]) <= TOL
+    _check_tokens(tok, ref)
+    assert all(int(t) not in nan_rows for t in tok)

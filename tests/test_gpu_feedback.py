@@ -9,7 +9,7 @@ import pytest
 
 from oracle import vv_oracle as O
 from int4_blockwise_gemv_amd import synth
-from gpu_util import host
+from gpu_util import STEP_PATHS, host
 from helpers import oracle_model
 
 pytestmark = pytest.mark.gpu
@@ -41,12 +41,14 @@ def _oracle_loop(m, table, emb, pos, K, V, steps, stops, cap):
     return hist, binding, done, pos
 
 
-@pytest.mark.parametrize("path", ["layered", "persistent"])
+@pytest.mark.parametrize("path", STEP_PATHS)
 def test_closed_loop_greedy_graph(cuda, path):
     import torch
     from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
     steps, cap = 8, 40
-    pos0 = [5] if path == "persistent" else [5, 17, 0]   # the persistent path takes batch 1
+    pos0 = [5, 17, 0] if path == "layered" else [5]   # the chained path serves batch 1
+    if path == "chained":
+        cap = 80                                        # >= 2 attention splits
     B = len(pos0)
     w = synth.Workload("loop", TINY, B, max(pos0), cap, (3,))
     glob = synth.model_globals(TINY, 3, B, True)

@@ -223,3 +223,136 @@ def test_gemv_deterministic(cuda):
     a = _gemv_gpu(q, s, N, K, x)
     b = _gemv_gpu(q, s, N, K, x)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMV on the MatMulNBits row-major bytes (vv_gemv_int4 with VV_LAYOUT_ROWMAJOR)
+# ---------------------------------------------------------------------------------------------
+
+def _gemv_rowmajor_gpu(q, s, N, K, x16, bias16=None, out_f16=False):
+    import torch
+    from int4_blockwise_gemv_amd import vv
+    M = x16.shape[0]
+    lay = vv.VV_LAYOUT_ROWMAJOR
+    ws = torch.zeros(vv.gemv_workspace(M, N, K, lay), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16 if out_f16 else torch.float32, device="cuda")
+    bd = dev(bias16) if bias16 is not None else None
+    vv.gemv_int4(q, s, bd, dev(x16), N, K, y, ws, layout=lay)
+    torch.cuda.synchronize()
+    return host(y).astype(np.float64)
+
+
+@pytest.mark.parametrize("mode", ["ternary", "absmax"])
+@pytest.mark.parametrize("shape", PROJ_SHAPES)
+def test_gemv_rowmajor_projection_shapes(cuda, shape, mode):
+    """The row-major kernel on the GPU packer's MatMulNBits output, every projection shape."""
+    N, K = shape
+    W = synth.master_weight(6, 0, synth.T_V, N, K)
+    x = synth.fp16_normal(6, 0, synth.T_X, (1, K))
+    ref = O.gemv(*O.pack(W, mode), x)
+    q, s = _pack_gpu(W, mode)
+    y = _gemv_rowmajor_gpu(q, s, N, K, x)
+    err = rel_err(y, ref)
+    print(f"row-major gemv {shape} {mode}: max rel err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 16])
+@pytest.mark.parametrize("shape", [(100, 96), (1, 32), (130, 2080), (7, 4096), (256, 8960)])
+def test_gemv_rowmajor_batched_ragged_with_bias(cuda, shape, M):
+    """Ragged rows (not a multiple of the 16 rows of a workgroup), K past one 2048-element chunk
+    and not a multiple of it, batches 1..16, bias, fp32 and fp16 outputs."""
+    N, K = shape
+    W = synth.master_weight(7, 0, synth.T_K, N, K)
+    x = synth.fp16_normal(7, M, synth.T_X, (M, K))
+    b = synth.bias(7, 0, synth.T_BK, N)
+    ref = O.gemv(*O.pack(W, "absmax"), x, b)
+    q, s = _pack_gpu(W, "absmax")
+    assert rel_err(_gemv_rowmajor_gpu(q, s, N, K, x, b), ref) <= TOL
+    assert rel_err(_gemv_rowmajor_gpu(q, s, N, K, x, b, out_f16=True), ref) <= TOL
+
+
+def test_gemv_rowmajor_one_hot_columns_exact(cuda):
+    """x = e_k returns column k of the dequantised matrix exactly: pins the nibble order of the
+    row-major bytes (element 2j low nibble, 2j+1 high nibble) in the kernel's pairing."""
+    N, K = 70, 2112
+    W = synth.master_weight(8, 0, synth.T_O, N, K)
+    pq, ps = O.pack(W, "absmax")
+    deq = O.dequant(pq, ps)
+    q, s = _pack_gpu(W, "absmax")
+    ks = [0, 1, 2, 3, 4, 5, 6, 7, 8, 30, 31, 32, 2047, 2048, 2111]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1
+    for r0 in range(0, len(ks), 16):
+        y = _gemv_rowmajor_gpu(q, s, N, K, x[r0:r0 + 16])
+        for i, k in enumerate(ks[r0:r0 + 16]):
+            assert np.array_equal(y[i], deq[:, k]), k
+
+
+# ---------------------------------------------------------------------------------------------
+# degenerate weights: all-zero tensors and blocks, subnormal scales
+# ---------------------------------------------------------------------------------------------
+
+def test_pack_all_zero_ternary_tensor(cuda):
+    """mean|W| = 0: every code 8, every scale 0 (both layouts); the GEMV then returns the bias."""
+    N, K = 96, 160
+    W = np.zeros((N, K), np.float32)
+    ref_q, ref_s = O.pack(W, "ternary")
+    assert (O.unpack_nibbles(ref_q) == 8).all() and (ref_s == 0).all()
+    q, s = _pack_gpu(W, "ternary")
+    assert np.array_equal(host(q).reshape(ref_q.shape), ref_q)
+    assert np.array_equal(host_u16(s).reshape(ref_s.shape), ref_s)
+    tq, ts = _pack_gpu(W, "ternary", tiled=True)
+    want_q, want_s = codes_to_tiled(O.unpack_nibbles(ref_q), ref_s)
+    assert np.array_equal(host(tq), want_q) and np.array_equal(host_u16(ts), want_s)
+    x = synth.fp16_normal(9, 0, synth.T_X, (2, K))
+    b = synth.bias(9, 0, synth.T_BQ, N)
+    assert np.array_equal(_gemv_gpu(tq, ts, N, K, x, b), np.tile(b.astype(np.float64), (2, 1)))
+    assert np.array_equal(_gemv_rowmajor_gpu(q, s, N, K, x, b), np.tile(b.astype(np.float64), (2, 1)))
+
+
+def test_pack_absmax_all_zero_blocks(cuda):
+    """General int4 with all-zero blocks (scale 0, codes 8), a whole zero row and a block whose
+    only nonzero is a subnormal fp32 (absmax/7 underflows fp16 to 0: codes 8 too)."""
+    N, K = 70, 256
+    W = synth.master_weight(10, 0, synth.T_UP, N, K).copy()
+    W[3, 32:64] = 0.0
+    W[5, :] = 0.0
+    W[9, 0:32] = 0.0
+    W[9, 7] = np.float32(1e-40)
+    W[69, 224:256] = 0.0
+    ref_q, ref_s = O.pack(W, "absmax")
+    assert ref_s[3, 1] == 0 and (ref_s[5] == 0).all() and ref_s[9, 0] == 0
+    assert (O.unpack_nibbles(ref_q)[5] == 8).all()
+    q, s = _pack_gpu(W, "absmax")
+    assert np.array_equal(host(q).reshape(ref_q.shape), ref_q)
+    assert np.array_equal(host_u16(s).reshape(ref_s.shape), ref_s)
+    tq, ts = _pack_gpu(W, "absmax", tiled=True)
+    want_q, want_s = codes_to_tiled(O.unpack_nibbles(ref_q), ref_s)
+    assert np.array_equal(host(tq), want_q) and np.array_equal(host_u16(ts), want_s)
+    x = synth.fp16_normal(10, 0, synth.T_X, (1, K))
+    ref = O.gemv(ref_q, ref_s, x)
+    assert rel_err(_gemv_gpu(tq, ts, N, K, x), ref) <= TOL
+    assert rel_err(_gemv_rowmajor_gpu(q, s, N, K, x), ref) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_gemv_subnormal_scales(cuda, M):
+    """fp16 subnormal block scales (bits 0x0001..0x03ff, values down to 2^-24) are used exactly:
+    both layouts against the oracle's exact dequantisation."""
+    rng = np.random.default_rng(11)
+    N, K = 130, 320
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sbits = rng.integers(1, 0x400, size=(N, K // 32)).astype(np.uint16)
+    sbits[0, 0] = 0x0001
+    sbits[1, :] = 0x03FF
+    pq = O.pack_nibbles(codes)
+    x = synth.fp16_normal(11, M, synth.T_X, (M, K))
+    ref = O.gemv(pq, sbits, x)
+    assert np.max(np.abs(ref)) > 0
+    tq, ts = codes_to_tiled(codes, sbits)
+    y = _gemv_gpu(dev(tq), dev(ts), N, K, x)
+    assert rel_err(y, ref) <= TOL
+    y2 = _gemv_rowmajor_gpu(dev(pq.reshape(-1)), dev(sbits.reshape(-1)), N, K, x)
+    assert rel_err(y2, ref) <= TOL

@@ -192,3 +192,22 @@ def test_prefill_1p5b_width_fp32_kv(cuda):
     case = PrefillCase(synth.QWEN2_1P5B, 1, [0, 27], 300, 364, kv="f32")
     case.run()
     _compare(case, case.oracle())
+
+
+def test_prefill_workspace_reused_for_a_shorter_prompt(cuda):
+    """One state (and so one prefill workspace, sized by the first, longer prompt) serves a 64-token
+    prompt and then a 17-token one: the argmax keys sit at an offset that does not depend on S, so
+    the second call finds them cleared, and both results match the oracle."""
+    import torch
+    case = PrefillCase(TINY, 12, range(2), 64, 96)
+    case.run()
+    _compare(case, case.oracle())
+    short = PrefillCase.__new__(PrefillCase)
+    short.__dict__.update(case.__dict__)
+    short.S = 17
+    short.emb = _prompt(TINY, 13, 17)
+    case.ds.k.zero_()
+    case.ds.v.zero_()
+    torch.cuda.synchronize()
+    short.run()
+    _compare(short, short.oracle())

@@ -1,12 +1,11 @@
-"""GPU parity of the whole decode step (vv_decode_step) against the oracle's decode step, for both
-implementations (the persistent single-launch kernel and the layered one-launch-per-stage path),
-plus graph replay == eager and run-to-run determinism."""
+"""GPU parity of the whole decode step (vv_decode_step) against the oracle's decode step, for every
+implementation of the step (vv_state.path), plus graph replay == eager and run-to-run determinism."""
 import numpy as np
 import pytest
 
 from oracle import vv_oracle as O
 from int4_blockwise_gemv_amd import synth
-from gpu_util import host, host_u16, rel_err
+from gpu_util import STEP_PATHS, host, host_u16, rel_err
 from helpers import oracle_model
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +51,7 @@ class Case:
         import torch
         self.ds.step()
         torch.cuda.synchronize()
-        assert self.ds.status() == 0, "an in-kernel wait of the persistent step gave up"
+        assert self.ds.status() == 0, "a bounded in-kernel wait of the step gave up"
 
 
 def _check_tokens(tok, ref_logits):
@@ -82,12 +81,13 @@ def _compare(case, ref):
             keep = np.ones(case.w.cap, bool)
             keep[p] = False
             assert np.array_equal(gk[i, b][:, keep], case.K[i][b][:, keep].astype(np.float64))
+            assert np.array_equal(gv[i, b][:, keep], case.V[i][b][:, keep].astype(np.float64))
 
 
 TINY = synth.TinyShape(layers=2, hidden=256, n_q=4, n_kv=2, head_dim=128, inter=512, vocab=1000)
 
 
-PATHS = ["persistent", "layered"]
+PATHS = STEP_PATHS
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -114,13 +114,6 @@ def test_step_1p5b_width_fp32_kv(cuda):
     _compare(case, case.oracle())
 
 
-def test_step_persistent_rejects_fp32_kv(cuda):
-    from int4_blockwise_gemv_amd import vv
-    case = Case(TINY, 0, range(2), [5], 16, path="persistent", kv="f32")
-    with pytest.raises(vv.VVError):
-        case.ds.step()
-
-
 def test_step_tiny_batched_layered(cuda):
     case = Case(TINY, 0, range(2), [47, 0, 12], 48, path="layered")
     case.run()
@@ -145,17 +138,11 @@ def test_step_1p5b_width_batch16_ragged(cuda):
     _compare(case, case.oracle())
 
 
-def test_step_persistent_rejects_batch3(cuda):
-    from int4_blockwise_gemv_amd import vv
-    with pytest.raises(vv.VVError) as e:
-        Case(TINY, 0, range(2), [47, 0, 12], 48, path="persistent").run()
-    assert e.value.status == vv.VV_ERR_UNSUPPORTED
-
-
 @pytest.mark.parametrize("path", PATHS)
 def test_step_tiny_absmax_group7(cuda, path):
     shp = synth.TinyShape(layers=3, hidden=384, n_q=7, n_kv=1, head_dim=128, inter=640, vocab=777, mode="absmax")
-    case = Case(shp, 1, range(3), [20] if path == "persistent" else [20, 5], 40, path=path)
+    pos, cap = ([20, 5], 40) if path == "layered" else ([20], 70)   # the chained path: batch 1, >= 2 splits
+    case = Case(shp, 1, range(3), pos, cap, path=path)
     case.run()
     _compare(case, case.oracle())
 
@@ -164,20 +151,24 @@ def test_step_tiny_absmax_group7(cuda, path):
 def test_step_no_rope_no_bias(cuda, path):
     shp = synth.TinyShape(layers=1, hidden=256, n_q=2, n_kv=2, head_dim=128, inter=256, vocab=300, qkv_bias=False,
                           rope_theta=0.0)
-    case = Case(shp, 2, range(1), [9], 16, path=path)
+    case = Case(shp, 2, range(1), [9], 16 if path == "layered" else 80, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
-def test_step_persistent_more_layers_than_one_launch(cuda):
-    """34 layers: the persistent path splits them over two launches (32 + 2)."""
+@pytest.mark.parametrize("path", PATHS)
+def test_step_tiny_34_layers(cuda, path):
+    """34 layers end to end at tiny width: logits, token and every layer's K/V slot against the
+    oracle's 34-layer step, and the residual stream after every layer against the oracle's."""
     shp = synth.TinyShape(layers=34, hidden=256, n_q=4, n_kv=2, head_dim=128, inter=256, vocab=500)
-    case = Case(shp, 6, range(34), [70], 80, path="persistent", trace=True)
+    case = Case(shp, 6, range(34), [70], 80, path=path, trace=True)
     case.run()
-    _compare(case, case.oracle())
-    lay = Case(shp, 6, range(34), [70], 80, path="layered", trace=True)
-    lay.run()
-    assert rel_err(host(case.ds.trace).astype(np.float64), host(lay.ds.trace).astype(np.float64)) <= TOL
+    tr = {}
+    ref = case.oracle(tr)
+    _compare(case, ref)
+    gtr = host(case.ds.trace).astype(np.float64)
+    for li in range(35):
+        assert rel_err(gtr[li], tr["h"][li]) <= TOL, li
 
 
 def test_step_zero_layers(cuda):
@@ -199,7 +190,7 @@ def test_step_1p5b_width_two_layers(cuda, path):
 @pytest.mark.parametrize("seed", range(1, 10))
 def test_step_1p5b_width_seeds(cuda, seed):
     """The other seeds of the 1.5B-shaped workload (two sampled layers each, P = 4096)."""
-    case = Case(synth.QWEN2_1P5B, seed, [seed, 27 - seed], [4096], 4097, path="layered")
+    case = Case(synth.QWEN2_1P5B, seed, [seed, 27 - seed], [4096], 4097, path="auto")
     case.run()
     _compare(case, case.oracle())
 
@@ -217,24 +208,30 @@ def test_step_7b_width_one_layer(cuda, path):
 @pytest.mark.parametrize("seed", range(1, 5))
 def test_step_7b_width_seeds(cuda, seed):
     """The other seeds of the 7B-shaped workload (one sampled layer each, P = 4000)."""
-    case = Case(synth.QWEN2_7B, seed, [3 * seed], [4000], 4001, path="layered")
+    case = Case(synth.QWEN2_7B, seed, [3 * seed], [4000], 4001, path="auto")
     case.run()
     _compare(case, case.oracle())
 
 
-@pytest.mark.parametrize("path,pos", [("layered", [2048, 2048]), ("layered", [2048, 1500]), ("persistent", [2048])])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("pos", [[2048, 2048], [2048, 1500], [2048]])
 def test_step_0p5b_cfg_pair(cuda, path, pos):
     """The Realtime-0.5B shape (hidden 896, 14/2 heads): the lock-step CFG pair (batch 2) and one
     sequence, two sampled layers, full lm_head (not a multiple of 256 wide: the VALU kernel)."""
+    if path == "chained" and len(pos) > 1:
+        pytest.skip("the chained path serves batch 1 (the pair takes the layered path)")
     case = Case(synth.QWEN2_0P5B, 0, [0, 19], pos, 2049, path=path)
     case.run()
     _compare(case, case.oracle())
 
 
-@pytest.mark.parametrize("path,pos", [("layered", [30, 7]), ("persistent", [30])])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("pos", [[30, 7], [30]])
 def test_graph_replay_equals_eager_and_determinism(cuda, path, pos):
     import torch
-    case = Case(TINY, 4, range(2), pos, 40, trace=True, path=path)
+    if path == "chained" and len(pos) > 1:
+        pytest.skip("the chained path serves batch 1")
+    case = Case(TINY, 4, range(2), pos, 40 if path == "layered" else 100, trace=True, path=path)
     case.run()
     ref = [host(case.ds.logits).copy(), host(case.ds.token).copy(), host_u16(case.ds.k).copy(),
            host(case.ds.trace).copy()]
@@ -285,7 +282,8 @@ def test_graph_replay_fused_merge(cuda):
 def test_graph_follows_device_positions(cuda, path):
     """One captured graph serves successive positions: replays at pos, pos+1 == eager steps."""
     import torch
-    case = Case(TINY, 5, range(2), [10], 16, path=path)
+    cap = 16 if path == "layered" else 80
+    case = Case(TINY, 5, range(2), [10], cap, path=path)
     g = case.ds.graph()
     try:
         outs = []
@@ -295,7 +293,7 @@ def test_graph_follows_device_positions(cuda, path):
             torch.cuda.synchronize()
             outs.append(host(case.ds.logits).copy())
         # eager from the same starting cache
-        case2 = Case(TINY, 5, range(2), [10], 16, path=path)
+        case2 = Case(TINY, 5, range(2), [10], cap, path=path)
         for i, p in enumerate((10, 11)):
             case2.ds.pos.fill_(p)
             case2.run()
@@ -304,39 +302,13 @@ def test_graph_follows_device_positions(cuda, path):
         g.close()
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("path", PATHS)
-def test_step_1p5b_full_depth_layerwise(cuda, path):
-    """28 layers at 1.5B width (P = 4096, seed 0): every layer's GPU output h is checked against
-    the oracle layer applied to the GPU's own input h for sampled layers, and the logits against
-    the oracle lm_head on the GPU's final h."""
-    shape = synth.QWEN2_1P5B
-    case = Case(shape, 0, range(shape.layers), [4096], 4097, trace=True, path=path)
-    case.run()
-    tr = host(case.ds.trace).astype(np.float64)
-    assert np.all(np.isfinite(tr))
-    m_all = None
-    for li in (0, 13, 27):
-        m = oracle_model(shape, 0, [li], glob=case.glob)
-        Kc, Vc = [case.K[li].copy()], [case.V[li].copy()]
-        h = O.layer_step(m.layers[0], m, tr[li], case.pos, Kc[0], Vc[0])
-        e = rel_err(tr[li + 1], h)
-        print(f"layer {li}: rel err {e:.2e}")
-        assert e <= TOL
-    m = oracle_model(shape, 0, [], glob=case.glob)
-    f = O.rmsnorm(tr[-1], m.gf, m.eps)
-    logits, _, _ = O.lm_head_argmax(m.lm, f)
-    assert rel_err(host(case.ds.logits)[0], logits[0]) <= TOL
-    _check_tokens(host(case.ds.token), logits)
-
-
 @pytest.mark.parametrize("path", PATHS)
 def test_step_kernel_timing_events(path):
     """Timing events: one start/stop pair per operation, each holding its kernels' own times."""
     import ctypes as C
     import torch
-    case = Case(TINY, 7, range(2), [33], 40, path=path)
-    n_ops = 2 if path == "persistent" else 5 * 2 + 2
+    case = Case(TINY, 7, range(2), [33], 40 if path == "layered" else 100, path=path)
+    n_ops = 5 * 2 + 2 if path == "layered" else 2 * 2 + 2
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)]
     for e in evs:
         e.record()
@@ -357,3 +329,48 @@ def test_step_kernel_timing_events(path):
     ref_logits, _, _, _, _, _ = case.oracle()
     logits = host(case.ds.logits)
     assert rel_err(logits, ref_logits) < TOL
+
+
+@pytest.mark.parametrize("cap", [65, 300, 8192])
+def test_chained_graph_replays_interleaved_with_eager(cuda, cap):
+    """The chained path's tagged words carry the step counter: graph replays interleaved with eager
+    steps give bit-identical results (2, 5 and 128 attention splits: the merge segment's smallest,
+    middle and largest plans), and agree with the oracle and with the layered path."""
+    import torch
+    pos = [cap - 1]
+    case = Case(TINY, 10, range(2), pos, cap, trace=True, path="chained")
+    case.run()
+    ref = [host(case.ds.logits).copy(), host(case.ds.token).copy(), host(case.ds.trace).copy(),
+           host_u16(case.ds.k).copy()]
+    g = case.ds.graph()
+    try:
+        for r in range(5):
+            g.launch()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+            assert np.array_equal(host(case.ds.token), ref[1]), r
+            assert np.array_equal(host(case.ds.trace), ref[2]), r
+            assert np.array_equal(host_u16(case.ds.k), ref[3]), r
+            case.run()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+    finally:
+        g.close()
+    assert case.ds.status() == 0
+    _compare(case, case.oracle())
+    lay = Case(TINY, 10, range(2), pos, cap, trace=True, path="layered")
+    lay.run()
+    assert rel_err(host(case.ds.trace).astype(np.float64), host(lay.ds.trace).astype(np.float64)) <= TOL
+
+
+def test_chained_path_rejects_what_it_does_not_serve(cuda):
+    """Batch 2, a single attention split (cap 64), fp32 caches: VV_ERR_UNSUPPORTED before any launch;
+    AUTO takes the layered path for them."""
+    from int4_blockwise_gemv_amd import vv
+    for pos, cap, kv in (([5, 3], 80, "f16"), ([5], 64, "f16"), ([5], 80, "f32")):
+        case = Case(TINY, 0, range(2), pos, cap, path="chained", kv=kv)
+        with pytest.raises(vv.VVError) as e:
+            case.ds.step()
+        assert e.value.status == vv.VV_ERR_UNSUPPORTED
+        auto = Case(TINY, 0, range(2), pos, cap, path="auto", kv=kv)
+        auto.run()
+        _compare(auto, auto.oracle())
