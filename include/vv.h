@@ -215,7 +215,8 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
  *                    and wait for them on tagged words (1 + 2 L + 1 kernels); batch 1, fp16
  *                    caches, n_layers >= 1 and 2..128 attention splits (cap 65..8192 positions),
  *                    else VV_ERR_UNSUPPORTED.
- *   VV_PATH_AUTO     the layered path (measured faster for the 7B-shaped step).
+ *   VV_PATH_AUTO     the chained path where it applies and hidden <= 2048 (measured faster for
+ *                    the 1.5B-shaped step), else the layered one (faster at the 7B width).
  * Both are deterministic; their results agree to rounding (K-splits and merge order differ).
  * The split-K GEMV hand-offs, the merges, the chained segments and the lm_head argmax wait on
  * other workgroups of their own launch, only on workgroups with smaller indices; each wait is

@@ -139,7 +139,6 @@ __device__ void seg_merge(const ChainParams& P, int bid, uint32_t ebase, CLds& L
   const uint16_t oh = (uint16_t)__shfl_down((int)o16, 1, kWave);
   const uint32_t tag = ebase + P.mrg_add;
   if ((lane & 1) == 0) publish_u64(P.xo + ((size_t)h * 128 + d) / 2, tag_h2(tag, o16, oh));
-  if (lane == 0) publish_u64(P.xo_gate + 2 * h + half, tag_f32(tag, 0.f));   // this half is out
 }
 
 // ---- one GEMV segment (batch 1): the decomposition, dequantisation and split-K hand-off of the
@@ -177,30 +176,21 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + bstep * i, nb - 1) * kTileRows);
   __builtin_amdgcn_sched_barrier(0);
 
-  // The activation slice: two tagged words (four fp16) per thread, loaded once right behind the
-  // weight loads.  Waiting is done by wave 0 alone, on the slice's gate words (one per producer
-  // tile or attention head-half, each stored after its producer's data words), so that the many
-  // workgroups that wait for an earlier segment re-read a few words per round rather than their
-  // whole slice; the other waves wait at the barrier.  A data word still stale after its gate
-  // opened (the gate's store became visible first) is reloaded.
+  // The activation slice: two tagged words (four fp16) per thread, polled after the weight loads
+  // were issued (the first poll returns behind them, so a workgroup whose weights arrive after its
+  // inputs polls once).  (Waiting on a few summary words per producer instead, and reading the
+  // slice once after them, measured slower: the extra round trip lands on every hop.)
   const int ec = min(e0 + 4 * tid, K - 4);
   const uint32_t xtag = ebase + g.xin_add;
   const uint64_t* xp = g.xin + ec / 2;
   uint64_t t0 = collect_u64(xp), t1 = collect_u64(xp + 1);
-  if (w == 0) {
-    const int ga = e0 / g.gate_span;
-    const int gn = min((e0 + W * 8 * kBlock + g.gate_span - 1) / g.gate_span, K / g.gate_span) - ga;
-    const uint64_t* gp = g.gate + ga + min(lane, gn - 1);
-    wait_word(gp, collect_u64(gp), xtag, P.status);
-  }
-  __syncthreads();
   for (uint32_t it = 0; !__all(has_tag(t0, xtag) && has_tag(t1, xtag)); ++it) {
     if (it >= kSpinLimit) {
       give_up(P.status);
       t0 = t1 = 0x7e007e00u;          // fp16 NaN pairs
       break;
     }
-    if (it) __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(2);
     t0 = collect_u64(xp);
     t1 = collect_u64(xp + 1);
   }
@@ -257,7 +247,6 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
       const uint16_t a16 = f2h(silu(gt) * u);
       const uint16_t ah = (uint16_t)__shfl_down((int)a16, 1, kWave);
       if (lane < 32 && (lane & 1) == 0 && n < g.N) publish_u64(g.act + n / 2, tag_h2(otag, a16, ah));
-      if (lane == 0) publish_u64(g.act_gate + tile, tag_f32(otag, 0.f));     // this tile's outputs are out
     }
   } else {   // EPI_RESID: h += tot; the next norm's numerator and sum(h^2) of the tile
     hv = wait_word(P.h + nc, hv, ebase + g.hin_add, P.status);

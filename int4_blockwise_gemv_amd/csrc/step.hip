@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_feedback(const int32_t* __restrict__ to
 
 struct Layout {
   size_t status, h, g, gf, qkv, o, act, sumsq, rope, ws_qkv, ws_o, ws_gu, ws_down, ws_attn, ws_lm, otag, epoch;
-  size_t th, txq, tssq, txm, tssm, txo, txd, txog, txdg;   // tagged words of the chained path (batch 1)
+  size_t th, txq, tssq, txm, tssm, txo, txd;   // tagged words of the chained path (batch 1)
   size_t total;
 };
 
@@ -135,8 +135,6 @@ Layout layout_of(const Dims& d) {
   l.tssm = take((size_t)d.ntH * 8);
   l.txo = take((size_t)d.nq * kHeadDim / 2 * 8);
   l.txd = take((size_t)d.I / 2 * 8);
-  l.txog = take((size_t)d.nq * 2 * 8);
-  l.txdg = take((size_t)2 * d.ntI * 8);
   l.total = off;
   return l;
 }
@@ -153,10 +151,15 @@ bool chain_supported(const vv_model* m, const vv_state* s) {
   return a.nsplit >= 2 && a.nsplit <= kChainMaxSplits;
 }
 
-// AUTO takes the layered plan: on MI355X it is the faster of the two for the 7B-shaped step
+// AUTO takes the chained plan where it serves the state and the model is narrow (hidden <= 2048):
+// there the stages are small and the hops it saves dominate (1.5B-shaped step 893 against 985 us
+// on MI355X); at the 7B width a stage's dequantisation work, released all at once by its
+// dependency instead of overlapping its weight stream, costs more than the launches saved (1632
+// against 1515 us), so the layered plan stays.
+constexpr int kChainAutoMaxHidden = 2048;
 bool use_chain(const vv_model* m, const vv_state* s) {
-  (void)m;
-  return s->path == VV_PATH_CHAINED;
+  if (s->path == VV_PATH_CHAINED) return true;
+  return s->path == VV_PATH_AUTO && m->hidden <= kChainAutoMaxHidden && chain_supported(m, s);
 }
 
 // timed operations of one step (two events each): prep, then per layer q|k|v, attention, o,
@@ -299,7 +302,6 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     const vv_layer& y = m->layers[l];
     CSeg g = gemv_seg(SEG_QKV, y.qkv_q, y.qkv_s, d.nqkv, H, (int)cdiv(d.nqkv, kTileRows), lay.ws_qkv);
     g.xin = U64(lay.txq); g.xin_add = tagadd(l, XQ);
-    g.gate = U64(lay.tssq); g.gate_span = kTileRows;
     g.ssin = U64(lay.tssq); g.ss_add = tagadd(l, XQ);
     g.has_bias = y.qkv_bias != nullptr;
     g.bias = y.qkv_bias ? y.qkv_bias : y.g1;      // a readable stand-in when there is no bias
@@ -343,7 +345,7 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     int ns = 0;
     {  // merge of the split records: one workgroup per query head
       P.part = a.part; P.nsplit = a.nsplit; P.split = a.split; P.nq = d.nq; P.nkv = d.nkv;
-      P.xo = U64(lay.txo); P.xo_gate = U64(lay.txog); P.mrg_add = tagadd(l, XO);
+      P.xo = U64(lay.txo); P.mrg_add = tagadd(l, XO);
       CSeg mg{};
       mg.kind = SEG_MERGE;
       mg.blocks = (int)(cdiv(d.nq, kNumXcd) * kNumXcd);
@@ -352,7 +354,6 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     {  // o projection + residual -> the MLP's input
       CSeg g = gemv_seg(SEG_O, y.o_q, y.o_s, H, d.nq * kHeadDim, d.ntH, lay.ws_o);
       g.xin = U64(lay.txo); g.xin_add = tagadd(l, XO);
-      g.gate = U64(lay.txog); g.gate_span = 64;
       g.hin_add = tagadd(l, XQ); g.out_add = tagadd(l, XM);
       g.gamma = y.g2; g.xgout = U64(lay.txm); g.ssout = U64(lay.tssm);
       P.seg[ns++] = g;
@@ -360,15 +361,13 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     {  // gate/up + SiLU * up
       CSeg g = gemv_seg(SEG_GU, y.gu_q, y.gu_s, d.I, H, 2 * d.ntI, lay.ws_gu);
       g.xin = U64(lay.txm); g.xin_add = tagadd(l, XM);
-      g.gate = U64(lay.tssm); g.gate_span = kTileRows;
       g.ssin = U64(lay.tssm); g.ss_add = tagadd(l, XM);
-      g.act = U64(lay.txd); g.act_gate = U64(lay.txdg); g.out_add = tagadd(l, XD);
+      g.act = U64(lay.txd); g.out_add = tagadd(l, XD);
       P.seg[ns++] = g;
     }
     {  // down + residual -> the next layer's input (or the lm_head's)
       CSeg g = gemv_seg(SEG_DOWN, y.down_q, y.down_s, H, d.I, d.ntH, lay.ws_down);
       g.xin = U64(lay.txd); g.xin_add = tagadd(l, XD);
-      g.gate = U64(lay.txdg); g.gate_span = 32;      // a gate/up tile yields 32 outputs
       g.hin_add = tagadd(l, XM); g.out_add = tagadd(l + 1, XQ);
       g.gamma = last ? m->gf : m->layers[l + 1].g1;
       if (!last) { g.xgout = U64(lay.txq); g.ssout = U64(lay.tssq); }

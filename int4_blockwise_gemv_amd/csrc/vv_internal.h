@@ -352,7 +352,6 @@ struct CSeg {
   int N, K, ntiles, wpt, wpg;
   uint64_t* slots;                               // split-K hand-off slots [tile][wpt - 1][64]
   const uint64_t* xin; uint32_t xin_add;         // tagged input pairs [K / 2]
-  const uint64_t* gate; int gate_span;           // a tagged word per gate_span inputs, stored after them
   const uint64_t* ssin; uint32_t ss_add; int ss_n;   // QKV, GU: tagged sum(h^2) per tile (rstd)
   uint32_t hin_add;                              // O, DOWN: tag of the residual they add to
   uint32_t out_add;                              // tag of the words this segment writes
@@ -360,7 +359,7 @@ struct CSeg {
   const uint16_t* gamma;                         // O, DOWN: weight of the next RMSNorm
   uint64_t* xgout; uint64_t* ssout;              // O, DOWN: tagged fp16(gamma * h) pairs, sum(h^2) per tile
   float* trace; float* gf; float* sumsq;         // DOWN: optional plain copies (trace, lm_head inputs)
-  uint64_t* act; uint64_t* act_gate;             // GU: tagged SiLU(gate) * up pairs [N / 2], a gate per tile
+  uint64_t* act;                                 // GU: tagged SiLU(gate) * up pairs [N / 2]
 };
 struct ChainParams {
   int nseg;
@@ -377,7 +376,7 @@ struct ChainParams {
   double inv_freq[64];                           // theta^(-2i/128), i = 0..63 (host fp64)
   // SEG_MERGE: attention split records -> tagged fp16 pairs of the attention output [nq * 64]
   const float* part; int nsplit, split, nq, nkv;
-  uint64_t* xo; uint64_t* xo_gate; uint32_t mrg_add;   // xo_gate: a word per (head, 64-dim half)
+  uint64_t* xo; uint32_t mrg_add;
 };
 void chain_gemv_plan(CSeg& g);                  // fills wpt / wpg / blocks from ntiles and K
 hipError_t chain_launch(const ChainParams& P, hipStream_t st, KEv ev = {});
