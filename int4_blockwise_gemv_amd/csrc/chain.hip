@@ -12,8 +12,8 @@
 //   then the lm_head + argmax.
 // A segment's workgroups issue their weight loads first and then wait for their inputs, which
 // earlier segments of the same grid publish as 64-bit tagged words: a 32-bit tag (the step
-// counter times a stride, plus the layer and stage) and a payload of one fp32 or two fp16
-// values.  A word is stored once per step with a single atomic store, so a reader that sees the
+// counter times a stride, plus the layer and stage) and an fp32 payload (the activations keep
+// fp32 precision; the GEMV segments stage them as fp16 hi + lo parts).  A word is stored once per step with a single atomic store, so a reader that sees the
 // expected tag sees the value, and no word ever needs clearing (a stale word carries an older
 // tag).  Progress: a workgroup only waits for workgroups with smaller indices (earlier segments,
 // and within a segment the split-K writers dispatched before their reader on the same XCD), and
@@ -31,15 +31,12 @@ constexpr int kCT = kCW * kWave;           // threads per workgroup
 constexpr int kCItemK = kCW * 8 * kBlock;  // K elements per workgroup at most (8 groups of 8 blocks)
 
 union CLds {
-  struct { uint16_t xs[kCItemK]; float red[kCW][kWave]; } g;
+  struct { uint16_t xs[2][kCItemK]; float red[kCW][kWave]; } g;   // xs: hi and lo parts
   struct { float pm[kCW], pl[kCW]; float po[kCW][kWave]; } m;
 };
 
 __device__ __forceinline__ uint64_t tag_f32(uint32_t tag, float v) {
   return ((uint64_t)tag << 32) | __float_as_uint(v);
-}
-__device__ __forceinline__ uint64_t tag_h2(uint32_t tag, uint16_t lo, uint16_t hi) {
-  return ((uint64_t)tag << 32) | lo | ((uint32_t)hi << 16);
 }
 __device__ __forceinline__ bool has_tag(uint64_t v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
 __device__ __forceinline__ void give_up(int32_t* status) {
@@ -69,9 +66,7 @@ __device__ void seg_prep(const ChainParams& P, int bid, uint32_t ebase) {
     const float hv = h2f(P.emb[n]);
     publish_u64(P.h + n, tag_f32(tag, hv));
     if (P.trace0) P.trace0[n] = hv;
-    const uint16_t gv = f2h(h2f(P.g1[n]) * hv);
-    const uint16_t gh = (uint16_t)__shfl_down((int)gv, 1, kWave);
-    if ((lane & 1) == 0) publish_u64(P.xq + n / 2, tag_h2(tag, gv, gh));
+    publish_u64(P.xq + n, tag_f32(tag, h2f(P.g1[n]) * hv));
     const float ss = wave_sum(hv * hv);
     if (lane == 0) publish_u64(P.ssq + t, tag_f32(tag, ss));
   }
@@ -135,10 +130,7 @@ __device__ void seg_merge(const ChainParams& P, int bid, uint32_t ebase, CLds& L
     O = fmaf(f, L.m.po[w + k][lane], O);
     Ls = fmaf(f, L.m.pl[w + k], Ls);
   }
-  const uint16_t o16 = f2h(O / Ls);
-  const uint16_t oh = (uint16_t)__shfl_down((int)o16, 1, kWave);
-  const uint32_t tag = ebase + P.mrg_add;
-  if ((lane & 1) == 0) publish_u64(P.xo + ((size_t)h * 128 + d) / 2, tag_h2(tag, o16, oh));
+  publish_u64(P.xo + (size_t)h * 128 + d, tag_f32(ebase + P.mrg_add, O / Ls));
 }
 
 // ---- one GEMV segment (batch 1): the decomposition, dequantisation and split-K hand-off of the
@@ -176,46 +168,54 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + bstep * i, nb - 1) * kTileRows);
   __builtin_amdgcn_sched_barrier(0);
 
-  // The activation slice: two tagged words (four fp16) per thread, polled after the weight loads
-  // were issued (the first poll returns behind them, so a workgroup whose weights arrive after its
-  // inputs polls once).  (Waiting on a few summary words per producer instead, and reading the
-  // slice once after them, measured slower: the extra round trip lands on every hop.)
+  // The activation slice: four tagged fp32 words per thread, polled after the weight loads were
+  // issued (the first poll returns behind them, so a workgroup whose weights arrive after its
+  // inputs polls once), then staged in LDS as fp16 hi + lo parts.  (Waiting on a few summary
+  // words per producer instead, and reading the slice once after them, measured slower: the
+  // extra round trip lands on every hop.)
   const int ec = min(e0 + 4 * tid, K - 4);
   const uint32_t xtag = ebase + g.xin_add;
-  const uint64_t* xp = g.xin + ec / 2;
-  uint64_t t0 = collect_u64(xp), t1 = collect_u64(xp + 1);
-  for (uint32_t it = 0; !__all(has_tag(t0, xtag) && has_tag(t1, xtag)); ++it) {
+  const uint64_t* xp = g.xin + ec;
+  uint64_t t[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
+  for (uint32_t it = 0;
+       !__all(has_tag(t[0], xtag) && has_tag(t[1], xtag) && has_tag(t[2], xtag) && has_tag(t[3], xtag)); ++it) {
     if (it >= kSpinLimit) {
       give_up(P.status);
-      t0 = t1 = 0x7e007e00u;          // fp16 NaN pairs
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = 0x7fc00000u;   // fp32 NaN
       break;
     }
     __builtin_amdgcn_s_sleep(2);
-    t0 = collect_u64(xp);
-    t1 = collect_u64(xp + 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
   }
-  *reinterpret_cast<uint2*>(&L.g.xs[4 * tid]) = make_uint2((uint32_t)t0, (uint32_t)t1);
+  uint2 xh, xl;
+  split_hl4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]), __uint_as_float((uint32_t)t[2]),
+            __uint_as_float((uint32_t)t[3]), xh, xl);
+  *reinterpret_cast<uint2*>(&L.g.xs[0][4 * tid]) = xh;
+  *reinterpret_cast<uint2*>(&L.g.xs[1][4 * tid]) = xl;
   __syncthreads();
 
   float acc = 0.f;
   {
     const uint32_t m64 = vconst(0x54005400u);
     const int xb0 = w * 8 * kBlock;
-    const u32x4 cx = *reinterpret_cast<const u32x4*>(&L.g.xs[xb0 + min(lane, 31) * 8]);
-    const float corr = quad_sum(corr_quarter(cx));   // lane 4i + q: quarter q of block i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
       const uint32_t dw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-      const u32x4* xb = reinterpret_cast<const u32x4*>(&L.g.xs[xb0 + i * kBlock]);
-      float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr), 4 * i));
+      const u32x4* xb = reinterpret_cast<const u32x4*>(&L.g.xs[0][xb0 + i * kBlock]);
+      const u32x4* xlb = reinterpret_cast<const u32x4*>(&L.g.xs[1][xb0 + i * kBlock]);
+      float tt = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const u32x4 xv = xb[k];
-        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-        t = dot8_pairs(dw[k], x4, t, m64);
+        const u32x4 xv = xb[k], lv = xlb[k];
+        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w}, l4[4] = {lv.x, lv.y, lv.z, lv.w};
+        tt = dot8_exact_hl(dw[k], x4, l4, tt, m64);
       }
-      acc = fmaf(sc, t, acc);
+      acc = fmaf(sc, tt, acc);
     }
   }
   L.g.red[w][lane] = acc;
@@ -244,9 +244,7 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     } else {   // lanes 0-31: gate rows, 32-63: the same up rows
       const float gt = tot * rs;
       const float u = __shfl(tot, (lane & 31) + 32, kWave) * rs;
-      const uint16_t a16 = f2h(silu(gt) * u);
-      const uint16_t ah = (uint16_t)__shfl_down((int)a16, 1, kWave);
-      if (lane < 32 && (lane & 1) == 0 && n < g.N) publish_u64(g.act + n / 2, tag_h2(otag, a16, ah));
+      if (lane < 32 && n < g.N) publish_u64(g.act + n, tag_f32(otag, silu(gt) * u));
     }
   } else {   // EPI_RESID: h += tot; the next norm's numerator and sum(h^2) of the tile
     hv = wait_word(P.h + nc, hv, ebase + g.hin_add, P.status);
@@ -258,9 +256,7 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     const float ss = wave_sum(hn * hn);
     if (g.sumsq && lane == 0) g.sumsq[tile] = ss;
     if (g.xgout) {
-      const uint16_t g16 = f2h(gv);
-      const uint16_t gh = (uint16_t)__shfl_down((int)g16, 1, kWave);
-      if ((lane & 1) == 0) publish_u64(g.xgout + n / 2, tag_h2(otag, g16, gh));
+      publish_u64(g.xgout + n, tag_f32(otag, gv));
       if (lane == 0) publish_u64(g.ssout + tile, tag_f32(otag, ss));
     }
   }

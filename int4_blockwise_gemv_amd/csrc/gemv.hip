@@ -15,9 +15,11 @@
 // 0..3 and the odd ones in nibbles 4..7, so a shift and one AND-OR with the fp16 exponent of
 // 64.0 turn nibble pair (i, 4+i) into the fp16 pair (64 + q_2i, 64 + q_2i+1), which lines up
 // with the natural fp16 pair (x_2i, x_2i+1) of the activation; v_dot2_f32_f16 then multiplies
-// both with exact products and fp32 accumulation.  The offset 64 and the zero point 8 are
-// removed once per block by subtracting C_b = 72 * sum_j x_j; the block sum is scaled by the
-// block's fp16 scale in fp32.
+// both with exact products and fp32 accumulation.  With fp16 activations the offset 64 and the
+// zero point 8 are removed once per block by subtracting C_b = 72 * sum_j x_j; with fp32
+// activations (two fp16 parts, hi + lo) one packed fp16 add per pair makes the codes q - 8
+// first, so that no offset cancels in the fp32 sums.  The block sum is scaled by the block's
+// fp16 scale in fp32.
 //
 // Split-K: the waves of a workgroup are reduced in LDS; with wpt = 1 the workgroup finishes its
 // tile directly.  With wpt > 1 a tile's last K-chunk workgroup (kg = wpt - 1) is its reader and
@@ -122,10 +124,10 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
         hn = e.h[m] + tot[m];
         p.h[i] = hn;
         if (p.trace) p.trace[i] = hn;
-        if (p.has_gamma) {
+        if (p.has_gamma && p.g_out) {
           const float gv = e.gam * hn;
-          if (p.g_out) p.g_out[i] = f2h(gv);
-          if (p.gf_out) p.gf_out[i] = gv;
+          if (p.g_f32) reinterpret_cast<float*>(p.g_out)[i] = gv;
+          else reinterpret_cast<uint16_t*>(p.g_out)[i] = f2h(gv);
         }
       }
       const float ss = wave_sum(hn * hn);
@@ -137,7 +139,11 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
       if (m >= M) continue;
       const float g = tot[m] * e.rs[m];
       const float u = __shfl(tot[m], (lane & 31) + 32, kWave) * e.rs[m];
-      if (ok && lane < 32) p.act[(size_t)m * p.N + n] = f2h(silu(g) * u);
+      if (ok && lane < 32) {
+        const float a = silu(g) * u;
+        if (p.act_f32) reinterpret_cast<float*>(p.act)[(size_t)m * p.N + n] = a;
+        else reinterpret_cast<uint16_t*>(p.act)[(size_t)m * p.N + n] = f2h(a);
+      }
     }
   }
 }
@@ -162,17 +168,21 @@ __device__ void fused_merge(const GemvParams& p) {
   float Mw, Lw;
   const float Ow = merge_wave64(rec0, (size_t)kAttnMaxG * kAttnRec, 0, n, d, Mw, Lw);
   const uint32_t tag = p.epoch[0] * p.tag_mul + p.tag_add;
-  publish_u64(p.xtag + (size_t)h * 128 + d, ((uint64_t)tag << 32) | f2h(Ow / Lw));
+  publish_u64(p.xtag + (size_t)h * 128 + d, ((uint64_t)tag << 32) | __float_as_uint(Ow / Lw));
 }
 
-template <int MT, int EPI, int WMAX, bool XT>
+// XF: the activations are fp32 and are staged as two fp16 parts x = hi + lo (about 22 bits, so
+// they keep fp32 precision; each part meets the same code pairs); else they are fp16 as given.
+// XT implies XF (the merged attention output arrives as tagged fp32 words).
+template <int MT, int EPI, int WMAX, bool XT, bool XF>
 __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                                                   const uint4* __restrict__ sw,
-                                                                  const uint16_t* __restrict__ x) {
+                                                                  const void* __restrict__ xin) {
   constexpr int kItemK = WMAX * kBatch * kBlock;  // K elements per workgroup at most
-  __shared__ __align__(16) uint16_t xs[MT][kItemK];
+  constexpr int NP = XF ? 2 : 1;                  // activation parts in LDS
+  __shared__ __align__(16) uint16_t xs[NP][MT][kItemK];
   __shared__ float red[WMAX][MT][kTileRows];
-  static_assert(!XT || MT == 1, "the fused merge serves batch 1");
+  static_assert(!XT || (MT == 1 && XF), "the fused merge serves batch 1 with fp32 activations");
   if constexpr (XT) {
     if ((int)blockIdx.x < p.mrg_blocks) {
       fused_merge(p);
@@ -190,14 +200,19 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   const int lane = threadIdx.x & (kWave - 1);
   const int e0 = kg * W * kBatch * kBlock;          // first K element of this workgroup
 
-  // activation slice first (its loads return before the weights), 8 bytes per thread per row;
+  // activation slice first (its loads return before the weights), 4 elements per thread per row;
   // with XT it is polled after the weight loads instead (it is still being merged)
-  static_assert(kItemK <= 4 * 64 * WMAX, "one 8-byte activation load per thread covers the slice");
-  uint2 xr[MT];
+  static_assert(kItemK <= 4 * 64 * WMAX, "one 4-element activation load per thread covers the slice");
   const int ec = min(e0 + 4 * (int)threadIdx.x, K - 4);
+  float4 xf[MT];
+  uint2 xr[NP][MT];
   if constexpr (!XT) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xr[m] = *reinterpret_cast<const uint2*>(x + (size_t)min(m, M - 1) * K + ec);
+    for (int m = 0; m < MT; ++m) {
+      const size_t off = (size_t)min(m, M - 1) * K + ec;
+      if constexpr (XF) xf[m] = *reinterpret_cast<const float4*>(static_cast<const float*>(xin) + off);
+      else xr[0][m] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xin) + off);
+    }
   }
   EpiPre<MT> ep;
   epi_prefetch<MT, EPI>(p, tile, lane, ep);
@@ -230,25 +245,35 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
       if (it >= kSpinLimit) {
         if (p.status) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = 0x7e00u;     // fp16 NaN
+        for (int k = 0; k < 4; ++k) t[k] = 0x7fc00000u;     // fp32 NaN
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    xr[0] = make_uint2((uint32_t)(t[0] & 0xffffu) | ((uint32_t)(t[1] & 0xffffu) << 16),
-                       (uint32_t)(t[2] & 0xffffu) | ((uint32_t)(t[3] & 0xffffu) << 16));
+    xf[0] = make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
+                        __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3]));
+  }
+  if constexpr (XF) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) split_hl4(xf[m].x, xf[m].y, xf[m].z, xf[m].w, xr[0][m], xr[1][m]);
   }
 #pragma unroll
-  for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[m][4 * threadIdx.x]) = xr[m];
+  for (int c = 0; c < NP; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[c][m][4 * threadIdx.x]) = xr[c][m];
   __syncthreads();
 
   const uint32_t m64 = vconst(0x54005400u);
   const int xb0 = w * kBatch * kBlock;              // this wave's first element in the slice
-  float corr[MT];
+  float corr[MT];                                   // fp16 activations: the offset correction
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(&xs[m][xb0 + min(lane, 4 * kBatch - 1) * 8]);
-    corr[m] = quad_sum(corr_quarter(xv));           // lane 4i+q: quarter q of block i
+    if constexpr (XF) {
+      corr[m] = 0.f;                                // exact codes: nothing to remove
+    } else {
+      const int o = xb0 + min(lane, 4 * kBatch - 1) * 8;
+      corr[m] = quad_sum(corr_quarter(*reinterpret_cast<const u32x4*>(&xs[0][m][o])));  // lane 4i+q: quarter q of block i
+    }
   }
   float acc[MT];
 #pragma unroll
@@ -259,13 +284,20 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
     const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
-      float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+      const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[0][m][xb0 + i * kBlock]);
+      const u32x4* xl = reinterpret_cast<const u32x4*>(&xs[NP - 1][m][xb0 + i * kBlock]);
+      float t = XF ? 0.f : -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x4 xv = xb[k];
         const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-        t = dot8_pairs(d[k], x4, t, m64);
+        if constexpr (XF) {
+          const u32x4 lv = xl[k];
+          const uint32_t l4[4] = {lv.x, lv.y, lv.z, lv.w};
+          t = dot8_exact_hl(d[k], x4, l4, t, m64);
+        } else {
+          t = dot8_pairs(d[k], x4, t, m64);
+        }
       }
       acc[m] = fmaf(sc, t, acc[m]);
     }
@@ -305,11 +337,11 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   epilogue<MT, EPI>(p, tile, tot, ep, lane);
 }
 
-int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
-// Batches of at least kMfmaMinM rows go to the matrix-core kernel (gemv_mfma.hip), which always
-// computes 16 rows: its partials are sized for 16.
-constexpr int kMfmaMinM = 5;
+// Batches of at least kGemvMfmaMinM rows go to the matrix-core kernel (gemv_mfma.hip), which
+// always computes 16 rows: its partials are sized for 16.
+constexpr int kMfmaMinM = kGemvMfmaMinM;
 int part_rows(int M) { return M >= kMfmaMinM ? 16 : mt_of(M); }
 
 struct Plan { int kb, wpg, wpt, grid; };
@@ -369,29 +401,27 @@ void gemv_set_workspace(GemvParams& p, void* ws) {
 }
 
 namespace {
-template <int EPI>
+template <int EPI, bool XF>
 void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t st, KEv ev) {
   const dim3 g(p.grid + p.mrg_blocks), b(64 * p.wpg);
   const bool wide = p.wpg > kWavesLargeM;   // only batches <= 2 get 8-wave workgroups
   switch (mt_of(p.M)) {
     case 1:
-      if constexpr (EPI == EPI_RESID) {      // the o projection may take the fused merge
+      if constexpr (EPI == EPI_RESID && XF) {   // the o projection may take the fused merge
         if (p.mrg_blocks) {
-          if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, true>), g, b, st, ev, p, q, s, p.x);
-          else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, true>), g, b, st, ev, p, q, s, p.x);
+          if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, true, true>), g, b, st, ev, p, q, s, p.x);
+          else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, true, true>), g, b, st, ev, p, q, s, p.x);
           break;
         }
       }
-      if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, false>), g, b, st, ev, p, q, s, p.x);
-      else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x);
+      if (wide) VV_LAUNCH((k_gemv<1, EPI, kWavesSmallM, false, XF>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x);
       break;
     case 2:
-      if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM, false>), g, b, st, ev, p, q, s, p.x);
-      else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x);
+      if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM, false, XF>), g, b, st, ev, p, q, s, p.x);
+      else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x);
       break;
-    case 4: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
-    case 8: VV_LAUNCH((k_gemv<8, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
-    default: VV_LAUNCH((k_gemv<16, EPI, kWavesLargeM, false>), g, b, st, ev, p, q, s, p.x); break;
+    default: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x); break;
   }
 }
 }  // namespace
@@ -399,7 +429,7 @@ void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t
 hipError_t gemv_launch(const GemvParams& p0, hipStream_t st, KEv ev) {
   if (p0.M >= kMfmaMinM) return gemv_mfma_launch(p0, st, ev);
   GemvParams p = p0;
-  const uint16_t* any = p.x;            // readable stand-in for absent optional operands
+  const uint16_t* any = static_cast<const uint16_t*>(p.x);   // readable stand-in for absent operands
   p.rs_mask = p.rs_parts ? 1 : 0;
   if (!p.rs_parts) { p.rs_parts = reinterpret_cast<const float*>(any); p.rs_nparts = 0; }
   p.has_bias = p.bias ? 1 : 0;
@@ -408,10 +438,15 @@ hipError_t gemv_launch(const GemvParams& p0, hipStream_t st, KEv ev) {
   if (!p.gamma) p.gamma = any;
   const uint4* q = reinterpret_cast<const uint4*>(p.q);
   const uint4* s = reinterpret_cast<const uint4*>(p.s);
+  if (!p.x_f32) {   // fp16 activations: the stand-alone GEMV of the C ABI
+    if (p.epi != EPI_STORE) return hipErrorInvalidValue;
+    launch_epi<EPI_STORE, false>(p, q, s, st, ev);
+    return hipGetLastError();
+  }
   switch (p.epi) {
-    case EPI_STORE: launch_epi<EPI_STORE>(p, q, s, st, ev); break;
-    case EPI_RESID: launch_epi<EPI_RESID>(p, q, s, st, ev); break;
-    default: launch_epi<EPI_SILU>(p, q, s, st, ev); break;
+    case EPI_STORE: launch_epi<EPI_STORE, true>(p, q, s, st, ev); break;
+    case EPI_RESID: launch_epi<EPI_RESID, true>(p, q, s, st, ev); break;
+    default: launch_epi<EPI_SILU, true>(p, q, s, st, ev); break;
   }
   return hipGetLastError();
 }

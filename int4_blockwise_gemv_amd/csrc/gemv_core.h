@@ -29,6 +29,41 @@ __device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, floa
   return acc;
 }
 
+// the same over activations given as two fp16 parts x = hi + lo (about 22 significant bits, so
+// the activation keeps fp32 precision).  Here the code pairs are made exact first, 64 + q - 72 =
+// q - 8 by one packed fp16 add (small integers, so exact): the fp32 sums then carry no offset to
+// cancel.  (Accumulating 64 + q and removing 72 sum(x) per block leaves partial sums about 15
+// times the block's result, and with them an fp32 rounding error of about 2e-6 of the output,
+// the precision the lo part is there to keep.)  Each pair meets both parts.
+__device__ __forceinline__ float dot8_exact_hl(uint32_t d, const uint32_t* xh4, const uint32_t* xl4, float acc,
+                                               uint32_t m64) {
+  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
+  const h2_t p01 = as_h2(((d << 4) & 0x00F000F0u) | m64) + off;
+  const h2_t p23 = as_h2((d & 0x00F000F0u) | m64) + off;
+  const h2_t p45 = as_h2(((d >> 4) & 0x00F000F0u) | m64) + off;
+  const h2_t p67 = as_h2(((d >> 8) & 0x00F000F0u) | m64) + off;
+  acc = __builtin_amdgcn_fdot2(p01, as_h2(xh4[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p23, as_h2(xh4[1]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p45, as_h2(xh4[2]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p67, as_h2(xh4[3]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p01, as_h2(xl4[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p23, as_h2(xl4[1]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p45, as_h2(xl4[2]), acc, false);
+  acc = __builtin_amdgcn_fdot2(p67, as_h2(xl4[3]), acc, false);
+  return acc;
+}
+
+// four fp32 activations -> their fp16 hi parts (two pairs) and lo parts x - hi (two pairs)
+__device__ __forceinline__ void split_hl4(float a, float b, float c, float d, uint2& hi, uint2& lo) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b, hc = (_Float16)c, hd = (_Float16)d;
+  const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
+  const _Float16 lc = (_Float16)(c - (float)hc), ld = (_Float16)(d - (float)hd);
+  hi.x = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  hi.y = (uint32_t)__builtin_bit_cast(uint16_t, hc) | ((uint32_t)__builtin_bit_cast(uint16_t, hd) << 16);
+  lo.x = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+  lo.y = (uint32_t)__builtin_bit_cast(uint16_t, lc) | ((uint32_t)__builtin_bit_cast(uint16_t, ld) << 16);
+}
+
 // C for one quarter (8 elements) of a block: (64 + 8) * (x0 + ... + x7)
 __device__ __forceinline__ float corr_quarter(u32x4 xv) {
   const uint32_t c72 = 0x54805480u;  // fp16 (72, 72)

@@ -187,9 +187,9 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_mfma(GemvParams p, const uint4
         hn = p.h[i] + tot[r];
         p.h[i] = hn;
         if (p.trace) p.trace[i] = hn;
-        if (p.gamma) {
-          if (p.g_out) p.g_out[i] = f2h(gam * hn);
-          if (p.gf_out) p.gf_out[i] = gam * hn;
+        if (p.gamma && p.g_out) {
+          if (p.g_f32) reinterpret_cast<float*>(p.g_out)[i] = gam * hn;
+          else reinterpret_cast<uint16_t*>(p.g_out)[i] = f2h(gam * hn);
         }
       }
       const float ss = wave_sum(hn * hn);
@@ -201,21 +201,28 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_mfma(GemvParams p, const uint4
       const int m = 4 * w + r;
       const float gt = tot[r] * rs[r];
       const float up = __shfl(tot[r], (n & 31) + 32, kWave) * rs[r];
-      if (ok && n < 32 && m < M) p.act[(size_t)m * p.N + row] = f2h(silu(gt) * up);
+      if (ok && n < 32 && m < M) {
+        const float a = silu(gt) * up;
+        if (p.act_f32) reinterpret_cast<float*>(p.act)[(size_t)m * p.N + row] = a;
+        else reinterpret_cast<uint16_t*>(p.act)[(size_t)m * p.N + row] = f2h(a);
+      }
     }
   }
 }
 
 }  // namespace
 
+// the matrix-core kernel reads fp16 activations (x_f32 must be 0)
 hipError_t gemv_mfma_launch(const GemvParams& p, hipStream_t st, KEv ev) {
+  if (p.x_f32) return hipErrorInvalidValue;
   const uint4* q = reinterpret_cast<const uint4*>(p.q);
   const uint4* s = reinterpret_cast<const uint4*>(p.s);
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
   const dim3 g(p.grid), b(64 * kW);
   switch (p.epi) {
-    case EPI_STORE: VV_LAUNCH((k_gemv_mfma<EPI_STORE>), g, b, st, ev, p, q, s, p.x); break;
-    case EPI_RESID: VV_LAUNCH((k_gemv_mfma<EPI_RESID>), g, b, st, ev, p, q, s, p.x); break;
-    default: VV_LAUNCH((k_gemv_mfma<EPI_SILU>), g, b, st, ev, p, q, s, p.x); break;
+    case EPI_STORE: VV_LAUNCH((k_gemv_mfma<EPI_STORE>), g, b, st, ev, p, q, s, x); break;
+    case EPI_RESID: VV_LAUNCH((k_gemv_mfma<EPI_RESID>), g, b, st, ev, p, q, s, x); break;
+    default: VV_LAUNCH((k_gemv_mfma<EPI_SILU>), g, b, st, ev, p, q, s, x); break;
   }
   return hipGetLastError();
 }

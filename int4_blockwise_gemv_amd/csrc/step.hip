@@ -22,11 +22,12 @@ namespace {
 
 constexpr int kHeadDim = 128;
 
-// h = fp32(input_embeds); g = fp16(gamma * h) (or gf = gamma * h in fp32 when there are no
-// layers); per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64 pairs.
+// h = fp32(input_embeds); g = gamma * h in fp32 (g_f32) or fp16, or gf = gamma * h in fp32 when
+// there are no layers; per-tile sum of h^2; optional trace; RoPE (cos, sin) of pos[b] for the 64
+// pairs.
 __global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ emb, int H, int ntiles,
                                                   const uint16_t* __restrict__ gamma, float* __restrict__ h,
-                                                  uint16_t* __restrict__ g, float* __restrict__ gf,
+                                                  void* __restrict__ g, int g_f32, float* __restrict__ gf,
                                                   float* __restrict__ sumsq, float* __restrict__ trace,
                                                   const int32_t* __restrict__ pos, int cap, double theta,
                                                   float* __restrict__ rope) {
@@ -38,7 +39,10 @@ __global__ __launch_bounds__(64) void k_step_prep(const uint16_t* __restrict__ e
   h[i] = hv;
   if (trace) trace[i] = hv;
   const float gv = h2f(gamma[n]) * hv;
-  if (g) g[i] = f2h(gv);
+  if (g) {
+    if (g_f32) static_cast<float*>(g)[i] = gv;
+    else static_cast<uint16_t*>(g)[i] = f2h(gv);
+  }
   if (gf) gf[i] = gv;
   const float ss = wave_sum(hv * hv);
   if (lane == 0) sumsq[(size_t)b * ntiles + t] = ss;
@@ -110,11 +114,11 @@ Layout layout_of(const Dims& d) {
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
   l.status = take(sizeof(int32_t));   // sticky status word: a bounded wait that gave up sets it
   l.h = take((size_t)d.B * d.H * 4);
-  l.g = take((size_t)d.B * d.H * 2);
+  l.g = take((size_t)d.B * d.H * 4);                // activations: fp32 below the matrix-core batch, else fp16
   l.gf = take((size_t)d.B * d.H * 4);
   l.qkv = take((size_t)d.B * d.nqkv * 4);
-  l.o = take((size_t)d.B * d.nq * kHeadDim * 2);
-  l.act = take((size_t)d.B * d.I * 2);
+  l.o = take((size_t)d.B * d.nq * kHeadDim * 4);
+  l.act = take((size_t)d.B * d.I * 4);
   l.sumsq = take((size_t)d.B * d.ntH * 4);
   l.rope = take((size_t)d.B * 64 * 2 * 4);
   l.ws_qkv = take(gemv_workspace_bytes(d.B, (int)cdiv(d.nqkv, kTileRows), d.H / kBlock));
@@ -129,12 +133,12 @@ Layout layout_of(const Dims& d) {
   l.otag = take((size_t)d.nq * kHeadDim * sizeof(uint64_t));   // fused merge -> o projection (batch 1)
   l.epoch = take(sizeof(uint32_t));                              // step counter (tags of otag)
   l.th = take((size_t)d.H * 8);
-  l.txq = take((size_t)d.H / 2 * 8);
+  l.txq = take((size_t)d.H * 8);
   l.tssq = take((size_t)d.ntH * 8);
-  l.txm = take((size_t)d.H / 2 * 8);
+  l.txm = take((size_t)d.H * 8);
   l.tssm = take((size_t)d.ntH * 8);
-  l.txo = take((size_t)d.nq * kHeadDim / 2 * 8);
-  l.txd = take((size_t)d.I / 2 * 8);
+  l.txo = take((size_t)d.nq * kHeadDim * 8);
+  l.txd = take((size_t)d.I * 8);
   l.total = off;
   return l;
 }
@@ -390,11 +394,14 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   const Layout lay = layout_of(d);
   char* ws = static_cast<char*>(s->workspace);
   float* h = reinterpret_cast<float*>(ws + lay.h);
-  uint16_t* g = reinterpret_cast<uint16_t*>(ws + lay.g);
+  void* g = ws + lay.g;
   float* gf = reinterpret_cast<float*>(ws + lay.gf);
   float* qkv = reinterpret_cast<float*>(ws + lay.qkv);
-  uint16_t* o = reinterpret_cast<uint16_t*>(ws + lay.o);
-  uint16_t* act = reinterpret_cast<uint16_t*>(ws + lay.act);
+  void* o = ws + lay.o;
+  void* act = ws + lay.act;
+  // the projections' inputs: fp32 for the vector-ALU GEMV (staged as fp16 hi + lo parts, so the
+  // activations keep fp32 precision), fp16 for the matrix-core GEMV of batches >= 5
+  const int xf32 = s->batch < kGemvMfmaMinM;
   float* sumsq = reinterpret_cast<float*>(ws + lay.sumsq);
   float* rope = reinterpret_cast<float*>(ws + lay.rope);
   const int B = d.B, H = d.H;
@@ -404,7 +411,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
   int32_t* status = reinterpret_cast<int32_t*>(ws + lay.status);
   int op = 0;   // timing event pair of the next operation
   VV_LAUNCH(k_step_prep, dim3(B * d.ntH), dim3(64), st, event_pair(s, op++), s->input_embeds, H, d.ntH,
-            d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, d.L > 0 ? nullptr : gf, sumsq,
+            d.L > 0 ? m->layers[0].g1 : m->gf, h, d.L > 0 ? g : nullptr, xf32, d.L > 0 ? nullptr : gf, sumsq,
             s->h_trace, s->pos, s->cap, (double)m->rope_theta, rope);
   VV_HIP(hipGetLastError());
 
@@ -414,7 +421,7 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     const vv_layer& y = m->layers[l];
     {  // fused q|k|v projection, RMSNorm_1 folded in, bias added
       GemvParams p{};
-      p.q = y.qkv_q; p.s = y.qkv_s; p.x = g;
+      p.q = y.qkv_q; p.s = y.qkv_s; p.x = g; p.x_f32 = xf32;
       p.M = B; p.N = d.nqkv; p.K = H;
       p.ntiles = (int)cdiv(d.nqkv, kTileRows);
       p.epi = EPI_STORE; p.bias = y.qkv_bias; p.y = qkv; p.y_f16 = 0; p.ldy = d.nqkv;
@@ -438,15 +445,15 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       a.vc = static_cast<char*>(s->v_cache) + (size_t)l * layer_kv_bytes;
       a.kv_f32 = kv32;
       a.scale = 1.0f / sqrtf((float)kHeadDim);
-      a.out = o; a.out_f16 = 1;
+      a.out = o; a.out_f16 = !xf32;
       VV_HIP(attn_launch_with_rope(a, rope, st, event_pair(s, op++)));
     }
     {  // o projection + residual; writes fp16(g2 * h) and sum(h^2) for the MLP
       GemvParams p{};
-      p.q = y.o_q; p.s = y.o_s; p.x = o;
+      p.q = y.o_q; p.s = y.o_s; p.x = o; p.x_f32 = xf32;
       p.M = B; p.N = H; p.K = d.nq * kHeadDim;
       p.ntiles = d.ntH;
-      p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.sumsq_out = sumsq;
+      p.epi = EPI_RESID; p.h = h; p.gamma = y.g2; p.g_out = g; p.g_f32 = xf32; p.sumsq_out = sumsq;
       gemv_plan(p);
       p.status = status;
       gemv_set_workspace(p, ws + lay.ws_o);
@@ -462,10 +469,10 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     }
     {  // gate/up (32 gate + 32 up rows per tile) + SiLU(gate) * up, RMSNorm_2 folded in
       GemvParams p{};
-      p.q = y.gu_q; p.s = y.gu_s; p.x = g;
+      p.q = y.gu_q; p.s = y.gu_s; p.x = g; p.x_f32 = xf32;
       p.M = B; p.N = d.I; p.K = H;
       p.ntiles = 2 * d.ntI;
-      p.epi = EPI_SILU; p.act = act;
+      p.epi = EPI_SILU; p.act = act; p.act_f32 = xf32;
       p.rs_parts = sumsq; p.rs_nparts = d.ntH; p.rs_inv_n = inv_h; p.eps = m->eps;
       gemv_plan(p);
       p.status = status;
@@ -475,13 +482,13 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     {  // down projection + residual; feeds the next layer (or the lm_head)
       const bool last = l == d.L - 1;
       GemvParams p{};
-      p.q = y.down_q; p.s = y.down_s; p.x = act;
+      p.q = y.down_q; p.s = y.down_s; p.x = act; p.x_f32 = xf32;
       p.M = B; p.N = H; p.K = d.I;
       p.ntiles = d.ntH;
       p.epi = EPI_RESID; p.h = h;
       p.gamma = last ? m->gf : m->layers[l + 1].g1;
-      p.g_out = last ? nullptr : g;
-      p.gf_out = last ? gf : nullptr;
+      p.g_out = last ? static_cast<void*>(gf) : g;    // the lm_head takes gamma_f * h in fp32
+      p.g_f32 = last ? 1 : xf32;
       p.sumsq_out = sumsq;
       p.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * B * H : nullptr;
       gemv_plan(p);

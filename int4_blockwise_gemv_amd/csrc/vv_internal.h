@@ -249,7 +249,8 @@ struct KEv {
 struct GemvParams {
   const uint8_t* q;          // tiled nibbles
   const uint16_t* s;         // tiled scales
-  const uint16_t* x;         // fp16 [M][K]
+  const void* x;             // [M][K]: fp32 (x_f32, the VALU kernel splits it into fp16 hi + lo) or fp16
+  int x_f32;
   int M, N, K;               // N valid output rows (EPI_SILU: rows of gate = rows of up)
   int ntiles;                // tiles in the matrix
   float* part;               // workspace partials (matrix-core kernel)
@@ -267,12 +268,11 @@ struct GemvParams {
   // EPI_RESID
   float* h;                  // fp32 [M][N]
   const uint16_t* gamma;     // fp16 [N]
-  uint16_t* g_out;           // fp16 [M][N] = fp16(gamma * h)   (if gamma and g_out)
-  float* gf_out;             // fp32 [M][N] = gamma * h          (if gamma and gf_out)
+  void* g_out; int g_f32;    // [M][N] gamma * h, fp32 (g_f32) or fp16 (if gamma and g_out)
   float* sumsq_out;          // fp32 [M][ntiles]
   float* trace;              // fp32 [M][N] copy of h or null
   // EPI_SILU
-  uint16_t* act;             // fp16 [M][N]
+  void* act; int act_f32;    // [M][N] SiLU(gate) * up, fp32 (act_f32) or fp16
   // fused split-KV merge (batch 1, at most 64 splits): the first mrg_blocks workgroups merge the
   // attention records into tagged activation words xtag[k] = (tag << 32) | fp32 bits, which the
   // GEMV workgroups poll instead of reading x; tag = epoch[0] * tag_mul + tag_add (the step's
@@ -282,6 +282,9 @@ struct GemvParams {
   uint64_t* xtag; const uint32_t* epoch; uint32_t tag_mul, tag_add;
 };
 
+// batches of at least this many rows run on the matrix cores (fp16 activations); smaller ones on
+// the vector ALU (fp32 activations as fp16 hi + lo parts, or fp16)
+constexpr int kGemvMfmaMinM = 5;
 void gemv_plan(GemvParams& p);                       // fills kb/wpg/wpt/grid
 size_t gemv_workspace_bytes(int M, int ntiles, int nb);
 void gemv_set_workspace(GemvParams& p, void* ws);    // carves part/cnt from ws
@@ -340,7 +343,7 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev = {});
 // ---- chained launches of the batch-1 step (chain.hip) ------------------------------------------
 // One grid runs several stages as segments (consecutive ranges of workgroups, each a multiple of 8
 // so that a workgroup's index within its segment keeps its XCD).  Cross-segment data are 64-bit
-// tagged words (tag << 32 | one fp32 or two fp16); a tag is epoch * tag_mul + add.
+// tagged words (tag << 32 | fp32 bits); a tag is epoch * tag_mul + add.
 constexpr int kChainWaves = 8;        // waves per workgroup
 constexpr int kChainMaxSeg = 5;
 constexpr int kChainMaxSplits = 128;  // attention splits the merge segment takes
@@ -351,15 +354,15 @@ struct CSeg {
   const u32x4* q; const u32x4* s;
   int N, K, ntiles, wpt, wpg;
   uint64_t* slots;                               // split-K hand-off slots [tile][wpt - 1][64]
-  const uint64_t* xin; uint32_t xin_add;         // tagged input pairs [K / 2]
+  const uint64_t* xin; uint32_t xin_add;         // tagged inputs [K]
   const uint64_t* ssin; uint32_t ss_add; int ss_n;   // QKV, GU: tagged sum(h^2) per tile (rstd)
   uint32_t hin_add;                              // O, DOWN: tag of the residual they add to
   uint32_t out_add;                              // tag of the words this segment writes
   const uint16_t* bias; int has_bias; float* y;  // QKV: fp16 bias (readable stand-in if absent), fp32 out
   const uint16_t* gamma;                         // O, DOWN: weight of the next RMSNorm
-  uint64_t* xgout; uint64_t* ssout;              // O, DOWN: tagged fp16(gamma * h) pairs, sum(h^2) per tile
+  uint64_t* xgout; uint64_t* ssout;              // O, DOWN: tagged gamma * h [N], sum(h^2) per tile
   float* trace; float* gf; float* sumsq;         // DOWN: optional plain copies (trace, lm_head inputs)
-  uint64_t* act;                                 // GU: tagged SiLU(gate) * up pairs [N / 2]
+  uint64_t* act;                                 // GU: tagged SiLU(gate) * up [N]
 };
 struct ChainParams {
   int nseg;
@@ -369,12 +372,12 @@ struct ChainParams {
   float eps, inv_h;
   const uint32_t* epoch; uint32_t tag_mul;
   int32_t* status;
-  // SEG_PREP: embeddings -> h, fp16(g1 * h) pairs, sum(h^2) per tile, the RoPE table
+  // SEG_PREP: embeddings -> h, g1 * h, sum(h^2) per tile, the RoPE table
   uint32_t prep_add;
   const uint16_t* emb; const uint16_t* g1; uint64_t* xq; uint64_t* ssq; float* trace0;
   const int32_t* pos; int cap; int rope_on; float* rope;
   double inv_freq[64];                           // theta^(-2i/128), i = 0..63 (host fp64)
-  // SEG_MERGE: attention split records -> tagged fp16 pairs of the attention output [nq * 64]
+  // SEG_MERGE: attention split records -> the tagged attention output [nq * 128]
   const float* part; int nsplit, split, nq, nkv;
   uint64_t* xo; uint32_t mrg_add;
 };

@@ -4,10 +4,11 @@ captured graph of the step): the 1.5B-shaped step at P = 4096, the 7B-shaped ste
 1.5B shape with 16 ragged sequences (past lengths 512..8192).
 
 The oracle packs every layer itself from the seeded fp32 masters (in worker processes: the
-oracle's packing is plain numpy and takes seconds per layer) and runs its own whole step from the
-same input embeddings and caches.  Compared: the residual stream after every layer, the K/V each
-layer writes at the new position (and the rest of every cache untouched), the logits and the
-greedy token ("VibeVoice-1.5B — Current Status", Inference: incremental decoding reproduces the
+oracle's packing is plain numpy and takes seconds per layer).  Compared: every layer on the GPU's
+own input residual (its output residual and the K/V it writes, within 2e-3: the GEMV and attention
+outputs on identical inputs; the rest of every cache untouched), and the whole step against the
+oracle's own step from the same embeddings and caches (the residual stream after every layer, the
+K/V of every layer, the logits within 2e-3 and the greedy token) ("VibeVoice-1.5B — Current Status", Inference: incremental decoding reproduces the
 full computation; "vibevoice-asr-bitnet-onnx", tier table: int4 tiers token-exact against the
 reference)."""
 import numpy as np
@@ -20,7 +21,7 @@ from helpers import oracle_model, oracle_packs_parallel
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
-DRIFT_TOL = 1e-2
+DRIFT_TOL = TOL
 
 _PACKS = {}
 
@@ -44,7 +45,88 @@ def _check_tokens(tok, ref_logits):
             assert int(tok[b]) in set(int(t) for t in top2)
 
 
-def _end_to_end(wl_name, seed, path):
+def _gqa_rounded(q, K, V, length, scale, rng, u):
+    """The oracle's attention of one sequence with every score s held as fp32 holds it,
+    s (1 + u z): a score of size |s| then moves its probability by about u |s|, the rounding that
+    large (outlier) scores put on any fp32 softmax."""
+    nq, d = q.shape
+    grp = nq // K.shape[0]
+    out = np.empty((nq, d), np.float64)
+    for h in range(nq):
+        k = np.asarray(K[h // grp, :length], dtype=np.float64)
+        v = np.asarray(V[h // grp, :length], dtype=np.float64)
+        s = (k @ q[h]) * scale
+        if u:
+            s = s * (1.0 + u * rng.standard_normal(s.shape))
+        s = s - s.max()
+        p = np.exp(s)
+        out[h] = (p @ v) / p.sum()
+    return out
+
+
+def _layer_rounded(L, m, h, pos, Kc, Vc, rng, u):
+    """One layer built from the oracle's own steps, in its order, with every intermediate that an
+    fp32 computation of the layer holds multiplied by (1 + u z), z ~ N(0,1) drawn from rng: the
+    normalised inputs, q/k/v after the projection and after RoPE, every attention score, the
+    attention output, every projection output, the SiLU product and the residual after each add.
+    With u = 0 it is the oracle's layer step exactly (checked by the caller)."""
+    def r(a):
+        return a if u == 0 else a * (1.0 + u * rng.standard_normal(a.shape))
+    B = h.shape[0]
+    d, nq, nkv = m.head_dim, m.n_q, m.n_kv
+    pos = np.asarray(pos, dtype=np.int64)
+    a = r(O.rmsnorm(h, L.g1, m.eps))
+    q = r(O.gemv(*L.q, a, L.bq)).reshape(B, nq, d)
+    k = r(O.gemv(*L.k, a, L.bk)).reshape(B, nkv, d)
+    v = r(O.gemv(*L.v, a, L.bv)).reshape(B, nkv, d)
+    q = r(O.rope(q, pos, m.rope_theta))
+    k = r(O.rope(k, pos, m.rope_theta))
+    o = np.empty((B, nq, d), np.float64)
+    for b in range(B):
+        p = int(pos[b])
+        Kc[b, :, p] = k[b].astype(Kc.dtype)
+        Vc[b, :, p] = v[b].astype(Vc.dtype)
+        o[b] = r(_gqa_rounded(q[b], Kc[b], Vc[b], p + 1, 1.0 / np.sqrt(d), rng, u))
+    h = r(h + r(O.gemv(*L.o, o.reshape(B, nq * d))))
+    mm = r(O.rmsnorm(h, L.g2, m.eps))
+    act = r(O.silu(r(O.gemv(*L.gate, mm))) * r(O.gemv(*L.up, mm)))
+    return r(h + r(O.gemv(*L.down, act)))
+
+
+def _rounding_model(m, emb, lens, caches, tr, draws=4, u=2.0 ** -24):
+    """The workload's response to fp32 rounding, for `draws` independent draws of the rounded
+    layer (one sequence): per draw, the largest layer-local residual difference of the rounded
+    layer on the oracle's own input of every layer, and the whole-step residual drift, K/V drift
+    and logits difference of the rounded step, all against the oracle's exact step (tr).  Every
+    draw's two rows (its running step, and the oracle's input of the layer) go through each layer
+    together, so the oracle dequantises each projection once."""
+    assert len(lens) == 1
+    rng = np.random.default_rng(12345)
+    n = draws
+    pos = np.repeat(np.asarray(lens, np.int64), 2 * n)
+    p = int(lens[0])
+    h = np.repeat(np.asarray(emb, np.float16).astype(np.float64), n, axis=0)
+    local, drift, kv = np.zeros(n), np.zeros(n), np.zeros(n)
+    for li, L in enumerate(m.layers):
+        x = np.concatenate([h, np.repeat(tr["h"][li], n, axis=0)])
+        K = np.repeat(caches[li][0], 2 * n, axis=0)
+        V = np.repeat(caches[li][1], 2 * n, axis=0)
+        y = _layer_rounded(L, m, x, pos, K, V, rng, u)
+        h = y[:n]
+        ref = tr["h"][li + 1][0]
+        Kr, Vr = tr["K"][li][0, :, p].astype(np.float64), tr["V"][li][0, :, p].astype(np.float64)
+        for d in range(n):
+            drift[d] = max(drift[d], rel_err(h[d], ref))
+            local[d] = max(local[d], rel_err(y[n + d], ref))
+            kv[d] = max(kv[d], rel_err(K[d, :, p].astype(np.float64), Kr), rel_err(V[d, :, p].astype(np.float64), Vr))
+        del K, V
+    f = O.rmsnorm(h, m.gf, m.eps)
+    lp, _, _ = O.lm_head_argmax(m.lm, f)
+    lerr = np.array([rel_err(lp[d], tr["logits"][0]) for d in range(n)])
+    return local, drift, kv, lerr
+
+
+def _end_to_end(wl_name, seed, path, conditioned=False):
     import torch
     from int4_blockwise_gemv_amd.model import DeviceModel, DeviceState
     wl = synth.WORKLOADS[wl_name]
@@ -73,10 +155,12 @@ def _end_to_end(wl_name, seed, path):
     gtok = host(ds.token)
     assert np.all(np.isfinite(gtr))
 
+    print(f"{wl_name} [{path}]: GPU step done; oracle checks", flush=True)
     m = oracle_model(s, seed, range(s.layers), glob=glob, packs=_packs(s, seed))
     # (1) every layer on the GPU's own input residual: the layer's GEMV and attention outputs on
     #     identical inputs (the output residual and the K/V written at the new position)
     local = 0.0
+    local_res = []
     for li in range(s.layers):
         K0, V0 = caches[li]
         Kl, Vl = K0.copy(), V0.copy()
@@ -88,6 +172,7 @@ def _end_to_end(wl_name, seed, path):
             errs = (rel_err(gtr[li + 1][b], hl[b]), rel_err(gk[b, :, p], Kl[b, :, p]),
                     rel_err(gv[b, :, p], Vl[b, :, p]))
             local = max(local, *errs)
+            local_res.append(errs[0])
             assert max(errs) <= TOL, (li, b, errs)
             keep = np.ones(wl.cap, bool)
             keep[p] = False
@@ -114,11 +199,40 @@ def _end_to_end(wl_name, seed, path):
             kv_drift = max(kv_drift, rel_err(gk[b, :, p], Kc[li][b, :, p]), rel_err(gv[b, :, p], Vc[li][b, :, p]))
         del gk, gv
     lerr = max(rel_err(glog[b], logits[b]) for b in range(wl.batch))
-    print(f"{wl_name} seed {seed} [{path}]: layer-local worst {local:.2e}; whole step: residual drift {drift:.2e}, "
+    print(f"{wl_name} seed {seed} [{path}]: layer-local worst {local:.2e} (residual {max(local_res):.2e}); whole step: residual drift {drift:.2e}, "
           f"K/V drift {kv_drift:.2e}, logits {lerr:.2e}")
-    assert drift <= DRIFT_TOL and kv_drift <= DRIFT_TOL
-    assert lerr <= TOL
-    _check_tokens(gtok, logits)
+    if not conditioned:
+        assert drift <= DRIFT_TOL and kv_drift <= DRIFT_TOL
+        assert lerr <= TOL
+        _check_tokens(gtok, logits)
+        return
+    # An ill-conditioned workload: the whole step is held to what the workload itself makes of
+    # per-layer differences.  The rounding model (the oracle's layer with fp32-rounding-sized
+    # noise on every intermediate) gives both sides of that for each of its draws: its layer-local
+    # difference and its whole-step drift.  To first order the drift of any computation is its
+    # layer-local difference times that ratio; one draw's ratio varies about twofold from the next,
+    # so the GPU is held to twice its own layer-local difference times the largest ratio of four
+    # draws.
+    h0 = tr["h"][0][:1]
+    assert np.array_equal(_layer_rounded(m.layers[0], m, h0, lens[:1], caches[0][0][:1].copy(),
+                                         caches[0][1][:1].copy(), None, 0.0),
+                          O.layer_step(m.layers[0], m, h0, lens[:1], caches[0][0][:1].copy(), caches[0][1][:1].copy()))
+    tr["K"], tr["V"], tr["logits"] = Kc, Vc, logits
+    print("  rounding model: 4 draws through 28 layers", flush=True)
+    m_local, m_drift, m_kv, m_log = _rounding_model(m, glob["emb"], lens, caches, tr)
+    e = max(local_res)
+    k_res, k_kv, k_log = (2 * float(np.max(x / m_local)) * e for x in (m_drift, m_kv, m_log))
+    print("  rounding model draws: layer-local " + ", ".join(f"{x:.2e}" for x in m_local)
+          + "; residual drift " + ", ".join(f"{x:.2e}" for x in m_drift)
+          + "; logits " + ", ".join(f"{x:.2e}" for x in m_log))
+    print(f"  bounds at the GPU's layer-local {e:.2e}: residual {k_res:.2e}, K/V {k_kv:.2e}, logits {k_log:.2e}")
+    assert drift <= max(DRIFT_TOL, k_res) and kv_drift <= max(DRIFT_TOL, k_kv)
+    assert lerr <= max(TOL, k_log)
+    for b in range(wl.batch):
+        i, gap = O.argmax_with_gap(logits[b])
+        # the token where the top-two gap exceeds what the logit bound can move
+        if gap > 2 * max(TOL, k_log) * np.linalg.norm(logits[b], np.inf):
+            assert int(gtok[b]) == i, (b, int(gtok[b]), i, gap)
 
 
 @pytest.mark.timeout(600)
@@ -140,4 +254,9 @@ def test_end_to_end_7b_p4000(cuda, path):
 
 @pytest.mark.timeout(900)
 def test_end_to_end_7b_absmax_p16384_outliers(cuda):
-    _end_to_end("decode-7b-absmax-p16384", 0, "layered")
+    """General int4 weights over 16384 positions with 1% of the keys and values scaled by 8.  The
+    oracle itself amplifies a difference in its input about 3000-fold over the 28 layers (an input
+    perturbed by 1e-7 ends 3e-4 away), so beyond every layer within 2e-3 on its own input the whole
+    step is held to twice the GPU's layer-local difference times the largest drift-to-local ratio
+    of four draws of the oracle with fp32-rounding-sized noise on every intermediate."""
+    _end_to_end("decode-7b-absmax-p16384", 0, "layered", conditioned=True)
