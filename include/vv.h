@@ -181,6 +181,18 @@ size_t vv_lm_head_argmax_workspace(int B, int V, int H);
 int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H,
                       float* logits, int32_t* token, void* ws, size_t ws_bytes, void* stream);
 
+/* vv_lm_head_argmax for callers that cannot allocate device memory (code under hipGraph capture,
+ * serving loops, harnesses that forbid allocation): the same kernels and results, with the argmax
+ * keys in a library-held scratch array instead of a caller workspace.  The array is a 256 KiB
+ * file-scope device allocation that each GPU the library runs on holds until the process ends; the
+ * call itself allocates and frees nothing.  Calls needing more keys than it holds
+ * (vv_lm_head_argmax_workspace(B, V, H) > 256 KiB, e.g. 16 rows over more than about a million
+ * vocabulary rows) return VV_ERR_RANGE before launching anything.  Each call clears the keys it
+ * uses with a fill kernel first.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must not be issued. */
+int vv_lm_head_argmax_noalloc(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H,
+                              float* logits, int32_t* token, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Decode step (bitnet-onnx page, decoder_step contract:
  *   input_embeds [B,H], position_ids [B], past K/V [L,B,nkv,P,128]

@@ -8,6 +8,8 @@
 // tracked as a 64-bit key (order-preserving float bits, then the complemented index, so ties go
 // to the smallest index); each workgroup publishes its best key and the grid's last workgroup
 // polls them and picks the winner (the maximum does not depend on the order).
+#include <mutex>
+
 #include "vv_internal.h"
 
 namespace vv {
@@ -402,6 +404,51 @@ hipError_t lm_launch(const LmParams& p, hipStream_t st, KEv ev) {
 
 }  // namespace vv
 
+// ---- the allocation-free entry point's scratch ----------------------------------------------
+// The argmax keys of vv_lm_head_argmax_noalloc live in this file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, and is what the kernels receive.
+static __device__ __align__(256) uint64_t scratch[vv::kLmScratchBytes / sizeof(uint64_t)];
+
+namespace vv {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int scratch_address(void** out) {
+  int dev = -1;
+  VV_HIP(hipGetDevice(&dev));
+  VV_REQUIRE(dev >= 0 && dev < kMaxDevices, VV_ERR_RANGE, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    VV_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    VV_REQUIRE(p != nullptr, VV_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VV_OK;
+}
+
+int lm_validate(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H, const int32_t* token,
+                const char* fn) {
+  VV_REQUIRE(W && x && token, VV_ERR_NULL, "%s: NULL pointer", fn);
+  VV_REQUIRE(B >= 1 && B <= 16, VV_ERR_RANGE, "%s: B = %d not in 1..16", fn, B);
+  VV_REQUIRE(V >= 1, VV_ERR_RANGE, "%s: V = %d < 1", fn, V);
+  VV_REQUIRE(H >= 8 && H % 8 == 0 && H <= 8 * 64 * kMaxChunksPerLane, VV_ERR_SHAPE,
+             "%s: H = %d must be a multiple of 8 in [8, 4096]", fn, H);
+  VV_REQUIRE(lm_table_fits(V, H), VV_ERR_RANGE, "%s: a %d x %d fp16 table exceeds %lld bytes", fn, V, H,
+             (long long)kLmMaxTableBytes);
+  VV_REQUIRE(x_dtype == VV_F16 || x_dtype == VV_F32, VV_ERR_DTYPE, "%s: unknown x dtype", fn);
+  VV_REQUIRE(((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(x)) & 15) == 0, VV_ERR_RANGE,
+             "%s: W and x must be 16-byte aligned", fn);
+  return VV_OK;
+}
+}  // namespace vv
+
 using namespace vv;
 
 extern "C" {
@@ -414,16 +461,8 @@ size_t vv_lm_head_argmax_workspace(int B, int V, int H) {
 int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H, float* logits,
                       int32_t* token, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  VV_REQUIRE(W && x && token, VV_ERR_NULL, "vv_lm_head_argmax: NULL pointer");
-  VV_REQUIRE(B >= 1 && B <= 16, VV_ERR_RANGE, "vv_lm_head_argmax: B = %d not in 1..16", B);
-  VV_REQUIRE(V >= 1, VV_ERR_RANGE, "vv_lm_head_argmax: V = %d < 1", V);
-  VV_REQUIRE(H >= 8 && H % 8 == 0 && H <= 8 * 64 * kMaxChunksPerLane, VV_ERR_SHAPE,
-             "vv_lm_head_argmax: H = %d must be a multiple of 8 in [8, 4096]", H);
-  VV_REQUIRE(lm_table_fits(V, H), VV_ERR_RANGE, "vv_lm_head_argmax: a %d x %d fp16 table exceeds %lld bytes", V, H,
-             (long long)kLmMaxTableBytes);
-  VV_REQUIRE(x_dtype == VV_F16 || x_dtype == VV_F32, VV_ERR_DTYPE, "vv_lm_head_argmax: unknown x dtype");
-  VV_REQUIRE(((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(x)) & 15) == 0, VV_ERR_RANGE,
-             "vv_lm_head_argmax: W and x must be 16-byte aligned");
+  int rc = lm_validate(W, x, x_dtype, B, V, H, token, "vv_lm_head_argmax");
+  if (rc) return rc;
   const size_t need = vv_lm_head_argmax_workspace(B, V, H);
   VV_REQUIRE(ws && ws_bytes >= need, VV_ERR_WORKSPACE, "vv_lm_head_argmax: workspace needs %zu bytes", need);
   LmParams p{};
@@ -433,6 +472,32 @@ int vv_lm_head_argmax(const uint16_t* W, const void* x, int x_dtype, int B, int 
   lm_plan(p);
   lm_set_workspace(p, ws);
   VV_HIP(lm_launch(p, as_stream(stream)));
+  return VV_OK;
+}
+
+int vv_lm_head_argmax_noalloc(const uint16_t* W, const void* x, int x_dtype, int B, int V, int H, float* logits,
+                              int32_t* token, void* stream) {
+  clear_error();
+  int rc = lm_validate(W, x, x_dtype, B, V, H, token, "vv_lm_head_argmax_noalloc");
+  if (rc) return rc;
+  const size_t need = vv_lm_head_argmax_workspace(B, V, H);
+  VV_REQUIRE(need <= kLmScratchBytes, VV_ERR_RANGE,
+             "vv_lm_head_argmax_noalloc: %d rows x %d vocabulary rows need %zu bytes of argmax keys, more than "
+             "the %zu of its scratch (use vv_lm_head_argmax with a workspace)",
+             B, V, need, kLmScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  hipStream_t st = as_stream(stream);
+  // the keys this call uses start cleared (a fill kernel, not a memset: capture-safe)
+  VV_HIP(fill_zero(ws, need, st));
+  LmParams p{};
+  p.W = W; p.V = V; p.H = H; p.B = B;
+  p.x = x; p.x_f16 = x_dtype == VV_F16;
+  p.logits = logits; p.token = token;
+  lm_plan(p);
+  lm_set_workspace(p, ws);
+  VV_HIP(lm_launch(p, st));
   return VV_OK;
 }
 

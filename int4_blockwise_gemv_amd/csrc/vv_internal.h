@@ -333,6 +333,9 @@ struct LmParams {
 // every entry point that runs the lm_head rejects a table larger than this (VV_ERR_RANGE).
 constexpr int64_t kLmMaxTableBytes = 0x7fffffff;
 bool lm_table_fits(int64_t V, int64_t H);
+// the allocation-free lm_head's argmax keys: a file-scope device array of this size (lmhead.hip)
+constexpr size_t kLmScratchBytes = 256 * 1024;
+int scratch_address(void** out);   // the current device's address of that array
 void lm_plan(LmParams& p);
 size_t lm_workspace_bytes(int B, int V, int H);
 void lm_set_workspace(LmParams& p, void* ws);

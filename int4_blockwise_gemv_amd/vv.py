@@ -67,6 +67,7 @@ _SIGS = {
     "vv_gqa_decode": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _SZ, _P]),
     "vv_lm_head_argmax_workspace": (_SZ, [_I, _I, _I]),
     "vv_lm_head_argmax": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "vv_lm_head_argmax_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "vv_decode_step_workspace": (_SZ, [C.POINTER(vv_model), _I, _I]),
     "vv_decode_step": (_I, [C.POINTER(vv_model), C.POINTER(vv_state), _P]),
     "vv_decode_path": (_I, [C.POINTER(vv_model), C.POINTER(vv_state)]),
@@ -204,6 +205,14 @@ def lm_head_argmax(W, x, logits, token, ws, stream=None):
     B = x.shape[0]
     _check(lib().vv_lm_head_argmax(_ptr(W), _ptr(x), _dtype_code(x), B, V, H, _ptr(logits), _ptr(token), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)), "vv_lm_head_argmax")
+
+
+def lm_head_argmax_noalloc(W, x, logits, token, stream=None):
+    """vv_lm_head_argmax without a workspace (the library's scratch array holds the argmax keys)."""
+    V, H = W.shape
+    B = x.shape[0]
+    _check(lib().vv_lm_head_argmax_noalloc(_ptr(W), _ptr(x), _dtype_code(x), B, V, H, _ptr(logits), _ptr(token),
+                                           _stream(stream)), "vv_lm_head_argmax_noalloc")
 
 
 def stream_read(buf, sink, stream=None):

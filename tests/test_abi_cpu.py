@@ -209,3 +209,16 @@ def test_decode_step_validation():
     assert h.value is None
     assert L.vv_decode_graph_launch(None, None) == vvmod.VV_ERR_NULL
     assert L.vv_decode_graph_destroy(None) == vvmod.VV_OK
+
+
+def test_lm_head_noalloc_validation():
+    """The allocation-free lm_head rejects bad arguments, and inputs needing more argmax keys than its
+    256 KiB scratch, on the host (no GPU call is made on these paths)."""
+    L = _lib()
+    d = P(64)
+    assert L.vv_lm_head_argmax_noalloc(None, d, vvmod.VV_F32, 1, 100, 64, None, d, None) == vvmod.VV_ERR_NULL
+    assert L.vv_lm_head_argmax_noalloc(d, d, vvmod.VV_F32, 0, 100, 64, None, d, None) == vvmod.VV_ERR_RANGE
+    assert L.vv_lm_head_argmax_noalloc(d, d, vvmod.VV_F32, 1, 100, 60, None, d, None) == vvmod.VV_ERR_SHAPE
+    assert L.vv_lm_head_argmax_noalloc(d, d, 9, 1, 100, 64, None, d, None) == vvmod.VV_ERR_DTYPE
+    assert vvmod.lm_workspace(16, 3 << 20, 256) > 256 * 1024
+    assert L.vv_lm_head_argmax_noalloc(d, d, vvmod.VV_F32, 16, 3 << 20, 256, None, d, None) == vvmod.VV_ERR_RANGE
