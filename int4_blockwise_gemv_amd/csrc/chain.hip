@@ -31,7 +31,7 @@ constexpr int kCT = kCW * kWave;           // threads per workgroup
 constexpr int kCItemK = kCW * 8 * kBlock;  // K elements per workgroup at most (8 groups of 8 blocks)
 
 union CLds {
-  struct { uint16_t xs[2][kCItemK]; float red[kCW][kWave]; } g;   // xs: hi and lo parts
+  struct { uint32_t xd[kCItemK / kBlock * kDigitDwords]; float red[kCW][kWave]; } g;   // xd: digit images
   struct { float pm[kCW], pl[kCW]; float po[kCW][kWave]; } m;
 };
 
@@ -170,7 +170,7 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
 
   // The activation slice: four tagged fp32 words per thread, polled after the weight loads were
   // issued (the first poll returns behind them, so a workgroup whose weights arrive after its
-  // inputs polls once), then staged in LDS as fp16 hi + lo parts.  (Waiting on a few summary
+  // inputs polls once), then staged in LDS as the digit images of its 32-element blocks.  (Waiting on a few summary
   // words per producer instead, and reading the slice once after them, measured slower: the
   // extra round trip lands on every hop.)
   const int ec = min(e0 + 4 * tid, K - 4);
@@ -191,31 +191,21 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
 #pragma unroll
     for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
   }
-  uint2 xh, xl;
-  split_hl4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]), __uint_as_float((uint32_t)t[2]),
-            __uint_as_float((uint32_t)t[3]), xh, xl);
-  *reinterpret_cast<uint2*>(&L.g.xs[0][4 * tid]) = xh;
-  *reinterpret_cast<uint2*>(&L.g.xs[1][4 * tid]) = xl;
+  stage_digits(make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
+                           __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3])),
+               &L.g.xd[(tid / 8) * kDigitDwords]);
   __syncthreads();
 
   float acc = 0.f;
   {
-    const uint32_t m64 = vconst(0x54005400u);
-    const int xb0 = w * 8 * kBlock;
+    const int xb0 = w * 8;                          // this wave's first block in the slice
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
       const uint32_t dw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-      const u32x4* xb = reinterpret_cast<const u32x4*>(&L.g.xs[0][xb0 + i * kBlock]);
-      const u32x4* xlb = reinterpret_cast<const u32x4*>(&L.g.xs[1][xb0 + i * kBlock]);
-      float tt = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 xv = xb[k], lv = xlb[k];
-        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w}, l4[4] = {lv.x, lv.y, lv.z, lv.w};
-        tt = dot8_exact_hl(dw[k], x4, l4, tt, m64);
-      }
-      acc = fmaf(sc, tt, acc);
+      uint32_t lo[4], hi[4];
+      codes_to_bytes(dw, lo, hi);
+      acc = fmaf(sc, block_dot_digits(lo, hi, &L.g.xd[(xb0 + i) * kDigitDwords]), acc);
     }
   }
   L.g.red[w][lane] = acc;

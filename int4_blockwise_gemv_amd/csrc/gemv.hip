@@ -171,16 +171,18 @@ __device__ void fused_merge(const GemvParams& p) {
   publish_u64(p.xtag + (size_t)h * 128 + d, ((uint64_t)tag << 32) | __float_as_uint(Ow / Lw));
 }
 
-// XF: the activations are fp32 and are staged as two fp16 parts x = hi + lo (about 22 bits, so
-// they keep fp32 precision; each part meets the same code pairs); else they are fp16 as given.
-// XT implies XF (the merged attention output arrives as tagged fp32 words).
+// XF: the activations are fp32 and each 32-element block is staged as its 8-bit digit image
+// (22 bits relative to the block's largest magnitude; exact integer products with the codes);
+// else they are fp16 as given and meet the codes as fp16 pairs.  XT implies XF (the merged
+// attention output arrives as tagged fp32 words).
 template <int MT, int EPI, int WMAX, bool XT, bool XF>
 __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* __restrict__ qw,
                                                                   const uint4* __restrict__ sw,
                                                                   const void* __restrict__ xin) {
   constexpr int kItemK = WMAX * kBatch * kBlock;  // K elements per workgroup at most
-  constexpr int NP = XF ? 2 : 1;                  // activation parts in LDS
-  __shared__ __align__(16) uint16_t xs[NP][MT][kItemK];
+  // activations in LDS: fp16 as given, or (XF) the digit image of every 32-element block
+  __shared__ __align__(16) uint16_t xs[XF ? 1 : MT][XF ? 8 : kItemK];
+  __shared__ __align__(16) uint32_t xd[XF ? MT : 1][XF ? kItemK / kBlock * kDigitDwords : 4];
   __shared__ float red[WMAX][MT][kTileRows];
   static_assert(!XT || (MT == 1 && XF), "the fused merge serves batch 1 with fp32 activations");
   if constexpr (XT) {
@@ -202,16 +204,16 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
 
   // activation slice first (its loads return before the weights), 4 elements per thread per row;
   // with XT it is polled after the weight loads instead (it is still being merged)
-  static_assert(kItemK <= 4 * 64 * WMAX, "one 4-element activation load per thread covers the slice");
+  static_assert(kItemK == 4 * 64 * WMAX, "one 4-element activation load per thread covers the slice");
   const int ec = min(e0 + 4 * (int)threadIdx.x, K - 4);
   float4 xf[MT];
-  uint2 xr[NP][MT];
+  uint2 xr[MT];
   if constexpr (!XT) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const size_t off = (size_t)min(m, M - 1) * K + ec;
       if constexpr (XF) xf[m] = *reinterpret_cast<const float4*>(static_cast<const float*>(xin) + off);
-      else xr[0][m] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xin) + off);
+      else xr[m] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xin) + off);
     }
   }
   EpiPre<MT> ep;
@@ -253,53 +255,52 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
     xf[0] = make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
                         __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3]));
   }
-  if constexpr (XF) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) split_hl4(xf[m].x, xf[m].y, xf[m].z, xf[m].w, xr[0][m], xr[1][m]);
-  }
-#pragma unroll
-  for (int c = 0; c < NP; ++c)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) *reinterpret_cast<uint2*>(&xs[c][m][4 * threadIdx.x]) = xr[c][m];
-  __syncthreads();
-
-  const uint32_t m64 = vconst(0x54005400u);
-  const int xb0 = w * kBatch * kBlock;              // this wave's first element in the slice
-  float corr[MT];                                   // fp16 activations: the offset correction
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if constexpr (XF) {
-      corr[m] = 0.f;                                // exact codes: nothing to remove
-    } else {
-      const int o = xb0 + min(lane, 4 * kBatch - 1) * 8;
-      corr[m] = quad_sum(corr_quarter(*reinterpret_cast<const u32x4*>(&xs[0][m][o])));  // lane 4i+q: quarter q of block i
-    }
+    if constexpr (XF)   // 8 consecutive threads hold one block
+      stage_digits(xf[m], &xd[m][((int)threadIdx.x / 8) * kDigitDwords]);
+    else
+      *reinterpret_cast<uint2*>(&xs[m][4 * threadIdx.x]) = xr[m];
   }
+  __syncthreads();
+
+  const int xb0 = w * kBatch * kBlock;              // this wave's first element in the slice
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+  if constexpr (XF) {
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
-    const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+    for (int i = 0; i < kBatch; ++i) {
+      const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
+      const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+      uint32_t lo[4], hi[4];
+      codes_to_bytes(d, lo, hi);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[0][m][xb0 + i * kBlock]);
-      const u32x4* xl = reinterpret_cast<const u32x4*>(&xs[NP - 1][m][xb0 + i * kBlock]);
-      float t = XF ? 0.f : -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+      for (int m = 0; m < MT; ++m)
+        acc[m] = fmaf(sc, block_dot_digits(lo, hi, &xd[m][(xb0 / kBlock + i) * kDigitDwords]), acc[m]);
+    }
+  } else {
+    const uint32_t m64 = vconst(0x54005400u);
+    float corr[MT];   // the offset correction of the fp16 pairs, lane 4i + q: quarter q of block i
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 xv = xb[k];
-        const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-        if constexpr (XF) {
-          const u32x4 lv = xl[k];
-          const uint32_t l4[4] = {lv.x, lv.y, lv.z, lv.w};
-          t = dot8_exact_hl(d[k], x4, l4, t, m64);
-        } else {
+    for (int m = 0; m < MT; ++m)
+      corr[m] = quad_sum(corr_quarter(*reinterpret_cast<const u32x4*>(&xs[m][xb0 + min(lane, 4 * kBatch - 1) * 8])));
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float sc = i < nblk ? pick_scale(sv, i) : 0.f;
+      const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* xb = reinterpret_cast<const u32x4*>(&xs[m][xb0 + i * kBlock]);
+        float t = -__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[m]), 4 * i));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 xv = xb[k];
+          const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
           t = dot8_pairs(d[k], x4, t, m64);
         }
+        acc[m] = fmaf(sc, t, acc[m]);
       }
-      acc[m] = fmaf(sc, t, acc[m]);
     }
   }
 
@@ -424,6 +425,7 @@ void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t
     default: VV_LAUNCH((k_gemv<4, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x); break;
   }
 }
+
 }  // namespace
 
 hipError_t gemv_launch(const GemvParams& p0, hipStream_t st, KEv ev) {

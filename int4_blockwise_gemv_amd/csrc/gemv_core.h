@@ -29,39 +29,128 @@ __device__ __forceinline__ float dot8_pairs(uint32_t d, const uint32_t* x4, floa
   return acc;
 }
 
-// the same over activations given as two fp16 parts x = hi + lo (about 22 significant bits, so
-// the activation keeps fp32 precision).  Here the code pairs are made exact first, 64 + q - 72 =
-// q - 8 by one packed fp16 add (small integers, so exact): the fp32 sums then carry no offset to
-// cancel.  (Accumulating 64 + q and removing 72 sum(x) per block leaves partial sums about 15
-// times the block's result, and with them an fp32 rounding error of about 2e-6 of the output,
-// the precision the lo part is there to keep.)  Each pair meets both parts.
-__device__ __forceinline__ float dot8_exact_hl(uint32_t d, const uint32_t* xh4, const uint32_t* xl4, float acc,
-                                               uint32_t m64) {
-  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
-  const h2_t p01 = as_h2(((d << 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p23 = as_h2((d & 0x00F000F0u) | m64) + off;
-  const h2_t p45 = as_h2(((d >> 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p67 = as_h2(((d >> 8) & 0x00F000F0u) | m64) + off;
-  acc = __builtin_amdgcn_fdot2(p01, as_h2(xh4[0]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p23, as_h2(xh4[1]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p45, as_h2(xh4[2]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p67, as_h2(xh4[3]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p01, as_h2(xl4[0]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p23, as_h2(xl4[1]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p45, as_h2(xl4[2]), acc, false);
-  acc = __builtin_amdgcn_fdot2(p67, as_h2(xl4[3]), acc, false);
-  return acc;
+// The 8 codes of a dword as 4 exact fp16 pairs (q - 8) in element order: pair i holds the codes
+// of nibbles i and 4 + i.  Nibbles 0/4 and (after one byte shift) 2/6 sit in bits 0..3 of their
+// halves, where the fp16 magic 1024.0 (ulp 1) reads them as 1024 + q; nibbles 1/5 and 3/7 sit in
+// bits 4..7, where 64.0 (ulp 1/16) reads them as 64 + q.  One packed fp16 add of -1032 or -72
+// then leaves q - 8 exactly (small integers).  m1024, m64: the magics in VGPRs (vconst).
+__device__ __forceinline__ void code_pairs_exact(uint32_t d, uint32_t m1024, uint32_t m64, h2_t (&p)[4]) {
+  const h2_t o1024 = as_h2(0xE408E408u);     // (-1032, -1032)
+  const h2_t o64 = as_h2(0xD480D480u);       // (-72, -72)
+  const uint32_t d8 = d >> 8;
+  p[0] = as_h2((d & 0x000F000Fu) | m1024) + o1024;
+  p[1] = as_h2((d & 0x00F000F0u) | m64) + o64;
+  p[2] = as_h2((d8 & 0x000F000Fu) | m1024) + o1024;
+  p[3] = as_h2((d8 & 0x00F000F0u) | m64) + o64;
 }
 
-// four fp32 activations -> their fp16 hi parts (two pairs) and lo parts x - hi (two pairs)
-__device__ __forceinline__ void split_hl4(float a, float b, float c, float d, uint2& hi, uint2& lo) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b, hc = (_Float16)c, hd = (_Float16)d;
-  const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
-  const _Float16 lc = (_Float16)(c - (float)hc), ld = (_Float16)(d - (float)hd);
-  hi.x = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-  hi.y = (uint32_t)__builtin_bit_cast(uint16_t, hc) | ((uint32_t)__builtin_bit_cast(uint16_t, hd) << 16);
-  lo.x = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
-  lo.y = (uint32_t)__builtin_bit_cast(uint16_t, lc) | ((uint32_t)__builtin_bit_cast(uint16_t, ld) << 16);
+// ---- fp32 activations as 8-bit digits (the vector-ALU GEMVs' fp32 input) ----------------------
+// A 32-element block x_0..x_31 becomes X_i = rint(x_i 2^(22 - e)), with e the exponent of the
+// block's largest magnitude (|x| < 2^e), so |X_i| <= 2^22: each element keeps 22 bits relative
+// to that magnitude.  X_i is written as three signed bytes, X_i = d2 2^16 + d1 2^8 + d0 (the
+// bytes of X_i + 128 (1 + 2^8 + 2^16) less 128 each).  The products with the int4 codes are then
+// exact integer dot products (v_dot4_i32_i8 on the unsigned codes q), and the zero point comes off
+// exactly: sum_i (q_i - 8) d_ki = sum_i q_i d_ki - 8 sum_i d_ki.  Per digit level the block sum
+// is at most 32 * 15 * 128 in magnitude, and the levels combine exactly in fp32 up to one final
+// rounding.
+//
+// LDS image of one block (kDigitDwords dwords): level k = 0, 1, 2 takes dwords 8k .. 8k + 7, where
+// dword 2w holds the level-k digits of elements (0, 4, 1, 5) of word w (elements 8w .. 8w + 7)
+// and dword 2w + 1 those of elements (2, 6, 3, 7), the byte orders of (codes & 0x0F0F0F0F) and
+// ((codes >> 4) & 0x0F0F0F0F) for a code dword with the even elements in nibbles 0..3 and the
+// odd ones in nibbles 4..7; dword 24 is the scale 2^(e - 22) as fp32 (NaN when the block holds a
+// NaN or an infinity), dwords 25..27 are -8 sum_i d_ki for k = 0, 1, 2.
+constexpr int kDigitDwords = 28;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// sum / max over each group of 8 lanes (every lane gets its group's result)
+__device__ __forceinline__ int oct_sum(int v) {
+  v += dpp_i<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);   // quad_perm [2,3,0,1]
+  return v + dpp_i<0x141>(v);   // row_half_mirror: pairs the two quads of each 8 lanes
+}
+__device__ __forceinline__ float oct_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  return fmaxf(v, dpp_f<0x141>(v));
+}
+
+// One block's LDS image from the 8 consecutive lanes that hold it: lane r = lane % 8 holds
+// elements 4r .. 4r + 3 as v and writes its three level dwords; lane 0 of the 8 writes the scale
+// and the zero-point terms.  Every lane of the wave takes part (the cross-lane steps are DPP).
+__device__ __forceinline__ void stage_digits(float4 v, uint32_t* blk) {
+  const int r = (int)(threadIdx.x & 7);
+  const float a = oct_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  // fmaxf passes over NaNs: non-finite elements are counted on their own
+  constexpr float kMax = 3.40282347e38f;
+  const int bad = oct_sum((fabsf(v.x) <= kMax && fabsf(v.y) <= kMax && fabsf(v.z) <= kMax && fabsf(v.w) <= kMax) ? 0 : 1);
+  const int e = __builtin_amdgcn_frexp_expf(a);          // a < 2^e (0 for a = 0)
+  const int sh = 22 - e;
+  constexpr uint32_t kOff = 128u * (1u + 256u + 65536u);  // makes the three bytes unsigned
+  const uint32_t u0 = (uint32_t)((int)__builtin_rintf(__builtin_ldexpf(v.x, sh)) + (int)kOff);
+  const uint32_t u1 = (uint32_t)((int)__builtin_rintf(__builtin_ldexpf(v.y, sh)) + (int)kOff);
+  const uint32_t u2 = (uint32_t)((int)__builtin_rintf(__builtin_ldexpf(v.z, sh)) + (int)kOff);
+  const uint32_t u3 = (uint32_t)((int)__builtin_rintf(__builtin_ldexpf(v.w, sh)) + (int)kOff);
+  // level k of the 4 elements in element order, bytes less 128 (xor 0x80)
+  const uint32_t p01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);   // (u0.b0, u1.b0, u0.b1, u1.b1)
+  const uint32_t p23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
+  const uint32_t q01 = __builtin_amdgcn_perm(u1, u0, 0x06020602u);   // (u0.b2, u1.b2, ..)
+  const uint32_t q23 = __builtin_amdgcn_perm(u3, u2, 0x06020602u);
+  const uint32_t L[3] = {__builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u,
+                         __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u,
+                         __builtin_amdgcn_perm(q23, q01, 0x05040100u) ^ 0x80808080u};
+  // the pair of lanes holding word r / 2: the even lane writes elements (0, 4, 1, 5) of the word,
+  // the odd one (2, 6, 3, 7); perm(other, mine): bytes 4..7 are the partner's, 0..3 this lane's
+  const uint32_t sel = (r & 1) ? 0x03070206u : 0x05010400u;
+  int nd[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const uint32_t other = (uint32_t)dpp_i<0xB1>((int)L[k]);
+    blk[8 * k + r] = __builtin_amdgcn_perm(other, L[k], sel);
+    nd[k] = -8 * oct_sum(__builtin_amdgcn_sdot4((int)L[k], 0x01010101, 0, false));
+  }
+  if (r == 0) {
+    const float scale = bad ? __builtin_nanf("") : __builtin_ldexpf(1.0f, e - 22);
+    *reinterpret_cast<u32x4*>(blk + 24) = u32x4{__float_as_uint(scale), (uint32_t)nd[0], (uint32_t)nd[1], (uint32_t)nd[2]};
+  }
+}
+
+// The codes of one block (4 dwords, the tiled layout's order) split for v_dot4: lo[w] = the codes
+// of elements (0, 4, 1, 5) of word w as bytes, hi[w] those of (2, 6, 3, 7)
+__device__ __forceinline__ void codes_to_bytes(const uint32_t (&c)[4], uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo[w] = c[w] & 0x0F0F0F0Fu;
+    hi[w] = (c[w] >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+// sum_i (q_i - 8) x_i over one block for this lane's row: exact integer sums per digit level,
+// combined in fp32 (one rounding) and scaled by the block's power of two
+__device__ __forceinline__ float block_dot_digits(const uint32_t (&lo)[4], const uint32_t (&hi)[4],
+                                                  const uint32_t* blk) {
+  const u32x4 cs = *reinterpret_cast<const u32x4*>(blk + 24);
+  int S[3] = {(int)cs.y, (int)cs.z, (int)cs.w};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(blk + 8 * k);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(blk + 8 * k + 4);
+    int t = S[k];
+    t = __builtin_amdgcn_sdot4((int)lo[0], (int)a0.x, t, false);
+    t = __builtin_amdgcn_sdot4((int)hi[0], (int)a0.y, t, false);
+    t = __builtin_amdgcn_sdot4((int)lo[1], (int)a0.z, t, false);
+    t = __builtin_amdgcn_sdot4((int)hi[1], (int)a0.w, t, false);
+    t = __builtin_amdgcn_sdot4((int)lo[2], (int)a1.x, t, false);
+    t = __builtin_amdgcn_sdot4((int)hi[2], (int)a1.y, t, false);
+    t = __builtin_amdgcn_sdot4((int)lo[3], (int)a1.z, t, false);
+    t = __builtin_amdgcn_sdot4((int)hi[3], (int)a1.w, t, false);
+    S[k] = t;
+  }
+  const float t = fmaf((float)S[2], 65536.f, fmaf((float)S[1], 256.f, (float)S[0]));
+  return t * __uint_as_float(cs.x);
 }
 
 // C for one quarter (8 elements) of a block: (64 + 8) * (x0 + ... + x7)
@@ -169,16 +258,11 @@ __device__ __forceinline__ void block_to_operands(const u32x4& v, uint32_t (&t)[
   t[0] = t0; t[1] = t1; t[2] = t2; t[3] = t3;
 }
 
-// 8 codes of one dword (even elements in nibbles 0..3, odd in 4..7) -> 8 fp16 (q - 8), k order:
-// the nibble goes into the mantissa of fp16 64.0 (ulp 1/16, so the value reads 64 + q) and one
-// packed fp16 add subtracts 72, exactly
-__device__ __forceinline__ half8 codes_to_half8(uint32_t d, uint32_t m64) {
-  const h2_t off = as_h2(0xD480D480u);       // (-72, -72)
-  const h2_t p0 = as_h2(((d << 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p1 = as_h2((d & 0x00F000F0u) | m64) + off;
-  const h2_t p2 = as_h2(((d >> 4) & 0x00F000F0u) | m64) + off;
-  const h2_t p3 = as_h2(((d >> 8) & 0x00F000F0u) | m64) + off;
-  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+// 8 codes of one dword (even elements in nibbles 0..3, odd in 4..7) -> 8 fp16 (q - 8), k order
+__device__ __forceinline__ half8 codes_to_half8(uint32_t d, uint32_t m1024, uint32_t m64) {
+  h2_t p[4];
+  code_pairs_exact(d, m1024, m64, p);
+  return half8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
 }  // namespace vv

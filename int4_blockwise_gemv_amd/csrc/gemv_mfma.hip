@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_mfma(GemvParams p, const uint4
     u32x4 s4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) s4[g] = scl[w][16 * g + (lane & 15)];
-    const uint32_t m64 = vconst(0x54005400u);
+    const uint32_t m64 = vconst(0x54005400u), m1024 = vconst(0x64006400u);
     const uint16_t* xa = &xs[lane & 15][min(w, W - 1) * kBatchM * kBlock + 8 * (lane >> 4)];
 #pragma unroll
     for (int i = 0; i < kBatchM; ++i) {
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_mfma(GemvParams p, const uint4
       block_to_operands(wv[i], tg);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, codes_to_half8(tg[g], m64),
+        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, codes_to_half8(tg[g], m1024, m64),
                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const float sc = i < nblk ? pick_scale(s4[g], i) : 0.f;
         acc[g] += sc * d;

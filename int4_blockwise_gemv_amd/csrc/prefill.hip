@@ -36,22 +36,16 @@ struct PfGemm {
   uint16_t* act;                             // EPI_SILU: fp16 [S][N]
 };
 
-// 8 codes of one dword -> 8 fp16 (q - 8) * s, in the order of the decode GEMVs' codes_to_half8, then
-// one packed multiply by the block scale s2 = (s, s): exact for ternary codes (q - 8 in {-1, 0, 1});
-// for general int4 codes the product rounds once to fp16 (relative error <= 2^-11).  The nibble in
-// bits 0..3 of a 16-bit half goes into the mantissa of fp16 1024 (ulp 1: 1024 + q, less 1032) and
-// the one in bits 4..7 into that of fp16 64 (ulp 1/16: 64 + q, less 72), so one shift by 8 serves
-// the upper two nibbles; every step is exact.
-__device__ __forceinline__ half8 codes_to_half8_scaled(uint32_t d, uint32_t m64, h2_t s2) {
-  const uint32_t m1024 = 0x64006400u;        // (1024, 1024)
-  const h2_t off_lo = as_h2(0xE408E408u);    // (-1032, -1032)
-  const h2_t off_hi = as_h2(0xD480D480u);    // (-72, -72)
-  const uint32_t d8 = d >> 8;
-  const h2_t p0 = (as_h2((d & 0x000F000Fu) | m1024) + off_lo) * s2;
-  const h2_t p1 = (as_h2((d & 0x00F000F0u) | m64) + off_hi) * s2;
-  const h2_t p2 = (as_h2((d8 & 0x000F000Fu) | m1024) + off_lo) * s2;
-  const h2_t p3 = (as_h2((d8 & 0x00F000F0u) | m64) + off_hi) * s2;
-  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+// 8 codes of one dword -> 8 fp16 (q - 8) * s, in the order of the decode GEMVs' codes_to_half8: the
+// exact code pairs, then one packed multiply by the block scale s2 = (s, s): exact for ternary codes
+// (q - 8 in {-1, 0, 1}); for general int4 codes the product rounds once to fp16 (relative error
+// <= 2^-11).
+__device__ __forceinline__ half8 codes_to_half8_scaled(uint32_t d, uint32_t m1024, uint32_t m64, h2_t s2) {
+  h2_t p[4];
+  code_pairs_exact(d, m1024, m64, p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = p[i] * s2;
+  return half8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
 // (s, s) for the fp16 scale of block i (0..7) out of a lane's 4 scale dwords
@@ -112,7 +106,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_pf_gemm(PfGemm p) {   // tw
     for (int i = 0; i < 8; ++i) wv[i] = qt[(size_t)min(grp * 8 + i, nb - 1) * kTileRows];
   };
 
-  const uint32_t m64 = vconst(0x54005400u);
+  const uint32_t m64 = vconst(0x54005400u), m1024 = vconst(0x64006400u);
   f32x4 acc[TG][4];
 #pragma unroll
   for (int j = 0; j < TG; ++j)
@@ -142,7 +136,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_pf_gemm(PfGemm p) {   // tw
       block_to_operands(wv[i], tq);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const half8 bop = codes_to_half8_scaled(tq[g], m64, scale_pair(s4[g], i));
+        const half8 bop = codes_to_half8_scaled(tq[g], m1024, m64, scale_pair(s4[g], i));
 #pragma unroll
         for (int j = 0; j < TG; ++j) acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], bop, acc[j][g], 0, 0, 0);
       }

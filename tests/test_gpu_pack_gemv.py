@@ -152,15 +152,16 @@ def test_gemv_projection_shapes(cuda, shape, mode):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("mode", ["ternary", "absmax"])
 @pytest.mark.parametrize("shape", [(37888, 3584), (40000, 3616)])
-def test_gemv_two_groups_per_wave(cuda, shape, mode):
-    """Batch-1 grids with more 8-block groups than the chip holds waves at once take two groups per
-    wave: the 7B gate|up row count, and a ragged one (rows past a whole tile; K = 113 blocks, so the
-    last wave holds one group and a group past K)."""
+def test_gemv_grids_beyond_one_round(cuda, shape, mode, M):
+    """Batch-1 and -2 grids with more workgroups than the chip holds at once (the later ones start
+    as the first ones end): the 7B gate|up row count, and a ragged one (rows past a whole tile;
+    K = 113 blocks, so a tile's last group holds a single block)."""
     N, K = shape
     W = synth.master_weight(4, 0, synth.T_Q, N, K)
-    x = synth.fp16_normal(4, 0, synth.T_X, (1, K))
+    x = synth.fp16_normal(4, 0, synth.T_X, (M, K))
     ref = O.gemv(*O.pack(W, mode), x)
     q, s = _pack_gpu(W, mode, tiled=True)
     y = _gemv_gpu(q, s, N, K, x)
