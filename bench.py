@@ -1,15 +1,16 @@
 """Decode-step benchmark (one JSON line on stdout).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials T] [--workload decode-7b-p4000]
-                [--also decode-1.5b-p4096] [--seed 0]
+                [--also decode-1.5b-p4096,...] [--seed 0]
 
 One step = one vv_decode_step (28 layers of fused QKV GEMV, attention with KV append, o GEMV,
 gate/up GEMV + SiLU, down GEMV, then lm_head + argmax) replayed from a hipGraph on seeded
 synthetic weights, KV cache and input already resident in HBM.  Each trial times K back-to-back
 replays bracketed by torch.cuda.synchronize(); `value` and `ms_per_step` are the median of T
 trials (min and max are reported beside them).  The headline workload is the 7B-shaped step;
-the 1.5B-shaped step (the other shape of the metric) is measured in the same run and reported
-under `workloads`.
+the 1.5B-shaped step (the other shape of the metric), the 7B shape with general int4 weights over
+16384 positions with outliers, 16 ragged 1.5B sequences and the 0.5B classifier-free-guidance
+pair are measured in the same run and reported under `workloads`.
 
 Also reported, per workload:
   hbm          algorithmic bytes per step (packed int4 nibbles + fp16 scales + fp16 lm_head + K/V
@@ -433,7 +434,7 @@ def single_layer_bench(wl, args):
         "metric": "single-layer GEMV + GQA per second (cold: distinct copies streamed from HBM)",
         "value": 1e6 / cold_us, "unit": "GEMV+GQA/s", "n_gpus": 1, "steps": n, "warmup": 20,
         "ms_per_step": cold_us * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations, fp32 accumulate", "data": "synthetic (seeded)",
+        "dtype": "int4 weights, fp32 activations (exact int8-digit dot products), fp32 accumulate", "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "N": N, "K": K, "n_q": nq, "n_kv": nkv, "past": P, "quant": "ternary",
                    "copies": copies},
         "hot_us": hot_us, "cold_us": cold_us, "hot_us_trials": hot, "cold_us_trials": cold,
@@ -518,7 +519,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--workload", default="decode-7b-p4000")
-    ap.add_argument("--also", default="decode-1.5b-p4096",
+    ap.add_argument("--also", default="decode-1.5b-p4096,decode-7b-absmax-p16384,decode-1.5b-b16-ragged,"
+                                      "decode-0.5b-cfg-b2",
                     help="comma-separated workloads measured in the same run (reported under `workloads`), "
                          "or 'none'")
     ap.add_argument("--seed", type=int, default=0)
@@ -581,7 +583,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "dtype": "int4 weights, fp32 activations (exact int8-digit dot products), fp32 accumulate",
         "data": "synthetic (seeded N(0,0.02) fp32 masters ternarised on the GPU, fp16 N(0,1) KV/inputs)",
         "config": head["config"],
         "trials": {"n": args.trials, "us_per_step_median": head["us_per_step"],

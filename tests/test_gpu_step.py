@@ -278,6 +278,43 @@ def test_graph_replay_fused_merge(cuda):
     _compare(case, case.oracle())
 
 
+# 8 query heads of 128: the o projection takes 4-wave workgroups (K = 1024, four 8-block groups per
+# tile) behind 8 merge waves per head pair
+WIDE8 = synth.TinyShape(layers=2, hidden=512, n_q=8, n_kv=2, head_dim=128, inter=1024, vocab=1000)
+
+
+@pytest.mark.parametrize("pos", [[2], [63], [64], [200], [1099]])
+def test_step_wide_heads_many_splits(cuda, pos):
+    """Batch 1 with 8 query heads over 18 splits (cap 1100; positions in the first split only, at
+    split edges and in the last split): the merge in the o projection's launch over up to 18 splits."""
+    case = Case(WIDE8, 3, range(2), pos, 1100, path="layered")
+    case.run()
+    _compare(case, case.oracle())
+
+
+def test_graph_replay_wide_heads_many_splits(cuda):
+    """Graph replays interleaved with eager steps at the 8-head shape over 16 splits: the fused
+    merge's hand-off words carry the step counter, so a dozen steps give bit-identical results."""
+    import torch
+    case = Case(WIDE8, 9, range(2), [777], 1000, trace=True, path="layered")
+    case.run()
+    ref = [host(case.ds.logits).copy(), host(case.ds.token).copy(), host(case.ds.trace).copy()]
+    g = case.ds.graph()
+    try:
+        for r in range(6):
+            g.launch()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+            assert np.array_equal(host(case.ds.token), ref[1]), r
+            assert np.array_equal(host(case.ds.trace), ref[2]), r
+            case.run()
+            assert np.array_equal(host(case.ds.logits), ref[0]), r
+    finally:
+        g.close()
+    assert case.ds.status() == 0
+    _compare(case, case.oracle())
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_graph_follows_device_positions(cuda, path):
     """One captured graph serves successive positions: replays at pos, pos+1 == eager steps."""
