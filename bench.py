@@ -434,7 +434,7 @@ def single_layer_bench(wl, args):
         "metric": "single-layer GEMV + GQA per second (cold: distinct copies streamed from HBM)",
         "value": 1e6 / cold_us, "unit": "GEMV+GQA/s", "n_gpus": 1, "steps": n, "warmup": 20,
         "ms_per_step": cold_us * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights, fp32 activations (exact int8-digit dot products), fp32 accumulate", "data": "synthetic (seeded)",
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate", "data": "synthetic (seeded)",
         "config": {"workload": wl.name, "N": N, "K": K, "n_q": nq, "n_kv": nkv, "past": P, "quant": "ternary",
                    "copies": copies},
         "hot_us": hot_us, "cold_us": cold_us, "hot_us_trials": hot, "cold_us_trials": cold,
