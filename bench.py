@@ -344,7 +344,7 @@ def measure_decode(wl, args, headline):
         dom_ms = kb["gateup"]
         dom_bytes = proj_bytes(s, ("gate", "up"))
         dom_name = "gate/up int4 GEMV (+SiLU*up)"
-        prof = read_profile_mean(wl.name, "void k_gemv<1, 2, 8, false, true>")
+        prof = read_profile_mean(wl.name, "void vv::(anonymous namespace)::k_gemv<1, 2, 8, false, true>")
         traffic = read_traffic("gateup_7b" if s.hidden == 3584 else "gateup_1p5b")
         share = dom_ms * s.layers / med
     rec["roofline"] = {
