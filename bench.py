@@ -140,8 +140,9 @@ def build_inputs(wl, seed, path="auto", kv="f16"):
 
 
 def op_names(n_layers, path):
-    if path == "chained":   # the last layer's chained launch has no q|k|v segment: timed apart
-        return ["prep_qkv"] + ["attn", "chain"] * (n_layers - 1) + ["attn", "chain_last"] + ["lm_head"]
+    if path == "chained":   # the last layer's MLP launch has no q|k|v segment: timed apart
+        return (["prep_qkv"] + ["attn", "chain_mo", "chain"] * (n_layers - 1) + ["attn", "chain_mo", "chain_last"]
+                + ["lm_head"])
     return ["prep"] + ["qkv", "attn", "o", "gateup", "down"] * n_layers + ["lm_head"]
 
 
@@ -288,7 +289,8 @@ def proj_bytes(s, names):
 
 def eager_sum(kb, L, path):
     if path == "chained":
-        return kb["prep_qkv"] + kb["attn"] * L + kb["chain"] * (L - 1) + kb["chain_last"] + kb["lm_head"]
+        return (kb["prep_qkv"] + (kb["attn"] + kb["chain_mo"]) * L + kb["chain"] * (L - 1) + kb["chain_last"]
+                + kb["lm_head"])
     return sum(kb[k] for k in ("qkv", "attn", "o", "gateup", "down")) * L + kb["prep"] + kb["lm_head"]
 
 
@@ -333,11 +335,11 @@ def measure_decode(wl, args, headline):
                    "past": int(lens.max()), "quant": s.mode, "seed": args.seed, "path": path, "kv": args.kv},
     }
     if path == "chained":
-        # the chained launch of layers 0..L-2: merge, o, gate/up, down and the next layer's q|k|v
+        # the chained MLP launch of layers 0..L-2: gate/up, down and the next layer's q|k|v
         dom_ms = kb["chain"]
-        dom_bytes = proj_bytes(s, ("o", "gate", "up", "down", "q", "k", "v"))
-        dom_name = "chained launch (merge | o | gate/up | down | next q|k|v int4 GEMVs)"
-        prof = read_profile_mean(wl.name, "void vv::(anonymous namespace)::k_chain<false>")
+        dom_bytes = proj_bytes(s, ("gate", "up", "down", "q", "k", "v"))
+        dom_name = "chained MLP launch (gate/up | down | next q|k|v int4 GEMVs)"
+        prof = read_profile_mean(wl.name, "void vv::(anonymous namespace)::k_chain<2>")
         traffic = read_traffic("chain_7b" if s.hidden == 3584 else "chain_1p5b")
         share = (kb["chain"] * (s.layers - 1) + kb["chain_last"]) / med
     else:

@@ -8,18 +8,22 @@
 // 2 us of idle HBM (the ramp of the next grid and the tail of the last one), so the step runs as
 //   launch 0:      [prep | q|k|v of layer 0]
 //   per layer l:   attention(l)   (its own launch: RoPE, KV append, split records)
-//                  [merge(l) | o(l) | gate/up(l) | down(l) | q|k|v(l+1)]
+//                  [merge(l) | o(l)]
+//                  [gate/up(l) | down(l) | q|k|v(l+1)]
 //   then the lm_head + argmax.
-// A segment's workgroups issue their weight loads first and then wait for their inputs, which
-// earlier segments of the same grid publish as 64-bit tagged words: a 32-bit tag (the step
-// counter times a stride, plus the layer and stage) and an fp32 payload (the activations keep
-// fp32 precision; the GEMV segments stage them as fp16 hi + lo parts).  A word is stored once per step with a single atomic store, so a reader that sees the
-// expected tag sees the value, and no word ever needs clearing (a stale word carries an older
-// tag).  Progress: a workgroup only waits for workgroups with smaller indices (earlier segments,
-// and within a segment the split-K writers dispatched before their reader on the same XCD), and
-// each XCD dispatches its workgroups in increasing index, so the smallest unfinished workgroup
-// always runs to completion.  Every wait is bounded: one that gives up sets the step's status
-// word and continues with NaN instead of hanging.
+// (One launch for all five stages of a layer is slower: the MLP's waves, dispatched with the
+// merge and o, hold their places while they wait, and their first reads of the MLP input miss.)
+// A segment's workgroups read their inputs once, issue their weight loads, and then wait for any
+// input that was not there yet.  Earlier segments (of the same grid or an earlier launch) publish
+// them as 64-bit tagged words: a 32-bit tag (the step counter times a stride, plus the layer and
+// stage) and an fp32 payload (the activations keep fp32 precision; the GEMV segments stage them as
+// 8-bit digit images).  A word is stored once per step with a single atomic store, so a reader
+// that sees the expected tag sees the value, and no word ever needs clearing (a stale word carries
+// an older tag).  Progress: a workgroup only waits for workgroups with smaller indices (earlier
+// segments, and within a segment the split-K writers dispatched before their reader on the same
+// XCD) or of an earlier launch, and each XCD dispatches its workgroups in increasing index, so the
+// smallest unfinished workgroup always runs to completion.  Every wait is bounded: one that gives
+// up sets the step's status word and continues with NaN instead of hanging.
 #include "vv_internal.h"
 #include "gemv_core.h"
 
@@ -148,14 +152,25 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
   const int n = EPI == EPI_SILU ? tile * 32 + (lane & 31) : tile * kTileRows + lane;
   const int nc = min(n, g.N - 1);
   uint64_t ssv = 0, hv = 0;
-  if (EPI != EPI_RESID) ssv = collect_u64(g.ssin + min(lane, g.ss_n - 1));
-  if (EPI == EPI_RESID) hv = collect_u64(P.h + nc);
+  if (EPI != EPI_RESID) ssv = peek_u64(g.ssin + min(lane, g.ss_n - 1));
+  if (EPI == EPI_RESID) hv = peek_u64(P.h + nc);
   const uint32_t p16 = EPI == EPI_STORE ? g.bias[nc * g.has_bias] : EPI == EPI_RESID ? g.gamma[nc] : 0u;
 
   // this wave's group: 8 blocks and their 8 scales (scales first: block 0 needs them).  No load
   // sits behind a branch (a load whose result merges with a default at a join makes the compiler
   // wait for every load issued so far): a wave past the workgroup's W groups re-reads the last
   // block of the group before it, 1 KiB that its neighbour is fetching anyway, and gets scale 0.
+  // The activation slice: four tagged fp32 words per thread, read once (cached) before the
+  // weight loads, so that checking them waits for nothing else (vector loads complete in order,
+  // and a check behind the weight loads would hold the digit staging until the whole group had
+  // arrived); polled, behind the weights, only if a tag was not there yet.
+  const int ec = min(e0 + 4 * tid, K - 4);
+  const uint32_t xtag = ebase + g.xin_add;
+  const uint64_t* xp = g.xin + ec;
+  uint64_t t[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) t[k] = peek_u64(xp + k);
+
   const int grp = kg * W + min(w, W - 1);
   const int b0 = active ? grp * 8 : min(grp * 8 + 7, nb - 1);
   const int bstep = active ? 1 : 0;
@@ -168,28 +183,24 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     wv[i] = __builtin_nontemporal_load(qt + (size_t)min(b0 + bstep * i, nb - 1) * kTileRows);
   __builtin_amdgcn_sched_barrier(0);
 
-  // The activation slice: four tagged fp32 words per thread, polled after the weight loads were
-  // issued (the first poll returns behind them, so a workgroup whose weights arrive after its
-  // inputs polls once), then staged in LDS as the digit images of its 32-element blocks.  (Waiting on a few summary
-  // words per producer instead, and reading the slice once after them, measured slower: the
-  // extra round trip lands on every hop.)
-  const int ec = min(e0 + 4 * tid, K - 4);
-  const uint32_t xtag = ebase + g.xin_add;
-  const uint64_t* xp = g.xin + ec;
-  uint64_t t[4];
+  // Poll until every tag is there, then stage the slice in LDS as the digit images of its
+  // 32-element blocks.  (Waiting on a few summary words per producer instead, and reading the
+  // slice once after them, measured slower: the extra round trip lands on every hop.)
+  // The first check stays outside the loop: a check shared with the loop's re-reads would wait
+  // as if the words had been loaded last.
+  if (!__all(has_tag(t[0], xtag) && has_tag(t[1], xtag) && has_tag(t[2], xtag) && has_tag(t[3], xtag))) {
+    for (uint32_t it = 0;; ++it) {
+      if (it >= kSpinLimit) {
+        give_up(P.status);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
-  for (uint32_t it = 0;
-       !__all(has_tag(t[0], xtag) && has_tag(t[1], xtag) && has_tag(t[2], xtag) && has_tag(t[3], xtag)); ++it) {
-    if (it >= kSpinLimit) {
-      give_up(P.status);
+        for (int k = 0; k < 4; ++k) t[k] = 0x7fc00000u;   // fp32 NaN
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t[k] = 0x7fc00000u;   // fp32 NaN
-      break;
+      for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
+      if (__all(has_tag(t[0], xtag) && has_tag(t[1], xtag) && has_tag(t[2], xtag) && has_tag(t[3], xtag))) break;
     }
-    __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = collect_u64(xp + k);
   }
   stage_digits(make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
                            __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3])),
@@ -253,42 +264,33 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
 }
 
 // 8 waves per SIMD (at most 64 VGPRs): the weight streams of the GEMV segments need the
-// occupancy.  The segments sit at fixed positions (FIRST: prep, q|k|v; else merge, o, gate/up,
-// down and, unless nseg == 4, q|k|v), so every segment field is read at a constant offset.
-template <bool FIRST>
+// occupancy.  One instance per launch, with its segments at fixed positions (so every segment
+// field is read at a constant offset): CH_FIRST prep, q|k|v; CH_MO merge, o; CH_MLP gate/up,
+// down and, if nseg == 3, the next layer's q|k|v.
+template <int KIND>
 __global__ __launch_bounds__(kCT, 8) void k_chain(ChainParams P) {
   __shared__ CLds L;
   const uint32_t ebase = P.epoch[0] * P.tag_mul;
   int b = blockIdx.x;
-  if (FIRST) {
-    if (b < P.seg[0].blocks) {
-      seg_prep(P, b, ebase);
-      return;
-    }
-    seg_gemv<EPI_STORE>(P, P.seg[1], b - P.seg[0].blocks, ebase, L);
-    return;
-  }
   if (b < P.seg[0].blocks) {
-    seg_merge(P, b, ebase, L);
+    if constexpr (KIND == CH_FIRST) seg_prep(P, b, ebase);
+    else if constexpr (KIND == CH_MO) seg_merge(P, b, ebase, L);
+    else seg_gemv<EPI_SILU>(P, P.seg[0], b, ebase, L);
     return;
   }
   b -= P.seg[0].blocks;
-  if (b < P.seg[1].blocks) {
+  if constexpr (KIND == CH_FIRST) {
+    seg_gemv<EPI_STORE>(P, P.seg[1], b, ebase, L);
+  } else if constexpr (KIND == CH_MO) {
     seg_gemv<EPI_RESID>(P, P.seg[1], b, ebase, L);
-    return;
+  } else {
+    if (b < P.seg[1].blocks) {
+      seg_gemv<EPI_RESID>(P, P.seg[1], b, ebase, L);
+      return;
+    }
+    b -= P.seg[1].blocks;
+    if (P.nseg > 2) seg_gemv<EPI_STORE>(P, P.seg[2], b, ebase, L);
   }
-  b -= P.seg[1].blocks;
-  if (b < P.seg[2].blocks) {
-    seg_gemv<EPI_SILU>(P, P.seg[2], b, ebase, L);
-    return;
-  }
-  b -= P.seg[2].blocks;
-  if (b < P.seg[3].blocks) {
-    seg_gemv<EPI_RESID>(P, P.seg[3], b, ebase, L);
-    return;
-  }
-  b -= P.seg[3].blocks;
-  if (P.nseg > 4) seg_gemv<EPI_STORE>(P, P.seg[4], b, ebase, L);
 }
 
 }  // namespace
@@ -304,8 +306,15 @@ void chain_gemv_plan(CSeg& g) {
 hipError_t chain_launch(const ChainParams& P, hipStream_t st, KEv ev) {
   int grid = 0;
   for (int i = 0; i < P.nseg; ++i) grid += P.seg[i].blocks;
-  if (P.seg[0].kind == SEG_PREP) VV_LAUNCH((k_chain<true>), dim3(grid), dim3(kCT), st, ev, P);
-  else VV_LAUNCH((k_chain<false>), dim3(grid), dim3(kCT), st, ev, P);
+  const int k0 = P.seg[0].kind, k1 = P.nseg > 1 ? P.seg[1].kind : -1;
+  if (k0 == SEG_PREP && P.nseg == 2 && k1 == SEG_QKV)
+    VV_LAUNCH((k_chain<CH_FIRST>), dim3(grid), dim3(kCT), st, ev, P);
+  else if (k0 == SEG_MERGE && P.nseg == 2 && k1 == SEG_O)
+    VV_LAUNCH((k_chain<CH_MO>), dim3(grid), dim3(kCT), st, ev, P);
+  else if (k0 == SEG_GU && k1 == SEG_DOWN && (P.nseg == 2 || (P.nseg == 3 && P.seg[2].kind == SEG_QKV)))
+    VV_LAUNCH((k_chain<CH_MLP>), dim3(grid), dim3(kCT), st, ev, P);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

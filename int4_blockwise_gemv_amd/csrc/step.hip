@@ -145,7 +145,7 @@ Layout layout_of(const Dims& d) {
 
 size_t step_bytes(const vv_model* m, int B, int cap) { return align_up(layout_of(dims_of(m, B, cap)).total, 256); }
 
-// The chained path (two launches per layer) serves batch 1 over fp16 caches with 2..128
+// The chained path (three launches per layer) serves batch 1 over fp16 caches with 2..128
 // attention splits; everything else takes the layered path (five launches per layer).
 bool chain_supported(const vv_model* m, const vv_state* s) {
   if (s->batch != 1 || s->kv_dtype == VV_F32 || m->n_layers < 1) return false;
@@ -156,10 +156,10 @@ bool chain_supported(const vv_model* m, const vv_state* s) {
 }
 
 // AUTO takes the chained plan where it serves the state and the model is narrow (hidden <= 2048):
-// there the stages are small and the hops it saves dominate (1.5B-shaped step 893 against 985 us
-// on MI355X); at the 7B width a stage's dequantisation work, released all at once by its
-// dependency instead of overlapping its weight stream, costs more than the launches saved (1632
-// against 1515 us), so the layered plan stays.
+// there the stages are small and the hops it saves dominate (1.5B-shaped step 935 against 1037 us
+// on MI355X); at the 7B width a segment's waves cannot all be resident, and those waiting for
+// their inputs hold the places that later weight streams need (1705 against 1561 us with every
+// stage of a layer chained, 1648 with the three-launch plan), so the layered plan stays.
 constexpr int kChainAutoMaxHidden = 2048;
 bool use_chain(const vv_model* m, const vv_state* s) {
   if (s->path == VV_PATH_CHAINED) return true;
@@ -167,10 +167,10 @@ bool use_chain(const vv_model* m, const vv_state* s) {
 }
 
 // timed operations of one step (two events each): prep, then per layer q|k|v, attention, o,
-// gate/up, down, then the lm_head; chained: prep + q|k|v of layer 0, per layer attention and the
-// chained launch, then the lm_head
+// gate/up, down, then the lm_head; chained: prep + q|k|v of layer 0, per layer attention,
+// [merge | o] and [gate/up | down | next q|k|v], then the lm_head
 int step_ops(const vv_model* m, const vv_state* s) {
-  return use_chain(m, s) ? 2 * m->n_layers + 2 : 5 * m->n_layers + 2;
+  return use_chain(m, s) ? 3 * m->n_layers + 2 : 5 * m->n_layers + 2;
 }
 
 int validate(const vv_model* m, const vv_state* s, const char* fn) {
@@ -263,7 +263,7 @@ int enqueue_feedback(const vv_model* m, const vv_state* s, hipStream_t st) {
   return VV_OK;
 }
 
-// The chained path: [prep | q|k|v(0)], then per layer the attention and [merge | o | gate/up |
+// The chained path: [prep | q|k|v(0)], then per layer the attention, [merge | o] and [gate/up |
 // down | q|k|v(l+1)], then the lm_head.  Tags: stage st of layer l is 1 + 4 l + st (st: 0 the
 // q|k|v input and residual, 1 the attention output, 2 the MLP input and residual, 3 SiLU * up),
 // added to epoch * (4 (L + 1) + 1); the epoch advances at the end of every step.
@@ -345,43 +345,41 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       ap.out = nullptr; ap.out_f16 = 1;
       VV_HIP(attn_launch_with_rope(ap, rope, st, event_pair(s, op++)));
     }
-    ChainParams P = base;
-    int ns = 0;
-    {  // merge of the split records: one workgroup per query head
+    {  // [merge | o]: the split records -> the attention output -> o + residual, the MLP's input
+      ChainParams P = base;
       P.part = a.part; P.nsplit = a.nsplit; P.split = a.split; P.nq = d.nq; P.nkv = d.nkv;
       P.xo = U64(lay.txo); P.mrg_add = tagadd(l, XO);
       CSeg mg{};
       mg.kind = SEG_MERGE;
       mg.blocks = (int)(cdiv(d.nq, kNumXcd) * kNumXcd);
-      P.seg[ns++] = mg;
-    }
-    {  // o projection + residual -> the MLP's input
+      P.seg[0] = mg;
       CSeg g = gemv_seg(SEG_O, y.o_q, y.o_s, H, d.nq * kHeadDim, d.ntH, lay.ws_o);
       g.xin = U64(lay.txo); g.xin_add = tagadd(l, XO);
       g.hin_add = tagadd(l, XQ); g.out_add = tagadd(l, XM);
       g.gamma = y.g2; g.xgout = U64(lay.txm); g.ssout = U64(lay.tssm);
-      P.seg[ns++] = g;
+      P.seg[1] = g;
+      P.nseg = 2;
+      VV_HIP(chain_launch(P, st, event_pair(s, op++)));
     }
-    {  // gate/up + SiLU * up
-      CSeg g = gemv_seg(SEG_GU, y.gu_q, y.gu_s, d.I, H, 2 * d.ntI, lay.ws_gu);
+    {  // [gate/up | down | q|k|v(l+1)]
+      ChainParams P = base;
+      CSeg g = gemv_seg(SEG_GU, y.gu_q, y.gu_s, d.I, H, 2 * d.ntI, lay.ws_gu);   // + SiLU * up
       g.xin = U64(lay.txm); g.xin_add = tagadd(l, XM);
       g.ssin = U64(lay.tssm); g.ss_add = tagadd(l, XM);
       g.act = U64(lay.txd); g.out_add = tagadd(l, XD);
-      P.seg[ns++] = g;
-    }
-    {  // down + residual -> the next layer's input (or the lm_head's)
-      CSeg g = gemv_seg(SEG_DOWN, y.down_q, y.down_s, H, d.I, d.ntH, lay.ws_down);
+      P.seg[0] = g;
+      g = gemv_seg(SEG_DOWN, y.down_q, y.down_s, H, d.I, d.ntH, lay.ws_down);   // + residual
       g.xin = U64(lay.txd); g.xin_add = tagadd(l, XD);
       g.hin_add = tagadd(l, XM); g.out_add = tagadd(l + 1, XQ);
       g.gamma = last ? m->gf : m->layers[l + 1].g1;
       if (!last) { g.xgout = U64(lay.txq); g.ssout = U64(lay.tssq); }
       else { g.gf = gf; g.sumsq = sumsq; }
       g.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * H : nullptr;
-      P.seg[ns++] = g;
+      P.seg[1] = g;
+      P.nseg = 2;
+      if (!last) P.seg[P.nseg++] = qkv_seg(l + 1);
+      VV_HIP(chain_launch(P, st, event_pair(s, op++)));
     }
-    if (!last) P.seg[ns++] = qkv_seg(l + 1);
-    P.nseg = ns;
-    VV_HIP(chain_launch(P, st, event_pair(s, op++)));
   }
   const int rc = enqueue_lm(m, s, gf, sumsq, ws + lay.ws_lm, status, epoch, st, event_pair(s, op++));
   if (rc) return rc;

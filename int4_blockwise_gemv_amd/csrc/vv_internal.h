@@ -152,6 +152,11 @@ __device__ __forceinline__ float collect_f32(const float* p) {
 __device__ __forceinline__ uint64_t collect_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A first, cached read of a tagged word.  collect_u64 is the same 64-bit load with the agent-scope
+// bit, which makes it skip this XCD's L2; this one may be served by a stale cached copy, but tag
+// and value come from one 64-bit store, so a word that carries the expected tag is the current
+// one, and any other sends the reader on to collect_u64.
+__device__ __forceinline__ uint64_t peek_u64(const uint64_t* p) { return *p; }
 // all of this wave's earlier memory operations have completed (s_waitcnt 0); also a compiler barrier
 __device__ __forceinline__ void wait_published() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -348,9 +353,11 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t st, KEv ev = {});
 // so that a workgroup's index within its segment keeps its XCD).  Cross-segment data are 64-bit
 // tagged words (tag << 32 | fp32 bits); a tag is epoch * tag_mul + add.
 constexpr int kChainWaves = 8;        // waves per workgroup
-constexpr int kChainMaxSeg = 5;
+constexpr int kChainMaxSeg = 3;
 constexpr int kChainMaxSplits = 128;  // attention splits the merge segment takes
 enum ChainSegKind { SEG_PREP = 0, SEG_MERGE, SEG_QKV, SEG_O, SEG_GU, SEG_DOWN };
+// the three launches of the chained step: [prep | q|k|v], [merge | o], [gate/up | down (| q|k|v)]
+enum ChainLaunch { CH_FIRST = 0, CH_MO, CH_MLP };
 struct CSeg {
   int kind, blocks;
   // GEMV segments (batch 1, tiled weights; wpt workgroups of wpg waves per tile)
