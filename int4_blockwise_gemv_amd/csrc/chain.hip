@@ -228,7 +228,7 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
     const int nw = g.wpt - 1;
     uint64_t* sl = g.slots + (size_t)tile * nw * kTileRows;
     if (kg < nw) {   // writer: tagged partial into the tile's slot kg, then done
-      publish_u64(&sl[(size_t)kg * kTileRows + lane], kFresh | __float_as_uint(tot));
+      slot_store(&sl[(size_t)kg * kTileRows + lane], kFresh | __float_as_uint(tot));
       return;
     }
     tot = poll_sum(sl + lane, nw, kTileRows, P.status) + tot;

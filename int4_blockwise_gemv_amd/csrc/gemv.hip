@@ -327,7 +327,7 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   if (kg < nw) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      if (m < M) publish_u64(&sl[((size_t)kg * MT + m) * kTileRows + lane], kFresh | __float_as_uint(tot[m]));
+      if (m < M) slot_store(&sl[((size_t)kg * MT + m) * kTileRows + lane], kFresh | __float_as_uint(tot[m]));
     return;
   }
 #pragma unroll

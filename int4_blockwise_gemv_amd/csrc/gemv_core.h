@@ -174,8 +174,20 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // ---- split-K hand-off without atomics (the VALU GEMV) ---------------------------------------------
 // A writer stores its partial as a 64-bit (tag, fp32 bits) word into its slot and exits; the reader
 // polls the slots, adds them in a fixed order and clears them.
+//
+// The writers of a tile and its reader run on one XCD (split_role deals each tile's workgroups to
+// one XCD; workgroup i of a launch runs on XCD i % 8), which has one L2 behind all its CUs.  So a
+// slot word is written only as far as that L2 (workgroup scope: the store is not written through
+// to memory, which would queue it behind the weight stream), and the reader's agent-scope loads,
+// which skip the CU's own L1, find it there.  A slot word is one aligned 64-bit store, so a reader
+// that sees the tag sees the value.  Kernel boundaries write the L2s back, so a slot region may be
+// reused by a later launch with another tile-to-XCD deal.
 constexpr uint64_t kFresh = 1ull << 32;     // tag of a filled hand-off slot (cleared slots are 0)
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait gives up (seconds)
+
+__device__ __forceinline__ void slot_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // Sum of the n tagged fp32 values at p[k * stride], k in order, once every tag is set; then clears
 // the slots.  Polls kPollBatch slots at a time (every lane of the wave takes part in the vote):
@@ -204,7 +216,7 @@ __device__ __forceinline__ float poll_sum(uint64_t* p, int n, size_t stride, int
     for (int k = 0; k < kPollBatch; ++k)
       if (k0 + k < n) {
         s += __uint_as_float((uint32_t)v[k]);
-        publish_u64(p + (size_t)(k0 + k) * stride, 0);
+        slot_store(p + (size_t)(k0 + k) * stride, 0);
       }
   }
   return s;
