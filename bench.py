@@ -139,7 +139,17 @@ def build_inputs(wl, seed, path="auto", kv="f16"):
     return dm, ds, lens
 
 
-def op_names(n_layers, path):
+# the chained plan splits the MLP launch into [gate/up] and [down | next q|k|v] above this width
+CHAIN_SPLIT_MLP_HIDDEN = 2048
+
+
+def op_names(n_layers, path, hidden=0, batch=1):
+    if path == "layered" and batch == 1:   # down and the next layer's q|k|v share a launch
+        return (["prep", "qkv"] + ["attn", "o", "gateup", "down_qkv"] * (n_layers - 1)
+                + ["attn", "o", "gateup", "down"] + ["lm_head"])
+    if path == "chained" and hidden > CHAIN_SPLIT_MLP_HIDDEN:
+        return (["prep_qkv"] + ["attn", "chain_mo", "chain_gu", "chain_dq"] * (n_layers - 1)
+                + ["attn", "chain_mo", "chain_gu", "chain_d_last"] + ["lm_head"])
     if path == "chained":   # the last layer's MLP launch has no q|k|v segment: timed apart
         return (["prep_qkv"] + ["attn", "chain_mo", "chain"] * (n_layers - 1) + ["attn", "chain_mo", "chain_last"]
                 + ["lm_head"])
@@ -154,7 +164,7 @@ def kernel_breakdown(ds, n_layers, steps, path):
     reports), not the time the stream reaches a marker."""
     import ctypes as C
     import torch
-    names = op_names(n_layers, path)
+    names = op_names(n_layers, path, ds.model.shape.hidden, ds.batch)
     n_ev = 2 * len(names)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in evs:  # torch creates the HIP event on first record
@@ -288,9 +298,15 @@ def proj_bytes(s, names):
 
 
 def eager_sum(kb, L, path):
+    if path == "chained" and "chain_gu" in kb:
+        return (kb["prep_qkv"] + (kb["attn"] + kb["chain_mo"] + kb["chain_gu"]) * L + kb["chain_dq"] * (L - 1)
+                + kb["chain_d_last"] + kb["lm_head"])
     if path == "chained":
         return (kb["prep_qkv"] + (kb["attn"] + kb["chain_mo"]) * L + kb["chain"] * (L - 1) + kb["chain_last"]
                 + kb["lm_head"])
+    if "down_qkv" in kb:
+        return (kb["prep"] + kb["qkv"] + (kb["attn"] + kb["o"] + kb["gateup"]) * L + kb["down_qkv"] * (L - 1)
+                + kb["down"] + kb["lm_head"])
     return sum(kb[k] for k in ("qkv", "attn", "o", "gateup", "down")) * L + kb["prep"] + kb["lm_head"]
 
 
@@ -334,7 +350,15 @@ def measure_decode(wl, args, headline):
                    "n_q": s.n_q, "n_kv": s.n_kv, "head_dim": s.head_dim, "vocab": s.vocab, "batch": wl.batch,
                    "past": int(lens.max()), "quant": s.mode, "seed": args.seed, "path": path, "kv": args.kv},
     }
-    if path == "chained":
+    if path == "chained" and "chain_gu" in kb:
+        # wide models: gate/up in a chained launch of its own
+        dom_ms = kb["chain_gu"]
+        dom_bytes = proj_bytes(s, ("gate", "up"))
+        dom_name = "chained gate/up launch (int4 GEMV + SiLU*up)"
+        prof = read_profile_mean(wl.name, "void vv::(anonymous namespace)::k_chain<3>")
+        traffic = None
+        share = dom_ms * s.layers / med
+    elif path == "chained":
         # the chained MLP launch of layers 0..L-2: gate/up, down and the next layer's q|k|v
         dom_ms = kb["chain"]
         dom_bytes = proj_bytes(s, ("gate", "up", "down", "q", "k", "v"))

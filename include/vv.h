@@ -220,11 +220,13 @@ int vv_lm_head_argmax_noalloc(const uint16_t* W, const void* x, int x_dtype, int
  *   VV_PATH_LAYERED  one launch per stage: 1 + 5 L + 1 kernels (plus a split merge per layer
  *                    when the cache is split, except at batch 1 over fp16 caches with at most 64
  *                    splits, where the o projection's launch does the merge); any batch up to
- *                    max_batch, fp16 or fp32 caches.
+ *                    max_batch, fp16 or fp32 caches.  At batch 1 each layer's down projection
+ *                    and the next layer's q|k|v share one launch (2 + 4 L + 1 kernels).
  *   VV_PATH_CHAINED  three launches per layer: the attention, one grid running the split merge
  *                    and o, and one running gate/up, down and the next layer's q|k|v, as
  *                    consecutive segments whose workgroups start their weight streams before
  *                    their inputs are ready and wait for them on tagged words (1 + 3 L + 1
+ *                    kernels); above hidden 2048 gate/up runs in a launch of its own (1 + 4 L + 1
  *                    kernels); batch 1, fp16 caches, n_layers >= 1 and 2..128 attention
  *                    splits (cap 65..8192 positions), else VV_ERR_UNSUPPORTED.
  *   VV_PATH_AUTO     the chained path where it applies and hidden <= 2048 (measured faster for
@@ -277,10 +279,13 @@ typedef struct vv_state {
                                       operation i's kernels (hipExtLaunchKernel's kernel
                                       timestamps, not stream markers).  Layered: prep, then
                                       per layer qkv, attention (+ split merge), o, gate/up,
-                                      down, then lm_head: 2*(5*n_layers + 2) events.  Chained:
-                                      prep + qkv of layer 0, per layer attention, merge + o and
-                                      gate/up + down + the next qkv, then lm_head:
-                                      2*(3*n_layers + 2) events.  NULL
+                                      down, then lm_head: 2*(5*n_layers + 2) events; at batch 1
+                                      prep, qkv of layer 0, per layer attention, o, gate/up and
+                                      down + the next qkv, then lm_head: 2*(4*n_layers + 3).
+                                      Chained: prep + qkv of layer 0, per layer attention,
+                                      merge + o and gate/up + down + the next qkv (above hidden
+                                      2048: gate/up, then down + the next qkv), then lm_head:
+                                      2*(3*n_layers + 2) (2*(4*n_layers + 2)) events.  NULL
                                       disables; graphs reject it. */
   int n_events;                    /* entries in events */
   int path;                        /* VV_PATH_AUTO (0), VV_PATH_LAYERED or VV_PATH_CHAINED */

@@ -139,8 +139,10 @@ __device__ void seg_merge(const ChainParams& P, int bid, uint32_t ebase, CLds& L
 
 // ---- one GEMV segment (batch 1): the decomposition, dequantisation and split-K hand-off of the
 // layered GEMV kernel, with tagged inputs and outputs --------------------------------------------
-template <int EPI>
+// PLAIN (EPI_RESID only): the input and the residual are plain fp32 written before this launch
+template <int EPI, bool PLAIN = false>
 __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t ebase, CLds& L) {
+  static_assert(!PLAIN || EPI == EPI_RESID, "plain inputs: the residual segment after a kernel boundary");
   const int K = g.K, nb = K / kBlock, ng = (nb + 7) / 8, W = g.wpg;
   int tile, kg;
   if (!split_role(g.ntiles, g.wpt, tile, kg, bid)) return;
@@ -153,7 +155,7 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
   const int nc = min(n, g.N - 1);
   uint64_t ssv = 0, hv = 0;
   if (EPI != EPI_RESID) ssv = peek_u64(g.ssin + min(lane, g.ss_n - 1));
-  if (EPI == EPI_RESID) hv = peek_u64(P.h + nc);
+  if (EPI == EPI_RESID) hv = PLAIN ? (uint64_t)__float_as_uint(g.hp[nc]) : peek_u64(P.h + nc);
   const uint32_t p16 = EPI == EPI_STORE ? g.bias[nc * g.has_bias] : EPI == EPI_RESID ? g.gamma[nc] : 0u;
 
   // this wave's group: 8 blocks and their 8 scales (scales first: block 0 needs them).  No load
@@ -168,8 +170,13 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
   const uint32_t xtag = ebase + g.xin_add;
   const uint64_t* xp = g.xin + ec;
   uint64_t t[4];
+  if constexpr (PLAIN) {
+    const float4 xv = *reinterpret_cast<const float4*>(g.xp + ec);
+    t[0] = tag_f32(xtag, xv.x); t[1] = tag_f32(xtag, xv.y); t[2] = tag_f32(xtag, xv.z); t[3] = tag_f32(xtag, xv.w);
+  } else {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) t[k] = peek_u64(xp + k);
+    for (int k = 0; k < 4; ++k) t[k] = peek_u64(xp + k);
+  }
 
   const int grp = kg * W + min(w, W - 1);
   const int b0 = active ? grp * 8 : min(grp * 8 + 7, nb - 1);
@@ -248,9 +255,13 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
       if (lane < 32 && n < g.N) publish_u64(g.act + n, tag_f32(otag, silu(gt) * u));
     }
   } else {   // EPI_RESID: h += tot; the next norm's numerator and sum(h^2) of the tile
-    hv = wait_word(P.h + nc, hv, ebase + g.hin_add, P.status);
+    if constexpr (!PLAIN) hv = wait_word(P.h + nc, hv, ebase + g.hin_add, P.status);
     const float hn = __uint_as_float((uint32_t)hv) + tot;
-    publish_u64(P.h + n, tag_f32(otag, hn));
+    if constexpr (PLAIN) {
+      if (n < g.N) g.hp[n] = hn;
+    } else {
+      publish_u64(P.h + n, tag_f32(otag, hn));
+    }
     if (g.trace) g.trace[n] = hn;
     const float gv = h2f((uint16_t)p16) * hn;
     if (g.gf) g.gf[n] = gv;
@@ -275,14 +286,19 @@ __global__ __launch_bounds__(kCT, 8) void k_chain(ChainParams P) {
   if (b < P.seg[0].blocks) {
     if constexpr (KIND == CH_FIRST) seg_prep(P, b, ebase);
     else if constexpr (KIND == CH_MO) seg_merge(P, b, ebase, L);
+    else if constexpr (KIND == CH_DQ) seg_gemv<EPI_RESID>(P, P.seg[0], b, ebase, L);
+    else if constexpr (KIND == CH_LDQ) seg_gemv<EPI_RESID, true>(P, P.seg[0], b, ebase, L);
     else seg_gemv<EPI_SILU>(P, P.seg[0], b, ebase, L);
     return;
   }
+  if constexpr (KIND == CH_GU) return;
   b -= P.seg[0].blocks;
   if constexpr (KIND == CH_FIRST) {
     seg_gemv<EPI_STORE>(P, P.seg[1], b, ebase, L);
   } else if constexpr (KIND == CH_MO) {
     seg_gemv<EPI_RESID>(P, P.seg[1], b, ebase, L);
+  } else if constexpr (KIND == CH_DQ || KIND == CH_LDQ) {
+    if (P.nseg > 1) seg_gemv<EPI_STORE>(P, P.seg[1], b, ebase, L);
   } else {
     if (b < P.seg[1].blocks) {
       seg_gemv<EPI_RESID>(P, P.seg[1], b, ebase, L);
@@ -313,6 +329,12 @@ hipError_t chain_launch(const ChainParams& P, hipStream_t st, KEv ev) {
     VV_LAUNCH((k_chain<CH_MO>), dim3(grid), dim3(kCT), st, ev, P);
   else if (k0 == SEG_GU && k1 == SEG_DOWN && (P.nseg == 2 || (P.nseg == 3 && P.seg[2].kind == SEG_QKV)))
     VV_LAUNCH((k_chain<CH_MLP>), dim3(grid), dim3(kCT), st, ev, P);
+  else if (k0 == SEG_GU && P.nseg == 1)   // alone in its launch: exactly the waves of its groups
+    VV_LAUNCH((k_chain<CH_GU>), dim3(grid), dim3(kWave * P.seg[0].wpg), st, ev, P);
+  else if (k0 == SEG_DOWN && (P.nseg == 1 || (P.nseg == 2 && k1 == SEG_QKV)) && P.seg[0].xp)
+    VV_LAUNCH((k_chain<CH_LDQ>), dim3(grid), dim3(kCT), st, ev, P);
+  else if (k0 == SEG_DOWN && (P.nseg == 1 || (P.nseg == 2 && k1 == SEG_QKV)))
+    VV_LAUNCH((k_chain<CH_DQ>), dim3(grid), dim3(kCT), st, ev, P);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

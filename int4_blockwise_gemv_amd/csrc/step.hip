@@ -3,12 +3,16 @@
 // decoder_step contract ("vibevoice-asr-bitnet-onnx" page, graph contracts):
 //   input_embeds [B,H], position_ids [B], past K/V -> logits [B,V], present K/V (one more slot)
 // on the Qwen2 layer of the 1.5B STATUS page (Architecture): pre-RMSNorm, q/k/v bias, GQA,
-// SiLU-gated MLP, residual adds.  One step is 1 + 5 L + 1 kernels:
+// SiLU-gated MLP, residual adds.  The layered plan is 1 + 5 L + 1 kernels:
 //   prep (embeddings -> residual stream, RoPE table)
 //   per layer: QKV GEMV (RMSNorm folded in) | attention (+RoPE, KV append) and its split merge
 //              (a kernel of its own, or at batch 1 over fp16 caches the leading workgroups of the
 //              o GEMV's launch) | o GEMV + residual | gate/up GEMV + SiLU*up | down GEMV + residual
 //   lm_head + argmax (final RMSNorm folded in).
+// At batch 1 each down GEMV shares its launch with the next layer's QKV GEMV (the chained GEMV
+// segments of chain.hip: the QKV workgroups stream their weights while down finishes, then wait
+// for its tagged output), so a step is 2 + 4 L + 1 launches.  The chained plan (enqueue_chain_step)
+// goes further for narrow models.
 // RMSNorm is folded into the GEMVs: the producer of h writes fp16(gamma * h) and per-tile sums of
 // h^2; the consumer scales its row sums by rstd = 1/sqrt(mean(h^2) + eps).  Positions are read
 // from device memory, so one captured graph serves every step.
@@ -161,6 +165,8 @@ bool chain_supported(const vv_model* m, const vv_state* s) {
 // their inputs hold the places that later weight streams need (1705 against 1561 us with every
 // stage of a layer chained, 1648 with the three-launch plan), so the layered plan stays.
 constexpr int kChainAutoMaxHidden = 2048;
+// wide models: the gate/up grid is more than one round of resident workgroups on its own
+bool chain_split_mlp(const vv_model* m) { return m->hidden > kChainAutoMaxHidden; }
 bool use_chain(const vv_model* m, const vv_state* s) {
   if (s->path == VV_PATH_CHAINED) return true;
   return s->path == VV_PATH_AUTO && m->hidden <= kChainAutoMaxHidden && chain_supported(m, s);
@@ -169,8 +175,14 @@ bool use_chain(const vv_model* m, const vv_state* s) {
 // timed operations of one step (two events each): prep, then per layer q|k|v, attention, o,
 // gate/up, down, then the lm_head; chained: prep + q|k|v of layer 0, per layer attention,
 // [merge | o] and [gate/up | down | next q|k|v], then the lm_head
+// The layered plan at batch 1 (fp32 activations, the chained GEMV segments' batch) runs each down
+// projection together with the next layer's q|k|v in one launch: 4 launches per layer after the
+// first layer's q|k|v.
+bool layered_fuses_down_qkv(const vv_state* s) { return s->batch == 1; }
+
 int step_ops(const vv_model* m, const vv_state* s) {
-  return use_chain(m, s) ? 3 * m->n_layers + 2 : 5 * m->n_layers + 2;
+  if (!use_chain(m, s)) return layered_fuses_down_qkv(s) && m->n_layers > 0 ? 4 * m->n_layers + 3 : 5 * m->n_layers + 2;
+  return (chain_split_mlp(m) ? 4 : 3) * m->n_layers + 2;
 }
 
 int validate(const vv_model* m, const vv_state* s, const char* fn) {
@@ -331,6 +343,7 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
     VV_HIP(chain_launch(P, st, event_pair(s, op++)));
   }
   const size_t layer_kv_bytes = (size_t)d.nkv * (size_t)s->cap * kHeadDim * 2;
+  const bool split_mlp = chain_split_mlp(m);
   for (int l = 0; l < L; ++l) {
     const vv_layer& y = m->layers[l];
     const bool last = l == L - 1;
@@ -361,13 +374,19 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       P.nseg = 2;
       VV_HIP(chain_launch(P, st, event_pair(s, op++)));
     }
-    {  // [gate/up | down | q|k|v(l+1)]
+    {  // [gate/up | down | q|k|v(l+1)], or (wide models) [gate/up] and [down | q|k|v(l+1)]
       ChainParams P = base;
       CSeg g = gemv_seg(SEG_GU, y.gu_q, y.gu_s, d.I, H, 2 * d.ntI, lay.ws_gu);   // + SiLU * up
       g.xin = U64(lay.txm); g.xin_add = tagadd(l, XM);
       g.ssin = U64(lay.tssm); g.ss_add = tagadd(l, XM);
       g.act = U64(lay.txd); g.out_add = tagadd(l, XD);
       P.seg[0] = g;
+      P.nseg = 1;
+      if (split_mlp) {
+        VV_HIP(chain_launch(P, st, event_pair(s, op++)));
+        P = base;
+        P.nseg = 0;
+      }
       g = gemv_seg(SEG_DOWN, y.down_q, y.down_s, H, d.I, d.ntH, lay.ws_down);   // + residual
       g.xin = U64(lay.txd); g.xin_add = tagadd(l, XD);
       g.hin_add = tagadd(l, XM); g.out_add = tagadd(l + 1, XQ);
@@ -375,8 +394,7 @@ int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       if (!last) { g.xgout = U64(lay.txq); g.ssout = U64(lay.tssq); }
       else { g.gf = gf; g.sumsq = sumsq; }
       g.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * H : nullptr;
-      P.seg[1] = g;
-      P.nseg = 2;
+      P.seg[P.nseg++] = g;
       if (!last) P.seg[P.nseg++] = qkv_seg(l + 1);
       VV_HIP(chain_launch(P, st, event_pair(s, op++)));
     }
@@ -415,9 +433,18 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
 
   const bool kv32 = s->kv_dtype == VV_F32;
   const size_t layer_kv_bytes = (size_t)B * d.nkv * (size_t)s->cap * kHeadDim * (kv32 ? 4 : 2);
+  // batch 1: the down projection and the next layer's q|k|v share one launch (the q|k|v
+  // workgroups stream their weights while down finishes, then wait for its tagged output)
+  const bool fuse_dq = layered_fuses_down_qkv(s);
+  ChainParams cbase{};
+  cbase.H = H; cbase.eps = m->eps; cbase.inv_h = inv_h;
+  cbase.epoch = reinterpret_cast<const uint32_t*>(ws + lay.epoch);
+  cbase.tag_mul = 4u * (uint32_t)(d.L + 1) + 1u; cbase.status = status;
+  cbase.pos = s->pos; cbase.cap = s->cap;
+  cbase.h = reinterpret_cast<uint64_t*>(ws + lay.th);
   for (int l = 0; l < d.L; ++l) {
     const vv_layer& y = m->layers[l];
-    {  // fused q|k|v projection, RMSNorm_1 folded in, bias added
+    if (!fuse_dq || l == 0) {  // fused q|k|v projection, RMSNorm_1 folded in, bias added
       GemvParams p{};
       p.q = y.qkv_q; p.s = y.qkv_s; p.x = g; p.x_f32 = xf32;
       p.M = B; p.N = d.nqkv; p.K = H;
@@ -477,7 +504,47 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_set_workspace(p, ws + lay.ws_gu);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
-    {  // down projection + residual; feeds the next layer (or the lm_head)
+    if (fuse_dq) {  // [down + residual | q|k|v of the next layer]
+      const bool last = l == d.L - 1;
+      ChainParams P = cbase;
+      CSeg dn{};
+      dn.kind = SEG_DOWN;
+      dn.q = reinterpret_cast<const u32x4*>(y.down_q); dn.s = reinterpret_cast<const u32x4*>(y.down_s);
+      dn.N = H; dn.K = d.I; dn.ntiles = d.ntH;
+      dn.slots = reinterpret_cast<uint64_t*>(ws + lay.ws_down);
+      dn.ss_n = d.ntH;
+      chain_gemv_plan(dn);
+      dn.xp = static_cast<const float*>(act); dn.hp = h;
+      dn.xin = reinterpret_cast<const uint64_t*>(ws + lay.txd);   // unused (plain input), readable
+      dn.out_add = 1u + 4u * (uint32_t)(l + 1);   // the chained tags: stage 0 (q|k|v input) of layer l + 1
+      dn.gamma = last ? m->gf : m->layers[l + 1].g1;
+      dn.trace = s->h_trace ? s->h_trace + (size_t)(l + 1) * H : nullptr;
+      if (last) {
+        dn.gf = gf; dn.sumsq = sumsq;
+      } else {
+        dn.xgout = reinterpret_cast<uint64_t*>(ws + lay.txq);
+        dn.ssout = reinterpret_cast<uint64_t*>(ws + lay.tssq);
+      }
+      P.seg[0] = dn;
+      P.nseg = 1;
+      if (!last) {
+        const vv_layer& yn = m->layers[l + 1];
+        CSeg qs{};
+        qs.kind = SEG_QKV;
+        qs.q = reinterpret_cast<const u32x4*>(yn.qkv_q); qs.s = reinterpret_cast<const u32x4*>(yn.qkv_s);
+        qs.N = d.nqkv; qs.K = H; qs.ntiles = (int)cdiv(d.nqkv, kTileRows);
+        qs.slots = reinterpret_cast<uint64_t*>(ws + lay.ws_qkv);
+        qs.ss_n = d.ntH;
+        chain_gemv_plan(qs);
+        qs.xin = dn.xgout; qs.xin_add = dn.out_add;
+        qs.ssin = dn.ssout; qs.ss_add = dn.out_add;
+        qs.has_bias = yn.qkv_bias != nullptr;
+        qs.bias = yn.qkv_bias ? yn.qkv_bias : yn.g1;   // a readable stand-in when there is no bias
+        qs.y = qkv;
+        P.seg[P.nseg++] = qs;
+      }
+      VV_HIP(chain_launch(P, st, event_pair(s, op++)));
+    } else {  // down projection + residual; feeds the next layer (or the lm_head)
       const bool last = l == d.L - 1;
       GemvParams p{};
       p.q = y.down_q; p.s = y.down_s; p.x = act; p.x_f32 = xf32;

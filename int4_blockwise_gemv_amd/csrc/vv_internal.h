@@ -357,7 +357,7 @@ constexpr int kChainMaxSeg = 3;
 constexpr int kChainMaxSplits = 128;  // attention splits the merge segment takes
 enum ChainSegKind { SEG_PREP = 0, SEG_MERGE, SEG_QKV, SEG_O, SEG_GU, SEG_DOWN };
 // the three launches of the chained step: [prep | q|k|v], [merge | o], [gate/up | down (| q|k|v)]
-enum ChainLaunch { CH_FIRST = 0, CH_MO, CH_MLP };
+enum ChainLaunch { CH_FIRST = 0, CH_MO, CH_MLP, CH_GU, CH_DQ, CH_LDQ };
 struct CSeg {
   int kind, blocks;
   // GEMV segments (batch 1, tiled weights; wpt workgroups of wpg waves per tile)
@@ -373,6 +373,9 @@ struct CSeg {
   uint64_t* xgout; uint64_t* ssout;              // O, DOWN: tagged gamma * h [N], sum(h^2) per tile
   float* trace; float* gf; float* sumsq;         // DOWN: optional plain copies (trace, lm_head inputs)
   uint64_t* act;                                 // GU: tagged SiLU(gate) * up [N]
+  // DOWN after a kernel boundary (the layered plan's [down | next q|k|v] launch): plain fp32
+  // input xp [K] and residual hp [N], updated in place (no tags to wait for)
+  const float* xp; float* hp;
 };
 struct ChainParams {
   int nseg;

@@ -345,7 +345,7 @@ def test_step_kernel_timing_events(path):
     import ctypes as C
     import torch
     case = Case(TINY, 7, range(2), [33], 40 if path == "layered" else 100, path=path)
-    n_ops = 5 * 2 + 2 if path == "layered" else 3 * 2 + 2
+    n_ops = 4 * 2 + 3 if path == "layered" else 3 * 2 + 2   # batch 1: down | next q|k|v in one launch
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ops)]
     for e in evs:
         e.record()
