@@ -155,20 +155,21 @@ __device__ void epilogue(const GemvParams& p, int tile, const float (&tot)[MT], 
 // into the operand (a group past the end of K re-reads the last block and gets scale 0, rows
 // past M re-read row M-1 and are never stored), so all loads of a wave are in flight together.
 // Fused split-KV merge (the leading p.mrg_blocks workgroups of an XT launch): wave w of workgroup
-// i merges item i W + w = (query head, 64-dim half) of batch row 0 over at most 64 splits and stores
-// each dim as a tagged word (tag << 32) | fp16 bits of the normalised output.
+// i merges item i W + w = (batch row, query head, 64-dim half) over at most 64 splits and stores
+// each dim as a tagged word (tag << 32) | fp32 bits of the normalised output, at [row][head][dim].
 __device__ void fused_merge(const GemvParams& p) {
   const int W = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int item = blockIdx.x * W + w;
-  if (item >= 2 * p.mrg_nq) return;
-  const int h = item >> 1, d = 64 * (item & 1) + lane;
+  if (item >= 2 * p.mrg_nq * p.M) return;
+  const int b = item / (2 * p.mrg_nq), bi = item % (2 * p.mrg_nq);
+  const int h = bi >> 1, d = 64 * (bi & 1) + lane;
   const int g = p.mrg_nq / p.mrg_nkv, kvh = h / g, hh = h % g;
-  const int n = attn_splits(p.mrg_pos, nullptr, 0, p.mrg_cap, p.mrg_split);
-  const float* rec0 = p.mrg_part + ((size_t)kvh * p.mrg_nsplit * kAttnMaxG + hh) * kAttnRec;
+  const int n = attn_splits(p.mrg_pos, nullptr, b, p.mrg_cap, p.mrg_split);
+  const float* rec0 = p.mrg_part + (((size_t)b * p.mrg_nkv + kvh) * p.mrg_nsplit * kAttnMaxG + hh) * kAttnRec;
   float Mw, Lw;
   const float Ow = merge_wave64(rec0, (size_t)kAttnMaxG * kAttnRec, 0, n, d, Mw, Lw);
   const uint32_t tag = p.epoch[0] * p.tag_mul + p.tag_add;
-  publish_u64(p.xtag + (size_t)h * 128 + d, ((uint64_t)tag << 32) | __float_as_uint(Ow / Lw));
+  publish_u64(p.xtag + ((size_t)b * p.mrg_nq + h) * 128 + d, ((uint64_t)tag << 32) | __float_as_uint(Ow / Lw));
 }
 
 // XF: the activations are fp32 and each 32-element block is staged as its 8-bit digit image
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   __shared__ __align__(16) uint16_t xs[XF ? 1 : MT][XF ? 8 : kItemK];
   __shared__ __align__(16) uint32_t xd[XF ? MT : 1][XF ? kItemK / kBlock * kDigitDwords : 4];
   __shared__ float red[WMAX][MT][kTileRows];
-  static_assert(!XT || (MT == 1 && XF), "the fused merge serves batch 1 with fp32 activations");
+  static_assert(!XT || (MT <= 2 && XF), "the fused merge serves batches 1 and 2 with fp32 activations");
   if constexpr (XT) {
     if ((int)blockIdx.x < p.mrg_blocks) {
       fused_merge(p);
@@ -233,27 +234,34 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemv(GemvParams p, const uint4* _
   // keep the LDS write of the activations behind the weight loads (its wait would hold them back)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (XT) {
-    // the merged attention output of this step and layer: 4 tagged words per thread (bounded wait)
+    // the merged attention output of this step and layer: 4 tagged words per thread and row
+    // (bounded wait)
     const uint32_t tag = p.epoch[0] * p.tag_mul + p.tag_add;
-    uint64_t t[4];
+    uint64_t t[MT][4];
     for (uint32_t it = 0;; ++it) {
       bool ok = true;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        t[k] = collect_u64(p.xtag + ec + k);
-        ok = ok && (uint32_t)(t[k] >> 32) == tag;
-      }
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          t[m][k] = collect_u64(p.xtag + (size_t)min(m, M - 1) * K + ec + k);
+          ok = ok && (uint32_t)(t[m][k] >> 32) == tag;
+        }
       if (__all(ok)) break;
       if (it >= kSpinLimit) {
         if (p.status) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t[k] = 0x7fc00000u;     // fp32 NaN
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) t[m][k] = 0x7fc00000u;     // fp32 NaN
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    xf[0] = make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
-                        __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3]));
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      xf[m] = make_float4(__uint_as_float((uint32_t)t[m][0]), __uint_as_float((uint32_t)t[m][1]),
+                          __uint_as_float((uint32_t)t[m][2]), __uint_as_float((uint32_t)t[m][3]));
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -419,6 +427,13 @@ void launch_epi(const GemvParams& p, const uint4* q, const uint4* s, hipStream_t
       else VV_LAUNCH((k_gemv<1, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x);
       break;
     case 2:
+      if constexpr (EPI == EPI_RESID && XF) {   // the o projection may take the fused merge
+        if (p.mrg_blocks) {
+          if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM, true, true>), g, b, st, ev, p, q, s, p.x);
+          else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM, true, true>), g, b, st, ev, p, q, s, p.x);
+          break;
+        }
+      }
       if (wide) VV_LAUNCH((k_gemv<2, EPI, kWavesSmallM, false, XF>), g, b, st, ev, p, q, s, p.x);
       else VV_LAUNCH((k_gemv<2, EPI, kWavesLargeM, false, XF>), g, b, st, ev, p, q, s, p.x);
       break;

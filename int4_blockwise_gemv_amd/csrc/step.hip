@@ -134,7 +134,7 @@ Layout layout_of(const Dims& d) {
   attn_plan(ap);
   l.ws_attn = take(attn_workspace_bytes(d.B, d.nq, d.nkv, ap.nsplit));
   l.ws_lm = take(lm_workspace_bytes(d.B, d.V, d.H));
-  l.otag = take((size_t)d.nq * kHeadDim * sizeof(uint64_t));   // fused merge -> o projection (batch 1)
+  l.otag = take((size_t)d.B * d.nq * kHeadDim * sizeof(uint64_t));   // fused merge -> o projection
   l.epoch = take(sizeof(uint32_t));                              // step counter (tags of otag)
   l.th = take((size_t)d.H * 8);
   l.txq = take((size_t)d.H * 8);
@@ -456,12 +456,12 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_set_workspace(p, ws + lay.ws_qkv);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
-    // batch 1 over fp16 caches with at most 64 splits: the o projection's launch also merges the
+    // batches 1 and 2 over fp16 caches with at most 64 splits: the o projection's launch also merges the
     // attention's split records (its leading workgroups), so the merge needs no launch of its own
     AttnParams a{};
     a.B = B; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
     attn_plan(a);
-    const bool fuse_merge = B == 1 && !kv32 && a.nsplit > 1 && a.nsplit <= 64;
+    const bool fuse_merge = B <= 2 && !kv32 && a.nsplit > 1 && a.nsplit <= 64;
     {  // attention with RoPE and KV append
       attn_set_workspace(a, ws + lay.ws_attn);
       a.skip_merge = fuse_merge;
@@ -482,8 +482,8 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_plan(p);
       p.status = status;
       gemv_set_workspace(p, ws + lay.ws_o);
-      if (fuse_merge) {   // one wave per (query head, 64-dim half), whole rounds of 8 workgroups
-        p.mrg_blocks = (int)(cdiv(cdiv(2 * d.nq, p.wpg), 8) * 8);
+      if (fuse_merge) {   // one wave per (row, query head, 64-dim half), whole rounds of 8 workgroups
+        p.mrg_blocks = (int)(cdiv(cdiv(2 * d.nq * B, p.wpg), 8) * 8);
         p.mrg_part = a.part; p.mrg_pos = s->pos; p.mrg_nsplit = a.nsplit; p.mrg_split = a.split;
         p.mrg_cap = s->cap; p.mrg_nq = d.nq; p.mrg_nkv = d.nkv;
         p.xtag = reinterpret_cast<uint64_t*>(ws + lay.otag);
