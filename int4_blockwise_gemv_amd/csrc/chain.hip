@@ -277,7 +277,9 @@ __device__ void seg_gemv(const ChainParams& P, const CSeg& g, int bid, uint32_t 
 // 8 waves per SIMD (at most 64 VGPRs): the weight streams of the GEMV segments need the
 // occupancy.  One instance per launch, with its segments at fixed positions (so every segment
 // field is read at a constant offset): CH_FIRST prep, q|k|v; CH_MO merge, o; CH_MLP gate/up,
-// down and, if nseg == 3, the next layer's q|k|v.
+// down and, if nseg == 3, the next layer's q|k|v; CH_GU gate/up alone; CH_DQ down and, if
+// nseg == 2, the next layer's q|k|v; CH_LDQ the same with down's input and residual plain fp32
+// (the layered plan's batch-1 launch).
 template <int KIND>
 __global__ __launch_bounds__(kCT, 8) void k_chain(ChainParams P) {
   __shared__ CLds L;

@@ -356,7 +356,9 @@ constexpr int kChainWaves = 8;        // waves per workgroup
 constexpr int kChainMaxSeg = 3;
 constexpr int kChainMaxSplits = 128;  // attention splits the merge segment takes
 enum ChainSegKind { SEG_PREP = 0, SEG_MERGE, SEG_QKV, SEG_O, SEG_GU, SEG_DOWN };
-// the three launches of the chained step: [prep | q|k|v], [merge | o], [gate/up | down (| q|k|v)]
+// the launches of the chained step: [prep | q|k|v], [merge | o], [gate/up | down (| q|k|v)], or
+// for wide models [gate/up] and [down (| q|k|v)]; and the layered plan's batch-1
+// [down (plain inputs) | q|k|v]
 enum ChainLaunch { CH_FIRST = 0, CH_MO, CH_MLP, CH_GU, CH_DQ, CH_LDQ };
 struct CSeg {
   int kind, blocks;
