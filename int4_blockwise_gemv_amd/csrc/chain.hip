@@ -9,8 +9,11 @@
 //   launch 0:      [prep | q|k|v of layer 0]
 //   per layer l:   attention(l)   (its own launch: RoPE, KV append, split records)
 //                  [merge(l) | o(l)]
-//                  [gate/up(l) | down(l) | q|k|v(l+1)]
+//                  [gate/up(l) | down(l) | q|k|v(l+1)]   (wide models: [gate/up(l)], then
+//                                                         [down(l) | q|k|v(l+1)])
 //   then the lm_head + argmax.
+// The layered step borrows the [down(l) | q|k|v(l+1)] launch at batch 1, with down reading plain
+// inputs written before the launch.
 // (One launch for all five stages of a layer is slower: the MLP's waves, dispatched with the
 // merge and o, hold their places while they wait, and their first reads of the MLP input miss.)
 // A segment's workgroups read their inputs once, issue their weight loads, and then wait for any

@@ -149,8 +149,9 @@ Layout layout_of(const Dims& d) {
 
 size_t step_bytes(const vv_model* m, int B, int cap) { return align_up(layout_of(dims_of(m, B, cap)).total, 256); }
 
-// The chained path (three launches per layer) serves batch 1 over fp16 caches with 2..128
-// attention splits; everything else takes the layered path (five launches per layer).
+// The chained path (three launches per layer, four for wide models) serves batch 1 over fp16
+// caches with 2..128 attention splits; everything else takes the layered path (five launches per
+// layer, four at batch 1).
 bool chain_supported(const vv_model* m, const vv_state* s) {
   if (s->batch != 1 || s->kv_dtype == VV_F32 || m->n_layers < 1) return false;
   AttnParams a{};
@@ -173,8 +174,10 @@ bool use_chain(const vv_model* m, const vv_state* s) {
 }
 
 // timed operations of one step (two events each): prep, then per layer q|k|v, attention, o,
-// gate/up, down, then the lm_head; chained: prep + q|k|v of layer 0, per layer attention,
-// [merge | o] and [gate/up | down | next q|k|v], then the lm_head
+// gate/up, down, then the lm_head (at batch 1: prep, q|k|v of layer 0, per layer attention, o,
+// gate/up, [down | next q|k|v], then the lm_head); chained: prep + q|k|v of layer 0, per layer
+// attention, [merge | o] and [gate/up | down | next q|k|v] (wide models: [gate/up], [down | next
+// q|k|v]), then the lm_head
 // The layered plan at batch 1 (fp32 activations, the chained GEMV segments' batch) runs each down
 // projection together with the next layer's q|k|v in one launch: 4 launches per layer after the
 // first layer's q|k|v.
@@ -276,7 +279,7 @@ int enqueue_feedback(const vv_model* m, const vv_state* s, hipStream_t st) {
 }
 
 // The chained path: [prep | q|k|v(0)], then per layer the attention, [merge | o] and [gate/up |
-// down | q|k|v(l+1)], then the lm_head.  Tags: stage st of layer l is 1 + 4 l + st (st: 0 the
+// down | q|k|v(l+1)] (wide models: [gate/up] and [down | q|k|v(l+1)]), then the lm_head.  Tags: stage st of layer l is 1 + 4 l + st (st: 0 the
 // q|k|v input and residual, 1 the attention output, 2 the MLP input and residual, 3 SiLU * up),
 // added to epoch * (4 (L + 1) + 1); the epoch advances at the end of every step.
 int enqueue_chain_step(const vv_model* m, const vv_state* s, hipStream_t st) {
