@@ -222,3 +222,23 @@ def test_lm_head_noalloc_validation():
     assert L.vv_lm_head_argmax_noalloc(d, d, 9, 1, 100, 64, None, d, None) == vvmod.VV_ERR_DTYPE
     assert vvmod.lm_workspace(16, 3 << 20, 256) > 256 * 1024
     assert L.vv_lm_head_argmax_noalloc(d, d, vvmod.VV_F32, 16, 3 << 20, 256, None, d, None) == vvmod.VV_ERR_RANGE
+
+
+def test_decode_step_event_count_follows_the_launch_plan():
+    """The layered plan times one operation per launch: at batch 1 each down projection shares its
+    launch with the next layer's q|k|v (prep, q|k|v of layer 0, 4 per layer, lm_head: 4 L + 3 pairs),
+    at larger batches 5 L + 2 pairs.  Checked on the rejection of one event too few (host only)."""
+    L = _lib()
+    vv = vvmod
+    layers = (vv.vv_layer * 2)()
+    for i in range(2):
+        layers[i] = vv.vv_layer(*([64] * 8), None, 64, 64)
+    m = _model_struct(n_layers=2, layers=C.cast(layers, C.POINTER(vv.vv_layer)))
+    m._keep = layers
+    lay = vv.VV_PATH_LAYERED
+    for batch, pairs in ((1, 4 * 2 + 3), (2, 5 * 2 + 2)):
+        need = vv.step_workspace(m, batch, 64)
+        evs = (C.c_void_p * (2 * pairs - 1))()
+        st = _state(need, batch=batch, events=C.cast(evs, C.POINTER(C.c_void_p)), n_events=2 * pairs - 1, path=lay)
+        assert L.vv_decode_step(C.byref(m), C.byref(st), None) == vv.VV_ERR_RANGE
+        assert f"at least {2 * pairs} entries" in L.vv_last_error().decode()
