@@ -218,8 +218,8 @@ int vv_lm_head_argmax_noalloc(const uint16_t* W, const void* x, int x_dtype, int
  *
  * Two launch plans compute the same step (vv_state.path):
  *   VV_PATH_LAYERED  one launch per stage: 1 + 5 L + 1 kernels (plus a split merge per layer
- *                    when the cache is split, except at batches 1 and 2 over fp16 caches with at most
- *                    64 splits, where the o projection's launch does the merge); any batch up to
+ *                    when the cache is split, except at batches 1 and 2 with at most 64 splits, where
+ *                    the o projection's launch does the merge); any batch up to
  *                    max_batch, fp16 or fp32 caches.  At batch 1 each layer's down projection
  *                    and the next layer's q|k|v share one launch (2 + 4 L + 1 kernels).
  *   VV_PATH_CHAINED  three launches per layer: the attention, one grid running the split merge

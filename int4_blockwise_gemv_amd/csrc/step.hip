@@ -459,12 +459,13 @@ int enqueue_step(const vv_model* m, const vv_state* s, hipStream_t st) {
       gemv_set_workspace(p, ws + lay.ws_qkv);
       VV_HIP(gemv_launch(p, st, event_pair(s, op++)));
     }
-    // batches 1 and 2 over fp16 caches with at most 64 splits: the o projection's launch also merges the
-    // attention's split records (its leading workgroups), so the merge needs no launch of its own
+    // batches 1 and 2 with at most 64 splits (either cache precision: the split records are fp32
+    // alike): the o projection's launch also merges the attention's split records (its leading
+    // workgroups), so the merge needs no launch of its own
     AttnParams a{};
     a.B = B; a.nq = d.nq; a.nkv = d.nkv; a.cap = s->cap;
     attn_plan(a);
-    const bool fuse_merge = B <= 2 && !kv32 && a.nsplit > 1 && a.nsplit <= 64;
+    const bool fuse_merge = B <= 2 && a.nsplit > 1 && a.nsplit <= 64;
     {  // attention with RoPE and KV append
       attn_set_workspace(a, ws + lay.ws_attn);
       a.skip_merge = fuse_merge;
